@@ -1,0 +1,184 @@
+"""ctypes front end of the CPU oracle (oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the bench's
+CPU-baseline leg may import this package; the product library never does.
+
+Inputs are CPU torch tensors (float32, or bfloat16 whose bits the C code
+widens exactly) in the library's layouts: q [B,Hq,Tq,d], K and V
+[B,Hkv,T_cap,d].  Outputs are numpy arrays; attention rows are float64.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the oracle with gcc: -O2, OpenMP over independent problems, no fast-math."""
+    tmp = out + ".tmp"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", src, "-o", tmp, "-lm"],
+                   check=True)
+    os.replace(tmp, out)
+    return out
+
+
+class Shape(C.Structure):
+    _fields_ = [("B", C.c_int64), ("Hq", C.c_int64), ("Hkv", C.c_int64), ("Tq", C.c_int64),
+                ("T", C.c_int64), ("T_cap", C.c_int64), ("d", C.c_int64), ("k", C.c_int64),
+                ("block_k", C.c_int64), ("block_q", C.c_int64), ("causal", C.c_int32),
+                ("dtype", C.c_int32)]
+
+
+class Trace(C.Structure):
+    _fields_ = [("max_rounds", C.c_int32), ("cap", C.c_int32), ("rounds", C.c_int32),
+                ("n_cand", C.c_void_p), ("cand_start", C.c_void_p), ("cand_end", C.c_void_p),
+                ("cand_centre", C.c_void_p), ("cand_score", C.c_void_p),
+                ("cand_kept", C.c_void_p), ("rel_margin", C.c_void_p)]
+
+
+def load(path: str | None = None):
+    """Load the oracle library (building it first if it is not there).
+
+    `path` selects another build of the same source (the mutation tests use it).
+    """
+    global _lib
+    if path is None and _lib is not None:
+        return _lib
+    p = path or _LIB
+    if path is None and not os.path.exists(p):
+        build()
+    lib = C.CDLL(p)
+    P, I64, I32 = C.c_void_p, C.c_int64, C.c_int32
+    lib.or_mask_one.argtypes = [C.POINTER(Shape), P, P, I64, I64, I64, P, P, P, C.POINTER(Trace)]
+    lib.or_mask_all.argtypes = [C.POINTER(Shape), P, P, P, P, P, I32]
+    lib.or_attn_row.argtypes = [C.POINTER(Shape), P, P, P, P, P, I64, I64, I64, P]
+    lib.or_attn_all.argtypes = [C.POINTER(Shape), P, P, P, P, P, P, I32]
+    for f in (lib.or_mask_one, lib.or_mask_all, lib.or_attn_row, lib.or_attn_all):
+        f.restype = C.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _ptr(t) -> int:
+    if isinstance(t, np.ndarray):
+        assert t.flags["C_CONTIGUOUS"]
+        return t.ctypes.data
+    assert t.device.type == "cpu" and t.is_contiguous(), "oracle inputs are contiguous CPU tensors"
+    return t.data_ptr()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return 0
+    if t.dtype == torch.bfloat16:
+        return 1
+    raise TypeError(f"oracle takes float32 or bfloat16, not {t.dtype}")
+
+
+def shape(q, K, *, T, k, block_k, block_q, causal=1) -> Shape:
+    B, Hq, Tq, d = q.shape
+    assert K.shape[0] == B and K.shape[3] == d and q.dtype == K.dtype
+    return Shape(B, Hq, K.shape[1], Tq, T, K.shape[2], d, k, block_k, block_q, int(causal),
+                 _dtype_code(q))
+
+
+def nthreads(n: int | None = None) -> int:
+    if n is not None:
+        return n
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except Exception:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def mask_all(q, K, *, T, k, block_k, block_q, causal=1, threads=None, lib=None):
+    """Indices [B,Hkv,NQB,K_b], nnz [B,Hkv,NQB] and the min relative cut margin per problem."""
+    lib = lib or load()
+    s = shape(q, K, T=T, k=k, block_k=block_k, block_q=block_q, causal=causal)
+    nqb = -(-s.Tq // block_q)
+    kb = k // block_k
+    idx = np.full((s.B, s.Hkv, nqb, kb), -1, np.int32)
+    nnz = np.zeros((s.B, s.Hkv, nqb), np.int32)
+    margin = np.zeros((s.B, s.Hkv, nqb), np.float64)
+    rc = lib.or_mask_all(C.byref(s), _ptr(q), _ptr(K), idx.ctypes.data, nnz.ctypes.data,
+                         margin.ctypes.data, nthreads(threads))
+    assert rc == 0
+    return idx, nnz, margin
+
+
+def mask_one(q, K, b, g, qb, *, T, k, block_k, block_q, causal=1, trace=False, lib=None,
+             max_rounds=64):
+    """One problem; with trace=True also the per-round candidates (sorted by rank)."""
+    lib = lib or load()
+    s = shape(q, K, T=T, k=k, block_k=block_k, block_q=block_q, causal=causal)
+    kb = k // block_k
+    idx = np.full(kb, -1, np.int32)
+    nnz = np.zeros(1, np.int32)
+    margin = np.zeros(1, np.float64)
+    tr_ptr = None
+    bufs = None
+    if trace:
+        cap = 2 * kb
+        bufs = dict(n_cand=np.zeros(max_rounds, np.int32),
+                    cand_start=np.zeros((max_rounds, cap), np.int64),
+                    cand_end=np.zeros((max_rounds, cap), np.int64),
+                    cand_centre=np.zeros((max_rounds, cap), np.int64),
+                    cand_score=np.zeros((max_rounds, cap), np.float64),
+                    cand_kept=np.zeros((max_rounds, cap), np.int32),
+                    rel_margin=np.zeros(max_rounds, np.float64))
+        tr = Trace(max_rounds, cap, 0, *(bufs[n].ctypes.data for n in
+                                         ("n_cand", "cand_start", "cand_end", "cand_centre",
+                                          "cand_score", "cand_kept", "rel_margin")))
+        tr_ptr = C.byref(tr)
+    rc = lib.or_mask_one(C.byref(s), _ptr(q), _ptr(K), b, g, qb, idx.ctypes.data,
+                         nnz.ctypes.data, margin.ctypes.data, tr_ptr)
+    assert rc == 0
+    out = {"indices": idx, "nnz": int(nnz[0]), "margin": float(margin[0])}
+    if trace:
+        R = tr.rounds
+        rounds = []
+        for r in range(R):
+            n = int(bufs["n_cand"][r])
+            rounds.append({
+                "start": bufs["cand_start"][r, :n].copy(), "end": bufs["cand_end"][r, :n].copy(),
+                "centre": bufs["cand_centre"][r, :n].copy(),
+                "score": bufs["cand_score"][r, :n].copy(),
+                "kept": bufs["cand_kept"][r, :n].astype(bool),
+                "rel_margin": float(bufs["rel_margin"][r])})
+        out["rounds"] = rounds
+    return out
+
+
+def attn_all(q, K, V, indices, nnz, *, T, k, block_k, block_q, causal=1, threads=None, lib=None):
+    """Exact attention over the listed blocks, float64 [B,Hq,Tq,d]."""
+    lib = lib or load()
+    s = shape(q, K, T=T, k=k, block_k=block_k, block_q=block_q, causal=causal)
+    indices = np.ascontiguousarray(indices, np.int32)
+    nnz = np.ascontiguousarray(nnz, np.int32)
+    out = np.zeros((s.B, s.Hq, s.Tq, s.d), np.float64)
+    rc = lib.or_attn_all(C.byref(s), _ptr(q), _ptr(K), _ptr(V), indices.ctypes.data,
+                         nnz.ctypes.data, out.ctypes.data, nthreads(threads))
+    assert rc == 0
+    return out
+
+
+def attn_row(q, K, V, indices, nnz, b, h, i, *, T, k, block_k, block_q, causal=1, lib=None):
+    lib = lib or load()
+    s = shape(q, K, T=T, k=k, block_k=block_k, block_q=block_q, causal=causal)
+    indices = np.ascontiguousarray(indices, np.int32)
+    nnz = np.ascontiguousarray(nnz, np.int32)
+    out = np.zeros(s.d, np.float64)
+    rc = lib.or_attn_row(C.byref(s), _ptr(q), _ptr(K), _ptr(V), indices.ctypes.data,
+                         nnz.ctypes.data, b, h, i, out.ctypes.data)
+    assert rc == 0
+    return out

@@ -1,0 +1,291 @@
+/*
+ * CPU oracle for HiP mask estimation and block-sparse attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or
+ * load this file's library: only the test suite, the smoke check and the
+ * bench's CPU-baseline leg do.  It shares no code with the GPU library.
+ *
+ * Plain, slow and literal on purpose: scalar loops, every value widened to
+ * double (fp32 and bf16 inputs convert to double exactly), no blocking, no
+ * fusion, no reordering beyond what the method states.
+ *
+ * Sources (the web pages this follows):
+ *  - "A Training-free Sub-quadratic Cost Transformer Model Serving Framework
+ *    With Hierarchically Pruned Attention", Author Rebuttal to the Reviewer
+ *    RsGC, Q2: the four-step iteration (split T into k chunks; halve every
+ *    chunk; score each chunk by the dot product of the query with the key at
+ *    the chunk's centre; keep the global top-k and repeat until a chunk is no
+ *    larger than b_k).  Same page, reviewer NLBm, Q1: queries and keys are
+ *    grouped in blocks b_q and b_k.
+ *  - Same page, reviewer NLBm, W2: the sparse attention kernel takes, per
+ *    row, the indices of the non-zero blocks and their count (nnz).
+ *  - Summary page "A Training-Free Sub-quadratic Cost Transformer Model
+ *    Serving Framework with Hierarchically Pruned Attention", Approach:
+ *    chunks are represented by their centre tokens; top-k is approximate.
+ *
+ * Readings taken where the pages are silent (each is pinned by a test):
+ *  R1 chunk boundaries live on key-block boundaries; the search stops when
+ *     every chunk is one block.  K_b = k / block_k chunks are kept.
+ *  R2 initial chunks [floor(i*N/K_b), floor((i+1)*N/K_b)), i < K_b.
+ *  R3 a chunk [a,e) of >= 2 blocks splits at m = a + floor((e-a)/2);
+ *     1-block chunks pass through unsplit and are scored again.
+ *  R4 centre token of [a,e): floor((a*b_k + min(e*b_k, T_p)) / 2), the upper
+ *     middle of its tokens.
+ *  R5 chunk score: max over the query heads of the KV group and the rows of
+ *     the query block of q . k_centre (raw dot product, no 1/sqrt(d)); with a
+ *     causal mask, a row at position p votes only for centres t <= p; no
+ *     voter gives -inf.
+ *  R6 ranking: score descending, then chunk start ascending.
+ *  R7 if the query block sees no more than K_b blocks, all are selected.
+ *  R8 attention: exact softmax of q . k / sqrt(d) over the tokens of the
+ *     first nnz listed blocks that the row may see (token < T_p, and token
+ *     <= its position when causal); an empty set gives a zero row; listed
+ *     ids outside [0, N_p) are ignored.
+ *
+ * Layouts (contiguous, head-major): q [B,Hq,Tq,d]; K, V [B,Hkv,T_cap,d] with
+ * rows 0..T-1 valid; indices [B,Hkv,NQB,K_b] (ascending, -1 past nnz);
+ * nnz [B,Hkv,NQB]; query head h belongs to KV head h / (Hq/Hkv).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_F32 0
+#define OR_BF16 1
+
+typedef struct {
+  int64_t B, Hq, Hkv, Tq, T, T_cap, d;
+  int64_t k, block_k, block_q;
+  int32_t causal, dtype;
+} or_shape;
+
+/* Optional search trace of one problem; arrays hold max_rounds * cap. */
+typedef struct {
+  int32_t max_rounds, cap; /* cap >= 2*K_b */
+  int32_t rounds;          /* out */
+  int32_t *n_cand;         /* [max_rounds] */
+  int64_t *cand_start, *cand_end, *cand_centre; /* [max_rounds*cap] */
+  double *cand_score;
+  int32_t *cand_kept;
+  double *rel_margin;      /* [max_rounds] */
+} or_trace;
+
+static double elem(const void *base, int32_t dtype, int64_t i) {
+  if (dtype == OR_F32) return (double)((const float *)base)[i];
+  uint32_t bits = (uint32_t)((const uint16_t *)base)[i] << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+static int64_t nqb_of(const or_shape *s) { return (s->Tq + s->block_q - 1) / s->block_q; }
+
+/* Query rows [*r0, *r1) of query block qb and the number of visible keys. */
+static int64_t rows_and_tp(const or_shape *s, int64_t qb, int64_t *r0, int64_t *r1) {
+  *r0 = qb * s->block_q;
+  *r1 = *r0 + s->block_q < s->Tq ? *r0 + s->block_q : s->Tq;
+  if (!s->causal) return s->T;
+  return s->T - s->Tq + (*r1 - 1) + 1; /* position of the last row, plus one */
+}
+
+static int64_t position(const or_shape *s, int64_t i) { return s->T - s->Tq + i; }
+
+static double dot_qk(const or_shape *s, const void *q, const void *K, int64_t b, int64_t h,
+                     int64_t i, int64_t g, int64_t t) {
+  int64_t qo = ((b * s->Hq + h) * s->Tq + i) * s->d;
+  int64_t ko = ((b * s->Hkv + g) * s->T_cap + t) * s->d;
+  double acc = 0.0;
+  for (int64_t x = 0; x < s->d; x++) acc += elem(q, s->dtype, qo + x) * elem(K, s->dtype, ko + x);
+  return acc;
+}
+
+typedef struct {
+  int64_t a, e, t;
+  double score;
+} cand_t;
+
+/* R6: true when x ranks before y. */
+static int ranks_before(const cand_t *x, const cand_t *y) {
+  if (x->score != y->score) return x->score > y->score;
+  return x->a < y->a;
+}
+
+static int cmp_i32(const void *x, const void *y) {
+  int32_t u = *(const int32_t *)x, v = *(const int32_t *)y;
+  return (u > v) - (u < v);
+}
+
+int or_mask_one(const or_shape *s, const void *q, const void *K, int64_t b, int64_t g, int64_t qb,
+                int32_t *idx, int32_t *nnz, double *margin, or_trace *tr) {
+  const int64_t G = s->Hq / s->Hkv;
+  const int64_t Kb = s->k / s->block_k;
+  int64_t r0, r1;
+  const int64_t Tp = rows_and_tp(s, qb, &r0, &r1);
+  const int64_t Np = (Tp + s->block_k - 1) / s->block_k;
+  if (tr) tr->rounds = 0;
+  for (int64_t j = 0; j < Kb; j++) idx[j] = -1;
+
+  if (Np <= Kb) { /* R7: the block sees few enough keys to attend to all */
+    for (int64_t j = 0; j < Np; j++) idx[j] = (int32_t)j;
+    *nnz = (int32_t)Np;
+    *margin = INFINITY;
+    return 0;
+  }
+
+  /* Step 1: uniform split into K_b chunks (R2). */
+  int64_t *ca = malloc(sizeof(int64_t) * Kb), *ce = malloc(sizeof(int64_t) * Kb);
+  cand_t *cand = malloc(sizeof(cand_t) * 2 * Kb);
+  if (!ca || !ce || !cand) { free(ca); free(ce); free(cand); return -1; }
+  for (int64_t i = 0; i < Kb; i++) {
+    ca[i] = i * Np / Kb;
+    ce[i] = (i + 1) * Np / Kb;
+  }
+  double min_rel = INFINITY;
+  int32_t round = 0;
+
+  for (;;) {
+    int wide = 0;
+    for (int64_t i = 0; i < Kb; i++) wide |= (ce[i] - ca[i] >= 2);
+    if (!wide) break; /* Step 4 exit: every chunk is a single block */
+
+    /* Step 2: halve every chunk (R3). */
+    int64_t n = 0;
+    for (int64_t i = 0; i < Kb; i++) {
+      if (ce[i] - ca[i] >= 2) {
+        int64_t m = ca[i] + (ce[i] - ca[i]) / 2;
+        cand[n].a = ca[i]; cand[n].e = m; n++;
+        cand[n].a = m; cand[n].e = ce[i]; n++;
+      } else {
+        cand[n].a = ca[i]; cand[n].e = ce[i]; n++;
+      }
+    }
+
+    /* Step 3: score each candidate by its centre key (R4, R5). */
+    for (int64_t c = 0; c < n; c++) {
+      int64_t lo = cand[c].a * s->block_k;
+      int64_t hi = cand[c].e * s->block_k < Tp ? cand[c].e * s->block_k : Tp;
+      int64_t t = (lo + hi) / 2;
+      double best = -INFINITY;
+      for (int64_t h = g * G; h < (g + 1) * G; h++)
+        for (int64_t i = r0; i < r1; i++) {
+          if (s->causal && position(s, i) < t) continue;
+          double v = dot_qk(s, q, K, b, h, i, g, t);
+          if (v > best) best = v;
+        }
+      cand[c].t = t;
+      cand[c].score = best;
+    }
+
+    /* Step 4: global top-K_b by (score desc, start asc): a stable insertion sort. */
+    for (int64_t c = 1; c < n; c++) {
+      cand_t x = cand[c];
+      int64_t j = c - 1;
+      while (j >= 0 && ranks_before(&x, &cand[j])) { cand[j + 1] = cand[j]; j--; }
+      cand[j + 1] = x;
+    }
+    double rel = INFINITY;
+    if (n > Kb && cand[Kb].score != -INFINITY) {
+      double hiS = cand[Kb - 1].score, loS = cand[Kb].score;
+      double den = fabs(hiS) > fabs(loS) ? fabs(hiS) : fabs(loS);
+      rel = den == 0.0 ? 0.0 : (hiS - loS) / den;
+    }
+    if (rel < min_rel) min_rel = rel;
+
+    if (tr && round < tr->max_rounds) {
+      tr->n_cand[round] = (int32_t)n;
+      tr->rel_margin[round] = rel;
+      for (int64_t c = 0; c < n && c < tr->cap; c++) {
+        int64_t o = (int64_t)round * tr->cap + c;
+        tr->cand_start[o] = cand[c].a;
+        tr->cand_end[o] = cand[c].e;
+        tr->cand_centre[o] = cand[c].t;
+        tr->cand_score[o] = cand[c].score;
+        tr->cand_kept[o] = c < Kb;
+      }
+    }
+    for (int64_t i = 0; i < Kb; i++) { ca[i] = cand[i].a; ce[i] = cand[i].e; }
+    round++;
+  }
+  if (tr) tr->rounds = round;
+
+  for (int64_t i = 0; i < Kb; i++) idx[i] = (int32_t)ca[i];
+  qsort(idx, (size_t)Kb, sizeof(int32_t), cmp_i32);
+  *nnz = (int32_t)Kb;
+  *margin = min_rel;
+  free(ca); free(ce); free(cand);
+  return 0;
+}
+
+int or_mask_all(const or_shape *s, const void *q, const void *K, int32_t *indices, int32_t *nnz,
+                double *margin, int32_t nthreads) {
+  const int64_t Kb = s->k / s->block_k, nqb = nqb_of(s);
+  const int64_t P = s->B * s->Hkv * nqb;
+  int err = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads) reduction(| : err)
+  for (int64_t p = 0; p < P; p++) {
+    int64_t b = p / (s->Hkv * nqb), g = (p / nqb) % s->Hkv, qb = p % nqb;
+    err |= or_mask_one(s, q, K, b, g, qb, indices + p * Kb, nnz + p, margin + p, NULL);
+  }
+  return err ? -1 : 0;
+}
+
+/* R8: one output row in fp64. */
+int or_attn_row(const or_shape *s, const void *q, const void *K, const void *V,
+                const int32_t *indices, const int32_t *nnz, int64_t b, int64_t h, int64_t i,
+                double *out) {
+  const int64_t G = s->Hq / s->Hkv, Kb = s->k / s->block_k, nqb = nqb_of(s);
+  const int64_t g = h / G, qb = i / s->block_q;
+  int64_t r0, r1;
+  const int64_t Tp = rows_and_tp(s, qb, &r0, &r1);
+  const int64_t Np = (Tp + s->block_k - 1) / s->block_k;
+  const int64_t limit = s->causal ? position(s, i) : s->T - 1; /* last visible token */
+  const int64_t p = (b * s->Hkv + g) * nqb + qb;
+  const int32_t *list = indices + p * Kb;
+  int64_t cnt = nnz[p];
+  if (cnt < 0) cnt = 0;
+  if (cnt > Kb) cnt = Kb;
+  const double scale = 1.0 / sqrt((double)s->d);
+
+  for (int64_t x = 0; x < s->d; x++) out[x] = 0.0;
+  /* pass 1: the largest logit, for a stable softmax */
+  double mx = -INFINITY;
+  int64_t seen = 0;
+  for (int64_t n = 0; n < cnt; n++) {
+    int64_t blk = list[n];
+    if (blk < 0 || blk >= Np) continue;
+    for (int64_t t = blk * s->block_k; t < (blk + 1) * s->block_k && t < Tp; t++) {
+      if (t > limit) continue;
+      double l = dot_qk(s, q, K, b, h, i, g, t) * scale;
+      if (l > mx) mx = l;
+      seen++;
+    }
+  }
+  if (seen == 0) return 0;
+  /* pass 2: weights and the weighted sum of values */
+  double den = 0.0;
+  for (int64_t n = 0; n < cnt; n++) {
+    int64_t blk = list[n];
+    if (blk < 0 || blk >= Np) continue;
+    for (int64_t t = blk * s->block_k; t < (blk + 1) * s->block_k && t < Tp; t++) {
+      if (t > limit) continue;
+      double w = exp(dot_qk(s, q, K, b, h, i, g, t) * scale - mx);
+      den += w;
+      int64_t vo = ((b * s->Hkv + g) * s->T_cap + t) * s->d;
+      for (int64_t x = 0; x < s->d; x++) out[x] += w * elem(V, s->dtype, vo + x);
+    }
+  }
+  for (int64_t x = 0; x < s->d; x++) out[x] /= den;
+  return 0;
+}
+
+int or_attn_all(const or_shape *s, const void *q, const void *K, const void *V,
+                const int32_t *indices, const int32_t *nnz, double *out, int32_t nthreads) {
+  const int64_t R = s->B * s->Hq * s->Tq;
+#pragma omp parallel for schedule(dynamic, 4) num_threads(nthreads)
+  for (int64_t r = 0; r < R; r++) {
+    int64_t b = r / (s->Hq * s->Tq), h = (r / s->Tq) % s->Hq, i = r % s->Tq;
+    or_attn_row(s, q, K, V, indices, nnz, b, h, i, out + r * s->d);
+  }
+  return 0;
+}

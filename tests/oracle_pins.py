@@ -1,0 +1,375 @@
+"""Pins of the CPU oracle against facts fixed by the pages and by mathematics.
+
+Each check takes a loaded oracle library (so the mutation test can run the
+same checks against deliberately broken builds) and raises AssertionError on
+failure.  Nothing here calls the GPU library.
+
+Kinds of pin used (no check re-derives the oracle's own formulas):
+  * hand-traced worked examples (tests/golden/*.json);
+  * dense reduction: with k >= the visible keys the method is dense softmax
+    attention, compared with torch's scaled_dot_product_attention in float64;
+  * exact top-k on tiny inputs when a trace certificate holds (brute force);
+  * closed forms: all-zero queries give ties everywhere, so the kept blocks
+    are the prefix and the output is the mean of V;
+  * invariants: convex combinations of V, constant V, a dominant key,
+    scale invariance of the mask, equivariance under batch / head permutation,
+    the chunk tree structure and the round count.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _line_inputs(s, *, d=64, Hq=1, Hkv=1, Tq=1, T_cap=None, q_scale=None, seed=0):
+    """q rows = scale * e_0, K[t] = s(t) * e_0 in every KV head: score(t) = scale * s(t) exactly."""
+    T = len(s)
+    T_cap = T if T_cap is None else T_cap
+    q = torch.zeros(1, Hq, Tq, d)
+    scales = q_scale if q_scale is not None else [1.0] * Tq
+    for i in range(Tq):
+        q[0, :, i, 0] = scales[i]
+    K = torch.zeros(1, Hkv, T_cap, d)
+    K[0, :, :T, 0] = torch.tensor(s, dtype=torch.float32)
+    g = torch.Generator().manual_seed(seed)
+    V = torch.randn(1, Hkv, T_cap, d, generator=g)
+    return q, K, V
+
+
+def _s_from(g, T):
+    if "s" in g:
+        return [float(x) for x in g["s"]]
+    s = [0.0] * T
+    for t, v in g["s_sparse"].items():
+        s[int(t)] = float(v)
+    return s
+
+
+def _check_trace(got_rounds, want_rounds):
+    assert len(got_rounds) == len(want_rounds), (len(got_rounds), len(want_rounds))
+    for r, (got, want) in enumerate(zip(got_rounds, want_rounds)):
+        cands = sorted(zip(got["start"].tolist(), got["end"].tolist(), got["centre"].tolist()))
+        assert cands == sorted(tuple(c) for c in want["candidates"]), (r, cands, want["candidates"])
+        kept = sorted((int(a), int(e)) for a, e, k in zip(got["start"], got["end"], got["kept"]) if k)
+        assert kept == sorted(tuple(c) for c in want["kept"]), (r, kept, want["kept"])
+
+
+def _run_golden(lib, name):
+    g = _golden(name)
+    sh = g["shape"]
+    T = sh["T"]
+    q, K, _ = _line_inputs(_s_from(g, T), Hq=sh["Hq"], Hkv=sh["Hkv"], Tq=sh["Tq"],
+                           T_cap=sh.get("T_cap"), q_scale=g.get("q_scale_per_row"))
+    res = oracle.mask_one(q, K, 0, 0, 0, T=T, k=sh["k"], block_k=sh["block_k"],
+                          block_q=sh["block_q"], causal=sh["causal"], trace=True, lib=lib)
+    assert res["indices"].tolist() == g["expected_indices"], (name, res["indices"].tolist())
+    assert res["nnz"] == len(g["expected_indices"])
+    _check_trace(res["rounds"], g["trace"])
+    return g, res
+
+
+# ---------------------------------------------------------------- golden traces
+
+def pin_monotone_counterexample(lib):
+    g, res = _run_golden(lib, "monotone_counterexample.json")
+    s = np.array(g["s"], np.float32)
+    top2 = sorted(np.argsort(-s, kind="stable")[:2].tolist())
+    assert top2 == g["brute_force_top2"]
+    assert res["indices"].tolist() != top2
+    # the reported margin is the smallest relative gap at a cut (values as fp32)
+    rels = [(np.float64(np.float32(a)) - np.float64(np.float32(b))) / abs(np.float64(np.float32(a)))
+            for a, b in g["cut_pairs"]]
+    assert math.isclose(res["margin"], min(rels), rel_tol=1e-12), (res["margin"], rels)
+
+
+def pin_centre_tokens(lib):
+    _run_golden(lib, "centre_rule_tokens.json")
+
+
+def pin_centre_blocks(lib):
+    _run_golden(lib, "centre_rule_blocks.json")
+
+
+def pin_centre_partial_block(lib):
+    _run_golden(lib, "centre_partial_block.json")
+
+
+def pin_uneven_partition(lib):
+    g, res = _run_golden(lib, "uneven_partition.json")
+    rels = [(a - b) / abs(a) for a, b in g["cut_pairs"]]
+    assert math.isclose(res["margin"], min(rels), rel_tol=1e-12)
+
+
+def pin_causal_vote(lib):
+    _run_golden(lib, "causal_vote.json")
+
+
+# ---------------------------------------------------------------- group maximum
+
+def pin_group_max(lib):
+    """Hq=4, Hkv=2: head h reads unit direction e_h, KV head g carries two score
+    series; the chunk score must be the max over the group's two heads only."""
+    T, d = 32, 64
+    rng = np.random.default_rng(7)
+    q = torch.zeros(1, 4, 1, d)
+    for h in range(4):
+        q[0, h, 0, h] = 1.0
+    series = rng.permutation(4 * T).astype(np.float32).reshape(4, T) / 7.0  # distinct values
+    K = torch.zeros(1, 2, T, d)
+    for h in range(4):
+        K[0, h // 2, :, h] = torch.from_numpy(series[h])
+    for g in range(2):
+        res = oracle.mask_one(q, K, 0, g, 0, T=T, k=4, block_k=1, block_q=1, trace=True, lib=lib)
+        for rnd in res["rounds"]:
+            for t, sc in zip(rnd["centre"], rnd["score"]):
+                want = max(series[2 * g][t], series[2 * g + 1][t])
+                assert sc == want, (g, t, sc, want)
+
+
+# ---------------------------------------------------------------- dense reduction
+
+def _dense_reference(q, K, V, T, causal):
+    """Dense softmax attention in float64 with torch SDPA (GQA by head expansion)."""
+    B, Hq, Tq, d = q.shape
+    G = Hq // K.shape[1]
+    q64 = q.double()
+    K64 = K[:, :, :T].double().repeat_interleave(G, dim=1)
+    V64 = V[:, :, :T].double().repeat_interleave(G, dim=1)
+    mask = None
+    if causal:
+        pos = torch.arange(Tq) + (T - Tq)
+        mask = torch.arange(T)[None, :] <= pos[:, None]
+    return F.scaled_dot_product_attention(q64, K64, V64, attn_mask=mask).numpy()
+
+
+def pin_dense_reduction(lib):
+    rng = torch.Generator().manual_seed(3)
+    cases = [  # (B, Hq, Hkv, Tq, T, d, block_k, block_q, causal)
+        (2, 4, 2, 1, 100, 64, 8, 1, 1),
+        (1, 4, 2, 40, 100, 64, 8, 16, 1),
+        (1, 2, 1, 7, 37, 32, 4, 1, 1),
+        (1, 4, 2, 24, 70, 64, 16, 8, 0),
+    ]
+    for (B, Hq, Hkv, Tq, T, d, bk, bq, causal) in cases:
+        q = torch.randn(B, Hq, Tq, d, generator=rng)
+        K = torch.randn(B, Hkv, T, d, generator=rng)
+        V = torch.randn(B, Hkv, T, d, generator=rng)
+        nblk = -(-T // bk)
+        k = nblk * bk  # k >= T: every block is visible to the search
+        idx, nnz, margin = oracle.mask_all(q, K, T=T, k=k, block_k=bk, block_q=bq, causal=causal,
+                                           threads=2, lib=lib)
+        nqb = -(-Tq // bq)
+        for qb in range(nqb):
+            last = min((qb + 1) * bq, Tq) - 1
+            Tp = (T - Tq + last + 1) if causal else T
+            Np = -(-Tp // bk)
+            assert (nnz[:, :, qb] == Np).all()
+            assert (idx[:, :, qb, :Np] == np.arange(Np)).all()
+            assert (idx[:, :, qb, Np:] == -1).all()
+        assert np.isinf(margin).all()
+        out = oracle.attn_all(q, K, V, idx, nnz, T=T, k=k, block_k=bk, block_q=bq, causal=causal,
+                              threads=2, lib=lib)
+        ref = _dense_reference(q, K, V, T, causal)
+        err = np.abs(out - ref).max()
+        assert err < 1e-10, (B, Hq, Hkv, Tq, T, err)
+
+
+# ---------------------------------------------------------------- exact top-k
+
+def _topk_run(lib, s, k):
+    q, K, _ = _line_inputs(list(s))
+    return oracle.mask_one(q, K, 0, 0, 0, T=len(s), k=k, block_k=1, block_q=1, trace=True, lib=lib)
+
+
+def pin_exact_topk_monotone(lib):
+    for T in (8, 64, 256):
+        for k in (1, 2, 4):
+            if k >= T:
+                continue
+            inc = np.arange(T, dtype=np.float32)
+            assert _topk_run(lib, inc, k)["indices"].tolist() == list(range(T - k, T))
+            dec = inc[::-1].copy()
+            assert _topk_run(lib, dec, k)["indices"].tolist() == list(range(k))
+
+
+def pin_exact_topk_disjoint_chunks(lib):
+    """Increasing inside each initial chunk, value ranges of chunks disjoint."""
+    rng = np.random.default_rng(11)
+    for trial in range(40):
+        k = int(rng.choice([2, 4]))
+        T = k * int(rng.choice([4, 8, 16]))
+        chunk = T // k
+        order = rng.permutation(k)
+        s = np.zeros(T, np.float32)
+        for c in range(k):
+            s[c * chunk:(c + 1) * chunk] = order[c] * 1000 + np.sort(rng.choice(900, chunk, replace=False))
+        got = _topk_run(lib, s, k)["indices"].tolist()
+        want = sorted(np.argsort(-s, kind="stable")[:k].tolist())
+        assert got == want, (trial, got, want)
+
+
+def pin_exact_topk_certified(lib):
+    """Random distinct scores: whenever the trace shows every kept chunk's maximum
+    at least every dropped chunk's maximum, in every round, the result is the
+    exact top-k (induction on rounds)."""
+    rng = np.random.default_rng(5)
+    certified = 0
+    for trial in range(400):
+        k = int(rng.choice([1, 2, 3]))
+        T = int(rng.choice([8, 12, 16, 24]))
+        s = rng.permutation(T).astype(np.float32)
+        res = _topk_run(lib, s, k)
+        ok = True
+        for rnd in res["rounds"]:
+            mx = [s[a:e].max() for a, e in zip(rnd["start"], rnd["end"])]
+            kept = [m for m, kp in zip(mx, rnd["kept"]) if kp]
+            dropped = [m for m, kp in zip(mx, rnd["kept"]) if not kp]
+            if dropped and min(kept) < max(dropped):
+                ok = False
+                break
+        if ok:
+            certified += 1
+            want = sorted(np.argsort(-s, kind="stable")[:k].tolist())
+            assert res["indices"].tolist() == want, (trial, s, res["indices"])
+    assert certified >= 50, certified
+
+
+# ---------------------------------------------------------------- structure
+
+def pin_tree_structure(lib):
+    """Round count, candidate count, and the chunk tree: the candidates of a round
+    tile exactly the chunks kept by the previous round, each chunk splits into at
+    most two halves, and final blocks lie in a kept chunk of every round."""
+    import synth_inputs as si
+    w = si.workload("tiny_decode")
+    x = si.make_inputs(w)
+    res = oracle.mask_one(x["q"], x["K"], 0, 0, 0, T=w.T, k=w.k, block_k=w.block_k,
+                          block_q=w.block_q, trace=True, lib=lib)
+    Np, Kb = w.T // w.block_k, w.kb
+    R = int(math.ceil(math.log2(Np / Kb)))
+    assert len(res["rounds"]) == R == 3
+    for rnd in res["rounds"]:
+        assert len(rnd["start"]) == 2 * Kb and int(rnd["kept"].sum()) == Kb
+    # uneven cases: causal prefill-like block counts
+    rng = torch.Generator().manual_seed(9)
+    for T in (449 * 8, 500 * 8, 37 * 8 + 3):
+        q = torch.randn(1, 2, 1, 64, generator=rng)
+        K = torch.randn(1, 1, T + 64, 64, generator=rng)  # spare capacity rows past T
+        Kb = 32 if T > 1000 else 5
+        res = oracle.mask_one(q, K, 0, 0, 0, T=T, k=Kb * 8, block_k=8, block_q=1, trace=True,
+                              lib=lib)
+        Np = -(-T // 8)
+        prev = [(i * Np // Kb, (i + 1) * Np // Kb) for i in range(Kb)]
+        assert len(res["rounds"]) <= math.ceil(math.log2(-(-Np // Kb)))
+        final = res["indices"].tolist()
+        assert len(set(final)) == Kb and all(0 <= b < Np for b in final)
+        for rnd in res["rounds"]:
+            cands = sorted(zip(rnd["start"].tolist(), rnd["end"].tolist()))
+            tiles = []
+            for a, e in sorted(prev):
+                kids = [c for c in cands if a <= c[0] and c[1] <= e]
+                assert 1 <= len(kids) <= 2 and kids[0][0] == a and kids[-1][1] == e
+                if len(kids) == 2:
+                    assert kids[0][1] == kids[1][0] == a + (e - a) // 2
+                else:
+                    assert e - a == 1
+                tiles += kids
+            assert tiles == cands
+            prev = [(int(a), int(e)) for a, e, kp in zip(rnd["start"], rnd["end"], rnd["kept"]) if kp]
+            for b in final:
+                assert any(a <= b < e for a, e in prev)
+        assert all(e - a == 1 for a, e in prev)
+
+
+# ---------------------------------------------------------------- closed forms
+
+def pin_zero_query_ties(lib):
+    """q = 0: every score is exactly 0, ties go to the lower start, the kept
+    blocks are the prefix 0..K_b-1 and attention is the mean of V over them."""
+    rng = torch.Generator().manual_seed(1)
+    for (Tq, bq, T, bk, k) in ((1, 1, 200, 8, 48), (20, 4, 150, 8, 40), (33, 16, 301, 16, 64)):
+        q = torch.zeros(1, 4, Tq, 64)
+        K = torch.randn(1, 2, T + 64, 64, generator=rng)  # spare capacity rows past T
+        V = torch.randn(1, 2, T + 64, 64, generator=rng)
+        idx, nnz, margin = oracle.mask_all(q, K, T=T, k=k, block_k=bk, block_q=bq, threads=2, lib=lib)
+        Kb = k // bk
+        assert (idx == np.arange(Kb)).all() and (nnz == Kb).all()
+        assert (margin == 0).all()
+        out = oracle.attn_all(q, K, V, idx, nnz, T=T, k=k, block_k=bk, block_q=bq, threads=2, lib=lib)
+        Vn = V.double().numpy()
+        for h in range(4):
+            for i in range(Tq):
+                pos = T - Tq + i
+                hi = min(Kb * bk, pos + 1)
+                want = Vn[0, h // 2, :hi].mean(axis=0)
+                assert np.abs(out[0, h, i] - want).max() < 1e-12
+
+
+# ---------------------------------------------------------------- attention invariants
+
+def pin_attention_invariants(lib):
+    import synth_inputs as si
+    w = si.workload("tiny_decode")
+    x = si.make_inputs(w)
+    kw = dict(T=w.T, k=w.k, block_k=w.block_k, block_q=w.block_q, causal=w.causal, lib=lib)
+    idx, nnz, _ = oracle.mask_all(x["q"], x["K"], threads=2, **kw)
+    out = oracle.attn_all(x["q"], x["K"], x["V"], idx, nnz, threads=2, **kw)
+    toks = np.concatenate([np.arange(b * w.block_k, (b + 1) * w.block_k) for b in idx[0, 0, 0]])
+    Vsel = x["V"][0, 0, toks].double().numpy()
+    assert (out[0, 0, 0] >= Vsel.min(0) - 1e-12).all() and (out[0, 0, 0] <= Vsel.max(0) + 1e-12).all()
+    # constant V
+    Vc = torch.full_like(x["V"], 0.375)
+    oc = oracle.attn_all(x["q"], x["K"], Vc, idx, nnz, threads=2, **kw)
+    assert np.abs(oc - 0.375).max() < 1e-12
+    # one dominant key: its V row comes out (margin of 60 in the logit)
+    q = torch.zeros_like(x["q"])
+    q[0, 0, 0, 0] = 1.0
+    K = torch.zeros_like(x["K"])
+    t_star = int(toks[len(toks) // 2])
+    K[0, 0, t_star, 0] = 60.0 * math.sqrt(w.d)
+    od = oracle.attn_all(q, K, x["V"], idx, nnz, threads=2, **kw)
+    # the other weights are e^-60 each, far below one ulp of the result
+    assert np.abs(od[0, 0, 0] - x["V"][0, 0, t_star].double().numpy()).max() < 1e-14
+
+
+def pin_mask_invariances(lib):
+    """Doubling q leaves the mask unchanged (exact in binary floating point);
+    permuting batch entries or KV heads (with their query groups) permutes it."""
+    import synth_inputs as si
+    w = si.workload("decode_32k", T=4096, k=512, B=2)
+    x = si.make_inputs(w)
+    kw = dict(T=w.T, k=w.k, block_k=w.block_k, block_q=w.block_q, causal=w.causal, threads=4, lib=lib)
+    q = x["q"].float()
+    K = x["K"].float()
+    idx, nnz, _ = oracle.mask_all(q, K, **kw)
+    idx2, _, _ = oracle.mask_all(q * 2, K, **kw)
+    assert (idx == idx2).all()
+    G = w.G
+    perm_g = [3, 0, 7, 1, 6, 2, 5, 4]
+    perm_h = [g * G + j for g in perm_g for j in range(G)]
+    qp = q[[1, 0]][:, perm_h].contiguous()
+    Kp = K[[1, 0]][:, perm_g].contiguous()
+    idxp, _, _ = oracle.mask_all(qp, Kp, **kw)
+    assert (idxp == idx[[1, 0]][:, perm_g]).all()
+
+
+ALL_PINS = [
+    pin_monotone_counterexample, pin_centre_tokens, pin_centre_blocks, pin_centre_partial_block,
+    pin_uneven_partition, pin_causal_vote, pin_group_max, pin_dense_reduction,
+    pin_exact_topk_monotone, pin_exact_topk_disjoint_chunks, pin_exact_topk_certified,
+    pin_tree_structure, pin_zero_query_ties, pin_attention_invariants, pin_mask_invariances,
+]

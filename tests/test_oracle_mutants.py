@@ -1,0 +1,57 @@
+"""Plant plausible mistakes in copies of the oracle and check that the pins catch
+each one.  CPU only: every mutant is built from a patched copy of oracle.c in
+a temporary directory, loaded beside the real oracle, and run through the same
+pin checks."""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+# (name, original text, planted mistake)
+MUTANTS = [
+    ("centre_lower_middle", "int64_t t = (lo + hi) / 2;", "int64_t t = (lo + hi - 1) / 2;"),
+    ("centre_ignores_partial_block",
+     "int64_t hi = cand[c].e * s->block_k < Tp ? cand[c].e * s->block_k : Tp;",
+     "int64_t hi = cand[c].e * s->block_k;"),
+    ("split_ceil_midpoint", "int64_t m = ca[i] + (ce[i] - ca[i]) / 2;",
+     "int64_t m = ca[i] + (ce[i] - ca[i] + 1) / 2;"),
+    ("tie_prefers_higher_start", "return x->a < y->a;", "return x->a > y->a;"),
+    ("keeps_lowest_scores", "if (x->score != y->score) return x->score > y->score;",
+     "if (x->score != y->score) return x->score < y->score;"),
+    ("no_causal_vote", "if (s->causal && position(s, i) < t) continue;", "if (0) continue;"),
+    ("causal_vote_off_by_one", "if (s->causal && position(s, i) < t) continue;",
+     "if (s->causal && position(s, i) <= t) continue;"),
+    ("strided_head_group", "for (int64_t h = g * G; h < (g + 1) * G; h++)",
+     "for (int64_t h = g; h < s->Hq; h += s->Hkv)"),
+    ("first_row_only", "for (int64_t i = r0; i < r1; i++) {", "for (int64_t i = r0; i < r0 + 1; i++) {"),
+    ("ceil_initial_partition", "ca[i] = i * Np / Kb;\n    ce[i] = (i + 1) * Np / Kb;",
+     "ca[i] = (i * Np + Kb - 1) / Kb;\n    ce[i] = ((i + 1) * Np + Kb - 1) / Kb;"),
+    ("attn_no_scale", "const double scale = 1.0 / sqrt((double)s->d);", "const double scale = 1.0;"),
+    ("attn_no_causal_mask", "if (t > limit) continue;\n      double w", "double w"),
+    ("attn_value_head_of_query", "int64_t vo = ((b * s->Hkv + g) * s->T_cap + t) * s->d;",
+     "int64_t vo = ((b * s->Hkv + h % s->Hkv) * s->T_cap + t) * s->d;"),
+    ("margin_not_relative", "rel = den == 0.0 ? 0.0 : (hiS - loS) / den;", "rel = hiS - loS;"),
+    ("dense_case_skipped", "if (Np <= Kb) {", "if (Np < 0) {"),
+    ("score_sum_over_group", "if (v > best) best = v;",
+     "best = (best == -INFINITY) ? v : best + v;"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique in oracle.c"
+    mpath = tmp_path / f"{name}.c"
+    mpath.write_text(src.replace(old, new))
+    lib = oracle.load(oracle.build(str(mpath), str(tmp_path / f"lib{name}.so")))
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(lib)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches mutant {name}"
