@@ -1,0 +1,143 @@
+/*
+ * hipsa.h -- HiP (Hierarchically Pruned attention) mask estimation and
+ * block-sparse attention for AMD Instinct MI355X (gfx950).
+ *
+ * The method (web page "A Training-free Sub-quadratic Cost Transformer Model
+ * Serving Framework With Hierarchically Pruned Attention", Author Rebuttal to
+ * the Reviewer RsGC, Q2): split the keys a query block can see into k chunks;
+ * halve every chunk; score each half by the dot product of the query with the
+ * key token at the half's centre; keep the k best halves over the whole
+ * sequence; repeat until every chunk is one key block.  The sparse attention
+ * then runs over the kept blocks only, given per query block the list of
+ * block indices and its length nnz (same page, reviewer NLBm, W2).  The mask
+ * is estimated by one call and consumed by another so that a caller can reuse
+ * it across decode steps (summary page "A Training-Free Sub-quadratic Cost
+ * Transformer Model Serving Framework with Hierarchically Pruned Attention",
+ * Limitations: the mask refresh interval trades quality for latency).
+ *
+ * Conventions shared by every call
+ * ---------------------------------
+ *  - All tensor arguments are DEVICE pointers owned by the caller.  The
+ *    library never allocates, frees or keeps them past the call.
+ *  - Layouts are contiguous and head-major:
+ *        q, out   [B, Hq, Tq, d]
+ *        K, V     [B, Hkv, T_cap, d]   rows 0..T-1 are the valid keys
+ *        indices  [B, Hkv, NQB, K_b]   int32, NQB = ceil(Tq / block_q)
+ *        nnz      [B, Hkv, NQB]        int32
+ *    with K_b = k / block_k.  Query head h belongs to KV head h / (Hq / Hkv);
+ *    the mask is shared by all query heads of a KV head (their scores are
+ *    combined with a max).
+ *  - Query row i sits at absolute position T - Tq + i.  With causal != 0 it
+ *    sees keys 0..T-Tq+i; with causal == 0 every row sees keys 0..T-1.  A
+ *    query block's visible length T_p is the visible length of its last row;
+ *    it covers N_p = ceil(T_p / block_k) key blocks, the last possibly partial.
+ *  - dtype selects the element type of q, K, V and out: HIPSA_F32 (float) or
+ *    HIPSA_BF16 (bfloat16 bits).  Dot products and softmax accumulate in fp32;
+ *    outputs are rounded to the element type with round-to-nearest-even.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream), never synchronises, keeps no state between calls and is safe
+ *    to call from several host threads.  Calls that share a workspace must be
+ *    ordered on one stream.
+ *  - Return value: HIPSA_OK (0) or a negative hipsa_status.  Every argument
+ *    check runs on the host before any HIP call, so an invalid call touches no
+ *    device memory.  hipsa_last_error() returns a message for the calling
+ *    thread's last failure.  Faults inside a kernel surface at the caller's
+ *    next synchronisation with the stream.
+ *
+ * Supported shapes: d in {64, 128}; block_k in {8, 16, 32, 64}; 1 <= K_b <= 512;
+ * 1 <= Hq/Hkv <= 16; T <= T_cap < 2^31.  block_q = 1 (decode, and
+ * per-row problems for any Tq) works for both dtypes; block_q = 64 (chunked
+ * prefill) requires HIPSA_BF16.
+ */
+#ifndef HIPSA_H
+#define HIPSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { HIPSA_F32 = 0, HIPSA_BF16 = 1 } hipsa_dtype;
+
+typedef enum {
+  HIPSA_OK = 0,
+  HIPSA_ERR_NULL = -1,      /* a required pointer is NULL                          */
+  HIPSA_ERR_SHAPE = -2,     /* inconsistent or unsupported B, H, T, Tq, d, T_cap    */
+  HIPSA_ERR_BLOCK = -3,     /* unsupported k, block_k or block_q                    */
+  HIPSA_ERR_DTYPE = -4,     /* unsupported dtype, or dtype/block_q combination      */
+  HIPSA_ERR_WORKSPACE = -5, /* workspace smaller than hipsa_workspace_bytes()       */
+  HIPSA_ERR_HIP = -6        /* a HIP runtime call or kernel launch failed           */
+} hipsa_status;
+
+typedef struct hipsa_desc {
+  int64_t B;      /* batch entries (sequences)                                   */
+  int64_t Hq;     /* query heads; a multiple of Hkv                              */
+  int64_t Hkv;    /* key/value heads                                             */
+  int64_t Tq;     /* query rows per sequence (1 for decode); 1 <= Tq <= T        */
+  int64_t T;      /* valid keys per sequence, >= 1                               */
+  int64_t T_cap;  /* allocated key rows per head (row stride of K and V), >= T   */
+  int64_t d;      /* head dimension                                              */
+  int32_t causal; /* non-zero: row i sees keys <= T - Tq + i                     */
+  int32_t dtype;  /* hipsa_dtype                                                 */
+} hipsa_desc;
+
+/*
+ * Hierarchical top-k key-block selection (rebuttal page, reviewer RsGC, Q2;
+ * block sizes b_q and b_k from reviewer NLBm, Q1).
+ *
+ * For each (b, kv head g, query block qb):
+ *   - if N_p <= K_b every block is selected (nnz = N_p);
+ *   - otherwise chunks start as [floor(i*N_p/K_b), floor((i+1)*N_p/K_b)),
+ *     i < K_b (in blocks).  Each round splits every chunk of >= 2 blocks
+ *     [a,e) at a + floor((e-a)/2) (one-block chunks pass through), scores each
+ *     candidate by max over the group's query heads and the block's rows (a
+ *     causal row votes only for centres at or before its position) of the raw
+ *     dot product q . K[t], where t = floor((a*block_k + min(e*block_k, T_p))/2)
+ *     is the candidate's centre token, and keeps the K_b best by (score
+ *     descending, start ascending).  Rounds repeat until every kept chunk is
+ *     one block.
+ * Writes indices[b,g,qb,0..nnz-1] in ascending order, -1 after them, and
+ * nnz[b,g,qb].  q, K: element type `dtype`.  k: keys to keep, a multiple of
+ * block_k.  block_q: 1 or 64.  The workspace is unused by this call (pass
+ * NULL and 0, or any buffer).
+ */
+int hip_mask_estimate(const hipsa_desc *desc, const void *q, const void *K, int64_t k,
+                      int64_t block_k, int64_t block_q, int32_t *indices, int32_t *nnz,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Block-sparse attention over listed key blocks (rebuttal page, reviewer NLBm,
+ * W2: the kernel takes each row's non-zero block indices and their count;
+ * reviewer KprR, W2: reported latency is masking plus sparse attention).
+ *
+ * out[b,h,i,:] = sum_t softmax_t(q[b,h,i,:] . K[b,g,t,:] / sqrt(d)) V[b,g,t,:]
+ * over the tokens t of blocks indices[b,g,qb,0..nnz-1] (g = h/(Hq/Hkv),
+ * qb = i/block_q) with t < T_p and, when causal, t <= T - Tq + i.  Block ids
+ * outside [0, N_p) are skipped, nnz is clamped to [0, K_b], and a row with no
+ * visible token gets zeros.  indices/nnz are typically hip_mask_estimate's
+ * output but may come from anywhere.  Needs a device workspace of at least
+ * hipsa_workspace_bytes() bytes (split-K partial results); its contents need
+ * no initialisation and are scratch after the call.
+ */
+int hip_sparse_attn(const hipsa_desc *desc, const void *q, const void *K, const void *V,
+                    const int32_t *indices, const int32_t *nnz, int64_t k, int64_t block_k,
+                    int64_t block_q, void *out, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+/* Device workspace bytes that hip_sparse_attn (and hip_mask_estimate) need for
+ * this shape (0 = none), or SIZE_MAX when the arguments are invalid (see
+ * hipsa_last_error()).  Empty problems (B == 0 or Tq == 0) need none, and
+ * every call on them returns HIPSA_OK without touching any pointer. */
+size_t hipsa_workspace_bytes(const hipsa_desc *desc, int64_t k, int64_t block_k,
+                             int64_t block_q);
+
+/* Message for the calling thread's last non-zero return ("" if none).  The
+ * pointer stays valid until that thread's next call into the library. */
+const char *hipsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HIPSA_H */

@@ -1,0 +1,150 @@
+"""Python binding of libhipsa: HiP mask estimation and block-sparse attention on MI355X.
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels of libhipsa.so; torch supplies device memory and the current stream.
+There is no fallback: importing this package fails if the library is not
+built (``python -m long_context_sparse_mask_amd.build``).
+
+Layouts (contiguous): q [B,Hq,Tq,d]; K, V [B,Hkv,T_cap,d] with the first T
+rows valid; indices [B,Hkv,NQB,k/block_k] int32; nnz [B,Hkv,NQB] int32.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch  # loads the HIP runtime first, so libhipsa binds to the same one
+
+__all__ = ["hip_mask_estimate", "hip_sparse_attn", "hipsa_workspace_bytes", "HipsaError",
+           "LIB_PATH", "lib"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhipsa.so")
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m long_context_sparse_mask_amd.build`")
+
+lib = C.CDLL(LIB_PATH)
+
+HIPSA_F32, HIPSA_BF16 = 0, 1
+SIZE_MAX = (1 << (8 * C.sizeof(C.c_size_t))) - 1
+
+
+class Desc(C.Structure):
+    _fields_ = [("B", C.c_int64), ("Hq", C.c_int64), ("Hkv", C.c_int64), ("Tq", C.c_int64),
+                ("T", C.c_int64), ("T_cap", C.c_int64), ("d", C.c_int64), ("causal", C.c_int32),
+                ("dtype", C.c_int32)]
+
+
+_P, _I64, _SZ = C.c_void_p, C.c_int64, C.c_size_t
+lib.hip_mask_estimate.argtypes = [C.POINTER(Desc), _P, _P, _I64, _I64, _I64, _P, _P, _P, _SZ, _P]
+lib.hip_mask_estimate.restype = C.c_int
+lib.hip_sparse_attn.argtypes = [C.POINTER(Desc), _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P,
+                                _SZ, _P]
+lib.hip_sparse_attn.restype = C.c_int
+lib.hipsa_workspace_bytes.argtypes = [C.POINTER(Desc), _I64, _I64, _I64]
+lib.hipsa_workspace_bytes.restype = C.c_size_t
+lib.hipsa_last_error.argtypes = []
+lib.hipsa_last_error.restype = C.c_char_p
+
+
+class HipsaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"hipsa error {code}: {msg}")
+        self.code = code
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise HipsaError(rc, lib.hipsa_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return HIPSA_BF16
+    if t.dtype == torch.float32:
+        return HIPSA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def make_desc(q: torch.Tensor, K: torch.Tensor, T: int | None = None, causal: bool = True) -> Desc:
+    B, Hq, Tq, d = q.shape
+    _, Hkv, T_cap, _ = K.shape
+    return Desc(B, Hq, Hkv, Tq, T_cap if T is None else T, T_cap, d, int(bool(causal)),
+                _dtype_code(q))
+
+
+def _stream(dev: torch.device, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev_ptr(t: torch.Tensor, name: str) -> int:
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def hipsa_workspace_bytes(q, K, k: int, block_k: int, block_q: int = 1, *, T=None,
+                          causal=True) -> int:
+    n = lib.hipsa_workspace_bytes(C.byref(make_desc(q, K, T, causal)), k, block_k, block_q)
+    if n == SIZE_MAX:
+        raise HipsaError(-2, lib.hipsa_last_error().decode())
+    return n
+
+
+def hip_mask_estimate(q, K, k: int, block_k: int, block_q: int = 1, *, T=None, causal=True,
+                      indices=None, nnz=None, stream=None):
+    """Per (batch, kv head, query block): the ids of the selected key blocks
+    (ascending, -1 padded) and their count.  Returns (indices, nnz)."""
+    desc = make_desc(q, K, T, causal)
+    nqb = -(-desc.Tq // block_q)
+    kb = k // block_k if block_k > 0 else 0
+    if indices is None:
+        indices = torch.empty((desc.B, desc.Hkv, nqb, kb), dtype=torch.int32, device=q.device)
+    if nnz is None:
+        nnz = torch.empty((desc.B, desc.Hkv, nqb), dtype=torch.int32, device=q.device)
+    if q.dtype != K.dtype:
+        raise TypeError("q and K must share a dtype")
+    if tuple(indices.shape) != (desc.B, desc.Hkv, nqb, kb) or indices.dtype != torch.int32:
+        raise ValueError("indices must be int32 [B, Hkv, NQB, k/block_k]")
+    if tuple(nnz.shape) != (desc.B, desc.Hkv, nqb) or nnz.dtype != torch.int32:
+        raise ValueError("nnz must be int32 [B, Hkv, NQB]")
+    if desc.B * desc.Tq == 0:
+        return indices, nnz
+    _check(lib.hip_mask_estimate(C.byref(desc), _dev_ptr(q, "q"), _dev_ptr(K, "K"), k, block_k,
+                                 block_q, _dev_ptr(indices, "indices"), _dev_ptr(nnz, "nnz"),
+                                 None, 0, _stream(q.device, stream)))
+    return indices, nnz
+
+
+def hip_sparse_attn(q, K, V, indices, nnz, k: int, block_k: int, block_q: int = 1, *, T=None,
+                    causal=True, out=None, workspace=None, stream=None):
+    """Softmax attention of every query row over the tokens of its listed key
+    blocks.  Returns out [B,Hq,Tq,d] in q's dtype."""
+    desc = make_desc(q, K, T, causal)
+    if not (q.dtype == K.dtype == V.dtype):
+        raise TypeError("q, K and V must share a dtype")
+    if V.shape != K.shape:
+        raise ValueError("V must have K's shape")
+    nqb = -(-desc.Tq // block_q)
+    kb = k // block_k if block_k > 0 else 0
+    if tuple(indices.shape) != (desc.B, desc.Hkv, nqb, kb) or indices.dtype != torch.int32:
+        raise ValueError("indices must be int32 [B, Hkv, NQB, k/block_k]")
+    if tuple(nnz.shape) != (desc.B, desc.Hkv, nqb) or nnz.dtype != torch.int32:
+        raise ValueError("nnz must be int32 [B, Hkv, NQB]")
+    if out is None:
+        out = torch.empty_like(q)
+    if desc.B * desc.Tq == 0:
+        return out
+    need = hipsa_workspace_bytes(q, K, k, block_k, block_q, T=T, causal=causal)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.hip_sparse_attn(C.byref(desc), _dev_ptr(q, "q"), _dev_ptr(K, "K"), _dev_ptr(V, "V"),
+                               _dev_ptr(indices, "indices"), _dev_ptr(nnz, "nnz"), k, block_k,
+                               block_q, _dev_ptr(out, "out"), ws_ptr, ws_len,
+                               _stream(q.device, stream)))
+    return out

@@ -1,0 +1,165 @@
+// Host entry points of libhipsa: argument checks, workspace sizing, dispatch.
+//
+// Every check runs before the first HIP call, so a rejected call has no
+// effect on the device.  Messages are kept per host thread.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "hipsa_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return HIPSA_OK;
+}
+
+bool pow2_in(int64_t v, int64_t lo, int64_t hi) {
+  return v >= lo && v <= hi && (v & (v - 1)) == 0;
+}
+
+// Checks shared by every entry point; fills `s` on success.
+int check_shape(const hipsa_desc *d, int64_t k, int64_t block_k, int64_t block_q,
+                hipsa::Shape *s) {
+  if (!d) return fail(HIPSA_ERR_NULL, "desc is NULL");
+  if (d->B < 0 || d->Hq < 1 || d->Hkv < 1 || d->Tq < 0)
+    return fail(HIPSA_ERR_SHAPE, "need B >= 0, Hq >= 1, Hkv >= 1, Tq >= 0 (got B=%lld Hq=%lld "
+                "Hkv=%lld Tq=%lld)", (long long)d->B, (long long)d->Hq, (long long)d->Hkv,
+                (long long)d->Tq);
+  if (d->Hq % d->Hkv != 0)
+    return fail(HIPSA_ERR_SHAPE, "Hq=%lld is not a multiple of Hkv=%lld", (long long)d->Hq,
+                (long long)d->Hkv);
+  if (d->Hq / d->Hkv > hipsa::kMaxGroup)
+    return fail(HIPSA_ERR_SHAPE, "Hq/Hkv=%lld exceeds %d", (long long)(d->Hq / d->Hkv),
+                hipsa::kMaxGroup);
+  if (d->T < 1) return fail(HIPSA_ERR_SHAPE, "T=%lld must be >= 1", (long long)d->T);
+  if (d->Tq > d->T)
+    return fail(HIPSA_ERR_SHAPE, "Tq=%lld exceeds T=%lld", (long long)d->Tq, (long long)d->T);
+  if (d->T_cap < d->T || d->T_cap >= (int64_t(1) << 31))
+    return fail(HIPSA_ERR_SHAPE, "need T <= T_cap < 2^31 (T=%lld T_cap=%lld)", (long long)d->T,
+                (long long)d->T_cap);
+  if (d->d != 64 && d->d != 128)
+    return fail(HIPSA_ERR_SHAPE, "head dim d=%lld unsupported (64 or 128)", (long long)d->d);
+  if (d->dtype != HIPSA_F32 && d->dtype != HIPSA_BF16)
+    return fail(HIPSA_ERR_DTYPE, "dtype=%d unsupported", (int)d->dtype);
+  if (!pow2_in(block_k, 8, 64))
+    return fail(HIPSA_ERR_BLOCK, "block_k=%lld unsupported (8, 16, 32 or 64)",
+                (long long)block_k);
+  if (k < block_k || k % block_k != 0)
+    return fail(HIPSA_ERR_BLOCK, "k=%lld must be a positive multiple of block_k=%lld",
+                (long long)k, (long long)block_k);
+  if (k / block_k > hipsa::kMaxKb)
+    return fail(HIPSA_ERR_BLOCK, "k/block_k=%lld exceeds %d", (long long)(k / block_k),
+                hipsa::kMaxKb);
+  if (block_q != 1 && block_q != 64)
+    return fail(HIPSA_ERR_BLOCK, "block_q=%lld unsupported (1 or 64)", (long long)block_q);
+  if (block_q == 64 && d->dtype != HIPSA_BF16)
+    return fail(HIPSA_ERR_DTYPE, "block_q=64 (prefill) needs bf16 inputs");
+  s->B = d->B; s->Hq = d->Hq; s->Hkv = d->Hkv; s->Tq = d->Tq; s->T = d->T; s->T_cap = d->T_cap;
+  s->d = d->d;
+  s->G = (int32_t)(d->Hq / d->Hkv);
+  s->Kb = (int32_t)(k / block_k);
+  s->bk = (int32_t)block_k;
+  s->bq = (int32_t)block_q;
+  s->causal = d->causal != 0;
+  s->dtype = d->dtype;
+  s->nqb = (d->Tq + block_q - 1) / block_q;
+  s->problems = d->B * d->Hkv * s->nqb;
+  // largest grid: decode attention launches problems x splits x G workgroups at most
+  const int64_t splits = ((int64_t)s->Kb * s->bk + 63) / 64;
+  if (s->problems * splits * s->G >= (int64_t(1) << 31))
+    return fail(HIPSA_ERR_SHAPE, "too many problems (%lld) for one launch",
+                (long long)s->problems);
+  return HIPSA_OK;
+}
+
+size_t workspace_for(const hipsa::Shape &s) {
+  if (s.problems == 0) return 0;
+  if (s.bq == 1) return hipsa::attn_decode_workspace(s);
+  return 0;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+  return fail(HIPSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int hip_mask_estimate(const hipsa_desc *desc, const void *q, const void *K, int64_t k,
+                      int64_t block_k, int64_t block_q, int32_t *indices, int32_t *nnz,
+                      void *workspace, size_t workspace_bytes, void *stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  hipsa::Shape s;
+  int rc = check_shape(desc, k, block_k, block_q, &s);
+  if (rc) return rc;
+  if (s.problems == 0) return ok();
+  if (!q || !K || !indices || !nnz)
+    return fail(HIPSA_ERR_NULL, "q, K, indices and nnz must be non-NULL");
+  hipsa::MaskArgs a{q, K, indices, nnz, s};
+  hipError_t e = s.bq == 1 ? hipsa::launch_mask_decode(a, (hipStream_t)stream)
+                           : hipsa::launch_mask_prefill(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "mask estimation launch");
+  return ok();
+}
+
+int hip_sparse_attn(const hipsa_desc *desc, const void *q, const void *K, const void *V,
+                    const int32_t *indices, const int32_t *nnz, int64_t k, int64_t block_k,
+                    int64_t block_q, void *out, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+  hipsa::Shape s;
+  int rc = check_shape(desc, k, block_k, block_q, &s);
+  if (rc) return rc;
+  if (s.problems == 0) return ok();
+  if (!q || !K || !V || !indices || !nnz || !out)
+    return fail(HIPSA_ERR_NULL, "q, K, V, indices, nnz and out must be non-NULL");
+  const size_t need = workspace_for(s);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(HIPSA_ERR_WORKSPACE, "workspace of %zu bytes at %p is too small: need %zu",
+                workspace_bytes, workspace, need);
+  hipsa::AttnArgs a{};
+  a.q = q; a.K = K; a.V = V; a.indices = indices; a.nnz = nnz; a.out = out;
+  a.ws = static_cast<float *>(workspace);
+  a.s = s;
+  a.scale = (float)(1.0 / __builtin_sqrt((double)s.d));
+  hipError_t e;
+  if (s.bq == 1) {
+    a.splits = hipsa::attn_decode_splits(s);
+    e = hipsa::launch_attn_decode(a, (hipStream_t)stream);
+  } else {
+    a.splits = 1;
+    e = hipsa::launch_attn_prefill(a, (hipStream_t)stream);
+  }
+  if (e != hipSuccess) return hip_fail(e, "sparse attention launch");
+  return ok();
+}
+
+size_t hipsa_workspace_bytes(const hipsa_desc *desc, int64_t k, int64_t block_k,
+                             int64_t block_q) {
+  hipsa::Shape s;
+  if (check_shape(desc, k, block_k, block_q, &s)) return SIZE_MAX;
+  g_err.clear();
+  return workspace_for(s);
+}
+
+const char *hipsa_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,126 @@
+"""The C ABI on the host: the library loads, exports every function that
+include/hipsa.h declares, and rejects invalid arguments before any HIP call
+(so these run without a GPU: no compute call is made)."""
+import ctypes as C
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hipsa.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(\w+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert _declared() == sorted(["hip_mask_estimate", "hip_sparse_attn",
+                                  "hipsa_workspace_bytes", "hipsa_last_error"])
+
+
+def test_library_exports_every_declared_symbol():
+    import long_context_sparse_mask_amd as hs
+    for name in _declared():
+        assert hasattr(hs.lib, name), name
+
+
+def test_header_compiles_as_c():
+    r = subprocess.run(["gcc", "-fsyntax-only", "-x", "c", "-std=c99", "-Wall", "-Werror", HEADER],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def _desc(**kw):
+    import long_context_sparse_mask_amd as hs
+    base = dict(B=1, Hq=32, Hkv=8, Tq=1, T=32768, T_cap=32768, d=128, causal=1, dtype=1)
+    base.update(kw)
+    return hs.Desc(**base)
+
+
+FAKE = C.c_void_p(0x1000)  # never dereferenced: every case below fails validation first
+
+
+def _mask(desc, k=2048, bk=64, bq=1, ptrs=(FAKE, FAKE, FAKE, FAKE)):
+    import long_context_sparse_mask_amd as hs
+    q, K, idx, nnz = ptrs
+    return hs.lib.hip_mask_estimate(C.byref(desc), q, K, k, bk, bq, idx, nnz, None, 0, None)
+
+
+ERR_NULL, ERR_SHAPE, ERR_BLOCK, ERR_DTYPE, ERR_WS = -1, -2, -3, -4, -5
+
+
+@pytest.mark.parametrize("kw,k,bk,bq,code", [
+    (dict(Hq=30), 2048, 64, 1, ERR_SHAPE),          # Hq % Hkv != 0
+    (dict(Hq=34, Hkv=2), 2048, 64, 1, ERR_SHAPE),   # group of 17 > 16
+    (dict(T=0, T_cap=0), 2048, 64, 1, ERR_SHAPE),
+    (dict(Tq=5, T=4, T_cap=4), 64, 64, 1, ERR_SHAPE),
+    (dict(T_cap=100), 2048, 64, 1, ERR_SHAPE),      # T > T_cap
+    (dict(T_cap=1 << 31), 2048, 64, 1, ERR_SHAPE),
+    (dict(d=96), 2048, 64, 1, ERR_SHAPE),
+    (dict(dtype=7), 2048, 64, 1, ERR_DTYPE),
+    (dict(), 2048, 48, 1, ERR_BLOCK),               # block_k not a power of two
+    (dict(), 2048, 128, 1, ERR_BLOCK),
+    (dict(), 2000, 64, 1, ERR_BLOCK),               # k % block_k
+    (dict(), 32, 64, 1, ERR_BLOCK),                 # k < block_k
+    (dict(), 64 * 513, 64, 1, ERR_BLOCK),           # K_b > 512
+    (dict(), 2048, 64, 32, ERR_BLOCK),              # block_q
+    (dict(dtype=0), 2048, 64, 64, ERR_DTYPE),       # fp32 prefill
+    (dict(B=-1), 2048, 64, 1, ERR_SHAPE),
+])
+def test_mask_rejects_invalid_arguments(kw, k, bk, bq, code):
+    import long_context_sparse_mask_amd as hs
+    assert _mask(_desc(**kw), k, bk, bq) == code
+    assert hs.lib.hipsa_last_error().decode() != ""
+
+
+def test_null_pointers_rejected():
+    import long_context_sparse_mask_amd as hs
+    assert _mask(_desc(), ptrs=(None, FAKE, FAKE, FAKE)) == ERR_NULL
+    assert hs.lib.hip_mask_estimate(None, FAKE, FAKE, 2048, 64, 1, FAKE, FAKE, None, 0, None) == ERR_NULL
+    d = _desc()
+    rc = hs.lib.hip_sparse_attn(C.byref(d), FAKE, FAKE, None, FAKE, FAKE, 2048, 64, 1, FAKE,
+                                FAKE, 1 << 30, None)
+    assert rc == ERR_NULL
+
+
+def test_workspace_query_and_undersized_workspace():
+    import long_context_sparse_mask_amd as hs
+    d = _desc(B=4, T=131072, T_cap=131072)
+    need = hs.lib.hipsa_workspace_bytes(C.byref(d), 2048, 64, 1)
+    # 32 problems x 32 splits of 64 tokens x 4 heads x (d + 2) floats
+    assert need == 32 * 32 * 4 * 130 * 4
+    rc = hs.lib.hip_sparse_attn(C.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 2048, 64, 1, FAKE,
+                                FAKE, need - 1, None)
+    assert rc == ERR_WS and "too small" in hs.lib.hipsa_last_error().decode()
+    bad = _desc(Hq=31)
+    assert hs.lib.hipsa_workspace_bytes(C.byref(bad), 2048, 64, 1) == hs.SIZE_MAX
+
+
+def test_empty_problem_is_a_no_op():
+    import long_context_sparse_mask_amd as hs
+    # B = 0 or Tq = 0: OK without reading any pointer (NULLs are fine)
+    for d in (_desc(B=0), _desc(Tq=0)):
+        assert _mask(d, ptrs=(None, None, None, None)) == 0
+        assert hs.lib.hip_sparse_attn(C.byref(d), None, None, None, None, None, 2048, 64, 1, None,
+                                      None, 0, None) == 0
+        assert hs.lib.hipsa_workspace_bytes(C.byref(d), 2048, 64, 1) == 0
+
+
+def test_product_path_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "long_context_sparse_mask_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                txt = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in txt.lower(), os.path.join(dirpath, f)
+    # and the binding refuses to load without the HIP library
+    code = ("import os, sys; sys.path.insert(0, %r); import long_context_sparse_mask_amd as m; "
+            "print(m.LIB_PATH)") % ROOT
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr

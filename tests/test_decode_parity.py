@@ -1,0 +1,145 @@
+"""GPU parity of the decode path (block_q = 1) against the CPU oracle.
+
+Every case runs hip_mask_estimate then hip_sparse_attn through the C ABI on
+seeded synthetic inputs and compares every problem and every output row with
+the oracle on the same bits.  The four decode workloads run at full size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth_inputs as si
+from parity_util import (ATOL, check_valid_lists, compare_attention, compare_masks, full_parity,
+                         run_gpu)
+
+pytestmark = pytest.mark.gpu
+
+_cache = {}
+
+
+def _inputs(w, T_cap=None):
+    key = (w, T_cap)
+    if key not in _cache:
+        _cache.clear()  # keep at most one large workload in host memory
+        _cache[key] = si.make_inputs(w, T_cap=T_cap)
+    return _cache[key]
+
+
+def _report(name, r):
+    print(f"[parity] {name}: problems={r['problems']} exempt={r['exempt']} "
+          f"max_err={r['max_err']:.3e}", flush=True)
+
+
+FULL = ["tiny_decode", "decode_32k", "decode_128k_b4", "decode_1m_needles"]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", FULL)
+def test_workload_full(name):
+    w = si.workload(name)
+    print(f"[case] {name} {w}", flush=True)
+    r = full_parity(_inputs(w), w)
+    _report(name, r)
+    assert r["exempt"] <= max(1, r["problems"] // 10)
+
+
+EDGE = {
+    # ragged last block, fp32, d=64
+    "f32_d64_ragged": dict(base="tiny_decode", T=1000),
+    # bf16 d=64, block_k=16, GQA 2, ragged
+    "bf16_d64_bk16_g2": dict(base="decode_32k", Hq=4, Hkv=2, d=64, T=5000, block_k=16, k=256),
+    # the largest K_b (512) with block_k=8
+    "bk8_kb512": dict(base="decode_32k", Hq=8, Hkv=2, T=20000, block_k=8, k=4096),
+    # block_k = 32, K_b = 7 (odd)
+    "bk32_kb7": dict(base="decode_32k", Hq=4, Hkv=1, T=9000, block_k=32, k=224),
+    # k >= T: dense attention over every block
+    "dense_k_ge_T": dict(base="decode_32k", Hq=4, Hkv=2, T=500, block_k=32, k=512),
+    # several query rows, each its own causal problem
+    "multi_row_causal": dict(base="decode_32k", Hq=8, Hkv=2, Tq=5, T=3000, k=512),
+    "multi_row_noncausal": dict(base="decode_32k", Hq=8, Hkv=2, Tq=3, T=3000, k=512, causal=0),
+    # group sizes 1, 8 and 16
+    "group1": dict(base="decode_32k", Hq=4, Hkv=4, T=4096, k=1024),
+    "group8": dict(base="decode_32k", Hq=16, Hkv=2, T=4096, k=1024),
+    "group16": dict(base="decode_32k", Hq=16, Hkv=1, T=4096, k=1024),
+    # fp32 at d=128, batch 3
+    "f32_d128_b3": dict(base="decode_32k", dtype="f32", B=3, Hq=4, Hkv=2, T=6000, k=1024),
+}
+
+
+@pytest.mark.parametrize("case", sorted(EDGE))
+def test_edge(case):
+    kw = dict(EDGE[case])
+    w = si.workload(kw.pop("base"), **kw)
+    print(f"[case] {case} {w}", flush=True)
+    r = full_parity(_inputs(w), w)
+    _report(case, r)
+    assert r["exempt"] <= max(1, r["problems"] // 10)
+
+
+def test_spare_capacity_rows():
+    w = si.workload("decode_32k", Hq=8, Hkv=2, T=3000, k=512)
+    x = _inputs(w, T_cap=3333)
+    # poison the unused rows: they must never be read
+    x["K"][:, :, w.T:] = 1e4
+    x["V"][:, :, w.T:] = 1e4
+    r = full_parity(x, w)
+    _report("spare_capacity", r)
+
+
+def test_zero_query_ties_exact():
+    """q = 0: every score is exactly 0 in any precision; the tie rule keeps the
+    lowest block ids and the output is the mean of V over them."""
+    w = si.workload("decode_32k", T=8192, k=1024)
+    x = dict(_inputs(w))
+    x["q"] = torch.zeros_like(x["q"])
+    idx, nnz, out = run_gpu(x, w)
+    assert (idx == np.arange(w.kb)).all() and (nnz == w.kb).all()
+    Vm = x["V"][:, :, :w.kb * w.block_k].double().mean(dim=2)  # [B,Hkv,d]
+    want = Vm.repeat_interleave(w.G, dim=1)[:, :, None, :].numpy()
+    compare_attention(out, want)
+
+
+def test_mask_scale_invariance_and_determinism():
+    w = si.workload("decode_32k", T=16384, k=1024)
+    x = _inputs(w)
+    a = run_gpu(x, w)
+    b = run_gpu(x, w)
+    assert (a[0] == b[0]).all() and (a[1] == b[1]).all()
+    assert torch.equal(a[2], b[2])
+    x2 = dict(x)
+    x2["q"] = x["q"] * 2  # exact in bf16
+    c = run_gpu(x2, w)
+    assert (a[0] == c[0]).all()
+
+
+def test_attention_with_oracle_indices_and_bad_lists():
+    """hip_sparse_attn on lists it did not make: the oracle's own, and lists with
+    out-of-range ids, negative ids and nnz outside [0, K_b]."""
+    import long_context_sparse_mask_amd as hs
+    w = si.workload("decode_32k", Hq=8, Hkv=2, T=4000, k=512)
+    x = _inputs(w)
+    kw = dict(T=w.T, k=w.k, block_k=w.block_k, block_q=w.block_q, causal=w.causal)
+    o_idx, o_nnz, _ = oracle.mask_all(x["q"], x["K"], **kw)
+    rng = np.random.default_rng(3)
+    bad_idx = o_idx.copy()
+    bad_idx[0, 0, 0, :3] = [-5, 10 ** 6, 63]       # 63 >= N_p = 63 -> skipped
+    bad_nnz = o_nnz.copy()
+    bad_nnz[0, 1, 0] = 99                          # clamped to K_b
+    bad_nnz[1 % w.B, 0, 0] = -3 if w.B > 1 else 0  # nothing to attend: zeros
+    bad_idx[0, 1, 0] = rng.permutation(62)[:w.kb]  # unsorted is fine
+    for I, N in ((o_idx, o_nnz), (bad_idx, bad_nnz)):
+        q, K, V = (x[n].cuda() for n in ("q", "K", "V"))
+        out = hs.hip_sparse_attn(q, K, V, torch.from_numpy(I).cuda(), torch.from_numpy(N).cuda(),
+                                 w.k, w.block_k, w.block_q, T=w.T)
+        ref = oracle.attn_all(x["q"], x["K"], x["V"], I, N, **kw)
+        compare_attention(out, ref)
+
+
+def test_empty_batch():
+    import long_context_sparse_mask_amd as hs
+    q = torch.zeros(0, 4, 1, 128, dtype=torch.bfloat16, device="cuda")
+    K = torch.zeros(0, 1, 256, 128, dtype=torch.bfloat16, device="cuda")
+    idx, nnz = hs.hip_mask_estimate(q, K, 128, 64, 1)
+    out = hs.hip_sparse_attn(q, K, K, idx, nnz, 128, 64, 1)
+    assert out.shape == q.shape
