@@ -45,7 +45,7 @@
  *    next synchronisation with the stream.
  *
  * Supported shapes: d in {64, 128}; block_k in {8, 16, 32, 64}; 1 <= K_b <= 512;
- * 1 <= Hq/Hkv <= 16; T <= T_cap < 2^31.  block_q = 1 (decode, and
+ * 1 <= Hq/Hkv <= 16; T <= T_cap <= 2^30.  block_q = 1 (decode, and
  * per-row problems for any Tq) works for both dtypes; block_q = 64 (chunked
  * prefill) requires HIPSA_BF16.
  */
@@ -75,7 +75,7 @@ typedef struct hipsa_desc {
   int64_t B;      /* batch entries (sequences)                                   */
   int64_t Hq;     /* query heads; a multiple of Hkv                              */
   int64_t Hkv;    /* key/value heads                                             */
-  int64_t Tq;     /* query rows per sequence (1 for decode); 1 <= Tq <= T        */
+  int64_t Tq;     /* query rows per sequence (1 for decode); 0 <= Tq <= T        */
   int64_t T;      /* valid keys per sequence, >= 1                               */
   int64_t T_cap;  /* allocated key rows per head (row stride of K and V), >= T   */
   int64_t d;      /* head dimension                                              */

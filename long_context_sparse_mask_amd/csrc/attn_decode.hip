@@ -37,60 +37,62 @@ __global__ __launch_bounds__(256) void attn_decode_split(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rg = tid / TPR, cs = tid % TPR;
   const int S = a.splits;
-  const int split = blockIdx.x % S;
-  const int64_t prob = blockIdx.x / S;
-  const int64_t i = prob % s.Tq;
-  const int64_t g = (prob / s.Tq) % s.Hkv;
-  const int64_t b = prob / (s.Tq * s.Hkv);
-  const int64_t Tp = s.causal ? s.T - s.Tq + i + 1 : s.T;
-  const int64_t Np = (Tp + s.bk - 1) / s.bk;
-  const int32_t cnt = min(max(a.nnz[prob], 0), s.Kb);
-  const int32_t *list = a.indices + prob * s.Kb;
-  const int bps = kTok / s.bk;  // blocks per split
+  const uint32_t split = blockIdx.x % (uint32_t)S;
+  const uint32_t prob = blockIdx.x / (uint32_t)S;
+  const uint32_t Tq = (uint32_t)s.Tq, Hkv = (uint32_t)s.Hkv;
+  const uint32_t i = prob % Tq, g = (prob / Tq) % Hkv, b = prob / (Tq * Hkv);
+  const int32_t Tp = s.causal ? (int32_t)(s.T - s.Tq + i + 1) : (int32_t)s.T;
+  const int32_t Np = (Tp + s.bk - 1) >> s.bk_shift;
+  const int32_t *list = a.indices + (int64_t)prob * s.Kb;
+  const int bps = kTok >> s.bk_shift;  // blocks per split
 
   __shared__ int32_t tok[kTok];
   __shared__ float pr[GMAX][kTok];
   __shared__ float red[RPP][HG][D];
   __shared__ float stat_m[GMAX], stat_l[GMAX];
 
+  // Issue the independent loads together: this lane's query slices, the
+  // count and the block id (one memory round trip instead of three).
+  float qv[GMAX][VEC];
+  {
+    const E *qbase =
+        reinterpret_cast<const E *>(a.q) + ((int64_t)(b * s.Hq + g * s.G) * Tq + i) * D;
+    uint4 r[GMAX];
+#pragma unroll
+    for (int h = 0; h < GMAX; h++)
+      r[h] = Vec<E>::raw(qbase + (int64_t)min(h, s.G - 1) * Tq * D + cs * VEC);
+#pragma unroll
+    for (int h = 0; h < GMAX; h++) Vec<E>::widen(r[h], h < s.G, qv[h]);
+  }
   if (tid < kTok) {
-    const int n = split * bps + tid / s.bk;
-    int32_t t = -1;
-    if (n < cnt) {
-      const int64_t blk = list[n];
-      if (blk >= 0 && blk < Np) {
-        const int64_t tt = blk * s.bk + tid % s.bk;
-        if (tt < Tp) t = (int32_t)tt;
-      }
-    }
-    tok[tid] = t;
+    const int n = split * bps + (tid >> s.bk_shift);
+    const int32_t cnt = a.nnz[prob];
+    const int32_t blk = list[n < s.Kb ? n : 0];
+    const bool okb = n < min(max(cnt, 0), s.Kb) && blk >= 0 && blk < Np;
+    const int32_t tt = okb ? (blk << s.bk_shift) + (tid & (s.bk - 1)) : 0;
+    tok[tid] = (okb && tt < Tp) ? tt : -1;
   }
   __syncthreads();
 
-  const int64_t kvoff = (b * s.Hkv + g) * s.T_cap * D;
+  const int64_t kvoff = (int64_t)(b * Hkv + g) * s.T_cap * D;
   const E *Kp = reinterpret_cast<const E *>(a.K) + kvoff;
   const E *Vp = reinterpret_cast<const E *>(a.V) + kvoff;
   float kv[RPT][VEC], vv[RPT][VEC];
+  {
+    uint4 rk[RPT], rv[RPT];
+    bool ok[RPT];
 #pragma unroll
-  for (int u = 0; u < RPT; u++) {
-    const int32_t t = tok[u * RPP + rg];
-    if (t >= 0) {
-      Vec<E>::load(Kp + (int64_t)t * D + cs * VEC, kv[u]);
-      Vec<E>::load(Vp + (int64_t)t * D + cs * VEC, vv[u]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < VEC; e++) { kv[u][e] = 0.f; vv[u][e] = 0.f; }
+    for (int u = 0; u < RPT; u++) {  // all K and V loads in flight together
+      const int32_t t = tok[u * RPP + rg];
+      ok[u] = t >= 0;
+      const int64_t row = (int64_t)(ok[u] ? t : 0) * D + cs * VEC;
+      rk[u] = Vec<E>::raw(Kp + row);
+      rv[u] = Vec<E>::raw(Vp + row);
     }
-  }
-  float qv[GMAX][VEC];
-  const E *qbase = reinterpret_cast<const E *>(a.q) + ((b * s.Hq + g * s.G) * s.Tq + i) * D;
 #pragma unroll
-  for (int h = 0; h < GMAX; h++) {
-    if (h < s.G) {
-      Vec<E>::load(qbase + (int64_t)h * s.Tq * D + cs * VEC, qv[h]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < VEC; e++) qv[h][e] = 0.f;
+    for (int u = 0; u < RPT; u++) {
+      Vec<E>::widen(rk[u], ok[u], kv[u]);
+      Vec<E>::widen(rv[u], ok[u], vv[u]);
     }
   }
 
@@ -122,7 +124,7 @@ __global__ __launch_bounds__(256) void attn_decode_split(AttnArgs a) {
   __syncthreads();
 
   // P.V, HG heads per LDS reduction pass
-  float *ws = a.ws + ((prob * S + split) * s.G) * (D + 2);
+  float *ws = a.ws + ((int64_t)(prob * S + split) * s.G) * (D + 2);
   for (int h0 = 0; h0 < s.G; h0 += HG) {
     float acc[HG][VEC];
 #pragma unroll
@@ -159,33 +161,63 @@ __global__ __launch_bounds__(256) void attn_decode_split(AttnArgs a) {
 }
 
 // Merge the splits of one (problem, query head): one workgroup of D lanes.
+// All loads of a phase are issued before any is used, so the merge costs two
+// memory round trips whatever the split count.
 template <typename E, int D>
 __global__ __launch_bounds__(128) void attn_decode_combine(AttnArgs a) {
+  constexpr int CH = 16;  // loads in flight per lane
   const Shape &s = a.s;
   const int S = a.splits;
-  const int64_t ph = blockIdx.x;
-  const int64_t prob = ph / s.G;
-  const int h = (int)(ph % s.G);
-  const int64_t i = prob % s.Tq;
-  const int64_t g = (prob / s.Tq) % s.Hkv;
-  const int64_t b = prob / (s.Tq * s.Hkv);
+  const uint32_t ph = blockIdx.x;
+  const uint32_t prob = ph / (uint32_t)s.G;
+  const int h = (int)(ph % (uint32_t)s.G);
+  const uint32_t Tq = (uint32_t)s.Tq, Hkv = (uint32_t)s.Hkv;
+  const uint32_t i = prob % Tq, g = (prob / Tq) % Hkv, b = prob / (Tq * Hkv);
   const int x = threadIdx.x;
-  if (x >= D) return;
-  const float *ws = a.ws + (prob * S * s.G + h) * (int64_t)(D + 2);
+  const float *ws = a.ws + ((int64_t)prob * S * s.G + h) * (int64_t)(D + 2);
   const int64_t stride = (int64_t)s.G * (D + 2);
+  __shared__ float wgt[kMaxKb * 64 / kTok];  // per-split weight exp(m_s - M), then l_s * weight
+  __shared__ float red[128];
+
+  // phase 1: every split's running max and sum
   float M = -INFINITY;
-  for (int sp = 0; sp < S; sp++) M = fmaxf(M, ws[sp * stride]);
-  float L = 0.f, acc = 0.f;
-  if (M != -INFINITY) {
-    for (int sp = 0; sp < S; sp++) {
-      const float m = ws[sp * stride];
-      const float w = (m == -INFINITY) ? 0.f : __expf(m - M);
-      L = fmaf(w, ws[sp * stride + 1], L);
-      acc = fmaf(w, ws[sp * stride + 2 + x], acc);
-    }
+  for (int sp = x; sp < S; sp += 128) M = fmaxf(M, ws[sp * stride]);
+  red[x] = M;
+  __syncthreads();
+  for (int w = 64; w >= 1; w >>= 1) {
+    if (x < w) red[x] = fmaxf(red[x], red[x + w]);
+    __syncthreads();
+  }
+  M = red[0];
+  __syncthreads();
+  float L = 0.f;
+  for (int sp = x; sp < S; sp += 128) {
+    const float m = ws[sp * stride];
+    const float w = (m == -INFINITY) ? 0.f : __expf(m - M);
+    wgt[sp] = w;
+    L = fmaf(w, ws[sp * stride + 1], L);
+  }
+  red[x] = L;
+  __syncthreads();
+  for (int w = 64; w >= 1; w >>= 1) {
+    if (x < w) red[x] += red[x + w];
+    __syncthreads();
+  }
+  L = red[0];
+  if (x >= D) return;
+
+  // phase 2: weighted sum of the unnormalised outputs, CH splits in flight
+  float acc = 0.f;
+  for (int sp0 = 0; sp0 < S; sp0 += CH) {
+    float o[CH];
+#pragma unroll
+    for (int u = 0; u < CH; u++) o[u] = sp0 + u < S ? ws[(sp0 + u) * stride + 2 + x] : 0.f;
+#pragma unroll
+    for (int u = 0; u < CH; u++)
+      if (sp0 + u < S) acc = fmaf(wgt[sp0 + u], o[u], acc);
   }
   const float v = L > 0.f ? acc / L : 0.f;
-  E *out = reinterpret_cast<E *>(a.out) + ((b * s.Hq + g * s.G + h) * s.Tq + i) * D;
+  E *out = reinterpret_cast<E *>(a.out) + ((int64_t)(b * s.Hq + g * s.G + h) * Tq + i) * D;
   store_elem(out + x, v);
 }
 

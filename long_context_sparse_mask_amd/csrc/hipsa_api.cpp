@@ -51,8 +51,8 @@ int check_shape(const hipsa_desc *d, int64_t k, int64_t block_k, int64_t block_q
   if (d->T < 1) return fail(HIPSA_ERR_SHAPE, "T=%lld must be >= 1", (long long)d->T);
   if (d->Tq > d->T)
     return fail(HIPSA_ERR_SHAPE, "Tq=%lld exceeds T=%lld", (long long)d->Tq, (long long)d->T);
-  if (d->T_cap < d->T || d->T_cap >= (int64_t(1) << 31))
-    return fail(HIPSA_ERR_SHAPE, "need T <= T_cap < 2^31 (T=%lld T_cap=%lld)", (long long)d->T,
+  if (d->T_cap < d->T || d->T_cap > (int64_t(1) << 30))
+    return fail(HIPSA_ERR_SHAPE, "need T <= T_cap <= 2^30 (T=%lld T_cap=%lld)", (long long)d->T,
                 (long long)d->T_cap);
   if (d->d != 64 && d->d != 128)
     return fail(HIPSA_ERR_SHAPE, "head dim d=%lld unsupported (64 or 128)", (long long)d->d);
@@ -76,6 +76,7 @@ int check_shape(const hipsa_desc *d, int64_t k, int64_t block_k, int64_t block_q
   s->G = (int32_t)(d->Hq / d->Hkv);
   s->Kb = (int32_t)(k / block_k);
   s->bk = (int32_t)block_k;
+  s->bk_shift = __builtin_ctzll((unsigned long long)block_k);
   s->bq = (int32_t)block_q;
   s->causal = d->causal != 0;
   s->dtype = d->dtype;

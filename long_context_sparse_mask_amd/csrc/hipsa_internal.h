@@ -15,6 +15,7 @@ constexpr int kMaxGroup = 16; // largest Hq / Hkv
 struct Shape {
   int64_t B, Hq, Hkv, Tq, T, T_cap, d;
   int32_t G, Kb, bk, bq, causal, dtype;
+  int32_t bk_shift;  // log2(bk)
   int64_t nqb;     // query blocks per (b, kv head)
   int64_t problems; // B * Hkv * nqb
 };
@@ -49,25 +50,41 @@ hipError_t launch_attn_prefill(const AttnArgs &a, hipStream_t st);
 
 // 16-byte vector loads widened to fp32.  bf16 widens exactly by a 16-bit shift.
 template <typename E> struct Vec;
+// raw() issues the load; widen() converts (and zeroes the slice when `keep`
+// is false), so a batch of loads can be issued without branches and all be
+// in flight at once.
 template <> struct Vec<float> {
   static constexpr int N = 4;
-  __device__ static inline void load(const float *p, float (&v)[4]) {
-    float4 x = *reinterpret_cast<const float4 *>(p);
-    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  __device__ static inline uint4 raw(const float *p) { return *reinterpret_cast<const uint4 *>(p); }
+  __device__ static inline void widen(uint4 x, bool keep, float (&v)[4]) {
+    v[0] = keep ? __uint_as_float(x.x) : 0.f;
+    v[1] = keep ? __uint_as_float(x.y) : 0.f;
+    v[2] = keep ? __uint_as_float(x.z) : 0.f;
+    v[3] = keep ? __uint_as_float(x.w) : 0.f;
   }
+  __device__ static inline void load(const float *p, float (&v)[4]) { widen(raw(p), true, v); }
 };
 template <> struct Vec<uint16_t> {
   static constexpr int N = 8;
-  __device__ static inline void load(const uint16_t *p, float (&v)[8]) {
-    uint4 x = *reinterpret_cast<const uint4 *>(p);
-    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  __device__ static inline uint4 raw(const uint16_t *p) {
+    return *reinterpret_cast<const uint4 *>(p);
+  }
+  __device__ static inline void widen(uint4 x, bool keep, float (&v)[8]) {
+    const uint32_t w[4] = {keep ? x.x : 0u, keep ? x.y : 0u, keep ? x.z : 0u, keep ? x.w : 0u};
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       v[2 * i] = __uint_as_float(w[i] << 16);
       v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
   }
+  __device__ static inline void load(const uint16_t *p, float (&v)[8]) { widen(raw(p), true, v); }
 };
+
+// MFMA operand / accumulator vectors (gfx950 bf16 matrix cores).
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+__device__ inline bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 // fp32 -> bf16 bits, round to nearest even (inputs here are finite).
 __device__ inline uint16_t f32_to_bf16(float f) {
@@ -88,20 +105,37 @@ __device__ inline uint64_t rank_key(float score, int32_t start) {
   return ((uint64_t)u << 32) | (uint32_t)(0x7fffffff - start);
 }
 
+// Cross-lane reductions.  DPP moves (quad permutes and row mirrors) run as
+// VALU operand modifiers, far cheaper than LDS-routed shuffles; only steps
+// that cross a 16-lane DPP row fall back to __shfl_xor.
+template <int CTRL> __device__ inline float dpp_mov(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xb1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4e;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- 7-i within 8 lanes
+constexpr int kDppMirror = 0x140;     // lane i <- 15-i within 16 lanes
+
+// Sum over aligned groups of W lanes (W a power of two <= 64); every lane of a
+// group ends with the group's sum.
 template <int W> __device__ inline float group_sum(float v) {
-#pragma unroll
-  for (int m = W / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  if (W >= 2) v += dpp_mov<kDppXor1>(v);
+  if (W >= 4) v += dpp_mov<kDppXor2>(v);
+  if (W >= 8) v += dpp_mov<kDppHalfMirror>(v);
+  if (W >= 16) v += dpp_mov<kDppMirror>(v);
+  if (W >= 32) v += __shfl_xor(v, 16, 64);
+  if (W >= 64) v += __shfl_xor(v, 32, 64);
   return v;
 }
 __device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-  return v;
+  v = fmaxf(v, dpp_mov<kDppXor1>(v));
+  v = fmaxf(v, dpp_mov<kDppXor2>(v));
+  v = fmaxf(v, dpp_mov<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_mov<kDppMirror>(v));
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  return fmaxf(v, __shfl_xor(v, 32, 64));
 }
-__device__ inline float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
-}
+__device__ inline float wave_sum(float v) { return group_sum<64>(v); }
 
 }  // namespace hipsa

@@ -8,43 +8,51 @@
 // Approach).
 //
 // One workgroup (256 threads, 4 wave64s) owns one problem (b, kv head g,
-// query row i) and runs every round.  Per round:
-//   1. each kept chunk of >= 2 blocks is split into two candidate slots,
-//      a one-block chunk fills one slot and leaves the other empty;
-//   2. candidate centre rows of K are read with coalesced 16-byte loads, a
-//      group of d/VEC consecutive lanes per row, all rows of the round in
-//      flight at once; lanes hold their slice of every query head of the
-//      group and reduce the G dot products with cross-lane adds, then take
-//      the max over heads;
-//   3. each candidate's rank is the number of keys above its own (key = score
-//      then lower start, both packed in one 64-bit integer), and the K_b best
-//      are written to the chunk list in rank order.
-// The round count is fixed by the data; rounds are serially dependent (the
-// next centres depend on this round's top-k), so this kernel is bound by the
-// latency of one dependent HBM gather per round, not by bandwidth.
+// query row i).  The candidate list (2*K_b slots; a one-block chunk fills one
+// slot of its pair and leaves the other empty) is double-buffered in LDS, so
+// a round is two phases separated by barriers:
+//   1. scoring.  Centre rows of K are read straight into matrix-core
+//      operands: for bf16 each wave scores 16 candidates per
+//      v_mfma_f32_16x16x32_bf16 tile against the query heads of the group
+//      (zero-padded to 16 rows), then takes the max over the valid head rows
+//      of the accumulator; fp32 inputs use 16-byte VALU dot products with DPP
+//      reductions instead.  Every load of a round is issued before any is used
+//      (an empty slot reads row 0 and discards it), so a round pays one memory
+//      latency;
+//   2. selection.  A candidate's rank is the number of keys above its own
+//      (key = score, then lower start, packed in one 64-bit integer); a
+//      kept candidate writes its two halves (or itself and an empty slot)
+//      straight into the other buffer, and a kept chunk wider than one block
+//      sets the flag that runs the next round.
+// Rounds are serially dependent (the next centres depend on this round's
+// top-k), so the kernel is bound by one dependent memory round trip plus the
+// round's LDS work per round, not by bandwidth.
+#include <type_traits>
+
 #include "hipsa_internal.h"
 
 namespace hipsa {
 namespace {
 
-template <typename E, int D, int GMAX>
-__global__ __launch_bounds__(256) void mask_decode_kernel(MaskArgs a) {
-  constexpr int VEC = Vec<E>::N;
-  constexpr int TPR = D / VEC;   // lanes per key row
-  constexpr int RPP = 256 / TPR; // rows per pass over the workgroup
-  constexpr int UNROLL = 8;      // rows in flight per lane
-  const Shape &s = a.s;
-  const int tid = threadIdx.x;
-  const int rg = tid / TPR, cs = tid % TPR;
+constexpr int kSpan = 16;  // keys compared per batch in the rank step
 
-  const int64_t prob = blockIdx.x;
-  const int64_t i = prob % s.Tq;
-  const int64_t g = (prob / s.Tq) % s.Hkv;
-  const int64_t b = prob / (s.Tq * s.Hkv);
-  const int64_t Tp = s.causal ? s.T - s.Tq + i + 1 : s.T;
-  const int32_t Np = (int32_t)((Tp + s.bk - 1) / s.bk);
+template <typename E, int D, int GMAX, int UNROLL>
+__global__ __launch_bounds__(256) void mask_decode_kernel(MaskArgs a) {
+  constexpr bool kMfma = std::is_same<E, uint16_t>::value;
+  constexpr int VEC = Vec<E>::N;
+  constexpr int TPR = D / VEC;   // VALU path: lanes per key row
+  constexpr int RPP = 256 / TPR; // VALU path: rows per pass
+  constexpr int KS = D / 32;     // MFMA path: k-steps of 32 over the head dim
+  const Shape &s = a.s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  const uint32_t prob = blockIdx.x;
+  const uint32_t Tq = (uint32_t)s.Tq, Hkv = (uint32_t)s.Hkv;
+  const uint32_t i = prob % Tq, g = (prob / Tq) % Hkv, b = prob / (Tq * Hkv);
+  const int32_t Tp = s.causal ? (int32_t)(s.T - s.Tq + i + 1) : (int32_t)s.T;
+  const int32_t Np = (Tp + s.bk - 1) >> s.bk_shift;
   const int32_t Kb = s.Kb;
-  int32_t *out = a.indices + prob * Kb;
+  int32_t *out = a.indices + (int64_t)prob * Kb;
 
   if (Np <= Kb) {  // the row sees few enough blocks to keep them all
     for (int j = tid; j < Kb; j += 256) out[j] = j < Np ? j : -1;
@@ -52,111 +60,216 @@ __global__ __launch_bounds__(256) void mask_decode_kernel(MaskArgs a) {
     return;
   }
 
-  __shared__ int32_t ca[kMaxKb], ce[kMaxKb];
-  __shared__ int32_t cand_a[2 * kMaxKb], cand_e[2 * kMaxKb];
-  __shared__ uint64_t key[2 * kMaxKb];
+  __shared__ int32_t cand_a[2][2 * kMaxKb], cand_e[2][2 * kMaxKb];
+  __shared__ uint64_t key[2 * kMaxKb + kSpan];
+  __shared__ int32_t rk[2 * kMaxKb];
+  __shared__ int32_t flag[2];
 
-  // This lane's slice of every query head in the group.
-  float qv[GMAX][VEC];
-  const E *qbase = reinterpret_cast<const E *>(a.q) + ((b * s.Hq + g * s.G) * s.Tq + i) * D;
+  const E *qbase = reinterpret_cast<const E *>(a.q) + ((int64_t)(b * s.Hq + g * s.G) * Tq + i) * D;
+  const E *Kbase = reinterpret_cast<const E *>(a.K) + (int64_t)(b * Hkv + g) * s.T_cap * D;
+
+  // Query operands, loaded once.  MFMA: lane l holds head l%16 (zero when
+  // past the group), dims 32*ks + 8*(l/16) .. +7.  VALU: every head, dims
+  // cs*VEC .. +VEC-1.
+  uint4 qa[kMfma ? KS : 1];
+  float qv[kMfma ? 1 : GMAX][VEC];
+  if constexpr (kMfma) {
+    const int h = lane & 15;
 #pragma unroll
-  for (int h = 0; h < GMAX; h++) {
-    if (h < s.G) {
-      Vec<E>::load(qbase + (int64_t)h * s.Tq * D + cs * VEC, qv[h]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < VEC; e++) qv[h][e] = 0.f;
+    for (int ks = 0; ks < KS; ks++) {
+      const uint4 r = Vec<E>::raw(qbase + (int64_t)min(h, s.G - 1) * Tq * D + 32 * ks + 8 * (lane >> 4));
+      qa[ks] = h < s.G ? r : make_uint4(0, 0, 0, 0);
     }
+  } else {
+    const int cs = tid % TPR;
+    uint4 r[GMAX];
+#pragma unroll
+    for (int h = 0; h < GMAX; h++)
+      r[h] = Vec<E>::raw(qbase + (int64_t)min(h, s.G - 1) * Tq * D + cs * VEC);
+#pragma unroll
+    for (int h = 0; h < GMAX; h++) Vec<E>::widen(r[h], h < s.G, qv[h]);
   }
-  const E *Kbase = reinterpret_cast<const E *>(a.K) + (b * s.Hkv + g) * s.T_cap * D;
-
-  for (int c = tid; c < Kb; c += 256) {  // initial uniform partition
-    ca[c] = (int32_t)((int64_t)c * Np / Kb);
-    ce[c] = (int32_t)((int64_t)(c + 1) * Np / Kb);
-  }
-  __syncthreads();
 
   const int n = 2 * Kb;
-  for (;;) {
-    int wide = 0;
-    for (int c = tid; c < Kb; c += 256) wide |= (ce[c] - ca[c] >= 2);
-    if (!__syncthreads_or(wide)) break;
+  for (int c = tid; c < Kb; c += 256) {  // halves of the uniform initial partition
+    const int32_t lo = (int32_t)((double)c * Np / Kb), hi = (int32_t)((double)(c + 1) * Np / Kb);
+    const bool split = hi - lo >= 2;
+    const int32_t m = lo + (hi - lo) / 2;
+    cand_a[0][2 * c] = lo;
+    cand_e[0][2 * c] = split ? m : hi;
+    cand_a[0][2 * c + 1] = split ? m : -1;
+    cand_e[0][2 * c + 1] = split ? hi : -1;
+  }
+  if (tid < kSpan) key[n + tid] = 0;  // padding read by the rank batches
+  if (tid == 0) flag[0] = 1;          // N_p > K_b: the first round always runs
+  __syncthreads();
 
-    for (int c = tid; c < Kb; c += 256) {  // halve every chunk
+  int cur = 0;
+  for (int round = 0;; round++, cur ^= 1) {
+    if (!flag[round & 1]) break;  // uniform: read after a barrier
+    if (tid == 0) flag[(round + 1) & 1] = 0;  // its last readers are two barriers back
+    const int32_t *ca = cand_a[cur], *ce = cand_e[cur];
+
+    // ---- 1. scoring
+    if constexpr (kMfma) {
+      const int ntile = (n + 15) / 16;
+      for (int t0 = wave; t0 < ntile; t0 += 4 * UNROLL) {
+        uint4 kr[UNROLL][KS];
+        bool live[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; u++) {
+          const int c = 16 * (t0 + 4 * u) + (lane & 15);
+          const int cc = c < n ? c : 0;
+          const int32_t lo_b = ca[cc], hi_b = ce[cc];
+          live[u] = c < n && lo_b >= 0;
+          const int32_t lo = lo_b << s.bk_shift, hi = min(hi_b << s.bk_shift, Tp);
+          const int32_t t = live[u] ? (lo + hi) >> 1 : 0;  // centre token (upper middle)
+#pragma unroll
+          for (int ks = 0; ks < KS; ks++)
+            kr[u][ks] = Vec<E>::raw(Kbase + (int64_t)t * D + 32 * ks + 8 * (lane >> 4));
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; u++) {
+          const int c = 16 * (t0 + 4 * u) + (lane & 15);
+          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ks++)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[ks]), as_bf16x8(kr[u][ks]),
+                                                          acc, 0, 0, 0);
+          // acc[r] = score of head 4*(lane/16)+r for candidate lane%16
+          float best = -INFINITY;
+#pragma unroll
+          for (int r = 0; r < 4; r++)
+            if (4 * (lane >> 4) + r < s.G) best = fmaxf(best, acc[r]);
+          if (GMAX > 4) best = fmaxf(best, __shfl_xor(best, 16, 64));
+          if (GMAX > 8) best = fmaxf(best, __shfl_xor(best, 32, 64));
+          if (lane < 16 && c < n) key[c] = live[u] ? rank_key(best, ca[c]) : 0ull;
+        }
+      }
+    } else {
+      const int rg = tid / TPR, cs = tid % TPR;
+      for (int base = 0; base < n; base += RPP * UNROLL) {
+        uint4 raw[UNROLL];
+        bool live[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; u++) {
+          const int c = base + u * RPP + rg;
+          const int cc = c < n ? c : 0;
+          const int32_t lo_b = ca[cc], hi_b = ce[cc];
+          live[u] = c < n && lo_b >= 0;
+          const int32_t lo = lo_b << s.bk_shift, hi = min(hi_b << s.bk_shift, Tp);
+          const int32_t t = live[u] ? (lo + hi) >> 1 : 0;  // centre token (upper middle)
+          raw[u] = Vec<E>::raw(Kbase + (int64_t)t * D + cs * VEC);
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; u++) {
+          const int c = base + u * RPP + rg;
+          float kv[VEC];
+          Vec<E>::widen(raw[u], live[u], kv);
+          float best = -INFINITY;
+#pragma unroll
+          for (int h = 0; h < GMAX; h++) {
+            float p = 0.f;
+#pragma unroll
+            for (int e = 0; e < VEC; e++) p = fmaf(qv[h][e], kv[e], p);
+            p = group_sum<TPR>(p);
+            if (h < s.G) best = fmaxf(best, p);
+          }
+          if (cs == 0 && c < n) key[c] = live[u] ? rank_key(best, ca[c]) : 0ull;
+        }
+      }
+    }
+    if (n > 256)
+      for (int c = tid; c < n; c += 256) rk[c] = 0;
+    __syncthreads();
+
+    // ---- 2. selection: rank = number of keys above; the K_b best write
+    // their halves into the other buffer.
+    int32_t *na = cand_a[cur ^ 1], *ne = cand_e[cur ^ 1];
+    auto emit = [&](int c, int r) {
       const int32_t lo = ca[c], hi = ce[c];
-      if (hi - lo >= 2) {
-        const int32_t m = lo + (hi - lo) / 2;
-        cand_a[2 * c] = lo; cand_e[2 * c] = m;
-        cand_a[2 * c + 1] = m; cand_e[2 * c + 1] = hi;
-      } else {
-        cand_a[2 * c] = lo; cand_e[2 * c] = hi;
-        cand_a[2 * c + 1] = -1; cand_e[2 * c + 1] = -1;
-      }
-    }
-    __syncthreads();
-
-    for (int base = 0; base < n; base += RPP * UNROLL) {  // score by centre keys
-      float kv[UNROLL][VEC];
-      bool live[UNROLL];
+      const bool split = hi - lo >= 2;
+      const int32_t m = lo + (hi - lo) / 2;
+      na[2 * r] = lo;
+      ne[2 * r] = split ? m : hi;
+      na[2 * r + 1] = split ? m : -1;
+      ne[2 * r + 1] = split ? hi : -1;
+      if (split) flag[(round + 1) & 1] = 1;
+    };
+    if (n <= 256) {
+      if (tid < n) {
+        const uint64_t kc = key[tid];
+        int r = 0;
+        for (int j0 = 0; j0 < n; j0 += kSpan) {
+          uint64_t kk[kSpan];
 #pragma unroll
-      for (int u = 0; u < UNROLL; u++) {
-        const int c = base + u * RPP + rg;
-        live[u] = c < n && cand_a[c] >= 0;
-        if (live[u]) {
-          const int64_t lo = (int64_t)cand_a[c] * s.bk;
-          const int64_t hi = min((int64_t)cand_e[c] * s.bk, Tp);
-          const int64_t t = (lo + hi) / 2;  // centre token (upper middle)
-          Vec<E>::load(Kbase + t * D + cs * VEC, kv[u]);
-        } else {
+          for (int u = 0; u < kSpan; u++) kk[u] = key[j0 + u];
 #pragma unroll
-          for (int e = 0; e < VEC; e++) kv[u][e] = 0.f;
+          for (int u = 0; u < kSpan; u++) r += kk[u] > kc;
         }
+        if (kc != 0 && r < Kb) emit(tid, r);
       }
+    } else {  // large K_b: several lanes per candidate, counts summed in LDS
+      const int parts = (n + kSpan - 1) / kSpan;
+      for (int t = tid; t < n * parts; t += 256) {
+        const int c = t % n, j0 = (t / n) * kSpan;
+        const uint64_t kc = key[c];
+        uint64_t kk[kSpan];
 #pragma unroll
-      for (int u = 0; u < UNROLL; u++) {
-        const int c = base + u * RPP + rg;
-        float best = -INFINITY;
+        for (int u = 0; u < kSpan; u++) kk[u] = key[j0 + u];
+        int r = 0;
 #pragma unroll
-        for (int h = 0; h < GMAX; h++) {
-          float p = 0.f;
-#pragma unroll
-          for (int e = 0; e < VEC; e++) p = fmaf(qv[h][e], kv[u][e], p);
-          p = group_sum<TPR>(p);
-          if (h < s.G) best = fmaxf(best, p);
-        }
-        if (cs == 0 && c < n) key[c] = live[u] ? rank_key(best, cand_a[c]) : 0ull;
+        for (int u = 0; u < kSpan; u++) r += kk[u] > kc;
+        if (r && kc) atomicAdd(&rk[c], r);
       }
-    }
-    __syncthreads();
-
-    for (int c = tid; c < n; c += 256) {  // global top-K_b by rank counting
-      const uint64_t kc = key[c];
-      if (kc == 0) continue;
-      int r = 0;
-      for (int j = 0; j < n; j++) r += key[j] > kc;
-      if (r < Kb) { ca[r] = cand_a[c]; ce[r] = cand_e[c]; }
+      __syncthreads();
+      for (int c = tid; c < n; c += 256)
+        if (key[c] != 0 && rk[c] < Kb) emit(c, rk[c]);
     }
     __syncthreads();
   }
 
-  for (int c = tid; c < Kb; c += 256) {  // ascending block ids
-    const int32_t v = ca[c];
+  // The kept one-block chunks sit at even slots of the current buffer;
+  // write them in ascending order (rank = number of smaller ids).
+  const int32_t *fin = cand_a[cur];
+  for (int c = tid; c < Kb; c += 256) {
+    const int32_t v = fin[2 * c];
     int r = 0;
-    for (int j = 0; j < Kb; j++) r += ca[j] < v;
+    for (int j0 = 0; j0 < Kb; j0 += kSpan) {
+      int32_t kk[kSpan];
+#pragma unroll
+      for (int u = 0; u < kSpan; u++) kk[u] = fin[2 * min(j0 + u, Kb - 1)];
+#pragma unroll
+      for (int u = 0; u < kSpan; u++) r += (j0 + u < Kb) && kk[u] < v;
+    }
     out[r] = v;
   }
   if (tid == 0) a.nnz[prob] = Kb;
 }
 
+template <typename E, int D, int GMAX>
+void launch_g(const MaskArgs &a, hipStream_t st) {
+  constexpr bool kMfma = std::is_same<E, uint16_t>::value;
+  constexpr int RPP = 256 / (D / Vec<E>::N);
+  const int n = 2 * a.s.Kb;
+  // loads in flight per lane per round: candidate tiles per wave (MFMA) or
+  // candidate rows per lane (VALU)
+  const int per = kMfma ? ((n + 15) / 16 + 3) / 4 : (n + RPP - 1) / RPP;
+  const dim3 grid((unsigned)a.s.problems), block(256);
+  if (per <= 1) hipLaunchKernelGGL((mask_decode_kernel<E, D, GMAX, 1>), grid, block, 0, st, a);
+  else if (per <= 2) hipLaunchKernelGGL((mask_decode_kernel<E, D, GMAX, 2>), grid, block, 0, st, a);
+  else if (per <= 4) hipLaunchKernelGGL((mask_decode_kernel<E, D, GMAX, 4>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((mask_decode_kernel<E, D, GMAX, 8>), grid, block, 0, st, a);
+}
+
 template <typename E, int D>
 hipError_t launch_d(const MaskArgs &a, hipStream_t st) {
-  const dim3 grid((unsigned)a.s.problems), block(256);
   const int G = a.s.G;
-  if (G <= 1) hipLaunchKernelGGL((mask_decode_kernel<E, D, 1>), grid, block, 0, st, a);
-  else if (G <= 2) hipLaunchKernelGGL((mask_decode_kernel<E, D, 2>), grid, block, 0, st, a);
-  else if (G <= 4) hipLaunchKernelGGL((mask_decode_kernel<E, D, 4>), grid, block, 0, st, a);
-  else if (G <= 8) hipLaunchKernelGGL((mask_decode_kernel<E, D, 8>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((mask_decode_kernel<E, D, 16>), grid, block, 0, st, a);
+  if (G <= 1) launch_g<E, D, 1>(a, st);
+  else if (G <= 2) launch_g<E, D, 2>(a, st);
+  else if (G <= 4) launch_g<E, D, 4>(a, st);
+  else if (G <= 8) launch_g<E, D, 8>(a, st);
+  else launch_g<E, D, 16>(a, st);
   return hipGetLastError();
 }
 

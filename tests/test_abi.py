@@ -61,7 +61,7 @@ ERR_NULL, ERR_SHAPE, ERR_BLOCK, ERR_DTYPE, ERR_WS = -1, -2, -3, -4, -5
     (dict(T=0, T_cap=0), 2048, 64, 1, ERR_SHAPE),
     (dict(Tq=5, T=4, T_cap=4), 64, 64, 1, ERR_SHAPE),
     (dict(T_cap=100), 2048, 64, 1, ERR_SHAPE),      # T > T_cap
-    (dict(T_cap=1 << 31), 2048, 64, 1, ERR_SHAPE),
+    (dict(T_cap=(1 << 30) + 1), 2048, 64, 1, ERR_SHAPE),
     (dict(d=96), 2048, 64, 1, ERR_SHAPE),
     (dict(dtype=7), 2048, 64, 1, ERR_DTYPE),
     (dict(), 2048, 48, 1, ERR_BLOCK),               # block_k not a power of two
@@ -119,8 +119,14 @@ def test_product_path_never_touches_the_oracle():
             if f.endswith((".py", ".hip", ".cpp", ".h")):
                 txt = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in txt.lower(), os.path.join(dirpath, f)
-    # and the binding refuses to load without the HIP library
-    code = ("import os, sys; sys.path.insert(0, %r); import long_context_sparse_mask_amd as m; "
-            "print(m.LIB_PATH)") % ROOT
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """A copy of the binding beside no libhipsa.so must refuse to import (no fallback)."""
+    import shutil
+    pkg = tmp_path / "long_context_sparse_mask_amd"
+    pkg.mkdir()
+    shutil.copy(os.path.join(ROOT, "long_context_sparse_mask_amd", "__init__.py"), pkg)
+    code = "import sys; sys.path.insert(0, %r); import long_context_sparse_mask_amd" % str(tmp_path)
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True)
-    assert r.returncode == 0, r.stderr
+    assert r.returncode != 0 and "not built" in r.stderr
