@@ -30,11 +30,10 @@
 #include <type_traits>
 
 #include "hipsa_internal.h"
+#include "mask_select.h"
 
 namespace hipsa {
 namespace {
-
-constexpr int kSpan = 16;  // keys compared per batch in the rank step
 
 template <typename E, int D, int GMAX, int UNROLL>
 __global__ __launch_bounds__(256) void mask_decode_kernel(MaskArgs a) {
@@ -91,15 +90,7 @@ __global__ __launch_bounds__(256) void mask_decode_kernel(MaskArgs a) {
   }
 
   const int n = 2 * Kb;
-  for (int c = tid; c < Kb; c += 256) {  // halves of the uniform initial partition
-    const int32_t lo = (int32_t)((double)c * Np / Kb), hi = (int32_t)((double)(c + 1) * Np / Kb);
-    const bool split = hi - lo >= 2;
-    const int32_t m = lo + (hi - lo) / 2;
-    cand_a[0][2 * c] = lo;
-    cand_e[0][2 * c] = split ? m : hi;
-    cand_a[0][2 * c + 1] = split ? m : -1;
-    cand_e[0][2 * c + 1] = split ? hi : -1;
-  }
+  initial_candidates(Np, Kb, cand_a[0], cand_e[0]);
   if (tid < kSpan) key[n + tid] = 0;  // padding read by the rank batches
   if (tid == 0) flag[0] = 1;          // N_p > K_b: the first round always runs
   __syncthreads();
@@ -179,71 +170,15 @@ __global__ __launch_bounds__(256) void mask_decode_kernel(MaskArgs a) {
         }
       }
     }
-    if (n > 256)
-      for (int c = tid; c < n; c += 256) rk[c] = 0;
     __syncthreads();
 
-    // ---- 2. selection: rank = number of keys above; the K_b best write
-    // their halves into the other buffer.
-    int32_t *na = cand_a[cur ^ 1], *ne = cand_e[cur ^ 1];
-    auto emit = [&](int c, int r) {
-      const int32_t lo = ca[c], hi = ce[c];
-      const bool split = hi - lo >= 2;
-      const int32_t m = lo + (hi - lo) / 2;
-      na[2 * r] = lo;
-      ne[2 * r] = split ? m : hi;
-      na[2 * r + 1] = split ? m : -1;
-      ne[2 * r + 1] = split ? hi : -1;
-      if (split) flag[(round + 1) & 1] = 1;
-    };
-    if (n <= 256) {
-      if (tid < n) {
-        const uint64_t kc = key[tid];
-        int r = 0;
-        for (int j0 = 0; j0 < n; j0 += kSpan) {
-          uint64_t kk[kSpan];
-#pragma unroll
-          for (int u = 0; u < kSpan; u++) kk[u] = key[j0 + u];
-#pragma unroll
-          for (int u = 0; u < kSpan; u++) r += kk[u] > kc;
-        }
-        if (kc != 0 && r < Kb) emit(tid, r);
-      }
-    } else {  // large K_b: several lanes per candidate, counts summed in LDS
-      const int parts = (n + kSpan - 1) / kSpan;
-      for (int t = tid; t < n * parts; t += 256) {
-        const int c = t % n, j0 = (t / n) * kSpan;
-        const uint64_t kc = key[c];
-        uint64_t kk[kSpan];
-#pragma unroll
-        for (int u = 0; u < kSpan; u++) kk[u] = key[j0 + u];
-        int r = 0;
-#pragma unroll
-        for (int u = 0; u < kSpan; u++) r += kk[u] > kc;
-        if (r && kc) atomicAdd(&rk[c], r);
-      }
-      __syncthreads();
-      for (int c = tid; c < n; c += 256)
-        if (key[c] != 0 && rk[c] < Kb) emit(c, rk[c]);
-    }
+    // ---- 2. selection: the K_b best write their halves into the other buffer
+    select_top(ca, ce, key, rk, n, Kb, cand_a[cur ^ 1], cand_e[cur ^ 1], &flag[(round + 1) & 1]);
     __syncthreads();
   }
 
-  // The kept one-block chunks sit at even slots of the current buffer;
-  // write them in ascending order (rank = number of smaller ids).
-  const int32_t *fin = cand_a[cur];
-  for (int c = tid; c < Kb; c += 256) {
-    const int32_t v = fin[2 * c];
-    int r = 0;
-    for (int j0 = 0; j0 < Kb; j0 += kSpan) {
-      int32_t kk[kSpan];
-#pragma unroll
-      for (int u = 0; u < kSpan; u++) kk[u] = fin[2 * min(j0 + u, Kb - 1)];
-#pragma unroll
-      for (int u = 0; u < kSpan; u++) r += (j0 + u < Kb) && kk[u] < v;
-    }
-    out[r] = v;
-  }
+  // the kept one-block chunks sit at the even slots of the current buffer
+  write_ascending(cand_a[cur], Kb, out);
   if (tid == 0) a.nnz[prob] = Kb;
 }
 

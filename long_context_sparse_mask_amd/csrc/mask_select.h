@@ -1,0 +1,105 @@
+// Selection step of the hierarchical top-k search, shared by the per-row
+// (decode) and per-query-block (prefill) mask kernels.
+//
+// Rebuttal page "A Training-free Sub-quadratic Cost Transformer Model Serving
+// Framework With Hierarchically Pruned Attention", reviewer RsGC, Q2, step 4:
+// keep the k most important chunks of all 2k candidates, then split them
+// again.  Candidates live in LDS as (start, end) block ranges, double
+// buffered; an empty slot has start -1 and key 0.  A candidate's key packs
+// its score (IEEE order mapped onto unsigned order) above the complement of
+// its start, so a larger key ranks first and equal scores prefer the lower
+// start.
+#pragma once
+
+#include "hipsa_internal.h"
+
+namespace hipsa {
+
+constexpr int kSpan = 16;  // keys compared per batch of LDS reads
+
+// Ranks the n candidates of buffer (ca, ce) by key and writes the halves of
+// the K_b best into buffer (na, ne) at slots 2*rank and 2*rank+1 (a one-block
+// chunk is copied to 2*rank with an empty slot after it).  Sets *more when a
+// kept chunk still spans several blocks.  `key` must hold n valid entries
+// followed by kSpan zeros; `rk` is n ints of scratch (used when n > 256).
+// Called by all 256 threads; contains barriers only when n > 256.
+__device__ inline void select_top(const int32_t *ca, const int32_t *ce, const uint64_t *key,
+                                  int32_t *rk, int n, int Kb, int32_t *na, int32_t *ne,
+                                  int32_t *more) {
+  const int tid = threadIdx.x;
+  auto emit = [&](int c, int r) {
+    const int32_t lo = ca[c], hi = ce[c];
+    const bool split = hi - lo >= 2;
+    const int32_t m = lo + (hi - lo) / 2;
+    na[2 * r] = lo;
+    ne[2 * r] = split ? m : hi;
+    na[2 * r + 1] = split ? m : -1;
+    ne[2 * r + 1] = split ? hi : -1;
+    if (split) *more = 1;
+  };
+  if (n <= 256) {
+    if (tid < n) {
+      const uint64_t kc = key[tid];
+      int r = 0;
+      for (int j0 = 0; j0 < n; j0 += kSpan) {
+        uint64_t kk[kSpan];
+#pragma unroll
+        for (int u = 0; u < kSpan; u++) kk[u] = key[j0 + u];
+#pragma unroll
+        for (int u = 0; u < kSpan; u++) r += kk[u] > kc;
+      }
+      if (kc != 0 && r < Kb) emit(tid, r);
+    }
+  } else {  // large K_b: several lanes per candidate, counts summed in LDS
+    for (int c = tid; c < n; c += 256) rk[c] = 0;
+    __syncthreads();
+    const int parts = (n + kSpan - 1) / kSpan;
+    for (int t = tid; t < n * parts; t += 256) {
+      const int c = t % n, j0 = (t / n) * kSpan;
+      const uint64_t kc = key[c];
+      uint64_t kk[kSpan];
+#pragma unroll
+      for (int u = 0; u < kSpan; u++) kk[u] = key[j0 + u];
+      int r = 0;
+#pragma unroll
+      for (int u = 0; u < kSpan; u++) r += kk[u] > kc;
+      if (r && kc) atomicAdd(&rk[c], r);
+    }
+    __syncthreads();
+    for (int c = tid; c < n; c += 256)
+      if (key[c] != 0 && rk[c] < Kb) emit(c, rk[c]);
+  }
+}
+
+// The K_b kept one-block chunks sit at the even slots of `fin`; writes their
+// block ids to out[0..K_b) in ascending order.
+__device__ inline void write_ascending(const int32_t *fin, int Kb, int32_t *out) {
+  for (int c = threadIdx.x; c < Kb; c += 256) {
+    const int32_t v = fin[2 * c];
+    int r = 0;
+    for (int j0 = 0; j0 < Kb; j0 += kSpan) {
+      int32_t kk[kSpan];
+#pragma unroll
+      for (int u = 0; u < kSpan; u++) kk[u] = fin[2 * min(j0 + u, Kb - 1)];
+#pragma unroll
+      for (int u = 0; u < kSpan; u++) r += (j0 + u < Kb) && kk[u] < v;
+    }
+    out[r] = v;
+  }
+}
+
+// Candidate slots 2c, 2c+1 from the halves of initial chunk c of the uniform
+// partition [floor(c*N_p/K_b), floor((c+1)*N_p/K_b)) (exact in double).
+__device__ inline void initial_candidates(int32_t Np, int Kb, int32_t *ca, int32_t *ce) {
+  for (int c = threadIdx.x; c < Kb; c += 256) {
+    const int32_t lo = (int32_t)((double)c * Np / Kb), hi = (int32_t)((double)(c + 1) * Np / Kb);
+    const bool split = hi - lo >= 2;
+    const int32_t m = lo + (hi - lo) / 2;
+    ca[2 * c] = lo;
+    ce[2 * c] = split ? m : hi;
+    ca[2 * c + 1] = split ? m : -1;
+    ce[2 * c + 1] = split ? hi : -1;
+  }
+}
+
+}  // namespace hipsa

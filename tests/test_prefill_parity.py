@@ -1,0 +1,120 @@
+"""GPU parity of the chunked-prefill path (block_q = 64, bf16) against the CPU oracle.
+
+Small cases compare every problem and every output row.  The 4096-token chunk
+at the end of a 32k sequence runs at full size in the bench's launch
+configuration and is compared on sampled query blocks (the oracle's search)
+and sampled output rows (the oracle's attention), which the oracle computes
+one at a time.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth_inputs as si
+from parity_util import (MARGIN, check_valid_lists, compare_attention, compare_masks, full_parity,
+                         run_gpu)
+
+pytestmark = pytest.mark.gpu
+
+
+def _report(name, r):
+    print(f"[parity] {name}: problems={r['problems']} exempt={r['exempt']} "
+          f"max_err={r['max_err']:.3e}", flush=True)
+
+
+SMALL = {
+    # several query blocks, causal, the last one ragged; T not a multiple of 64
+    "ragged_causal": dict(T=3000, Tq=200, Hq=8, Hkv=2, k=512),
+    # a chunk whose early query blocks see fewer than K_b blocks (dense rows)
+    "dense_early_blocks": dict(T=1100, Tq=1000, Hq=4, Hkv=1, k=512),
+    "bk8": dict(T=4096, Tq=128, Hq=4, Hkv=1, block_k=8, k=256),
+    "bk16": dict(T=4096, Tq=128, Hq=4, Hkv=1, block_k=16, k=256),
+    "bk32": dict(T=4096, Tq=192, Hq=4, Hkv=1, block_k=32, k=512),
+    "d64": dict(T=4096, Tq=128, Hq=8, Hkv=2, d=64, k=512),
+    "group1": dict(T=4096, Tq=128, Hq=2, Hkv=2, k=512),
+    "group2": dict(T=4096, Tq=128, Hq=4, Hkv=2, k=512),
+    "group8": dict(T=4096, Tq=128, Hq=8, Hkv=1, k=512),
+    "group16": dict(T=4096, Tq=64, Hq=16, Hkv=1, k=512),
+    "noncausal": dict(T=4096, Tq=130, Hq=4, Hkv=1, k=512, causal=0),
+    "batch2": dict(B=2, T=2048, Tq=128, Hq=4, Hkv=2, k=512),
+    "kb_odd": dict(T=4096, Tq=128, Hq=4, Hkv=1, k=7 * 64),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SMALL))
+def test_small_full(case):
+    w = si.workload("prefill_32k_chunk4k", **SMALL[case])
+    print(f"[case] {case} {w}", flush=True)
+    x = si.make_inputs(w)
+    r = full_parity(x, w)
+    _report(case, r)
+    assert r["exempt"] <= max(1, r["problems"] // 10)
+
+
+def test_zero_query_ties_exact():
+    w = si.workload("prefill_32k_chunk4k", T=4096, Tq=128, Hq=4, Hkv=1, k=512)
+    x = dict(si.make_inputs(w))
+    x["q"] = torch.zeros_like(x["q"])
+    idx, nnz, out = run_gpu(x, w)
+    assert (idx == np.arange(w.kb)).all() and (nnz == w.kb).all()
+    kw = dict(T=w.T, k=w.k, block_k=w.block_k, block_q=w.block_q, causal=w.causal)
+    ref = oracle.attn_all(x["q"], x["K"], x["V"], idx, nnz, **kw)
+    compare_attention(out, ref)
+
+
+def test_attention_with_oracle_indices():
+    import long_context_sparse_mask_amd as hs
+    w = si.workload("prefill_32k_chunk4k", T=3000, Tq=256, Hq=8, Hkv=2, k=512)
+    x = si.make_inputs(w)
+    kw = dict(T=w.T, k=w.k, block_k=w.block_k, block_q=w.block_q, causal=w.causal)
+    o_idx, o_nnz, _ = oracle.mask_all(x["q"], x["K"], **kw)
+    o_idx = o_idx.copy()
+    o_nnz = o_nnz.copy()
+    o_idx[0, 0, 0, :2] = [-1, 10 ** 6]  # out-of-range ids are skipped
+    o_nnz[0, 1, 1] = 0                  # nothing to attend: zeros
+    q, K, V = (x[n].cuda() for n in ("q", "K", "V"))
+    out = hs.hip_sparse_attn(q, K, V, torch.from_numpy(o_idx).cuda(), torch.from_numpy(o_nnz).cuda(),
+                             w.k, w.block_k, w.block_q, T=w.T)
+    ref = oracle.attn_all(x["q"], x["K"], x["V"], o_idx, o_nnz, **kw)
+    compare_attention(out, ref)
+
+
+def test_determinism():
+    w = si.workload("prefill_32k_chunk4k", T=4096, Tq=256, Hq=8, Hkv=2, k=512)
+    x = si.make_inputs(w)
+    a = run_gpu(x, w)
+    b = run_gpu(x, w)
+    assert (a[0] == b[0]).all() and torch.equal(a[2], b[2])
+
+
+@pytest.mark.timeout(900)
+def test_full_size_chunk_sampled():
+    """The 4096-token chunk at the end of a 32k sequence, 32/8 heads, k=2048:
+    all index lists checked for validity; 24 query blocks against the
+    oracle's search; 96 output rows against the oracle's attention."""
+    w = si.workload("prefill_32k_chunk4k")
+    x = si.make_inputs(w)
+    idx, nnz, out = run_gpu(x, w)
+    check_valid_lists(idx, nnz, w)
+    kw = dict(T=w.T, k=w.k, block_k=w.block_k, block_q=w.block_q, causal=w.causal)
+    rng = np.random.default_rng(17)
+    probs = [(0, 0, 0), (0, w.Hkv - 1, w.nqb - 1)] + [
+        (0, int(rng.integers(w.Hkv)), int(rng.integers(w.nqb))) for _ in range(22)]
+    exempt = 0
+    for (b, g, qb) in probs:
+        r = oracle.mask_one(x["q"], x["K"], b, g, qb, **kw)
+        if r["margin"] < MARGIN:
+            exempt += 1
+            continue
+        assert r["nnz"] == nnz[b, g, qb]
+        assert (r["indices"] == idx[b, g, qb]).all(), (b, g, qb)
+    assert exempt <= 4
+    got = out.float().cpu().numpy()
+    err = 0.0
+    for _ in range(96):
+        h, i = int(rng.integers(w.Hq)), int(rng.integers(w.Tq))
+        ref = oracle.attn_row(x["q"], x["K"], x["V"], idx, nnz, 0, h, i, **kw)
+        err = max(err, float(np.abs(got[0, h, i] - ref).max()))
+    print(f"[parity] prefill_32k_chunk4k sampled: exempt={exempt}/24 max_err={err:.3e}", flush=True)
+    assert err <= 2e-2
