@@ -117,9 +117,10 @@ int hip_mask_estimate(const hipsa_desc *desc, const void *q, const void *K, int6
  * qb = i/block_q) with t < T_p and, when causal, t <= T - Tq + i.  Block ids
  * outside [0, N_p) are skipped, nnz is clamped to [0, K_b], and a row with no
  * visible token gets zeros.  indices/nnz are typically hip_mask_estimate's
- * output but may come from anywhere.  Needs a device workspace of at least
- * hipsa_workspace_bytes() bytes (split-K partial results); its contents need
- * no initialisation and are scratch after the call.
+ * output but may come from anywhere.  Decode (block_q == 1) needs a device
+ * workspace of at least hipsa_workspace_bytes() bytes for split partial
+ * results; its contents need no initialisation and are scratch after the
+ * call.  Calls sharing a workspace must not run concurrently.
  */
 int hip_sparse_attn(const hipsa_desc *desc, const void *q, const void *K, const void *V,
                     const int32_t *indices, const int32_t *nnz, int64_t k, int64_t block_k,

@@ -182,6 +182,178 @@ __global__ __launch_bounds__(256) void mask_decode_kernel(MaskArgs a) {
   if (tid == 0) a.nnz[prob] = Kb;
 }
 
+// Pipelined variant for bf16 and K_b <= 64 (the decode workloads).  The
+// children of every current candidate are a superset of the next round's
+// candidates, so in round r waves 1-3 load and score all 4*K_b children of
+// C_r on the matrix cores while wave 0 ranks C_r with the keys the other
+// waves produced in round r-1.  The dependent memory latency then overlaps
+// the selection instead of following it, and a round needs one barrier.
+// Keys of the next round's candidates are looked up through `srcs` (the
+// child slot that holds each candidate's key).
+constexpr int kPipeMaxKb = 64;
+
+template <int D, int GMAX, int TPW>
+__device__ inline void score_children(const uint16_t *Kbase, const uint4 *qa, int32_t Tp, int bk_shift,
+                                      int G, const int32_t *ca, const int32_t *ce, int nslot,
+                                      bool children, int wi, int nw, uint64_t *dst) {
+  constexpr int KS = D / 32;
+  const int lane = threadIdx.x & 63;
+  const int ntile = (nslot + 15) / 16;
+  for (int t0 = wi; t0 < ntile; t0 += nw * TPW) {
+    uint4 kr[TPW][KS];
+    bool live[TPW];
+    int32_t start[TPW];
+#pragma unroll
+    for (int u = 0; u < TPW; u++) {
+      const int cs = 16 * (t0 + nw * u) + (lane & 15);
+      // slot cs: a current candidate, or child (cs & 1) of current candidate cs >> 1
+      const int c = children ? (cs >> 1) : cs;
+      const int cc = c < (children ? nslot / 2 : nslot) ? c : 0;
+      const int32_t plo = ca[cc], phi = ce[cc];
+      int32_t lo = plo, hi = phi;
+      bool ok = cs < nslot && plo >= 0;
+      if (children) {
+        const bool split = phi - plo >= 2;
+        const int32_t m = plo + (phi - plo) / 2;
+        const int j = cs & 1;
+        lo = (split && j) ? m : plo;
+        hi = (split && !j) ? m : phi;
+        ok = ok && (split || j == 0);
+      }
+      live[u] = ok;
+      start[u] = lo;
+      const int32_t tlo = lo << bk_shift, thi = min(hi << bk_shift, Tp);
+      const int32_t t = ok ? (tlo + thi) >> 1 : 0;  // centre token (upper middle)
+#pragma unroll
+      for (int ks = 0; ks < KS; ks++)
+        kr[u][ks] = *reinterpret_cast<const uint4 *>(Kbase + (int64_t)t * D + 32 * ks + 8 * (lane >> 4));
+    }
+#pragma unroll
+    for (int u = 0; u < TPW; u++) {
+      const int cs = 16 * (t0 + nw * u) + (lane & 15);
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ks++)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[ks]), as_bf16x8(kr[u][ks]), acc, 0, 0, 0);
+      float best = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; r++)
+        if (4 * (lane >> 4) + r < G) best = fmaxf(best, acc[r]);
+      if (GMAX > 4) best = fmaxf(best, __shfl_xor(best, 16, 64));
+      if (GMAX > 8) best = fmaxf(best, __shfl_xor(best, 32, 64));
+      if (lane < 16 && cs < nslot) dst[cs] = live[u] ? rank_key(best, start[u]) : 0ull;
+    }
+  }
+}
+
+template <int D, int GMAX, int TPW>
+__global__ __launch_bounds__(256) void mask_decode_pipe(MaskArgs a) {
+  constexpr int KS = D / 32;
+  const Shape &s = a.s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  const uint32_t prob = blockIdx.x;
+  const uint32_t Tq = (uint32_t)s.Tq, Hkv = (uint32_t)s.Hkv;
+  const uint32_t i = prob % Tq, g = (prob / Tq) % Hkv, b = prob / (Tq * Hkv);
+  const int32_t Tp = s.causal ? (int32_t)(s.T - s.Tq + i + 1) : (int32_t)s.T;
+  const int32_t Np = (Tp + s.bk - 1) >> s.bk_shift;
+  const int32_t Kb = s.Kb;
+  int32_t *out = a.indices + (int64_t)prob * Kb;
+
+  if (Np <= Kb) {
+    for (int j = tid; j < Kb; j += 256) out[j] = j < Np ? j : -1;
+    if (tid == 0) a.nnz[prob] = Np;
+    return;
+  }
+
+  __shared__ int32_t cand_a[2][2 * kPipeMaxKb], cand_e[2][2 * kPipeMaxKb];
+  __shared__ int32_t srcs[2][2 * kPipeMaxKb];
+  __shared__ uint64_t spec[2][4 * kPipeMaxKb];
+  __shared__ uint64_t key[2 * kPipeMaxKb + kSpan];
+  __shared__ int32_t flag[2];
+
+  const uint16_t *qbase = reinterpret_cast<const uint16_t *>(a.q) + ((int64_t)(b * s.Hq + g * s.G) * Tq + i) * D;
+  const uint16_t *Kbase = reinterpret_cast<const uint16_t *>(a.K) + (int64_t)(b * Hkv + g) * s.T_cap * D;
+  uint4 qa[KS];
+  {
+    const int h = lane & 15;
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) {
+      const uint4 r = *reinterpret_cast<const uint4 *>(qbase + (int64_t)min(h, s.G - 1) * Tq * D + 32 * ks + 8 * (lane >> 4));
+      qa[ks] = h < s.G ? r : make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  const int n = 2 * Kb;
+  initial_candidates(Np, Kb, cand_a[0], cand_e[0]);
+  for (int c = tid; c < n; c += 256) srcs[0][c] = c;
+  if (tid < kSpan) key[n + tid] = 0;
+  if (tid == 0) flag[0] = 1;  // N_p > K_b: the first round always runs
+  __syncthreads();
+  // keys of the first candidates (all waves), kept where round 0 looks them up
+  score_children<D, GMAX, TPW>(Kbase, qa, Tp, s.bk_shift, s.G, cand_a[0], cand_e[0], n, false,
+                               wave, 4, spec[1]);
+  __syncthreads();
+
+  int cur = 0;
+  for (int round = 0;; round++, cur ^= 1) {
+    if (!flag[round & 1]) break;  // uniform: read after a barrier
+    if (wave == 0) {
+      // gather this round's keys, rank them, emit the kept chunks' halves
+      if (lane == 0) flag[(round + 1) & 1] = 0;
+      const uint64_t *prev = spec[cur ^ 1];
+      for (int c = lane; c < n; c += 64) key[c] = prev[srcs[cur][c]];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int32_t *ca = cand_a[cur], *ce = cand_e[cur];
+      int32_t *na = cand_a[cur ^ 1], *ne = cand_e[cur ^ 1], *nsrc = srcs[cur ^ 1];
+      for (int c = lane; c < n; c += 64) {
+        const uint64_t kc = key[c];
+        int r = 0;
+        for (int j0 = 0; j0 < n; j0 += kSpan) {
+          uint64_t kk[kSpan];
+#pragma unroll
+          for (int u = 0; u < kSpan; u++) kk[u] = key[j0 + u];
+#pragma unroll
+          for (int u = 0; u < kSpan; u++) r += kk[u] > kc;
+        }
+        if (kc != 0 && r < Kb) {
+          const int32_t lo = ca[c], hi = ce[c];
+          const bool split = hi - lo >= 2;
+          const int32_t m = lo + (hi - lo) / 2;
+          na[2 * r] = lo;
+          ne[2 * r] = split ? m : hi;
+          na[2 * r + 1] = split ? m : -1;
+          ne[2 * r + 1] = split ? hi : -1;
+          nsrc[2 * r] = 2 * c;          // child slots of candidate c in this round's table
+          nsrc[2 * r + 1] = 2 * c + 1;
+          if (split) flag[(round + 1) & 1] = 1;
+        }
+      }
+    } else {
+      // speculative: score every child of every current candidate
+      score_children<D, GMAX, TPW>(Kbase, qa, Tp, s.bk_shift, s.G, cand_a[cur], cand_e[cur], 2 * n,
+                                   true, wave - 1, 3, spec[cur]);
+    }
+    __syncthreads();
+  }
+
+  write_ascending(cand_a[cur], Kb, out);
+  if (tid == 0) a.nnz[prob] = Kb;
+}
+
+template <int D, int GMAX>
+void launch_pipe(const MaskArgs &a, hipStream_t st) {
+  const int tiles = (4 * a.s.Kb + 15) / 16;  // child tiles per round, over 3 waves
+  const int per = (tiles + 2) / 3;
+  const dim3 grid((unsigned)a.s.problems), block(256);
+  if (per <= 1) hipLaunchKernelGGL((mask_decode_pipe<D, GMAX, 1>), grid, block, 0, st, a);
+  else if (per <= 2) hipLaunchKernelGGL((mask_decode_pipe<D, GMAX, 2>), grid, block, 0, st, a);
+  else if (per <= 4) hipLaunchKernelGGL((mask_decode_pipe<D, GMAX, 4>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((mask_decode_pipe<D, GMAX, 8>), grid, block, 0, st, a);
+}
+
 template <typename E, int D, int GMAX>
 void launch_g(const MaskArgs &a, hipStream_t st) {
   constexpr bool kMfma = std::is_same<E, uint16_t>::value;
@@ -200,6 +372,14 @@ void launch_g(const MaskArgs &a, hipStream_t st) {
 template <typename E, int D>
 hipError_t launch_d(const MaskArgs &a, hipStream_t st) {
   const int G = a.s.G;
+  if (std::is_same<E, uint16_t>::value && a.s.Kb <= kPipeMaxKb) {
+    if (G <= 1) launch_pipe<D, 1>(a, st);
+    else if (G <= 2) launch_pipe<D, 2>(a, st);
+    else if (G <= 4) launch_pipe<D, 4>(a, st);
+    else if (G <= 8) launch_pipe<D, 8>(a, st);
+    else launch_pipe<D, 16>(a, st);
+    return hipGetLastError();
+  }
   if (G <= 1) launch_g<E, D, 1>(a, st);
   else if (G <= 2) launch_g<E, D, 2>(a, st);
   else if (G <= 4) launch_g<E, D, 4>(a, st);

@@ -93,8 +93,8 @@ def test_workspace_query_and_undersized_workspace():
     import long_context_sparse_mask_amd as hs
     d = _desc(B=4, T=131072, T_cap=131072)
     need = hs.lib.hipsa_workspace_bytes(C.byref(d), 2048, 64, 1)
-    # 32 problems x 32 splits of 64 tokens x 4 heads x (d + 2) floats
-    assert need == 32 * 32 * 4 * 130 * 4
+    # 32 problems x 16 splits of 128 tokens x 4 heads x (d + 2) floats
+    assert need == 32 * 16 * 4 * 130 * 4
     rc = hs.lib.hip_sparse_attn(C.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 2048, 64, 1, FAKE,
                                 FAKE, need - 1, None)
     assert rc == ERR_WS and "too small" in hs.lib.hipsa_last_error().decode()
