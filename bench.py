@@ -86,6 +86,40 @@ def prefill_flops(w) -> dict:
     return {"mask": mask, "attn": attn, "total": mask + attn}
 
 
+# kernels behind each call, for matching the committed HBM counter summary
+CALL_KERNELS = {
+    ("decode", "hip_sparse_attn"): ("attn_decode_kernel", "attn_decode_combine"),
+    ("decode", "hip_mask_estimate"): ("mask_decode",),
+    ("prefill", "hip_sparse_attn"): ("attn_prefill_kernel",),
+    ("prefill", "hip_mask_estimate"): ("mask_prefill_kernel",),
+}
+
+
+def kernel_source_sha() -> str:
+    import hashlib
+    d = os.path.join(ROOT, "long_context_sparse_mask_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kind: str, call: str):
+    """HBM bytes per launch from profiles/hbm_traffic.md (FETCH_SIZE + WRITE_SIZE,
+    copy-calibrated), or None when the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+    try:
+        txt = open(path).read()
+        blob = json.loads(txt.split("```json", 1)[1].split("```", 1)[0])
+    except (OSError, IndexError, ValueError):
+        return None
+    if blob.get("source_sha") != kernel_source_sha():
+        return None
+    names = CALL_KERNELS[(kind, call)]
+    hits = [v["traffic_bytes"] for k, v in blob["kernels"].items() if k.startswith(names)]
+    return sum(hits) if hits else None
+
+
 def cpu_baseline(x, w, budget_s: float) -> dict:
     """The CPU oracle on the same seeded step, all host threads."""
     import oracle
@@ -255,7 +289,7 @@ def main():
         ach = byt / (t_ms * 1e-3) / 1e9
         line["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1),
                             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                            "traffic": None, "algorithmic_bytes": byt,
+                            "traffic": measured_traffic("decode", dom), "algorithmic_bytes": byt,
                             "launch_us": round(t_ms * 1e3, 3)}
         step_gbs = nb["step"] / (r["ms_per_step"] * 1e-3) / 1e9
         line["step_roofline"] = {"algorithmic_bytes": nb["step"], "achieved": round(step_gbs, 1),
@@ -275,7 +309,8 @@ def main():
         ach = f / (t_ms * 1e-3) / 1e12
         line["roofline"] = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2),
                             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                            "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                            "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
+                            "traffic": measured_traffic("prefill", dom),
                             "algorithmic_flops": f, "launch_us": round(t_ms * 1e3, 3)}
         line["step_roofline"] = {"algorithmic_flops": fl["total"], "achieved_tflops": round(tflops, 2),
                                  "mask_us": round(r["ms_mask"] * 1e3, 3),
