@@ -6,24 +6,25 @@
 // NLBm, W2).  Exact softmax over the listed blocks' visible tokens.
 //
 // Decode attention reads each selected K/V byte once (~4 flops per byte), so
-// it is bound by memory: the kernels keep many independent loads in flight
-// and add as few dependent round trips as possible.  The K_b*block_k selected
-// tokens of a problem are split over S workgroups of TOK tokens (TOK chosen
-// so the launch has >= 512 workgroups when it can).  A split workgroup:
-//   1. maps its TOK token slots to key rows (an invalid slot reads row 0 and
-//      is masked) and issues every query, K and V load of its slice at once.
-//      bf16 logits run on v_mfma_f32_16x16x32_bf16 (the group's query heads,
-//      zero-padded to 16 rows, against 16 key rows per tile read straight
-//      into the B operand); fp32 logits use 16-byte VALU dot products with
-//      DPP reductions;
-//   2. one wave per head takes the max and exponentials; P.V accumulates in
-//      fp32 on the VALU over coalesced V rows and is reduced across row
-//      groups once, through LDS;
-//   3. writes its (max, sum, unnormalised output) per head to the workspace.
-// A second kernel merges the S partials of each (problem, head) with
-// log-sum-exp weights and writes the output.  (Merging inside the split
-// kernel through a device-scope fence and an arrival counter measured
-// slower on gfx950: the fences serialise across workgroups.)
+// it is bound by memory.  The K_b*block_k selected tokens of a problem are
+// split over S workgroups of TOK tokens (TOK chosen so the launch has >= 512
+// workgroups when it can); each of the 4 waves of a split workgroup owns
+// TOK/4 token slots.  A wave maps its slots to key rows (an invalid slot
+// reads row 0 and is masked, so every load is issued unconditionally),
+// issues all of its query, K and V loads at once, and computes the softmax
+// statistics (max, sum) and the unnormalised P.V of its slots on its own.
+// The four waves are merged with log-sum-exp weights through LDS after one
+// barrier, and the workgroup writes (max, sum, output) per head to the
+// workspace.  A second kernel merges the S partials of each (problem, head)
+// and writes the output.  (Merging inside the split kernel through a
+// device-scope fence and an arrival counter measured slower on gfx950: the
+// fences serialise across workgroups.)
+//
+// After its loads land, a workgroup's remaining time is pure ALU work, which
+// sits in the kernel's tail, so the kernels keep it small: logits on the
+// matrix cores for bf16, no per-head tests inside unrolled loops (heads past
+// the group are computed and dropped), and no cross-lane reduction of the
+// outputs in the bf16 kernel.
 #include <type_traits>
 
 #include "hipsa_internal.h"
@@ -31,19 +32,24 @@
 namespace hipsa {
 namespace {
 
+// fp32 split workgroup (any dtype works; bf16 uses attn_decode_mfma).  A key
+// row is read by TPR = D/VEC lanes (16 bytes each); logits are VALU dot
+// products closed by DPP sums over the row's lanes, and P.V accumulates per
+// lane and is summed across the wave's row groups with DPP/permlane steps.
+// All GMAX heads are computed (the loads of heads past the group repeat the
+// last head); only the stores are limited to the group.
 template <typename E, int D, int GMAX, int TOK>
 __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
-  constexpr bool kMfma = std::is_same<E, uint16_t>::value;
   constexpr int VEC = Vec<E>::N;
-  constexpr int TPR = D / VEC;            // lanes per V row
-  constexpr int RPP = 256 / TPR;          // V rows per pass
-  constexpr int RPT = TOK / RPP;          // V rows per lane
-  constexpr int HG = GMAX < 4 ? GMAX : 4; // heads reduced per LDS pass
-  constexpr int KS = D / 32;              // MFMA k-steps
-  constexpr int KTW = TOK / 64;           // MFMA key tiles of 16 per wave
+  constexpr int TPR = D / VEC;            // lanes per key row (8, 16 or 32)
+  constexpr int RPW = 64 / TPR;           // rows per wave-wide load
+  constexpr int TPW = TOK / 4;            // token slots per wave
+  constexpr int RPL = TPW / RPW;          // K rows (and V rows) per lane
+  constexpr int HG = GMAX < 4 ? GMAX : 4; // heads per pass over the registers
+  static_assert(RPL >= 1 && TPW % RPW == 0, "split too small for the row mapping");
   const Shape &s = a.s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int rg = tid / TPR, cs = tid % TPR;
+  const int rgl = lane / TPR, cs = lane % TPR;
   const uint32_t S = (uint32_t)a.splits;
   const uint32_t split = blockIdx.x % S, prob = blockIdx.x / S;
   const uint32_t Tq = (uint32_t)s.Tq, Hkv = (uint32_t)s.Hkv;
@@ -54,157 +60,300 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
   const int32_t cnt = min(max(a.nnz[prob], 0), s.Kb);
   const int base_blk = (int)split * (TOK >> s.bk_shift);
 
-  __shared__ float pr[GMAX][TOK];
-  __shared__ float red[RPP][HG][D];
-  __shared__ float stat_m[GMAX], stat_l[GMAX];
-
-#define HIPSA_TOKEN(J, OUT)                                                     \
-  do {                                                                          \
-    const int n_ = base_blk + ((J) >> s.bk_shift);                              \
-    const int32_t blk_ = list[min(n_, s.Kb - 1)];                               \
-    const bool ok_ = n_ < cnt && blk_ >= 0 && blk_ < Np;                        \
-    const int32_t t_ = ((ok_ ? blk_ : 0) << s.bk_shift) + ((J) & (s.bk - 1));   \
-    OUT = (ok_ && t_ < Tp) ? t_ : -1;                                           \
-  } while (0)
+  __shared__ float wm[4][GMAX], wl[4][GMAX];
+  __shared__ float wo[4][GMAX][D];
 
   const int64_t kvoff = (int64_t)(b * Hkv + g) * s.T_cap * D;
   const E *Kp = reinterpret_cast<const E *>(a.K) + kvoff;
   const E *Vp = reinterpret_cast<const E *>(a.V) + kvoff;
   const E *qbase = reinterpret_cast<const E *>(a.q) + ((int64_t)(b * s.Hq + g * s.G) * Tq + i) * D;
 
-  // V rows of this lane (coalesced: TPR lanes per row), all in flight
-  uint4 vr[RPT];
-  int32_t vt[RPT];
+  // Token slot u of this lane: wave*TPW + u*RPW + rgl.  A slot past the list,
+  // or whose block id is out of range or past the causal limit, reads row 0
+  // and is masked, so every load is issued unconditionally.
+  int32_t tk[RPL];
+  uint4 kr[RPL], vr[RPL], qr[GMAX];
 #pragma unroll
-  for (int u = 0; u < RPT; u++) {
-    HIPSA_TOKEN(u * RPP + rg, vt[u]);
-    vr[u] = Vec<E>::raw(Vp + (int64_t)(vt[u] >= 0 ? vt[u] : 0) * D + cs * VEC);
+  for (int u = 0; u < RPL; u++) {
+    const int j = wave * TPW + u * RPW + rgl;
+    const int n = base_blk + (j >> s.bk_shift);
+    const int32_t blk = list[min(n, s.Kb - 1)];
+    const bool ok = n < cnt && blk >= 0 && blk < Np;
+    const int32_t t = ((ok ? blk : 0) << s.bk_shift) + (j & (s.bk - 1));
+    tk[u] = (ok && t < Tp) ? t : -1;
+    const int64_t row = (int64_t)(tk[u] >= 0 ? tk[u] : 0) * D + cs * VEC;
+    kr[u] = Vec<E>::raw(Kp + row);
+    vr[u] = Vec<E>::raw(Vp + row);
   }
+#pragma unroll
+  for (int h = 0; h < GMAX; h++) qr[h] = Vec<E>::raw(qbase + (int64_t)min(h, s.G - 1) * Tq * D + cs * VEC);
 
-  if constexpr (kMfma) {
-    // query heads of the group as the A operand: lane l holds head l%16
-    uint4 qa[KS];
-    {
-      const int h = lane & 15;
 #pragma unroll
-      for (int ks = 0; ks < KS; ks++) {
-        const uint4 r = Vec<E>::raw(qbase + (int64_t)min(h, s.G - 1) * Tq * D + 32 * ks + 8 * (lane >> 4));
-        qa[ks] = h < s.G ? r : make_uint4(0, 0, 0, 0);
-      }
-    }
-    // K rows as B operands: lane l holds key 16*kt + l%16, dims 32*ks + 8*(l/16)
-    uint4 kr[KTW][KS];
-    int32_t kt_tok[KTW];
+  for (int h0 = 0; h0 < GMAX; h0 += HG) {
+    float qv[HG][VEC];
 #pragma unroll
-    for (int u = 0; u < KTW; u++) {
-      HIPSA_TOKEN(16 * (wave + 4 * u) + (lane & 15), kt_tok[u]);
+    for (int hh = 0; hh < HG; hh++) Vec<E>::widen(qr[h0 + hh], true, qv[hh]);
+    // logits of this wave's slots: TPR lanes per row, DPP sums within a row group
+    float sc[RPL][HG];
 #pragma unroll
-      for (int ks = 0; ks < KS; ks++)
-        kr[u][ks] = Vec<E>::raw(Kp + (int64_t)(kt_tok[u] >= 0 ? kt_tok[u] : 0) * D + 32 * ks + 8 * (lane >> 4));
-    }
-#pragma unroll
-    for (int u = 0; u < KTW; u++) {
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS; ks++)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[ks]), as_bf16x8(kr[u][ks]), acc, 0, 0, 0);
-      // acc[r]: head 4*(lane/16) + r, key 16*(wave + 4u) + lane%16
-      const int j = 16 * (wave + 4 * u) + (lane & 15);
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
-        const int h = 4 * (lane >> 4) + r;
-        if (h < s.G) pr[h][j] = kt_tok[u] >= 0 ? acc[r] * a.scale : -INFINITY;
-      }
-    }
-  } else {
-    // fp32: K rows with the same mapping as V, VALU dot products
-    float qv[GMAX][VEC];
-    {
-      uint4 r[GMAX];
-#pragma unroll
-      for (int h = 0; h < GMAX; h++) r[h] = Vec<E>::raw(qbase + (int64_t)min(h, s.G - 1) * Tq * D + cs * VEC);
-#pragma unroll
-      for (int h = 0; h < GMAX; h++) Vec<E>::widen(r[h], h < s.G, qv[h]);
-    }
-    uint4 kraw[RPT];
-#pragma unroll
-    for (int u = 0; u < RPT; u++) kraw[u] = Vec<E>::raw(Kp + (int64_t)(vt[u] >= 0 ? vt[u] : 0) * D + cs * VEC);
-#pragma unroll
-    for (int u = 0; u < RPT; u++) {
+    for (int u = 0; u < RPL; u++) {
       float kv[VEC];
-      Vec<E>::widen(kraw[u], vt[u] >= 0, kv);
-      const int j = u * RPP + rg;
-#pragma unroll
-      for (int h = 0; h < GMAX; h++) {
-        float p = 0.f;
-#pragma unroll
-        for (int e = 0; e < VEC; e++) p = fmaf(qv[h][e], kv[e], p);
-        p = group_sum<TPR>(p);
-        if (cs == 0 && h < s.G) pr[h][j] = vt[u] >= 0 ? p * a.scale : -INFINITY;
-      }
-    }
-  }
-#undef HIPSA_TOKEN
-  __syncthreads();
-
-  // per-head max and exponentials: one wave per head, TOK/64 slots per lane
-  for (int h = wave; h < s.G; h += 4) {
-    float x[TOK / 64];
-    float m = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < TOK / 64; u++) {
-      x[u] = pr[h][lane + 64 * u];
-      m = fmaxf(m, x[u]);
-    }
-    m = wave_max(m);
-    float l = 0.f;
-#pragma unroll
-    for (int u = 0; u < TOK / 64; u++) {
-      const float e = x[u] == -INFINITY ? 0.f : __expf(x[u] - m);
-      pr[h][lane + 64 * u] = e;
-      l += e;
-    }
-    l = wave_sum(l);
-    if (lane == 0) { stat_m[h] = m; stat_l[h] = l; }
-  }
-  __syncthreads();
-
-  // P.V, HG heads per LDS reduction pass; partial results to the workspace
-  float *mine = a.ws + ((int64_t)(prob * S + split) * s.G) * (D + 2);
-  for (int h0 = 0; h0 < s.G; h0 += HG) {
-    float acc[HG][VEC];
-#pragma unroll
-    for (int hh = 0; hh < HG; hh++)
-#pragma unroll
-      for (int e = 0; e < VEC; e++) acc[hh][e] = 0.f;
-#pragma unroll
-    for (int u = 0; u < RPT; u++) {
-      float vv[VEC];
-      Vec<E>::widen(vr[u], vt[u] >= 0, vv);
-      const int j = u * RPP + rg;
+      Vec<E>::widen(kr[u], true, kv);
 #pragma unroll
       for (int hh = 0; hh < HG; hh++) {
-        const float p = (h0 + hh < s.G) ? pr[h0 + hh][j] : 0.f;
+        float p = 0.f;
 #pragma unroll
-        for (int e = 0; e < VEC; e++) acc[hh][e] = fmaf(p, vv[e], acc[hh][e]);
+        for (int e = 0; e < VEC; e++) p = fmaf(qv[hh][e], kv[e], p);
+        p = group_sum<TPR>(p);
+        sc[u][hh] = tk[u] >= 0 ? p * a.scale : -INFINITY;
       }
+    }
+    // softmax statistics of the wave's slots and P.V, all in registers
+    float acc[HG][VEC];
+#pragma unroll
+    for (int hh = 0; hh < HG; hh++) {
+      float m = sc[0][hh];
+#pragma unroll
+      for (int u = 1; u < RPL; u++) m = fmaxf(m, sc[u][hh]);
+      m = across_max<TPR>(m);
+      float l = 0.f;
+#pragma unroll
+      for (int u = 0; u < RPL; u++) {
+        sc[u][hh] = sc[u][hh] == -INFINITY ? 0.f : __expf(sc[u][hh] - m);
+        l += sc[u][hh];
+      }
+      l = across_sum<TPR>(l);
+      if (lane == 0) { wm[wave][h0 + hh] = m; wl[wave][h0 + hh] = l; }
+#pragma unroll
+      for (int e = 0; e < VEC; e++) acc[hh][e] = 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < RPL; u++) {
+      float vv[VEC];
+      Vec<E>::widen(vr[u], tk[u] >= 0, vv);
+#pragma unroll
+      for (int hh = 0; hh < HG; hh++)
+#pragma unroll
+        for (int e = 0; e < VEC; e++) acc[hh][e] = fmaf(sc[u][hh], vv[e], acc[hh][e]);
     }
 #pragma unroll
     for (int hh = 0; hh < HG; hh++)
 #pragma unroll
-      for (int e = 0; e < VEC; e++) red[rg][hh][cs * VEC + e] = acc[hh][e];
-    __syncthreads();
-    for (int o = tid; o < HG * D; o += 256) {
-      const int hh = o / D, x = o % D;
-      if (h0 + hh >= s.G) continue;
-      float sum = 0.f;
-#pragma unroll 8
-      for (int r = 0; r < RPP; r++) sum += red[r][hh][x];
-      float *dst = mine + (int64_t)(h0 + hh) * (D + 2);
-      dst[2 + x] = sum;
-      if (x == 0) { dst[0] = stat_m[h0 + hh]; dst[1] = stat_l[h0 + hh]; }
+      for (int e = 0; e < VEC; e++) acc[hh][e] = across_sum<TPR>(acc[hh][e]);
+    if (rgl == 0) {
+#pragma unroll
+      for (int hh = 0; hh < HG; hh++)
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4)
+          *reinterpret_cast<float4 *>(&wo[wave][h0 + hh][cs * VEC + e]) =
+              make_float4(acc[hh][e], acc[hh][e + 1], acc[hh][e + 2], acc[hh][e + 3]);
     }
-    __syncthreads();
+  }
+  __syncthreads();
+
+  // merge the four waves (log-sum-exp weights); partials to the workspace
+  float *mine = a.ws + ((int64_t)(prob * S + split) * s.G) * (D + 2);
+  for (int o = tid; o < s.G * D; o += 256) {
+    const int h = o / D, x = o % D;
+    float M = wm[0][h];
+#pragma unroll
+    for (int w = 1; w < 4; w++) M = fmaxf(M, wm[w][h]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+      const float c = wm[w][h] == -INFINITY ? 0.f : __expf(wm[w][h] - M);
+      L = fmaf(c, wl[w][h], L);
+      O = fmaf(c, wo[w][h][x], O);
+    }
+    float *dst = mine + (int64_t)h * (D + 2);
+    dst[2 + x] = O;
+    if (x == 0) { dst[0] = M; dst[1] = L; }
+  }
+}
+
+// bf16 split workgroup on the matrix cores.  Per wave, TPW = TOK/4 token
+// slots:
+//   * the query heads of the group are the A operand of
+//     v_mfma_f32_16x16x32_bf16 (lane l holds head l%16, zero past the
+//     group) and the wave's K rows, 16 per tile, the B operand (lane l holds
+//     slot 16u + l%16), so the logits of (head, slot) land in the
+//     accumulators: lane l, register r -> head 4*(l/16) + r, slot 16u + l%16;
+//   * softmax statistics are taken in that layout (DPP within 16-lane rows)
+//     and the probabilities go to a per-wave LDS table;
+//   * P.V runs with lanes owning output dimensions: one V row is one
+//     wave-wide load (D*2/64 bytes per lane), the probabilities are LDS
+//     broadcasts, and each lane accumulates its dimensions over every slot of
+//     the wave, so no cross-lane reduction of the outputs is needed.
+// Query loads are issued first: loads complete in order, so the first
+// matrix op then waits for the query and its K rows, not for the V rows
+// issued after them.
+template <int D, int GMAX, int TOK>
+__global__ __launch_bounds__(256) void attn_decode_mfma(AttnArgs a) {
+  constexpr int KS = D / 32;            // MFMA k-steps over the head dim
+  constexpr int TPW = TOK / 4;          // token slots per wave
+  constexpr int NT = TPW / 16;          // 16-slot tiles per wave
+  constexpr int LPV = D / 2 < 64 ? D / 2 : 64;  // lanes per V row (2 elements each)
+  constexpr int RPV = 64 / LPV;         // V rows per wave-wide load
+  constexpr int NV = TPW / RPV;         // V loads per lane
+  static_assert(NT >= 1 && TPW % RPV == 0, "split too small");
+  const Shape &s = a.s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t S = (uint32_t)a.splits;
+  const uint32_t split = blockIdx.x % S, prob = blockIdx.x / S;
+  const uint32_t Tq = (uint32_t)s.Tq, Hkv = (uint32_t)s.Hkv;
+  const uint32_t i = prob % Tq, g = (prob / Tq) % Hkv, b = prob / (Tq * Hkv);
+  const int32_t Tp = s.causal ? (int32_t)(s.T - s.Tq + i + 1) : (int32_t)s.T;
+  const int32_t Np = (Tp + s.bk - 1) >> s.bk_shift;
+  const int32_t *list = a.indices + (int64_t)prob * s.Kb;
+  const int32_t cnt = min(max(a.nnz[prob], 0), s.Kb);
+  const int base_blk = (int)split * (TOK >> s.bk_shift);
+
+  __shared__ __align__(16) float pw[4][GMAX][TPW];
+  __shared__ float wm[4][GMAX], wl[4][GMAX];
+  __shared__ __align__(16) float wo[4][GMAX][D];
+
+  const int64_t kvoff = (int64_t)(b * Hkv + g) * s.T_cap * D;
+  const uint16_t *Kp = reinterpret_cast<const uint16_t *>(a.K) + kvoff;
+  const uint16_t *Vp = reinterpret_cast<const uint16_t *>(a.V) + kvoff;
+  const uint16_t *qbase = reinterpret_cast<const uint16_t *>(a.q) + ((int64_t)(b * s.Hq + g * s.G) * Tq + i) * D;
+
+  // Token of slot lane % TPW of this wave (row of K/V), or -1 when the slot is
+  // past the list, its block id is out of range or the token is past the
+  // causal limit.  Such slots read row 0 and are masked, so every load is
+  // unconditional.  Other lanes' slots come by shuffle (readlane when the
+  // row is the same for the whole wave).
+  int32_t tk_lane;
+  {
+    const int j = wave * TPW + lane % TPW;
+    const int n = base_blk + (j >> s.bk_shift);
+    const int32_t blk = list[min(n, s.Kb - 1)];
+    const bool ok = n < cnt && blk >= 0 && blk < Np;
+    const int32_t t = ((ok ? blk : 0) << s.bk_shift) + (j & (s.bk - 1));
+    tk_lane = (ok && t < Tp) ? t : -1;
+  }
+
+  uint4 qa[KS];
+  {
+    const int h = lane & 15;
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) {
+      const uint4 r = *reinterpret_cast<const uint4 *>(qbase + (int64_t)min(h, s.G - 1) * Tq * D + 32 * ks + 8 * (lane >> 4));
+      qa[ks] = h < s.G ? r : make_uint4(0, 0, 0, 0);
+    }
+  }
+  int32_t kt[NT];
+  uint4 kr[NT][KS];
+#pragma unroll
+  for (int u = 0; u < NT; u++) {
+    kt[u] = __shfl(tk_lane, 16 * u + (lane & 15), 64);
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++)
+      kr[u][ks] = *reinterpret_cast<const uint4 *>(Kp + (int64_t)(kt[u] >= 0 ? kt[u] : 0) * D + 32 * ks + 8 * (lane >> 4));
+  }
+  int32_t vt[NV];
+  uint32_t vr[NV];
+#pragma unroll
+  for (int v = 0; v < NV; v++) {
+    vt[v] = RPV == 1 ? __builtin_amdgcn_readlane(tk_lane, v) : __shfl(tk_lane, RPV * v + lane / LPV, 64);
+    vr[v] = *reinterpret_cast<const uint32_t *>(Vp + (int64_t)(vt[v] >= 0 ? vt[v] : 0) * D + 2 * (lane % LPV));
+  }
+
+  // logits on the matrix cores, softmax statistics per head in the
+  // accumulator layout, probabilities to the wave's LDS table
+  f32x4_t acc[NT];
+#pragma unroll
+  for (int u = 0; u < NT; u++) {
+    acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++)
+      acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[ks]), as_bf16x8(kr[u][ks]), acc[u], 0, 0, 0);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; r++) {
+    const int h = 4 * (lane >> 4) + r;
+    float sc[NT];
+    float m = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < NT; u++) {
+      sc[u] = kt[u] >= 0 ? acc[u][r] * a.scale : -INFINITY;
+      m = fmaxf(m, sc[u]);
+    }
+    m = fmaxf(m, dpp_mov<kDppXor1>(m));
+    m = fmaxf(m, dpp_mov<kDppXor2>(m));
+    m = fmaxf(m, dpp_mov<kDppHalfMirror>(m));
+    m = fmaxf(m, dpp_mov<kDppMirror>(m));
+    float l = 0.f;
+#pragma unroll
+    for (int u = 0; u < NT; u++) {
+      const float e = sc[u] == -INFINITY ? 0.f : __expf(sc[u] - m);
+      l += e;
+      if (h < GMAX) pw[wave][h][16 * u + (lane & 15)] = e;
+    }
+    l = group_sum<16>(l);
+    if ((lane & 15) == 0 && h < s.G) { wm[wave][h] = m; wl[wave][h] = l; }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // P.V: lane owns dimensions 2*(lane % LPV) and +1 over the wave's slots;
+  // probabilities read 4 slots at a time (an LDS broadcast)
+  constexpr int VPG = 4 / RPV;  // V loads per group of 4 slots
+  const int half = lane / LPV;  // d = 64: which of the two rows of a load
+  float o[GMAX][2];
+#pragma unroll
+  for (int h = 0; h < GMAX; h++) o[h][0] = o[h][1] = 0.f;
+#pragma unroll
+  for (int g4 = 0; g4 < TPW / 4; g4++) {
+    // every one of the GMAX heads is computed (heads past the group have
+    // finite probabilities and are never stored): a per-head test inside
+    // this loop would become a select on every accumulator update
+    float4 p4[GMAX];
+#pragma unroll
+    for (int h = 0; h < GMAX; h++) p4[h] = *reinterpret_cast<const float4 *>(&pw[wave][h][4 * g4]);
+#pragma unroll
+    for (int vv = 0; vv < VPG; vv++) {
+      const int v = g4 * VPG + vv;
+      const uint32_t w = vt[v] >= 0 ? vr[v] : 0u;
+      const float v0 = __uint_as_float(w << 16), v1 = __uint_as_float(w & 0xffff0000u);
+#pragma unroll
+      for (int h = 0; h < GMAX; h++) {
+        float pj;
+        if (RPV == 1) pj = vv == 0 ? p4[h].x : vv == 1 ? p4[h].y : vv == 2 ? p4[h].z : p4[h].w;
+        else pj = vv == 0 ? (half ? p4[h].y : p4[h].x) : (half ? p4[h].w : p4[h].z);
+        o[h][0] = fmaf(pj, v0, o[h][0]);
+        o[h][1] = fmaf(pj, v1, o[h][1]);
+      }
+    }
+  }
+  if (RPV == 2) {  // d = 64: the two halves of the wave took alternate rows
+#pragma unroll
+    for (int h = 0; h < GMAX; h++) { o[h][0] = xor32_sum(o[h][0]); o[h][1] = xor32_sum(o[h][1]); }
+  }
+  if (lane < LPV) {
+#pragma unroll
+    for (int h = 0; h < GMAX; h++)
+      if (h < s.G) *reinterpret_cast<float2 *>(&wo[wave][h][2 * lane]) = make_float2(o[h][0], o[h][1]);
+  }
+  __syncthreads();
+
+  // merge the four waves (log-sum-exp weights); partials to the workspace
+  float *mine = a.ws + ((int64_t)(prob * S + split) * s.G) * (D + 2);
+  for (int oi = tid; oi < s.G * D; oi += 256) {
+    const int h = oi / D, x = oi % D;
+    float M = wm[0][h];
+#pragma unroll
+    for (int w = 1; w < 4; w++) M = fmaxf(M, wm[w][h]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+      const float c = wm[w][h] == -INFINITY ? 0.f : __expf(wm[w][h] - M);
+      L = fmaf(c, wl[w][h], L);
+      O = fmaf(c, wo[w][h][x], O);
+    }
+    float *dst = mine + (int64_t)h * (D + 2);
+    dst[2 + x] = O;
+    if (x == 0) { dst[0] = M; dst[1] = L; }
   }
 }
 
@@ -250,14 +399,18 @@ __global__ __launch_bounds__(128) void attn_decode_combine(AttnArgs a) {
   store_elem(out + x, v);
 }
 
-// tokens per split workgroup: the largest of 256, 128, 64 that still gives
-// >= 512 workgroups (64 when none does); fp32 at d=128 stops at 128
+// Tokens per split workgroup: 128 or 64, the larger when it still gives
+// >= 512 workgroups.  64 for fp32 at d = 128 (a lane's K and V rows must fit
+// in registers) and for groups of more than 8 query heads (the per-head
+// probabilities and outputs of a lane must fit); a bf16 wave also has at
+// most 63 loads in flight, which caps its slots at 32.
+template <typename E, int D>
+constexpr int max_tokens() { return (std::is_same<E, float>::value && D == 128) ? 64 : 128; }
+
 template <typename E, int D>
 int tokens_per_split(const Shape &s) {
   const int64_t total = (int64_t)s.Kb * s.bk;
-  const int maxtok = (std::is_same<E, float>::value && D == 128) ? 128 : 256;
-  for (int tok = maxtok; tok > 64; tok >>= 1)
-    if (s.problems * ((total + tok - 1) / tok) >= 512) return tok;
+  if (max_tokens<E, D>() >= 128 && s.G <= 8 && s.problems * ((total + 127) / 128) >= 512) return 128;
   return 64;
 }
 
@@ -269,14 +422,17 @@ int tokens_for(const Shape &s) {
 
 template <typename E, int D, int GMAX>
 void launch_t(const AttnArgs &a, hipStream_t st, int tok) {
+  constexpr int kMaxTok = max_tokens<E, D>();
   const dim3 grid((unsigned)(a.s.problems * a.splits)), block(256);
-  if (tok == 256) {
-    if constexpr (!(std::is_same<E, float>::value && D == 128))
-      hipLaunchKernelGGL((attn_decode_kernel<E, D, GMAX, 256>), grid, block, 0, st, a);
-  } else if (tok == 128) {
-    hipLaunchKernelGGL((attn_decode_kernel<E, D, GMAX, 128>), grid, block, 0, st, a);
+  if constexpr (std::is_same<E, uint16_t>::value) {
+    if (GMAX <= 8 && tok == 128) hipLaunchKernelGGL((attn_decode_mfma<D, (GMAX <= 8 ? GMAX : 8), 128>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((attn_decode_mfma<D, GMAX, 64>), grid, block, 0, st, a);
   } else {
-    hipLaunchKernelGGL((attn_decode_kernel<E, D, GMAX, 64>), grid, block, 0, st, a);
+    if (tok == 128) {
+      if constexpr (kMaxTok >= 128) hipLaunchKernelGGL((attn_decode_kernel<E, D, GMAX, 128>), grid, block, 0, st, a);
+    } else {
+      hipLaunchKernelGGL((attn_decode_kernel<E, D, GMAX, 64>), grid, block, 0, st, a);
+    }
   }
 }
 

@@ -105,9 +105,14 @@ __device__ inline uint64_t rank_key(float score, int32_t start) {
   return ((uint64_t)u << 32) | (uint32_t)(0x7fffffff - start);
 }
 
-// Cross-lane reductions.  DPP moves (quad permutes and row mirrors) run as
-// VALU operand modifiers, far cheaper than LDS-routed shuffles; only steps
-// that cross a 16-lane DPP row fall back to __shfl_xor.
+// Cross-lane reductions.  DPP moves (quad permutes, row mirrors and
+// rotates) run as VALU operand modifiers; steps that cross a 16-lane row use
+// gfx950's permlane swaps, which exchange rows (16 lanes) or halves (32
+// lanes) of a wave on the VALU instead of routing through LDS.  Called with
+// the same value as both operands, permlane16_swap returns the even rows
+// duplicated in .x and the odd rows duplicated in .y (permlane32_swap: the
+// low half and the high half), so combining .x with .y gives lane i and lane
+// i^16 (i^32) the same result.
 template <int CTRL> __device__ inline float dpp_mov(float v) {
   return __builtin_bit_cast(
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
@@ -116,6 +121,21 @@ constexpr int kDppXor1 = 0xb1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4e;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <- 7-i within 8 lanes
 constexpr int kDppMirror = 0x140;     // lane i <- 15-i within 16 lanes
+constexpr int kDppRor8 = 0x128;       // lane i <- (i+8) mod 16 within 16 lanes
+
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+__device__ inline u32x2_t swap16(float v) {
+  const unsigned u = __float_as_uint(v);
+  return __builtin_amdgcn_permlane16_swap(u, u, false, false);
+}
+__device__ inline u32x2_t swap32(float v) {
+  const unsigned u = __float_as_uint(v);
+  return __builtin_amdgcn_permlane32_swap(u, u, false, false);
+}
+__device__ inline float xor16_sum(float v) { const u32x2_t r = swap16(v); return __uint_as_float(r.x) + __uint_as_float(r.y); }
+__device__ inline float xor32_sum(float v) { const u32x2_t r = swap32(v); return __uint_as_float(r.x) + __uint_as_float(r.y); }
+__device__ inline float xor16_max(float v) { const u32x2_t r = swap16(v); return fmaxf(__uint_as_float(r.x), __uint_as_float(r.y)); }
+__device__ inline float xor32_max(float v) { const u32x2_t r = swap32(v); return fmaxf(__uint_as_float(r.x), __uint_as_float(r.y)); }
 
 // Sum over aligned groups of W lanes (W a power of two <= 64); every lane of a
 // group ends with the group's sum.
@@ -124,8 +144,22 @@ template <int W> __device__ inline float group_sum(float v) {
   if (W >= 4) v += dpp_mov<kDppXor2>(v);
   if (W >= 8) v += dpp_mov<kDppHalfMirror>(v);
   if (W >= 16) v += dpp_mov<kDppMirror>(v);
-  if (W >= 32) v += __shfl_xor(v, 16, 64);
-  if (W >= 64) v += __shfl_xor(v, 32, 64);
+  if (W >= 32) v = xor16_sum(v);
+  if (W >= 64) v = xor32_sum(v);
+  return v;
+}
+// Sum (max) over the lanes of a wave that share lane % W (W = 8, 16, 32 or 64):
+// the reduction across groups of W lanes.
+template <int W> __device__ inline float across_sum(float v) {
+  if (W <= 8) v += dpp_mov<kDppRor8>(v);
+  if (W <= 16) v = xor16_sum(v);
+  if (W <= 32) v = xor32_sum(v);
+  return v;
+}
+template <int W> __device__ inline float across_max(float v) {
+  if (W <= 8) v = fmaxf(v, dpp_mov<kDppRor8>(v));
+  if (W <= 16) v = xor16_max(v);
+  if (W <= 32) v = xor32_max(v);
   return v;
 }
 __device__ inline float wave_max(float v) {
@@ -133,8 +167,7 @@ __device__ inline float wave_max(float v) {
   v = fmaxf(v, dpp_mov<kDppXor2>(v));
   v = fmaxf(v, dpp_mov<kDppHalfMirror>(v));
   v = fmaxf(v, dpp_mov<kDppMirror>(v));
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  return fmaxf(v, __shfl_xor(v, 32, 64));
+  return across_max<16>(v);
 }
 __device__ inline float wave_sum(float v) { return group_sum<64>(v); }
 
