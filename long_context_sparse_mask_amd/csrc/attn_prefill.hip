@@ -6,24 +6,33 @@
 // reviewer NLBm, W2).  Exact causal softmax over the listed blocks' tokens.
 //
 // Prefill attention is a dense contraction per selected key tile, so it runs
-// on the matrix cores.  One workgroup of 8 wave64s serves one (b, kv head,
-// query block) and four query heads of the group: wave w takes head w/2 and
-// query rows 32*(w%2) .. +31, so every K/V tile fetched from memory feeds four
-// heads, and at ~190 registers per lane two waves share each SIMD (one's
-// softmax VALU work overlaps the other's MFMAs).  Per tile of 64 keys:
-//   - the workgroup stages K (row-major, padded rows) and V (transposed to
-//     d-major, so an MFMA operand can take 8 consecutive keys of one d) in a
-//     double-buffered LDS slot; the global loads of the next tile are issued
-//     before this tile's math, and one barrier per tile suffices;
-//   - each wave forms S^T = K . Q^T on v_mfma_f32_32x32x16_bf16 (keys down
-//     the rows, its 32 queries across the columns), so a query's 64 scores
-//     sit in one lane pair and the online-softmax max and sum need one
-//     cross-half exchange; tiles that need no causal or validity mask (the
-//     loader flags them) skip the per-element mask;
+// on the matrix cores (v_mfma_f32_32x32x16_bf16).  One workgroup of 8 wave64s
+// serves one (b, kv head, query block) and four query heads of the group:
+// wave w takes head w/2 and query rows 32*(w%2) .. +31, so every K/V tile
+// fetched from memory feeds four heads, and at ~190 registers per lane two
+// waves share each SIMD (one's softmax VALU work overlaps the other's
+// MFMAs).  (Giving each wave both query tiles of its head halves the LDS
+// operand reads per MFMA, but needs ~500 registers, leaves one wave per SIMD
+// and measured slower.)  Per tile of 64 keys:
+//   - the workgroup stages K and V row-major in a double-buffered LDS slot
+//     (16-byte stores); the global loads of the next tile are issued before
+//     this tile's math, and one barrier per tile suffices;
+//   - each wave forms S^T = K . Q^T (keys down the rows, its 32 queries
+//     across the columns), so a query's 64 scores sit in one lane pair and
+//     the online-softmax max and sum need one cross-half exchange; the two
+//     32-key halves of the tile are independent accumulation chains,
+//     interleaved (a dependent 32x32x16 MFMA issues ~45 cycles after its
+//     predecessor, an independent one after 32); tiles that need no causal or
+//     validity mask (the loader flags them) skip the per-element mask;
 //   - P^T is rounded to bf16 in registers and used directly as the B operand
-//     of O^T += V^T . P^T: the register order of S^T defines the key order of
-//     the k-steps, and V^T is read from LDS in that same order;
+//     of O^T += V^T . P^T.  The register order of S^T fixes which keys form
+//     each k-step; the V^T operand for those keys comes from the row-major V
+//     tile through gfx950's transposing LDS read (ds_read_b64_tr_b16: within
+//     each 16 lanes, lane i receives element i of the four 4-element row
+//     pieces the group addresses), so V needs no transposing stores;
 //   - the running output is rescaled only when some lane's running max moved.
+// LDS rows are padded (K: D+8, V: D+32 elements) so that the operand reads
+// of a 256-byte LDS pass fall in distinct banks.
 #include "hipsa_internal.h"
 
 namespace hipsa {
@@ -31,23 +40,90 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+// 4 consecutive 16-bit elements of row-major LDS, transposed across each
+// group of 16 lanes (see above).
+__device__ inline uint2 lds_read_tr16(const uint16_t *p) {
+  const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16_t *)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// Online softmax of one query tile over one key tile.  sacc[kt][r] holds the
+// score of key kt*32 + 8*(r/4) + 4*half + r%4 for this lane's query.  The
+// scores are copied to plain registers and masked there with selects: a
+// conditional write into the matrix-core accumulator vectors themselves
+// (under divergent control flow, with the accumulators spread over AGPRs)
+// lost updates at this kernel's register pressure.  Produces P^T in bf16 as
+// MFMA B operands and updates the running max m, sum l and output o.
+template <int DT>
+__device__ inline void online_softmax(const f32x16_t (&sacc)[2], bool masked, const int32_t *tokrow,
+                                      bool qvalid, int32_t qpos, bool causal, int half, float sl2,
+                                      float &m, float &l, f32x16_t (&o)[DT], bf16x8_t (&pf)[4]) {
+  float sv[2][16];
+#pragma unroll
+  for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) sv[kt][r] = sacc[kt][r];
+  if (masked) {  // uniform: some key of this tile is invalid or after a query of the block
+#pragma unroll
+    for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+      for (int gq = 0; gq < 4; gq++) {
+        const int4 t4 = *reinterpret_cast<const int4 *>(&tokrow[kt * 32 + 8 * gq + 4 * half]);
+        const int32_t tt[4] = {t4.x, t4.y, t4.z, t4.w};
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const bool ok = qvalid && tt[e] >= 0 && (!causal || tt[e] <= qpos);
+          sv[kt][4 * gq + e] = ok ? sv[kt][4 * gq + e] : -INFINITY;
+        }
+      }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) mx = fmaxf(mx, sv[kt][r]);
+  mx = xor32_max(mx) * sl2;  // scale > 0: max commutes
+  const float mnew = fmaxf(m, mx);
+  const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
+  const float msub = mnew == -INFINITY ? 0.f : mnew;
+  float ps = 0.f;
+#pragma unroll
+  for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(sv[kt][r], sl2, -msub));  // exp2(-inf) = 0
+      ps += p;
+      pf[kt * 2 + (r >> 3)][r & 7] = (__bf16)p;
+    }
+  l = fmaf(l, alpha, ps);
+  m = mnew;
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++) o[dt] *= alpha;
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnArgs a) {
   constexpr int KS = D / 16;   // k-steps of S^T over the head dim
   constexpr int DT = D / 32;   // 32-row tiles of O^T
   constexpr int BQ = 64, KT = 64;
   constexpr int KPAD = D + 8;  // K tile row stride (elements)
-  constexpr int VPAD = KT + 8; // V^T row stride (elements)
+  constexpr int VPAD = D + 32; // V tile row stride (elements)
   constexpr int TPR = D / 8;   // loader: lanes per K row
   constexpr int RPP = 512 / TPR;
-  constexpr int KP = KT / RPP; // loader: K rows per lane
-  constexpr int VP = D / 64;   // loader: V chunks of 8 dims per lane
+  constexpr int KP = KT / RPP; // loader: K rows (and V rows) per lane
   const Shape &s = a.s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
 
+  // query blocks of one KV head share an L2 (their key sets overlap)
+  const uint32_t item = xcd_swizzle(blockIdx.x, gridDim.x);
   const uint32_t hchunks = (uint32_t)(s.G + 3) / 4;
-  const uint32_t prob = blockIdx.x / hchunks, hc = blockIdx.x % hchunks;
+  const uint32_t prob = item / hchunks, hc = item % hchunks;
   const uint32_t nqb = (uint32_t)s.nqb, Hkv = (uint32_t)s.Hkv, Tq = (uint32_t)s.Tq;
   const uint32_t qb = prob % nqb, g = (prob / nqb) % Hkv, b = prob / (nqb * Hkv);
   const int h = (int)hc * 4 + (wave >> 1);
@@ -63,7 +139,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnArgs a) {
   const int ntiles = (cnt + bpt - 1) / bpt;
 
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * KPAD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VPAD];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][KT * VPAD];
   __shared__ __attribute__((aligned(16))) int32_t tok[2][KT];
   __shared__ int32_t tmask[2];
   __shared__ int32_t lst[kMaxKb];
@@ -87,10 +163,10 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnArgs a) {
   }
   __syncthreads();  // lst ready
 
-  // loader state: this lane's K rows, V key and token of the tile in flight
-  uint4 kreg[KP], vreg[VP];
+  // loader state: this lane's K and V rows of the tile in flight
+  uint4 kreg[KP], vreg[KP];
   int32_t vtok = -1;
-  const int krow0 = tid / TPR, kcol = (tid % TPR) * 8, vkey = tid & 63, vch = tid >> 6;
+  const int krow0 = tid / TPR, kcol = (tid % TPR) * 8;
   // token of slot J of tile TL, or -1 (branch-free so the loads stay in flight)
 #define HIPSA_TOKEN(TL, J, OUT)                                              \
   do {                                                                       \
@@ -105,30 +181,23 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnArgs a) {
     _Pragma("unroll") for (int u = 0; u < KP; u++) {                                           \
       int32_t t;                                                                               \
       HIPSA_TOKEN(TL, u * RPP + krow0, t);                                                     \
-      kreg[u] = *reinterpret_cast<const uint4 *>(Kg + (int64_t)(t >= 0 ? t : 0) * D + kcol);   \
+      const int64_t off_ = (int64_t)(t >= 0 ? t : 0) * D + kcol;                               \
+      kreg[u] = *reinterpret_cast<const uint4 *>(Kg + off_);                                   \
+      vreg[u] = *reinterpret_cast<const uint4 *>(Vg + off_);                                   \
     }                                                                                          \
-    HIPSA_TOKEN(TL, vkey, vtok);                                                               \
-    _Pragma("unroll") for (int u = 0; u < VP; u++)                                             \
-      vreg[u] = *reinterpret_cast<const uint4 *>(Vg + (int64_t)(vtok >= 0 ? vtok : 0) * D +    \
-                                                 (vch + 8 * u) * 8);                           \
+    HIPSA_TOKEN(TL, lane, vtok);                                                               \
   } while (0)
 #define HIPSA_LSTORE(BUF)                                                                      \
   do {                                                                                         \
-    _Pragma("unroll") for (int u = 0; u < KP; u++)                                             \
+    _Pragma("unroll") for (int u = 0; u < KP; u++) {                                           \
       *reinterpret_cast<uint4 *>(&Ks[BUF][(u * RPP + krow0) * KPAD + kcol]) = kreg[u];         \
-    _Pragma("unroll") for (int u = 0; u < VP; u++) {                                           \
-      const int d0 = (vch + 8 * u) * 8;                                                        \
-      const uint32_t w_[4] = {vreg[u].x, vreg[u].y, vreg[u].z, vreg[u].w};                     \
-      _Pragma("unroll") for (int e = 0; e < 4; e++) {                                          \
-        Vt[BUF][(d0 + 2 * e) * VPAD + vkey] = (uint16_t)(w_[e] & 0xffffu);                     \
-        Vt[BUF][(d0 + 2 * e + 1) * VPAD + vkey] = (uint16_t)(w_[e] >> 16);                     \
-      }                                                                                        \
+      *reinterpret_cast<uint4 *>(&Vs[BUF][(u * RPP + krow0) * VPAD + kcol]) = vreg[u];         \
     }                                                                                          \
-    if (tid < KT) {                                                                            \
-      tok[BUF][tid] = vtok;                                                                    \
+    if (wave == 0) {                                                                           \
+      tok[BUF][lane] = vtok;                                                                   \
       const bool bad_ = vtok < 0 || (s.causal && vtok > pos0);                                 \
       const uint64_t any_ = __builtin_amdgcn_ballot_w64(bad_);                                 \
-      if (tid == 0) tmask[BUF] = any_ != 0;                                                    \
+      if (lane == 0) tmask[BUF] = any_ != 0;                                                   \
     }                                                                                          \
   } while (0)
 
@@ -153,67 +222,31 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnArgs a) {
     // which keeps this code free of branches)
     HIPSA_GLOAD(min(tl + 1, ntiles - 1));
     if (active) {
-      // S^T: keys kt*32 + 8*(r/4) + 4*half + r%4, queries qt*32 + col
-      f32x16_t sacc[2];
+      // S^T: keys kt*32 + 8*(r/4) + 4*half + r%4, queries qt*32 + col; the two
+      // key halves are independent accumulation chains, interleaved
+      f32x16_t sacc[2] = {f32x16_t{}, f32x16_t{}};
 #pragma unroll
-      for (int kt = 0; kt < 2; kt++) {
-        uint4 kf[KS];
+      for (int ks = 0; ks < KS; ks++) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ks++)
-          kf[ks] = *reinterpret_cast<const uint4 *>(&Ks[buf][(kt * 32 + col) * KPAD + 16 * ks + 8 * half]);
-        f32x16_t acc = {};
-#pragma unroll
-        for (int ks = 0; ks < KS; ks++)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[ks]), as_bf16x8(qf[ks]), acc, 0, 0, 0);
-        sacc[kt] = acc;
-      }
-      if (tmask[buf]) {  // some key of this tile is invalid or after a query
-#pragma unroll
-        for (int kt = 0; kt < 2; kt++)
-#pragma unroll
-          for (int gq = 0; gq < 4; gq++) {
-            const int4 t4 = *reinterpret_cast<const int4 *>(&tok[buf][kt * 32 + 8 * gq + 4 * half]);
-            const int32_t tt[4] = {t4.x, t4.y, t4.z, t4.w};
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-              const bool ok = qvalid && tt[e] >= 0 && (!s.causal || tt[e] <= qpos);
-              if (!ok) sacc[kt][4 * gq + e] = -INFINITY;
-            }
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 2; kt++)
-#pragma unroll
-        for (int r = 0; r < 16; r++) mx = fmaxf(mx, sacc[kt][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;  // scale > 0: max commutes
-      const float mnew = fmaxf(m, mx);
-      const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
-      const float msub = mnew == -INFINITY ? 0.f : mnew;
-      bf16x8_t pf[4];
-      float ps = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 2; kt++)
-#pragma unroll
-        for (int r = 0; r < 16; r++) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kt][r], sl2, -msub));  // exp2(-inf) = 0
-          ps += p;
-          pf[kt * 2 + (r >> 3)][r & 7] = (__bf16)p;
+        for (int kt = 0; kt < 2; kt++) {
+          const uint4 kf = *reinterpret_cast<const uint4 *>(&Ks[buf][(kt * 32 + col) * KPAD + 16 * ks + 8 * half]);
+          sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[ks]), sacc[kt], 0, 0, 0);
         }
-      l = fmaf(l, alpha, ps);
-      m = mnew;
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-        for (int dt = 0; dt < DT; dt++) o[dt] *= alpha;
       }
-      // O^T += V^T . P^T over 4 k-steps of 16 keys
+      bf16x8_t pf[4];
+      online_softmax<DT>(sacc, tmask[buf] != 0, tok[buf], qvalid, qpos, s.causal != 0, half, sl2, m, l, o, pf);
+      // O^T += V^T . P^T over 4 k-steps of 16 keys.  Lane l (group g = l/16,
+      // L = l%16) names V row 16ks + 4*(g/2) + L/4 (+8 for the upper half of
+      // the fragment), columns dt*32 + 16*(g%2) + 4*(L%4) .. +3, and receives
+      // MFMA row dt*32 + l%32 for keys 16ks + 4*half (+8) .. +3.
+      const int vg = lane >> 4, vl = lane & 15;
 #pragma unroll
       for (int ks = 0; ks < 4; ks++)
 #pragma unroll
         for (int dt = 0; dt < DT; dt++) {
-          const uint16_t *vrow = &Vt[buf][(dt * 32 + col) * VPAD + 16 * ks + 4 * half];
-          const uint2 lo = *reinterpret_cast<const uint2 *>(vrow);
-          const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + 8);
+          const uint16_t *vp = &Vs[buf][(16 * ks + 4 * (vg >> 1) + (vl >> 2)) * VPAD + dt * 32 + 16 * (vg & 1) + 4 * (vl & 3)];
+          const uint2 lo = lds_read_tr16(vp);
+          const uint2 hi = lds_read_tr16(vp + 8 * VPAD);
           o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)),
                                                           pf[ks], o[dt], 0, 0, 0);
         }
@@ -226,7 +259,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnArgs a) {
 #undef HIPSA_TOKEN
 
   if (!active) return;
-  const float lt = l + __shfl_xor(l, 32, 64);
+  const float lt = xor32_sum(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (!qvalid) return;
   uint16_t *Og = reinterpret_cast<uint16_t *>(a.out) + ((int64_t)(b * s.Hq + g * s.G + h) * Tq + r0 + qq) * D;

@@ -48,6 +48,19 @@ hipError_t launch_attn_prefill(const AttnArgs &a, hipStream_t st);
 
 // ------------------------------------------------------------------ device helpers
 
+// Workgroup -> logical work item, XCD-aware.  gfx950 dispatches the
+// workgroups of a launch round-robin over its 8 XCDs (workgroup x runs on
+// XCD x % 8), and each XCD has its own L2.  This bijection on [0, P) gives
+// XCD j a contiguous range of logical items (ceil or floor of P/8), so items
+// that are adjacent in logical order (the query blocks of one KV head, which
+// select overlapping key blocks) share an L2.
+__device__ inline uint32_t xcd_swizzle(uint32_t x, uint32_t P) {
+  constexpr uint32_t kXcd = 8;
+  const uint32_t q = P / kXcd, r = P % kXcd, xcd = x % kXcd, i = x / kXcd;
+  return xcd < r ? xcd * (q + 1) + i : r * (q + 1) + (xcd - r) * q + i;
+}
+
+
 // 16-byte vector loads widened to fp32.  bf16 widens exactly by a 16-bit shift.
 template <typename E> struct Vec;
 // raw() issues the load; widen() converts (and zeroes the slice when `keep`

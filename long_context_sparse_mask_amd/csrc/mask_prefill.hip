@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void mask_prefill_kernel(MaskArgs a) {
   const Shape &s = a.s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  const uint32_t prob = blockIdx.x;
+  const uint32_t prob = xcd_swizzle(blockIdx.x, gridDim.x);  // query blocks of one KV head share an L2
   const uint32_t nqb = (uint32_t)s.nqb, Hkv = (uint32_t)s.Hkv, Tq = (uint32_t)s.Tq;
   const uint32_t qb = prob % nqb, g = (prob / nqb) % Hkv, b = prob / (nqb * Hkv);
   const int32_t r0 = (int32_t)qb * BQ;
