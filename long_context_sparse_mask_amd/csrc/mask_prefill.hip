@@ -24,7 +24,9 @@
 namespace hipsa {
 namespace {
 
-template <int D>
+// ONEHEAD: the group has at most 4 query heads, so each wave owns one head
+// for the whole search and keeps its query operands in registers.
+template <int D, bool ONEHEAD>
 __global__ __launch_bounds__(256) void mask_prefill_kernel(MaskArgs a) {
   constexpr int KS = D / 16;  // k-steps of 16 over the head dim
   constexpr int BQ = 64;
@@ -56,7 +58,26 @@ __global__ __launch_bounds__(256) void mask_prefill_kernel(MaskArgs a) {
   const uint16_t *Qb = reinterpret_cast<const uint16_t *>(a.q) + ((int64_t)(b * s.Hq + g * s.G) * Tq + r0) * D;
   const uint16_t *Kbase = reinterpret_cast<const uint16_t *>(a.K) + (int64_t)(b * Hkv + g) * s.T_cap * D;
   const int n = 2 * Kb, nct = (n + 31) / 32;
+  // staging of 64 candidates' centre rows: SLR lanes per row, SRP rows per
+  // pass, SP passes; rows padded to CRS elements (a column read of the 32
+  // rows of a tile then falls in distinct banks per 16 lanes)
+  constexpr int SLR = D / 8, SRP = 256 / SLR, SP = 64 / SRP, CRS = D + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t cst[64 * CRS];
+  uint4 srow[SP];
   const int half = lane >> 5, col = lane & 31;
+
+  // A operand: rows rt*32 + col of head h, dims 16*ks + 8*half .. +7
+  uint4 qa[2][KS];
+#define HIPSA_LOAD_QUERIES(H)                                                                    \
+  do {                                                                                           \
+    _Pragma("unroll") for (int rt = 0; rt < 2; rt++) {                                           \
+      const int row_ = min(rt * 32 + col, r1 - r0 - 1); /* ragged rows are masked below */       \
+      _Pragma("unroll") for (int ks = 0; ks < KS; ks++)                                          \
+        qa[rt][ks] = *reinterpret_cast<const uint4 *>(Qb + ((int64_t)(H) * Tq + row_) * D + 16 * ks + 8 * half); \
+    }                                                                                            \
+  } while (0)
+  auto load_queries = [&](int h) { HIPSA_LOAD_QUERIES(h); };
+  if (ONEHEAD) HIPSA_LOAD_QUERIES(min(wave, s.G - 1));
 
   initial_candidates(Np, Kb, cand_a[0], cand_e[0]);
   for (int c = tid; c < n + kSpan; c += 256) key[0][c] = key[1][c] = 0;
@@ -71,46 +92,57 @@ __global__ __launch_bounds__(256) void mask_prefill_kernel(MaskArgs a) {
     uint64_t *kcur = key[cur];
     for (int c = tid; c < n + kSpan; c += 256) key[cur ^ 1][c] = 0;  // read last round; free now
 
-    // ---- 1. scoring: waves take the group's heads in turn
-    for (int h = wave; h < s.G; h += 4) {
-      // A operand: rows rt*32 + col of this head, dims 16*ks + 8*half .. +7
-      uint4 qa[2][KS];
+    // ---- 1. scoring, 64 candidates at a time: the workgroup loads their
+    // centre rows once (whole rows, D/8 lanes each) into LDS, then every wave
+    // scores them for its heads with B operands read from LDS
+    for (int ct0 = 0; ct0 < nct; ct0 += 2) {
+      if (ct0 > 0) __syncthreads();  // previous candidates' rows fully read
 #pragma unroll
-      for (int rt = 0; rt < 2; rt++) {
-        const int row = min(rt * 32 + col, r1 - r0 - 1);  // clamp ragged rows (masked below)
-#pragma unroll
-        for (int ks = 0; ks < KS; ks++)
-          qa[rt][ks] = *reinterpret_cast<const uint4 *>(Qb + ((int64_t)h * Tq + row) * D + 16 * ks + 8 * half);
-      }
-      for (int ct = 0; ct < nct; ct++) {
-        const int c = 32 * ct + col;
+      for (int u = 0; u < SP; u++) {
+        const int rrow = u * SRP + tid / SLR;  // candidate 32*ct0 + rrow
+        const int c = 32 * ct0 + rrow;
         const int cc = c < n ? c : 0;
         const int32_t lo_b = ca[cc], hi_b = ce[cc];
         const bool live = c < n && lo_b >= 0;
         const int32_t lo = lo_b << s.bk_shift, hi = min(hi_b << s.bk_shift, Tp);
         const int32_t t = live ? (lo + hi) >> 1 : 0;  // centre token (upper middle)
-        uint4 kb[KS];
+        srow[u] = *reinterpret_cast<const uint4 *>(Kbase + (int64_t)t * D + 8 * (tid % SLR));
+      }
 #pragma unroll
-        for (int ks = 0; ks < KS; ks++)
-          kb[ks] = *reinterpret_cast<const uint4 *>(Kbase + (int64_t)t * D + 16 * ks + 8 * half);
-        float best = -INFINITY;
+      for (int u = 0; u < SP; u++)
+        *reinterpret_cast<uint4 *>(&cst[(u * SRP + tid / SLR) * CRS + 8 * (tid % SLR)]) = srow[u];
+      __syncthreads();
+      for (int h = wave; h < s.G; h += 4) {
+        if (!ONEHEAD) load_queries(h);
 #pragma unroll
-        for (int rt = 0; rt < 2; rt++) {
-          f32x16_t acc = {};
+        for (int u = 0; u < 2; u++) {
+          if (ct0 + u >= nct) break;  // uniform
+          const int c = 32 * (ct0 + u) + col;
+          const int cc = c < n ? c : 0;
+          const int32_t lo_b = ca[cc], hi_b = ce[cc];
+          const bool live = c < n && lo_b >= 0;
+          const int32_t lo = lo_b << s.bk_shift, hi = min(hi_b << s.bk_shift, Tp);
+          const int32_t t = live ? (lo + hi) >> 1 : 0;
+          float best = -INFINITY;
 #pragma unroll
-          for (int ks = 0; ks < KS; ks++)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa[rt][ks]), as_bf16x8(kb[ks]),
-                                                          acc, 0, 0, 0);
-          // acc[r]: row rt*32 + 8*(r/4) + 4*half + r%4, candidate column col
+          for (int rt = 0; rt < 2; rt++) {
+            f32x16_t acc = {};
 #pragma unroll
-          for (int r = 0; r < 16; r++) {
-            const int ri = rt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            const bool votes = r0 + ri < r1 && (!s.causal || pos0 + ri >= t);
-            if (votes) best = fmaxf(best, acc[r]);
+            for (int ks = 0; ks < KS; ks++) {
+              const uint4 kb = *reinterpret_cast<const uint4 *>(&cst[(32 * u + col) * CRS + 16 * ks + 8 * half]);
+              acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa[rt][ks]), as_bf16x8(kb), acc, 0, 0, 0);
+            }
+            // acc[r]: row rt*32 + 8*(r/4) + 4*half + r%4, candidate column col
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+              const int ri = rt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+              const bool votes = r0 + ri < r1 && (!s.causal || pos0 + ri >= t);
+              best = votes ? fmaxf(best, acc[r]) : best;
+            }
           }
+          best = xor32_max(best);
+          if (half == 0 && live) atomicMax((unsigned long long *)&kcur[c], (unsigned long long)rank_key(best, lo_b));
         }
-        best = fmaxf(best, __shfl_xor(best, 32, 64));
-        if (half == 0 && live) atomicMax((unsigned long long *)&kcur[c], (unsigned long long)rank_key(best, lo_b));
       }
     }
     __syncthreads();
@@ -120,6 +152,7 @@ __global__ __launch_bounds__(256) void mask_prefill_kernel(MaskArgs a) {
     __syncthreads();
   }
 
+#undef HIPSA_LOAD_QUERIES
   write_ascending(cand_a[cur], Kb, out);
   if (tid == 0) a.nnz[prob] = Kb;
 }
@@ -128,8 +161,14 @@ __global__ __launch_bounds__(256) void mask_prefill_kernel(MaskArgs a) {
 
 hipError_t launch_mask_prefill(const MaskArgs &a, hipStream_t st) {
   const dim3 grid((unsigned)a.s.problems), block(256);
-  if (a.s.d == 64) hipLaunchKernelGGL(mask_prefill_kernel<64>, grid, block, 0, st, a);
-  else hipLaunchKernelGGL(mask_prefill_kernel<128>, grid, block, 0, st, a);
+  const bool one = a.s.G <= 4;
+  if (a.s.d == 64) {
+    if (one) hipLaunchKernelGGL((mask_prefill_kernel<64, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((mask_prefill_kernel<64, false>), grid, block, 0, st, a);
+  } else {
+    if (one) hipLaunchKernelGGL((mask_prefill_kernel<128, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((mask_prefill_kernel<128, false>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
 
