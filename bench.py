@@ -88,7 +88,7 @@ def prefill_flops(w) -> dict:
 
 # kernels behind each call, for matching the committed HBM counter summary
 CALL_KERNELS = {
-    ("decode", "hip_sparse_attn"): ("attn_decode_kernel", "attn_decode_combine"),
+    ("decode", "hip_sparse_attn"): ("attn_decode_mfma", "attn_decode_kernel", "attn_decode_combine"),
     ("decode", "hip_mask_estimate"): ("mask_decode",),
     ("prefill", "hip_sparse_attn"): ("attn_prefill_kernel",),
     ("prefill", "hip_mask_estimate"): ("mask_prefill_kernel",),

@@ -1,0 +1,71 @@
+"""CPU checks of bench.py: the algorithmic byte and FLOP counts behind its
+roofline figures, and its command-line contract."""
+import os
+import re
+import subprocess
+import sys
+
+import bench
+import synth_inputs as si
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_rounds_of():
+    assert bench.rounds_of(2048, 32) == 6      # 64-block chunks halve six times
+    assert bench.rounds_of(32, 32) == 0        # dense: nothing to search
+    assert bench.rounds_of(10, 32) == 0
+    assert bench.rounds_of(100, 8) == 4        # chunks of 12-13 blocks: 13 -> 7 -> 4 -> 2 -> 1
+
+
+def test_decode_bytes_128k_b4():
+    """32 problems (4 sequences x 8 KV heads); 2048 blocks of 64 keys, 32 kept."""
+    nb = bench.decode_bytes(si.workload("decode_128k_b4"))
+    assert nb["rounds"] == 6
+    assert nb["centre"] == 3 * 2 ** 20         # 32 x 6 rounds x 64 centre rows x 256 B
+    assert nb["kv"] == 32 * 2 ** 20            # 32 x 2048 selected tokens x (K + V) 512 B
+    assert nb["q"] == 4 * 32 * 256
+    assert nb["step"] == 36_806_912
+    assert nb["step"] == nb["mask"] + nb["attn"] + nb["out"] - nb["q"]
+
+
+def test_decode_bytes_dense_case():
+    """k >= T: no search rounds, every block attended."""
+    w = si.workload("tiny_decode", k=1024)
+    nb = bench.decode_bytes(w)
+    assert nb["rounds"] == 0 and nb["centre"] == 0
+    assert nb["kv"] == 1 * 1 * 2 * 1024 * 64 * 4
+
+
+def test_prefill_flops_chunk():
+    fl = bench.prefill_flops(si.workload("prefill_32k_chunk4k"))
+    # every 64-row block of the chunk sees >= 32 blocks: 2048 selected keys,
+    # QK^T and PV at 2 flops per multiply-add
+    assert fl["attn"] == 64 * 32 * 64 * 2048 * 128 * 4
+    assert abs(fl["mask"] / 8.59e9 - 1) < 0.01
+
+
+def test_prefill_mask_flops_power_of_two():
+    """N_p = K_b * 2^R: every round scores exactly 2 K_b candidates."""
+    w = si.workload("prefill_32k_chunk4k", B=1, Hq=1, Hkv=1, T=4096, Tq=64, k=8 * 64)
+    fl = bench.prefill_flops(w)
+    ncand = 3 * 2 * 8                          # 64 blocks, 8 kept: 8 -> 4 -> 2 -> 1
+    assert fl["mask"] == 2 * 64 * 128 * ncand
+
+
+def test_call_kernels_name_real_kernels():
+    src = ""
+    d = os.path.join(ROOT, "long_context_sparse_mask_amd", "csrc")
+    for f in os.listdir(d):
+        src += open(os.path.join(d, f)).read()
+    kernels = set(re.findall(r"__global__.*?void\s+(\w+)\s*\(", src))
+    for names in bench.CALL_KERNELS.values():
+        for n in names:
+            assert any(k.startswith(n) for k in kernels), n
+
+
+def test_multi_gpu_request_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
