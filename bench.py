@@ -137,6 +137,33 @@ def cpu_baseline(x, w, budget_s: float) -> dict:
     return times, nt
 
 
+def cpu_baseline_prefill(si, budget_s: float) -> dict:
+    """The CPU oracle on a bounded sample of the prefill chunk: the last 256
+    query rows (4 of the 64 query blocks, each seeing 32 selected blocks like
+    every block of the chunk) at the same T, same shapes and distributions;
+    the time is scaled to the 4096-row chunk."""
+    import oracle
+    ws = si.workload("prefill_32k_chunk4k", Tq=256)
+    xs = si.make_inputs(ws)
+    kw = dict(T=ws.T, k=ws.k, block_k=ws.block_k, block_q=ws.block_q, causal=ws.causal)
+    nt = oracle.nthreads()
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < 1 or (time.perf_counter() - t_start < budget_s and len(times) < 3):
+        t0 = time.perf_counter()
+        idx, nnz, _ = oracle.mask_all(xs["q"], xs["K"], threads=nt, **kw)
+        oracle.attn_all(xs["q"], xs["K"], xs["V"], idx, nnz, threads=nt, **kw)
+        times.append(time.perf_counter() - t0)
+    full = si.workload("prefill_32k_chunk4k")
+    scale = full.Tq / ws.Tq
+    t = statistics.median(times) * scale
+    return {"value": round(full.Tq / t, 1), "unit": "tok/s", "cores": nt, "kind": "oracle",
+            "sample": f"last {ws.Tq} query rows of the 4096-row chunk at T={ws.T} "
+                      f"({ws.Tq // ws.block_q} of 64 query blocks, 32 heads), fp64 C + OpenMP, "
+                      f"median of {len(times)} runs, time scaled x{scale:g}",
+            "s_per_chunk": round(t, 2)}
+
+
 def host_cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -339,6 +366,8 @@ def main():
                            "mfma_frac": round(fl["total"] / (rp["ms_per_step"] * 1e-3) / 1e12
                                               / MFMA_BF16_PEAK_TFLOPS, 4),
                            "algorithmic_flops": fl["total"]}
+        if not args.no_cpu_baseline:
+            line["prefill"]["cpu_baseline"] = cpu_baseline_prefill(si, args.cpu_budget)
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
