@@ -285,7 +285,7 @@ def main():
                     help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py: this build runs on exactly one GPU (no multi-GPU path); use --gpus 1",
+        print("bench.py: the library runs on exactly one GPU (no multi-GPU path); use --gpus 1",
               file=sys.stderr)
         sys.exit(2)
 
