@@ -52,6 +52,27 @@ def test_small_full(case):
     assert r["exempt"] <= max(1, r["problems"] // 10)
 
 
+def test_spare_capacity_rows():
+    """K/V allocated beyond T (cache capacity): the unused rows hold huge
+    values and must never be read, neither as centres nor as keys."""
+    w = si.workload("prefill_32k_chunk4k", T=3000, Tq=200, Hq=8, Hkv=2, k=512)
+    x = dict(si.make_inputs(w, T_cap=3500))
+    x["K"][:, :, w.T:] = 1e4
+    x["V"][:, :, w.T:] = 1e4
+    r = full_parity(x, w)
+    _report("spare_capacity", r)
+    assert r["exempt"] <= max(1, r["problems"] // 10)
+
+
+def test_chunk_is_whole_sequence():
+    """Tq = T: the chunk starts at position 0, so its first query blocks see
+    fewer than K_b blocks (dense) and the rest are searched."""
+    w = si.workload("prefill_32k_chunk4k", T=1536, Tq=1536, Hq=4, Hkv=1, k=512)
+    r = full_parity(si.make_inputs(w), w)
+    _report("whole_sequence", r)
+    assert r["exempt"] <= max(1, r["problems"] // 10)
+
+
 def test_zero_query_ties_exact():
     w = si.workload("prefill_32k_chunk4k", T=4096, Tq=128, Hq=4, Hkv=1, k=512)
     x = dict(si.make_inputs(w))
