@@ -18,7 +18,8 @@ copies of the layer's K/V and 16 query sets, so selected blocks differ from
 step to step and the selected bytes come from HBM, not from the 256 MB
 last-level cache.  Per-kernel launch durations for the roofline are taken the
 same way from graphs of one kernel each, with HIP events on the stream that
-the kernels run on.
+the kernels run on.  Decode lines also carry `mask_reuse`: µs per step when
+the mask is re-estimated only every r_m steps (attention every step).
 """
 from __future__ import annotations
 
@@ -260,6 +261,19 @@ def run_workload(w, steps, warmup, torch, hs, si, with_cpu, cpu_budget,
 
     res = {"ms_per_step": ms / steps, "wall_s": wall, "ms_mask": ms_mask, "ms_attn": ms_attn,
            "shifts": shifts}
+    if w.block_q == 1:
+        # mask reuse: the mask estimated every r_m steps, attention every step
+        reuse = {}
+        for r_m in (2, 4, 8):
+            def step_r(j, r_m=r_m):
+                if j % r_m == 0:
+                    mask(j)
+                attn(j)
+            g_r = graph_of(step_r, steps, torch)
+            g_r.replay()
+            reuse[r_m] = time_graph(g_r, 1, torch) / steps
+            del g_r
+        res["ms_reuse"] = reuse
     if with_cpu:
         times, nt = cpu_baseline(x, w, cpu_budget)
         res["cpu"] = {"times": times, "threads": nt}
@@ -318,6 +332,10 @@ def main():
                             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
                             "traffic": measured_traffic("decode", dom), "algorithmic_bytes": byt,
                             "launch_us": round(t_ms * 1e3, 3)}
+        line["mask_reuse"] = {"r_m": [1] + sorted(r["ms_reuse"]),
+                              "us_per_step": [round(us, 3)] + [round(r["ms_reuse"][k] * 1e3, 3)
+                                                               for k in sorted(r["ms_reuse"])],
+                              "attention_only_us": round(r["ms_attn"] * 1e3, 3)}
         step_gbs = nb["step"] / (r["ms_per_step"] * 1e-3) / 1e9
         line["step_roofline"] = {"algorithmic_bytes": nb["step"], "achieved": round(step_gbs, 1),
                                  "frac": round(step_gbs / HBM_PEAK_GBS, 4),

@@ -87,6 +87,22 @@ def test_spare_capacity_rows():
     _report("spare_capacity", r)
 
 
+def test_mask_reuse_across_steps():
+    """A mask estimated for one step's queries drives attention for the next
+    step's queries (mask refresh every r_m steps): the attention is exact
+    over the reused lists."""
+    import long_context_sparse_mask_amd as hs
+    w = si.workload("decode_32k", Hq=8, Hkv=2, T=6000, k=512)
+    x = _inputs(w)
+    q1 = torch.randn(x["q"].shape, generator=torch.Generator().manual_seed(7)).to(x["q"].dtype)
+    q0, q1d, K, V = x["q"].cuda(), q1.cuda(), x["K"].cuda(), x["V"].cuda()
+    idx, nnz = hs.hip_mask_estimate(q0, K, w.k, w.block_k, 1, T=w.T)
+    out = hs.hip_sparse_attn(q1d, K, V, idx, nnz, w.k, w.block_k, 1, T=w.T)
+    kw = dict(T=w.T, k=w.k, block_k=w.block_k, block_q=1, causal=w.causal)
+    ref = oracle.attn_all(q1, x["K"], x["V"], idx.cpu().numpy(), nnz.cpu().numpy(), **kw)
+    compare_attention(out, ref)
+
+
 def test_zero_query_ties_exact():
     """q = 0: every score is exactly 0 in any precision; the tie rule keeps the
     lowest block ids and the output is the mean of V over them."""
