@@ -3,9 +3,10 @@
 TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the bench's
 CPU-baseline leg may import this package; the product library never does.
 
-Inputs are CPU torch tensors (float32, or bfloat16 whose bits the C code
-widens exactly) in the library's layouts: q [B,Hq,Tq,d], K and V
-[B,Hkv,T_cap,d].  Outputs are numpy arrays; attention rows are float64.
+Inputs are CPU torch tensors in the library's layouts: q [B,Hq,Tq,d], K and V
+[B,Hkv,T_cap,d].  q is float32 or bfloat16; K and V share one type, float32,
+bfloat16 or float8_e5m2 (the C code decodes every one of them to double
+exactly).  Outputs are numpy arrays; attention rows are float64.
 """
 from __future__ import annotations
 
@@ -35,7 +36,7 @@ class Shape(C.Structure):
     _fields_ = [("B", C.c_int64), ("Hq", C.c_int64), ("Hkv", C.c_int64), ("Tq", C.c_int64),
                 ("T", C.c_int64), ("T_cap", C.c_int64), ("d", C.c_int64), ("k", C.c_int64),
                 ("block_k", C.c_int64), ("block_q", C.c_int64), ("causal", C.c_int32),
-                ("dtype", C.c_int32)]
+                ("dtype", C.c_int32), ("kv_dtype", C.c_int32)]
 
 
 class Trace(C.Structure):
@@ -64,6 +65,8 @@ def load(path: str | None = None):
     lib.or_attn_all.argtypes = [C.POINTER(Shape), P, P, P, P, P, P, I32]
     for f in (lib.or_mask_one, lib.or_mask_all, lib.or_attn_row, lib.or_attn_all):
         f.restype = C.c_int
+    lib.or_e5m2_value.argtypes = [C.c_uint8]
+    lib.or_e5m2_value.restype = C.c_double
     if path is None:
         _lib = lib
     return lib
@@ -77,19 +80,27 @@ def _ptr(t) -> int:
     return t.data_ptr()
 
 
-def _dtype_code(t: torch.Tensor) -> int:
-    if t.dtype == torch.float32:
-        return 0
-    if t.dtype == torch.bfloat16:
-        return 1
-    raise TypeError(f"oracle takes float32 or bfloat16, not {t.dtype}")
+_CODES = {torch.float32: 0, torch.bfloat16: 1, torch.float8_e5m2: 2}
+
+
+def _dtype_code(t: torch.Tensor, kv: bool = False) -> int:
+    code = _CODES.get(t.dtype)
+    if code is None or (code == 2 and not kv):
+        raise TypeError(f"oracle does not take {t.dtype} for {'K/V' if kv else 'q'}")
+    return code
 
 
 def shape(q, K, *, T, k, block_k, block_q, causal=1) -> Shape:
     B, Hq, Tq, d = q.shape
-    assert K.shape[0] == B and K.shape[3] == d and q.dtype == K.dtype
+    assert K.shape[0] == B and K.shape[3] == d
     return Shape(B, Hq, K.shape[1], Tq, T, K.shape[2], d, k, block_k, block_q, int(causal),
-                 _dtype_code(q))
+                 _dtype_code(q), _dtype_code(K, kv=True))
+
+
+def e5m2_values(lib=None) -> np.ndarray:
+    """The oracle's decoding of all 256 E5M2 codes, float64 [256]."""
+    lib = lib or load()
+    return np.array([lib.or_e5m2_value(c) for c in range(256)], np.float64)
 
 
 def nthreads(n: int | None = None) -> int:
@@ -162,6 +173,7 @@ def mask_one(q, K, b, g, qb, *, T, k, block_k, block_q, causal=1, trace=False, l
 def attn_all(q, K, V, indices, nnz, *, T, k, block_k, block_q, causal=1, threads=None, lib=None):
     """Exact attention over the listed blocks, float64 [B,Hq,Tq,d]."""
     lib = lib or load()
+    assert K.dtype == V.dtype and K.shape == V.shape
     s = shape(q, K, T=T, k=k, block_k=block_k, block_q=block_q, causal=causal)
     indices = np.ascontiguousarray(indices, np.int32)
     nnz = np.ascontiguousarray(nnz, np.int32)
@@ -174,6 +186,7 @@ def attn_all(q, K, V, indices, nnz, *, T, k, block_k, block_q, causal=1, threads
 
 def attn_row(q, K, V, indices, nnz, b, h, i, *, T, k, block_k, block_q, causal=1, lib=None):
     lib = lib or load()
+    assert K.dtype == V.dtype and K.shape == V.shape
     s = shape(q, K, T=T, k=k, block_k=block_k, block_q=block_q, causal=causal)
     indices = np.ascontiguousarray(indices, np.int32)
     nnz = np.ascontiguousarray(nnz, np.int32)

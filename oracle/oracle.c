@@ -6,8 +6,8 @@
  * bench's CPU-baseline leg do.  It shares no code with the GPU library.
  *
  * Plain, slow and literal on purpose: scalar loops, every value widened to
- * double (fp32 and bf16 inputs convert to double exactly), no blocking, no
- * fusion, no reordering beyond what the method states.
+ * double (fp32, bf16 and fp8-e5m2 inputs convert to double exactly), no
+ * blocking, no fusion, no reordering beyond what the method states.
  *
  * Sources (the web pages this follows):
  *  - "A Training-free Sub-quadratic Cost Transformer Model Serving Framework
@@ -22,6 +22,9 @@
  *  - Summary page "A Training-Free Sub-quadratic Cost Transformer Model
  *    Serving Framework with Hierarchically Pruned Attention", Approach:
  *    chunks are represented by their centre tokens; top-k is approximate.
+ *  - SGLang pull request "Support Efficient Sparse HiP Attention (InfiniteHiP)
+ *    ...", the launch command for the Qwen2.5-VL model: HiP runs with the KV
+ *    cache stored as fp8 e5m2.
  *
  * Readings taken where the pages are silent (each is pinned by a test):
  *  R1 chunk boundaries live on key-block boundaries; the search stops when
@@ -41,6 +44,10 @@
  *     first nnz listed blocks that the row may see (token < T_p, and token
  *     <= its position when causal); an empty set gives a zero row; listed
  *     ids outside [0, N_p) are ignored.
+ *  R9 an fp8 KV cache stores each K and V element as one OCP E5M2 code with
+ *     no scale factor (the launch command names the format and nothing
+ *     else); the method then runs unchanged on the decoded values, with the
+ *     query in its own element type.
  *
  * Layouts (contiguous, head-major): q [B,Hq,Tq,d]; K, V [B,Hkv,T_cap,d] with
  * rows 0..T-1 valid; indices [B,Hkv,NQB,K_b] (ascending, -1 past nnz);
@@ -53,11 +60,14 @@
 
 #define OR_F32 0
 #define OR_BF16 1
+#define OR_E5M2 2
 
 typedef struct {
   int64_t B, Hq, Hkv, Tq, T, T_cap, d;
   int64_t k, block_k, block_q;
-  int32_t causal, dtype;
+  int32_t causal;
+  int32_t dtype;    /* element type of q */
+  int32_t kv_dtype; /* element type of K and V */
 } or_shape;
 
 /* Optional search trace of one problem; arrays hold max_rounds * cap. */
@@ -71,8 +81,21 @@ typedef struct {
   double *rel_margin;      /* [max_rounds] */
 } or_trace;
 
+/* One OCP 8-bit float in the E5M2 layout: sign bit, 5 exponent bits with
+ * bias 15, 2 mantissa bits.  Exponent 0 is zero or subnormal (m/4 * 2^-14);
+ * exponent 31 is infinity (m = 0) or NaN; otherwise (1 + m/4) * 2^(e-15). */
+double or_e5m2_value(uint8_t code) {
+  const int sign = code >> 7, e = (code >> 2) & 31, m = code & 3;
+  double mag;
+  if (e == 31) mag = m == 0 ? INFINITY : NAN;
+  else if (e == 0) mag = ldexp(m / 4.0, -14);
+  else mag = ldexp(1.0 + m / 4.0, e - 15);
+  return sign ? -mag : mag;
+}
+
 static double elem(const void *base, int32_t dtype, int64_t i) {
   if (dtype == OR_F32) return (double)((const float *)base)[i];
+  if (dtype == OR_E5M2) return or_e5m2_value(((const uint8_t *)base)[i]);
   uint32_t bits = (uint32_t)((const uint16_t *)base)[i] << 16;
   float f;
   memcpy(&f, &bits, sizeof f);
@@ -96,7 +119,7 @@ static double dot_qk(const or_shape *s, const void *q, const void *K, int64_t b,
   int64_t qo = ((b * s->Hq + h) * s->Tq + i) * s->d;
   int64_t ko = ((b * s->Hkv + g) * s->T_cap + t) * s->d;
   double acc = 0.0;
-  for (int64_t x = 0; x < s->d; x++) acc += elem(q, s->dtype, qo + x) * elem(K, s->dtype, ko + x);
+  for (int64_t x = 0; x < s->d; x++) acc += elem(q, s->dtype, qo + x) * elem(K, s->kv_dtype, ko + x);
   return acc;
 }
 
@@ -272,7 +295,7 @@ int or_attn_row(const or_shape *s, const void *q, const void *K, const void *V,
       double w = exp(dot_qk(s, q, K, b, h, i, g, t) * scale - mx);
       den += w;
       int64_t vo = ((b * s->Hkv + g) * s->T_cap + t) * s->d;
-      for (int64_t x = 0; x < s->d; x++) out[x] += w * elem(V, s->dtype, vo + x);
+      for (int64_t x = 0; x < s->d; x++) out[x] += w * elem(V, s->kv_dtype, vo + x);
     }
   }
   for (int64_t x = 0; x < s->d; x++) out[x] /= den;

@@ -3,7 +3,8 @@
 Both the CPU oracle and the GPU library consume what this module makes; it
 holds none of the method's arithmetic (no scoring, no selection, no softmax).
 It only draws random numbers, shapes keys along the sequence with an AR(1)
-recurrence, scales the key rows of "needle" blocks, and rounds to bf16.
+recurrence, scales the key rows of "needle" blocks, and rounds to the
+workload's element types.
 
 Why AR(1) keys: the HiP summary page ("A Training-Free Sub-quadratic Cost
 Transformer Model Serving Framework with Hierarchically Pruned Attention",
@@ -22,7 +23,9 @@ Recipe (per workload, seed s):
     stream; the K rows of those blocks (all batch entries and kv heads) are
     multiplied by `needle_scale`.
   * everything is drawn in float32 and, for bf16 workloads, rounded once to
-    bf16 with round-to-nearest-even (torch's CPU cast).
+    bf16 with round-to-nearest-even (torch's CPU cast).  "bf16_e5m2"
+    workloads (an fp8 KV cache) round q to bf16 and K, V to fp8 E5M2, also
+    once and to nearest even, from the same float32 draws.
 """
 from __future__ import annotations
 
@@ -42,7 +45,7 @@ class Workload:
     Hq: int
     Hkv: int
     d: int
-    dtype: str          # "f32" or "bf16"
+    dtype: str          # "f32", "bf16" or "bf16_e5m2" (bf16 q, fp8 E5M2 K/V)
     T: int              # keys per sequence
     Tq: int             # query rows (1 = decode)
     block_k: int
@@ -119,9 +122,13 @@ def _ar1_slice(seq: np.random.SeedSequence, T: int, d: int, rho: float) -> np.nd
     return np.ascontiguousarray(x.T, dtype=np.float32)
 
 
-def _to_dtype(a: np.ndarray, dtype: str) -> torch.Tensor:
+_Q_TYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "bf16_e5m2": torch.bfloat16}
+_KV_TYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "bf16_e5m2": torch.float8_e5m2}
+
+
+def _to_dtype(a: np.ndarray, tdt: torch.dtype) -> torch.Tensor:
     t = torch.from_numpy(a)
-    return t.to(torch.bfloat16) if dtype == "bf16" else t.clone()
+    return t.clone() if tdt == torch.float32 else t.to(tdt)
 
 
 def needle_blocks(w: Workload) -> list[int]:
@@ -141,10 +148,10 @@ def make_inputs(w: Workload, T_cap: int | None = None) -> dict:
     T_cap = w.T if T_cap is None else T_cap
     assert T_cap >= w.T
     s_q, s_k, s_v, _ = np.random.SeedSequence(w.seed).spawn(4)
-    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    q = _to_dtype(_normal(s_q, (w.B, w.Hq, w.Tq, w.d)), w.dtype)
-    K = torch.zeros((w.B, w.Hkv, T_cap, w.d), dtype=tdt)
-    V = torch.zeros((w.B, w.Hkv, T_cap, w.d), dtype=tdt)
+    qdt, kvdt = _Q_TYPE[w.dtype], _KV_TYPE[w.dtype]
+    q = _to_dtype(_normal(s_q, (w.B, w.Hq, w.Tq, w.d)), qdt)
+    K = torch.zeros((w.B, w.Hkv, T_cap, w.d), dtype=kvdt)
+    V = torch.zeros((w.B, w.Hkv, T_cap, w.d), dtype=kvdt)
     k_seqs = s_k.spawn(w.B * w.Hkv)
     v_seqs = s_v.spawn(w.B * w.Hkv)
     needles = needle_blocks(w)
@@ -154,9 +161,9 @@ def make_inputs(w: Workload, T_cap: int | None = None) -> dict:
         ks = _ar1_slice(k_seqs[i], w.T, w.d, w.rho)
         for blk in needles:
             ks[blk * w.block_k:(blk + 1) * w.block_k] *= np.float32(w.needle_scale)
-        K[b, g, :w.T] = _to_dtype(ks, w.dtype)
+        K[b, g, :w.T] = _to_dtype(ks, kvdt)
         del ks
-        V[b, g, :w.T] = _to_dtype(_normal(v_seqs[i], (w.T, w.d)), w.dtype)
+        V[b, g, :w.T] = _to_dtype(_normal(v_seqs[i], (w.T, w.d)), kvdt)
 
     with ThreadPoolExecutor(_threads()) as ex:
         list(ex.map(fill, range(w.B * w.Hkv)))

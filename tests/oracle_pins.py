@@ -13,7 +13,11 @@ Kinds of pin used (no check re-derives the oracle's own formulas):
     are the prefix and the output is the mean of V;
   * invariants: convex combinations of V, constant V, a dominant key,
     scale invariance of the mask, equivariance under batch / head permutation,
-    the chunk tree structure and the round count.
+    the chunk tree structure and the round count;
+  * fp8 (E5M2) K/V: the oracle's decoding of all 256 codes against a
+    hand-derived table, torch's float8_e5m2 conversion and the identity
+    "E5M2 is the upper byte of IEEE binary16"; the fp8 path against dense
+    attention on torch-decoded values and against the float32 path.
 """
 from __future__ import annotations
 
@@ -367,9 +371,57 @@ def pin_mask_invariances(lib):
     assert (idxp == idx[[1, 0]][:, perm_g]).all()
 
 
+# ---------------------------------------------------------------- fp8 (E5M2) K/V
+
+def pin_e5m2_codes(lib):
+    got = oracle.e5m2_values(lib)
+    table = _golden("e5m2_codes.json")["values"]
+    for code, want in table.items():
+        c = int(code, 16)
+        if want == "nan":
+            assert math.isnan(got[c]), (code, got[c])
+        else:
+            w = float(want)
+            assert got[c] == w and math.copysign(1.0, got[c]) == math.copysign(1.0, w), (code, got[c])
+    codes = torch.arange(256, dtype=torch.uint8)
+    via_torch = codes.view(torch.float8_e5m2).to(torch.float64).numpy()
+    via_half = (codes.numpy().astype(np.uint16) << 8).view(np.float16).astype(np.float64)
+    for ref in (via_torch, via_half):
+        assert np.array_equal(np.isnan(got), np.isnan(ref))
+        fin = ~np.isnan(ref)
+        assert np.array_equal(got[fin], ref[fin])
+        assert np.array_equal(np.signbit(got[fin]), np.signbit(ref[fin]))
+
+
+def pin_e5m2_kv(lib):
+    """fp8 K/V: dense reduction against torch on torch-decoded values, and the
+    same mask and outputs as the float32 path on those values."""
+    rng = torch.Generator().manual_seed(11)
+    B, Hq, Hkv, d, T, bk = 1, 4, 2, 64, 200, 8
+    q = torch.randn(B, Hq, 1, d, generator=rng).to(torch.bfloat16)
+    K8 = (torch.randn(B, Hkv, T, d, generator=rng) * 2).to(torch.float8_e5m2)
+    V8 = torch.randn(B, Hkv, T, d, generator=rng).to(torch.float8_e5m2)
+    Kf, Vf = K8.float(), V8.float()
+    nblk = -(-T // bk)
+    kw = dict(T=T, block_k=bk, block_q=1, causal=1, threads=2, lib=lib)
+    idx, nnz, _ = oracle.mask_all(q, K8, k=nblk * bk, **kw)
+    out = oracle.attn_all(q, K8, V8, idx, nnz, k=nblk * bk, **kw)
+    ref = _dense_reference(q.float(), Kf, Vf, T, 1)
+    assert np.abs(out - ref).max() < 1e-10
+    k = 5 * bk  # sparse: 5 of 25 blocks
+    idx8, nnz8, m8 = oracle.mask_all(q, K8, k=k, **kw)
+    idxf, nnzf, mf = oracle.mask_all(q, Kf, k=k, **kw)
+    assert (idx8 == idxf).all() and (nnz8 == nnzf).all() and np.array_equal(m8, mf)
+    o8 = oracle.attn_all(q, K8, V8, idx8, nnz8, k=k, **kw)
+    of = oracle.attn_all(q, Kf, Vf, idx8, nnz8, k=k, **kw)
+    assert np.array_equal(o8, of)
+    assert not np.array_equal(o8, out)  # the sparse result differs from the dense one
+
+
 ALL_PINS = [
     pin_monotone_counterexample, pin_centre_tokens, pin_centre_blocks, pin_centre_partial_block,
     pin_uneven_partition, pin_causal_vote, pin_group_max, pin_dense_reduction,
     pin_exact_topk_monotone, pin_exact_topk_disjoint_chunks, pin_exact_topk_certified,
     pin_tree_structure, pin_zero_query_ties, pin_attention_invariants, pin_mask_invariances,
+    pin_e5m2_codes, pin_e5m2_kv,
 ]

@@ -38,6 +38,15 @@ MUTANTS = [
     ("dense_case_skipped", "if (Np <= Kb) {", "if (Np < 0) {"),
     ("score_sum_over_group", "if (v > best) best = v;",
      "best = (best == -INFINITY) ? v : best + v;"),
+    ("e5m2_bias_16", "mag = ldexp(1.0 + m / 4.0, e - 15);", "mag = ldexp(1.0 + m / 4.0, e - 16);"),
+    ("e5m2_three_mantissa_bits", "mag = ldexp(1.0 + m / 4.0, e - 15);",
+     "mag = ldexp(1.0 + m / 8.0, e - 15);"),
+    ("e5m2_subnormal_as_normal", "else if (e == 0) mag = ldexp(m / 4.0, -14);",
+     "else if (e == 0) mag = ldexp(1.0 + m / 4.0, -15);"),
+    ("e5m2_sign_dropped", "return sign ? -mag : mag;", "return mag;"),
+    ("e5m2_infinity_as_nan", "if (e == 31) mag = m == 0 ? INFINITY : NAN;", "if (e == 31) mag = NAN;"),
+    ("key_type_of_query", "elem(K, s->kv_dtype, ko + x)", "elem(K, s->dtype, ko + x)"),
+    ("value_type_of_query", "elem(V, s->kv_dtype, vo + x)", "elem(V, s->dtype, vo + x)"),
 ]
 
 
