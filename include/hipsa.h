@@ -31,9 +31,17 @@
  *    sees keys 0..T-Tq+i; with causal == 0 every row sees keys 0..T-1.  A
  *    query block's visible length T_p is the visible length of its last row;
  *    it covers N_p = ceil(T_p / block_k) key blocks, the last possibly partial.
- *  - dtype selects the element type of q, K, V and out: HIPSA_F32 (float) or
- *    HIPSA_BF16 (bfloat16 bits).  Dot products and softmax accumulate in fp32;
- *    outputs are rounded to the element type with round-to-nearest-even.
+ *  - dtype selects the element types: HIPSA_F32 (q, K, V, out float),
+ *    HIPSA_BF16 (all bfloat16 bits) or HIPSA_BF16_E5M2 (q and out bfloat16;
+ *    K and V one byte per element, an OCP 8-bit float code in the E5M2
+ *    layout: an fp8 KV cache, as HiP is served with --kv-cache-dtype
+ *    fp8_e5m2 in the SGLang pull request "Support Efficient Sparse HiP
+ *    Attention (InfiniteHiP) ...", Qwen2.5-VL launch command).  E5M2 codes
+ *    are decoded exactly and carry no scale; K and V codes must be finite
+ *    (an infinity or NaN code gives unspecified outputs).  Dot products and
+ *    softmax accumulate in fp32; outputs are rounded to their element type
+ *    with round-to-nearest-even.
+ *  - q, K, V and out must be 16-byte aligned (HIPSA_ERR_ALIGN otherwise).
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream), never synchronises, keeps no state between calls and is safe
  *    to call from several host threads.  Calls that share a workspace must be
@@ -46,8 +54,8 @@
  *
  * Supported shapes: d in {64, 128}; block_k in {8, 16, 32, 64}; 1 <= K_b <= 512;
  * 1 <= Hq/Hkv <= 16; T <= T_cap <= 2^30.  block_q = 1 (decode, and
- * per-row problems for any Tq) works for both dtypes; block_q = 64 (chunked
- * prefill) requires HIPSA_BF16.
+ * per-row problems for any Tq) works for every dtype; block_q = 64 (chunked
+ * prefill) requires HIPSA_BF16 or HIPSA_BF16_E5M2.
  */
 #ifndef HIPSA_H
 #define HIPSA_H
@@ -59,7 +67,7 @@
 extern "C" {
 #endif
 
-typedef enum { HIPSA_F32 = 0, HIPSA_BF16 = 1 } hipsa_dtype;
+typedef enum { HIPSA_F32 = 0, HIPSA_BF16 = 1, HIPSA_BF16_E5M2 = 2 } hipsa_dtype;
 
 typedef enum {
   HIPSA_OK = 0,
@@ -68,7 +76,8 @@ typedef enum {
   HIPSA_ERR_BLOCK = -3,     /* unsupported k, block_k or block_q                    */
   HIPSA_ERR_DTYPE = -4,     /* unsupported dtype, or dtype/block_q combination      */
   HIPSA_ERR_WORKSPACE = -5, /* workspace smaller than hipsa_workspace_bytes()       */
-  HIPSA_ERR_HIP = -6        /* a HIP runtime call or kernel launch failed           */
+  HIPSA_ERR_HIP = -6,       /* a HIP runtime call or kernel launch failed           */
+  HIPSA_ERR_ALIGN = -7      /* q, K, V or out is not 16-byte aligned                */
 } hipsa_status;
 
 typedef struct hipsa_desc {
@@ -99,7 +108,7 @@ typedef struct hipsa_desc {
  *     descending, start ascending).  Rounds repeat until every kept chunk is
  *     one block.
  * Writes indices[b,g,qb,0..nnz-1] in ascending order, -1 after them, and
- * nnz[b,g,qb].  q, K: element type `dtype`.  k: keys to keep, a multiple of
+ * nnz[b,g,qb].  q, K: element types per `dtype`.  k: keys to keep, a multiple of
  * block_k.  block_q: 1 or 64.  The workspace is unused by this call (pass
  * NULL and 0, or any buffer).
  */

@@ -7,6 +7,8 @@ built (``python -m long_context_sparse_mask_amd.build``).
 
 Layouts (contiguous): q [B,Hq,Tq,d]; K, V [B,Hkv,T_cap,d] with the first T
 rows valid; indices [B,Hkv,NQB,k/block_k] int32; nnz [B,Hkv,NQB] int32.
+Element types (q, K/V): (float32, float32), (bfloat16, bfloat16), or
+(bfloat16, float8_e5m2) for an fp8 KV cache; out has q's type.
 """
 from __future__ import annotations
 
@@ -24,7 +26,7 @@ if not os.path.exists(LIB_PATH):
 
 lib = C.CDLL(LIB_PATH)
 
-HIPSA_F32, HIPSA_BF16 = 0, 1
+HIPSA_F32, HIPSA_BF16, HIPSA_BF16_E5M2 = 0, 1, 2
 SIZE_MAX = (1 << (8 * C.sizeof(C.c_size_t))) - 1
 
 
@@ -57,19 +59,23 @@ def _check(rc: int):
         raise HipsaError(rc, lib.hipsa_last_error().decode())
 
 
-def _dtype_code(t: torch.Tensor) -> int:
-    if t.dtype == torch.bfloat16:
-        return HIPSA_BF16
-    if t.dtype == torch.float32:
-        return HIPSA_F32
-    raise TypeError(f"unsupported dtype {t.dtype}")
+_TYPE_PAIRS = {(torch.float32, torch.float32): HIPSA_F32,
+               (torch.bfloat16, torch.bfloat16): HIPSA_BF16,
+               (torch.bfloat16, torch.float8_e5m2): HIPSA_BF16_E5M2}
+
+
+def _dtype_code(q: torch.Tensor, K: torch.Tensor) -> int:
+    code = _TYPE_PAIRS.get((q.dtype, K.dtype))
+    if code is None:
+        raise TypeError(f"unsupported element types q={q.dtype}, K={K.dtype}")
+    return code
 
 
 def make_desc(q: torch.Tensor, K: torch.Tensor, T: int | None = None, causal: bool = True) -> Desc:
     B, Hq, Tq, d = q.shape
     _, Hkv, T_cap, _ = K.shape
     return Desc(B, Hq, Hkv, Tq, T_cap if T is None else T, T_cap, d, int(bool(causal)),
-                _dtype_code(q))
+                _dtype_code(q, K))
 
 
 def _stream(dev: torch.device, stream) -> int:
@@ -105,8 +111,6 @@ def hip_mask_estimate(q, K, k: int, block_k: int, block_q: int = 1, *, T=None, c
         indices = torch.empty((desc.B, desc.Hkv, nqb, kb), dtype=torch.int32, device=q.device)
     if nnz is None:
         nnz = torch.empty((desc.B, desc.Hkv, nqb), dtype=torch.int32, device=q.device)
-    if q.dtype != K.dtype:
-        raise TypeError("q and K must share a dtype")
     if tuple(indices.shape) != (desc.B, desc.Hkv, nqb, kb) or indices.dtype != torch.int32:
         raise ValueError("indices must be int32 [B, Hkv, NQB, k/block_k]")
     if tuple(nnz.shape) != (desc.B, desc.Hkv, nqb) or nnz.dtype != torch.int32:
@@ -124,8 +128,8 @@ def hip_sparse_attn(q, K, V, indices, nnz, k: int, block_k: int, block_q: int = 
     """Softmax attention of every query row over the tokens of its listed key
     blocks.  Returns out [B,Hq,Tq,d] in q's dtype."""
     desc = make_desc(q, K, T, causal)
-    if not (q.dtype == K.dtype == V.dtype):
-        raise TypeError("q, K and V must share a dtype")
+    if K.dtype != V.dtype:
+        raise TypeError("K and V must share a dtype")
     if V.shape != K.shape:
         raise ValueError("V must have K's shape")
     nqb = -(-desc.Tq // block_q)

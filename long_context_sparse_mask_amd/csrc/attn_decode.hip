@@ -171,8 +171,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
   }
 }
 
-// bf16 split workgroup on the matrix cores.  Per wave, TPW = TOK/4 token
-// slots:
+// Split workgroup on the matrix cores for a bf16 query, with bf16 or fp8
+// (E5M2) K/V.  Per wave, TPW = TOK/4 token slots:
 //   * the query heads of the group are the A operand of
 //     v_mfma_f32_16x16x32_bf16 (lane l holds head l%16, zero past the
 //     group) and the wave's K rows, 16 per tile, the B operand (lane l holds
@@ -180,22 +180,26 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
 //     accumulators: lane l, register r -> head 4*(l/16) + r, slot 16u + l%16;
 //   * softmax statistics are taken in that layout (DPP within 16-lane rows)
 //     and the probabilities go to a per-wave LDS table;
-//   * P.V runs with lanes owning output dimensions: one V row is one
-//     wave-wide load (D*2/64 bytes per lane), the probabilities are LDS
-//     broadcasts, and each lane accumulates its dimensions over every slot of
-//     the wave, so no cross-lane reduction of the outputs is needed.
+//   * P.V runs with lanes owning output dimensions: a lane loads EPL
+//     consecutive elements of a V row (4 bytes, or 2 for fp8 at d = 64), the
+//     probabilities are LDS broadcasts, and each lane accumulates its
+//     dimensions over every slot of the wave; when a row takes half a wave
+//     the two halves take alternate rows and are summed once at the end.
+// fp8 K rows are loaded as 8-byte slices and widened to bf16 operands in
+// registers (exact: every E5M2 value is a bf16 value).
 // Query loads are issued first: loads complete in order, so the first
 // matrix op then waits for the query and its K rows, not for the V rows
 // issued after them.
-template <int D, int GMAX, int TOK>
+template <typename KE, int D, int GMAX, int TOK>
 __global__ __launch_bounds__(256) void attn_decode_mfma(AttnArgs a) {
   constexpr int KS = D / 32;            // MFMA k-steps over the head dim
   constexpr int TPW = TOK / 4;          // token slots per wave
   constexpr int NT = TPW / 16;          // 16-slot tiles per wave
-  constexpr int LPV = D / 2 < 64 ? D / 2 : 64;  // lanes per V row (2 elements each)
+  constexpr int EPL = (sizeof(KE) == 1 && D == 128) ? 4 : 2;  // V elements per lane
+  constexpr int LPV = D / EPL < 64 ? D / EPL : 64;  // lanes per V row
   constexpr int RPV = 64 / LPV;         // V rows per wave-wide load
   constexpr int NV = TPW / RPV;         // V loads per lane
-  static_assert(NT >= 1 && TPW % RPV == 0, "split too small");
+  static_assert(NT >= 1 && TPW % RPV == 0 && RPV <= 2, "split too small");
   const Shape &s = a.s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t S = (uint32_t)a.splits;
@@ -213,8 +217,8 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(AttnArgs a) {
   __shared__ __align__(16) float wo[4][GMAX][D];
 
   const int64_t kvoff = (int64_t)(b * Hkv + g) * s.T_cap * D;
-  const uint16_t *Kp = reinterpret_cast<const uint16_t *>(a.K) + kvoff;
-  const uint16_t *Vp = reinterpret_cast<const uint16_t *>(a.V) + kvoff;
+  const KE *Kp = reinterpret_cast<const KE *>(a.K) + kvoff;
+  const KE *Vp = reinterpret_cast<const KE *>(a.V) + kvoff;
   const uint16_t *qbase = reinterpret_cast<const uint16_t *>(a.q) + ((int64_t)(b * s.Hq + g * s.G) * Tq + i) * D;
 
   // Token of slot lane % TPW of this wave (row of K/V), or -1 when the slot is
@@ -242,20 +246,20 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(AttnArgs a) {
     }
   }
   int32_t kt[NT];
-  uint4 kr[NT][KS];
+  typename Kv8<KE>::raw_t kr[NT][KS];
 #pragma unroll
   for (int u = 0; u < NT; u++) {
     kt[u] = __shfl(tk_lane, 16 * u + (lane & 15), 64);
 #pragma unroll
     for (int ks = 0; ks < KS; ks++)
-      kr[u][ks] = *reinterpret_cast<const uint4 *>(Kp + (int64_t)(kt[u] >= 0 ? kt[u] : 0) * D + 32 * ks + 8 * (lane >> 4));
+      kr[u][ks] = Kv8<KE>::raw(Kp + (int64_t)(kt[u] >= 0 ? kt[u] : 0) * D + 32 * ks + 8 * (lane >> 4));
   }
   int32_t vt[NV];
-  uint32_t vr[NV];
+  typename KvN<KE, EPL>::raw_t vr[NV];
 #pragma unroll
   for (int v = 0; v < NV; v++) {
     vt[v] = RPV == 1 ? __builtin_amdgcn_readlane(tk_lane, v) : __shfl(tk_lane, RPV * v + lane / LPV, 64);
-    vr[v] = *reinterpret_cast<const uint32_t *>(Vp + (int64_t)(vt[v] >= 0 ? vt[v] : 0) * D + 2 * (lane % LPV));
+    vr[v] = KvN<KE, EPL>::raw(Vp + (int64_t)(vt[v] >= 0 ? vt[v] : 0) * D + EPL * (lane % LPV));
   }
 
   // logits on the matrix cores, softmax statistics per head in the
@@ -266,7 +270,7 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(AttnArgs a) {
     acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ks++)
-      acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[ks]), as_bf16x8(kr[u][ks]), acc[u], 0, 0, 0);
+      acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[ks]), as_bf16x8(Kv8<KE>::bf16(kr[u][ks])), acc[u], 0, 0, 0);
   }
 #pragma unroll
   for (int r = 0; r < 4; r++) {
@@ -296,13 +300,15 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(AttnArgs a) {
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // P.V: lane owns dimensions 2*(lane % LPV) and +1 over the wave's slots;
-  // probabilities read 4 slots at a time (an LDS broadcast)
+  // P.V: lane owns dimensions EPL*(lane % LPV) .. +EPL-1 over the wave's
+  // slots; probabilities read 4 slots at a time (an LDS broadcast)
   constexpr int VPG = 4 / RPV;  // V loads per group of 4 slots
-  const int half = lane / LPV;  // d = 64: which of the two rows of a load
-  float o[GMAX][2];
+  const int half = lane / LPV;  // RPV = 2: which of the two rows of a load
+  float o[GMAX][EPL];
 #pragma unroll
-  for (int h = 0; h < GMAX; h++) o[h][0] = o[h][1] = 0.f;
+  for (int h = 0; h < GMAX; h++)
+#pragma unroll
+    for (int e = 0; e < EPL; e++) o[h][e] = 0.f;
 #pragma unroll
   for (int g4 = 0; g4 < TPW / 4; g4++) {
     // every one of the GMAX heads is computed (heads past the group have
@@ -314,26 +320,33 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(AttnArgs a) {
 #pragma unroll
     for (int vv = 0; vv < VPG; vv++) {
       const int v = g4 * VPG + vv;
-      const uint32_t w = vt[v] >= 0 ? vr[v] : 0u;
-      const float v0 = __uint_as_float(w << 16), v1 = __uint_as_float(w & 0xffff0000u);
+      float vx[EPL];
+      KvN<KE, EPL>::widen(vr[v], vt[v] >= 0, vx);
 #pragma unroll
       for (int h = 0; h < GMAX; h++) {
         float pj;
         if (RPV == 1) pj = vv == 0 ? p4[h].x : vv == 1 ? p4[h].y : vv == 2 ? p4[h].z : p4[h].w;
         else pj = vv == 0 ? (half ? p4[h].y : p4[h].x) : (half ? p4[h].w : p4[h].z);
-        o[h][0] = fmaf(pj, v0, o[h][0]);
-        o[h][1] = fmaf(pj, v1, o[h][1]);
+#pragma unroll
+        for (int e = 0; e < EPL; e++) o[h][e] = fmaf(pj, vx[e], o[h][e]);
       }
     }
   }
-  if (RPV == 2) {  // d = 64: the two halves of the wave took alternate rows
+  if (RPV == 2) {  // the two halves of the wave took alternate rows
 #pragma unroll
-    for (int h = 0; h < GMAX; h++) { o[h][0] = xor32_sum(o[h][0]); o[h][1] = xor32_sum(o[h][1]); }
+    for (int h = 0; h < GMAX; h++)
+#pragma unroll
+      for (int e = 0; e < EPL; e++) o[h][e] = xor32_sum(o[h][e]);
   }
   if (lane < LPV) {
 #pragma unroll
-    for (int h = 0; h < GMAX; h++)
-      if (h < s.G) *reinterpret_cast<float2 *>(&wo[wave][h][2 * lane]) = make_float2(o[h][0], o[h][1]);
+    for (int h = 0; h < GMAX; h++) {
+      if (h >= s.G) continue;
+      if constexpr (EPL == 4)
+        *reinterpret_cast<float4 *>(&wo[wave][h][4 * lane]) = make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
+      else
+        *reinterpret_cast<float2 *>(&wo[wave][h][2 * lane]) = make_float2(o[h][0], o[h][1]);
+    }
   }
   __syncthreads();
 
@@ -415,18 +428,20 @@ int tokens_per_split(const Shape &s) {
 }
 
 int tokens_for(const Shape &s) {
-  if (s.dtype == HIPSA_BF16)
+  if (s.dtype != HIPSA_F32)  // bf16 query: the matrix-core kernel, for either K/V type
     return s.d == 64 ? tokens_per_split<uint16_t, 64>(s) : tokens_per_split<uint16_t, 128>(s);
   return s.d == 64 ? tokens_per_split<float, 64>(s) : tokens_per_split<float, 128>(s);
 }
 
-template <typename E, int D, int GMAX>
+// E: query / output element type; KE: K/V element type (E itself, or E5M2
+// codes under a bf16 query).
+template <typename E, typename KE, int D, int GMAX>
 void launch_t(const AttnArgs &a, hipStream_t st, int tok) {
   constexpr int kMaxTok = max_tokens<E, D>();
   const dim3 grid((unsigned)(a.s.problems * a.splits)), block(256);
   if constexpr (std::is_same<E, uint16_t>::value) {
-    if (GMAX <= 8 && tok == 128) hipLaunchKernelGGL((attn_decode_mfma<D, (GMAX <= 8 ? GMAX : 8), 128>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((attn_decode_mfma<D, GMAX, 64>), grid, block, 0, st, a);
+    if (GMAX <= 8 && tok == 128) hipLaunchKernelGGL((attn_decode_mfma<KE, D, (GMAX <= 8 ? GMAX : 8), 128>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((attn_decode_mfma<KE, D, GMAX, 64>), grid, block, 0, st, a);
   } else {
     if (tok == 128) {
       if constexpr (kMaxTok >= 128) hipLaunchKernelGGL((attn_decode_kernel<E, D, GMAX, 128>), grid, block, 0, st, a);
@@ -436,14 +451,14 @@ void launch_t(const AttnArgs &a, hipStream_t st, int tok) {
   }
 }
 
-template <typename E, int D>
+template <typename E, typename KE, int D>
 hipError_t launch_d(const AttnArgs &a, hipStream_t st) {
   const int G = a.s.G, tok = tokens_per_split<E, D>(a.s);
-  if (G <= 1) launch_t<E, D, 1>(a, st, tok);
-  else if (G <= 2) launch_t<E, D, 2>(a, st, tok);
-  else if (G <= 4) launch_t<E, D, 4>(a, st, tok);
-  else if (G <= 8) launch_t<E, D, 8>(a, st, tok);
-  else launch_t<E, D, 16>(a, st, tok);
+  if (G <= 1) launch_t<E, KE, D, 1>(a, st, tok);
+  else if (G <= 2) launch_t<E, KE, D, 2>(a, st, tok);
+  else if (G <= 4) launch_t<E, KE, D, 4>(a, st, tok);
+  else if (G <= 8) launch_t<E, KE, D, 8>(a, st, tok);
+  else launch_t<E, KE, D, 16>(a, st, tok);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_decode_combine<E, D>), dim3((unsigned)(a.s.problems * G)), dim3(128), 0, st, a);
@@ -463,8 +478,10 @@ size_t attn_decode_workspace(const Shape &s) {
 
 hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t st) {
   if (a.s.dtype == HIPSA_BF16)
-    return a.s.d == 64 ? launch_d<uint16_t, 64>(a, st) : launch_d<uint16_t, 128>(a, st);
-  return a.s.d == 64 ? launch_d<float, 64>(a, st) : launch_d<float, 128>(a, st);
+    return a.s.d == 64 ? launch_d<uint16_t, uint16_t, 64>(a, st) : launch_d<uint16_t, uint16_t, 128>(a, st);
+  if (a.s.dtype == HIPSA_BF16_E5M2)
+    return a.s.d == 64 ? launch_d<uint16_t, uint8_t, 64>(a, st) : launch_d<uint16_t, uint8_t, 128>(a, st);
+  return a.s.d == 64 ? launch_d<float, float, 64>(a, st) : launch_d<float, float, 128>(a, st);
 }
 
 }  // namespace hipsa

@@ -1,4 +1,5 @@
-// Block-sparse attention for query blocks of 64 rows (chunked prefill, bf16).
+// Block-sparse attention for query blocks of 64 rows (chunked prefill: bf16
+// queries, bf16 or fp8 E5M2 K/V).
 //
 // Input contract: per (b, kv head, query block) a list of key-block ids and
 // its length nnz (rebuttal page "A Training-free Sub-quadratic Cost
@@ -15,8 +16,9 @@
 // operand reads per MFMA, but needs ~500 registers, leaves one wave per SIMD
 // and measured slower.)  Per tile of 64 keys:
 //   - the workgroup stages K and V row-major in a double-buffered LDS slot
-//     (16-byte stores); the global loads of the next tile are issued before
-//     this tile's math, and one barrier per tile suffices;
+//     (16-byte stores of bf16; fp8 slices are loaded as 8 bytes and widened
+//     exactly to bf16 on the way in); the global loads of the next tile are
+//     issued before this tile's math, and one barrier per tile suffices;
 //   - each wave forms S^T = K . Q^T (keys down the rows, its 32 queries
 //     across the columns), so a query's 64 scores sit in one lane pair and
 //     the online-softmax max and sum need one cross-half exchange; the two
@@ -106,7 +108,7 @@ __device__ inline void online_softmax(const f32x16_t (&sacc)[2], bool masked, co
   }
 }
 
-template <int D>
+template <typename KE, int D>
 __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnArgs a) {
   constexpr int KS = D / 16;   // k-steps of S^T over the head dim
   constexpr int DT = D / 32;   // 32-row tiles of O^T
@@ -148,8 +150,8 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnArgs a) {
   for (int j = tid; j < cnt; j += 512) lst[j] = list[j];
 
   const int64_t kvoff = (int64_t)(b * Hkv + g) * s.T_cap * D;
-  const uint16_t *Kg = reinterpret_cast<const uint16_t *>(a.K) + kvoff;
-  const uint16_t *Vg = reinterpret_cast<const uint16_t *>(a.V) + kvoff;
+  const KE *Kg = reinterpret_cast<const KE *>(a.K) + kvoff;
+  const KE *Vg = reinterpret_cast<const KE *>(a.V) + kvoff;
   const int hq = min(h, s.G - 1);
   const uint16_t *Qg = reinterpret_cast<const uint16_t *>(a.q) + ((int64_t)(b * s.Hq + g * s.G + hq) * Tq + r0) * D;
 
@@ -164,7 +166,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnArgs a) {
   __syncthreads();  // lst ready
 
   // loader state: this lane's K and V rows of the tile in flight
-  uint4 kreg[KP], vreg[KP];
+  typename Kv8<KE>::raw_t kreg[KP], vreg[KP];
   int32_t vtok = -1;
   const int krow0 = tid / TPR, kcol = (tid % TPR) * 8;
   // token of slot J of tile TL, or -1 (branch-free so the loads stay in flight)
@@ -182,16 +184,16 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnArgs a) {
       int32_t t;                                                                               \
       HIPSA_TOKEN(TL, u * RPP + krow0, t);                                                     \
       const int64_t off_ = (int64_t)(t >= 0 ? t : 0) * D + kcol;                               \
-      kreg[u] = *reinterpret_cast<const uint4 *>(Kg + off_);                                   \
-      vreg[u] = *reinterpret_cast<const uint4 *>(Vg + off_);                                   \
+      kreg[u] = Kv8<KE>::raw(Kg + off_);                                                       \
+      vreg[u] = Kv8<KE>::raw(Vg + off_);                                                       \
     }                                                                                          \
     HIPSA_TOKEN(TL, lane, vtok);                                                               \
   } while (0)
 #define HIPSA_LSTORE(BUF)                                                                      \
   do {                                                                                         \
     _Pragma("unroll") for (int u = 0; u < KP; u++) {                                           \
-      *reinterpret_cast<uint4 *>(&Ks[BUF][(u * RPP + krow0) * KPAD + kcol]) = kreg[u];         \
-      *reinterpret_cast<uint4 *>(&Vs[BUF][(u * RPP + krow0) * VPAD + kcol]) = vreg[u];         \
+      *reinterpret_cast<uint4 *>(&Ks[BUF][(u * RPP + krow0) * KPAD + kcol]) = Kv8<KE>::bf16(kreg[u]); \
+      *reinterpret_cast<uint4 *>(&Vs[BUF][(u * RPP + krow0) * VPAD + kcol]) = Kv8<KE>::bf16(vreg[u]); \
     }                                                                                          \
     if (wave == 0) {                                                                           \
       tok[BUF][lane] = vtok;                                                                   \
@@ -280,8 +282,13 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnArgs a) {
 hipError_t launch_attn_prefill(const AttnArgs &a, hipStream_t st) {
   const unsigned hchunks = (unsigned)(a.s.G + 3) / 4;
   const dim3 grid((unsigned)(a.s.problems * hchunks)), block(512);
-  if (a.s.d == 64) hipLaunchKernelGGL(attn_prefill_kernel<64>, grid, block, 0, st, a);
-  else hipLaunchKernelGGL(attn_prefill_kernel<128>, grid, block, 0, st, a);
+  if (a.s.dtype == HIPSA_BF16_E5M2) {
+    if (a.s.d == 64) hipLaunchKernelGGL((attn_prefill_kernel<uint8_t, 64>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((attn_prefill_kernel<uint8_t, 128>), grid, block, 0, st, a);
+  } else {
+    if (a.s.d == 64) hipLaunchKernelGGL((attn_prefill_kernel<uint16_t, 64>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((attn_prefill_kernel<uint16_t, 128>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
 

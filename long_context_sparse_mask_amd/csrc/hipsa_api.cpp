@@ -56,7 +56,7 @@ int check_shape(const hipsa_desc *d, int64_t k, int64_t block_k, int64_t block_q
                 (long long)d->T_cap);
   if (d->d != 64 && d->d != 128)
     return fail(HIPSA_ERR_SHAPE, "head dim d=%lld unsupported (64 or 128)", (long long)d->d);
-  if (d->dtype != HIPSA_F32 && d->dtype != HIPSA_BF16)
+  if (d->dtype != HIPSA_F32 && d->dtype != HIPSA_BF16 && d->dtype != HIPSA_BF16_E5M2)
     return fail(HIPSA_ERR_DTYPE, "dtype=%d unsupported", (int)d->dtype);
   if (!pow2_in(block_k, 8, 64))
     return fail(HIPSA_ERR_BLOCK, "block_k=%lld unsupported (8, 16, 32 or 64)",
@@ -69,8 +69,9 @@ int check_shape(const hipsa_desc *d, int64_t k, int64_t block_k, int64_t block_q
                 hipsa::kMaxKb);
   if (block_q != 1 && block_q != 64)
     return fail(HIPSA_ERR_BLOCK, "block_q=%lld unsupported (1 or 64)", (long long)block_q);
-  if (block_q == 64 && d->dtype != HIPSA_BF16)
-    return fail(HIPSA_ERR_DTYPE, "block_q=64 (prefill) needs bf16 inputs");
+  if (block_q == 64 && d->dtype == HIPSA_F32)
+    return fail(HIPSA_ERR_DTYPE, "block_q=64 (prefill) needs a bf16 query (HIPSA_BF16 or "
+                "HIPSA_BF16_E5M2)");
   s->B = d->B; s->Hq = d->Hq; s->Hkv = d->Hkv; s->Tq = d->Tq; s->T = d->T; s->T_cap = d->T_cap;
   s->d = d->d;
   s->G = (int32_t)(d->Hq / d->Hkv);
@@ -96,6 +97,14 @@ size_t workspace_for(const hipsa::Shape &s) {
   return 0;
 }
 
+// Vector loads and stores of 16 bytes need 16-byte aligned bases.
+int check_aligned(const void *const *p, const char *const *names, int n) {
+  for (int i = 0; i < n; i++)
+    if (reinterpret_cast<uintptr_t>(p[i]) % 16 != 0)
+      return fail(HIPSA_ERR_ALIGN, "%s at %p is not 16-byte aligned", names[i], p[i]);
+  return HIPSA_OK;
+}
+
 int hip_fail(hipError_t e, const char *what) {
   return fail(HIPSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -115,6 +124,11 @@ int hip_mask_estimate(const hipsa_desc *desc, const void *q, const void *K, int6
   if (s.problems == 0) return ok();
   if (!q || !K || !indices || !nnz)
     return fail(HIPSA_ERR_NULL, "q, K, indices and nnz must be non-NULL");
+  {
+    const void *p[] = {q, K};
+    const char *nm[] = {"q", "K"};
+    if ((rc = check_aligned(p, nm, 2))) return rc;
+  }
   hipsa::MaskArgs a{q, K, indices, nnz, s};
   hipError_t e = s.bq == 1 ? hipsa::launch_mask_decode(a, (hipStream_t)stream)
                            : hipsa::launch_mask_prefill(a, (hipStream_t)stream);
@@ -132,6 +146,11 @@ int hip_sparse_attn(const hipsa_desc *desc, const void *q, const void *K, const 
   if (s.problems == 0) return ok();
   if (!q || !K || !V || !indices || !nnz || !out)
     return fail(HIPSA_ERR_NULL, "q, K, V, indices, nnz and out must be non-NULL");
+  {
+    const void *p[] = {q, K, V, out};
+    const char *nm[] = {"q", "K", "V", "out"};
+    if ((rc = check_aligned(p, nm, 4))) return rc;
+  }
   const size_t need = workspace_for(s);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(HIPSA_ERR_WORKSPACE, "workspace of %zu bytes at %p is too small: need %zu",

@@ -93,6 +93,73 @@ template <> struct Vec<uint16_t> {
   __device__ static inline void load(const uint16_t *p, float (&v)[8]) { widen(raw(p), true, v); }
 };
 
+// ------------------------------------------------------------------ fp8 K/V (OCP E5M2)
+// An E5M2 code is the upper byte of the IEEE binary16 encoding of the same
+// value, and every E5M2 value (2 mantissa bits, magnitudes 2^-16 .. 57344)
+// is also exactly a bf16 value.  So a code widens exactly through binary16
+// to fp32, and that fp32's upper half is its bf16 encoding.
+__device__ inline float e5m2_to_f32(uint32_t code) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)((code & 0xffu) << 8));
+}
+// Codes in bytes 0 and 1 of w -> two bf16 in one word (byte 0 in the low half).
+__device__ inline uint32_t e5m2x2_to_bf16x2(uint32_t w) {
+  const uint32_t lo = __float_as_uint(e5m2_to_f32(w));
+  const uint32_t hi = __float_as_uint(e5m2_to_f32(w >> 8));
+  return (lo >> 16) | (hi & 0xffff0000u);
+}
+
+// Eight consecutive elements of a K or V row as one bf16 matrix-core operand
+// (16 bytes).  raw() issues the load (16 bytes of bf16, or 8 bytes of E5M2
+// codes); bf16() converts once the load has landed, so a batch of loads can
+// all be in flight before the first conversion.
+template <typename KE> struct Kv8;
+template <> struct Kv8<uint16_t> {
+  using raw_t = uint4;
+  __device__ static inline raw_t raw(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+  __device__ static inline uint4 bf16(raw_t r) { return r; }
+};
+template <> struct Kv8<uint8_t> {
+  using raw_t = uint2;
+  __device__ static inline raw_t raw(const uint8_t *p) { return *reinterpret_cast<const uint2 *>(p); }
+  __device__ static inline uint4 bf16(raw_t r) {
+    return make_uint4(e5m2x2_to_bf16x2(r.x), e5m2x2_to_bf16x2(r.x >> 16), e5m2x2_to_bf16x2(r.y),
+                      e5m2x2_to_bf16x2(r.y >> 16));
+  }
+};
+
+// N consecutive elements of a V row (N*sizeof(KE) = 2 or 4 bytes) widened to
+// fp32; a load that is not kept reads as zeros.
+template <typename KE, int N> struct KvN;
+template <> struct KvN<uint16_t, 2> {
+  using raw_t = uint32_t;
+  __device__ static inline raw_t raw(const uint16_t *p) { return *reinterpret_cast<const uint32_t *>(p); }
+  __device__ static inline void widen(raw_t w, bool keep, float (&v)[2]) {
+    w = keep ? w : 0u;
+    v[0] = __uint_as_float(w << 16);
+    v[1] = __uint_as_float(w & 0xffff0000u);
+  }
+};
+template <> struct KvN<uint8_t, 2> {
+  using raw_t = uint32_t;
+  __device__ static inline raw_t raw(const uint8_t *p) { return *reinterpret_cast<const uint16_t *>(p); }
+  __device__ static inline void widen(raw_t w, bool keep, float (&v)[2]) {
+    w = keep ? w : 0u;
+    v[0] = e5m2_to_f32(w);
+    v[1] = e5m2_to_f32(w >> 8);
+  }
+};
+template <> struct KvN<uint8_t, 4> {
+  using raw_t = uint32_t;
+  __device__ static inline raw_t raw(const uint8_t *p) { return *reinterpret_cast<const uint32_t *>(p); }
+  __device__ static inline void widen(raw_t w, bool keep, float (&v)[4]) {
+    w = keep ? w : 0u;
+    v[0] = e5m2_to_f32(w);
+    v[1] = e5m2_to_f32(w >> 8);
+    v[2] = e5m2_to_f32(w >> 16);
+    v[3] = e5m2_to_f32(w >> 24);
+  }
+};
+
 // MFMA operand / accumulator vectors (gfx950 bf16 matrix cores).
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));

@@ -12,11 +12,12 @@
 // slot of its pair and leaves the other empty) is double-buffered in LDS, so
 // a round is two phases separated by barriers:
 //   1. scoring.  Centre rows of K are read straight into matrix-core
-//      operands: for bf16 each wave scores 16 candidates per
+//      operands: for a bf16 query each wave scores 16 candidates per
 //      v_mfma_f32_16x16x32_bf16 tile against the query heads of the group
 //      (zero-padded to 16 rows), then takes the max over the valid head rows
 //      of the accumulator; fp32 inputs use 16-byte VALU dot products with DPP
-//      reductions instead.  Every load of a round is issued before any is used
+//      reductions instead.  fp8 (E5M2) keys are loaded as 8-byte slices and
+//      widened exactly to bf16 operands in registers.  Every load of a round is issued before any is used
 //      (an empty slot reads row 0 and discards it), so a round pays one memory
 //      latency;
 //   2. selection.  A candidate's rank is the number of keys above its own
@@ -35,7 +36,7 @@
 namespace hipsa {
 namespace {
 
-template <typename E, int D, int GMAX, int UNROLL>
+template <typename E, typename KE, int D, int GMAX, int UNROLL>
 __global__ __launch_bounds__(256) void mask_decode_kernel(MaskArgs a) {
   constexpr bool kMfma = std::is_same<E, uint16_t>::value;
   constexpr int VEC = Vec<E>::N;
@@ -65,7 +66,7 @@ __global__ __launch_bounds__(256) void mask_decode_kernel(MaskArgs a) {
   __shared__ int32_t flag[2];
 
   const E *qbase = reinterpret_cast<const E *>(a.q) + ((int64_t)(b * s.Hq + g * s.G) * Tq + i) * D;
-  const E *Kbase = reinterpret_cast<const E *>(a.K) + (int64_t)(b * Hkv + g) * s.T_cap * D;
+  const KE *Kbase = reinterpret_cast<const KE *>(a.K) + (int64_t)(b * Hkv + g) * s.T_cap * D;
 
   // Query operands, loaded once.  MFMA: lane l holds head l%16 (zero when
   // past the group), dims 32*ks + 8*(l/16) .. +7.  VALU: every head, dims
@@ -105,7 +106,7 @@ __global__ __launch_bounds__(256) void mask_decode_kernel(MaskArgs a) {
     if constexpr (kMfma) {
       const int ntile = (n + 15) / 16;
       for (int t0 = wave; t0 < ntile; t0 += 4 * UNROLL) {
-        uint4 kr[UNROLL][KS];
+        typename Kv8<KE>::raw_t kr[UNROLL][KS];
         bool live[UNROLL];
 #pragma unroll
         for (int u = 0; u < UNROLL; u++) {
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(256) void mask_decode_kernel(MaskArgs a) {
           const int32_t t = live[u] ? (lo + hi) >> 1 : 0;  // centre token (upper middle)
 #pragma unroll
           for (int ks = 0; ks < KS; ks++)
-            kr[u][ks] = Vec<E>::raw(Kbase + (int64_t)t * D + 32 * ks + 8 * (lane >> 4));
+            kr[u][ks] = Kv8<KE>::raw(Kbase + (int64_t)t * D + 32 * ks + 8 * (lane >> 4));
         }
 #pragma unroll
         for (int u = 0; u < UNROLL; u++) {
@@ -125,8 +126,8 @@ __global__ __launch_bounds__(256) void mask_decode_kernel(MaskArgs a) {
           f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int ks = 0; ks < KS; ks++)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[ks]), as_bf16x8(kr[u][ks]),
-                                                          acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[ks]),
+                                                          as_bf16x8(Kv8<KE>::bf16(kr[u][ks])), acc, 0, 0, 0);
           // acc[r] = score of head 4*(lane/16)+r for candidate lane%16
           float best = -INFINITY;
 #pragma unroll
@@ -192,15 +193,15 @@ __global__ __launch_bounds__(256) void mask_decode_kernel(MaskArgs a) {
 // child slot that holds each candidate's key).
 constexpr int kPipeMaxKb = 64;
 
-template <int D, int GMAX, int TPW>
-__device__ inline void score_children(const uint16_t *Kbase, const uint4 *qa, int32_t Tp, int bk_shift,
+template <typename KE, int D, int GMAX, int TPW>
+__device__ inline void score_children(const KE *Kbase, const uint4 *qa, int32_t Tp, int bk_shift,
                                       int G, const int32_t *ca, const int32_t *ce, int nslot,
                                       bool children, int wi, int nw, uint64_t *dst) {
   constexpr int KS = D / 32;
   const int lane = threadIdx.x & 63;
   const int ntile = (nslot + 15) / 16;
   for (int t0 = wi; t0 < ntile; t0 += nw * TPW) {
-    uint4 kr[TPW][KS];
+    typename Kv8<KE>::raw_t kr[TPW][KS];
     bool live[TPW];
     int32_t start[TPW];
 #pragma unroll
@@ -226,7 +227,7 @@ __device__ inline void score_children(const uint16_t *Kbase, const uint4 *qa, in
       const int32_t t = ok ? (tlo + thi) >> 1 : 0;  // centre token (upper middle)
 #pragma unroll
       for (int ks = 0; ks < KS; ks++)
-        kr[u][ks] = *reinterpret_cast<const uint4 *>(Kbase + (int64_t)t * D + 32 * ks + 8 * (lane >> 4));
+        kr[u][ks] = Kv8<KE>::raw(Kbase + (int64_t)t * D + 32 * ks + 8 * (lane >> 4));
     }
 #pragma unroll
     for (int u = 0; u < TPW; u++) {
@@ -234,7 +235,7 @@ __device__ inline void score_children(const uint16_t *Kbase, const uint4 *qa, in
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ks++)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[ks]), as_bf16x8(kr[u][ks]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[ks]), as_bf16x8(Kv8<KE>::bf16(kr[u][ks])), acc, 0, 0, 0);
       float best = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 4; r++)
@@ -246,7 +247,7 @@ __device__ inline void score_children(const uint16_t *Kbase, const uint4 *qa, in
   }
 }
 
-template <int D, int GMAX, int TPW>
+template <typename KE, int D, int GMAX, int TPW>
 __global__ __launch_bounds__(256) void mask_decode_pipe(MaskArgs a) {
   constexpr int KS = D / 32;
   const Shape &s = a.s;
@@ -273,7 +274,7 @@ __global__ __launch_bounds__(256) void mask_decode_pipe(MaskArgs a) {
   __shared__ int32_t flag[2];
 
   const uint16_t *qbase = reinterpret_cast<const uint16_t *>(a.q) + ((int64_t)(b * s.Hq + g * s.G) * Tq + i) * D;
-  const uint16_t *Kbase = reinterpret_cast<const uint16_t *>(a.K) + (int64_t)(b * Hkv + g) * s.T_cap * D;
+  const KE *Kbase = reinterpret_cast<const KE *>(a.K) + (int64_t)(b * Hkv + g) * s.T_cap * D;
   uint4 qa[KS];
   {
     const int h = lane & 15;
@@ -291,7 +292,7 @@ __global__ __launch_bounds__(256) void mask_decode_pipe(MaskArgs a) {
   if (tid == 0) flag[0] = 1;  // N_p > K_b: the first round always runs
   __syncthreads();
   // keys of the first candidates (all waves), kept where round 0 looks them up
-  score_children<D, GMAX, TPW>(Kbase, qa, Tp, s.bk_shift, s.G, cand_a[0], cand_e[0], n, false,
+  score_children<KE, D, GMAX, TPW>(Kbase, qa, Tp, s.bk_shift, s.G, cand_a[0], cand_e[0], n, false,
                                wave, 4, spec[1]);
   __syncthreads();
 
@@ -333,7 +334,7 @@ __global__ __launch_bounds__(256) void mask_decode_pipe(MaskArgs a) {
       }
     } else {
       // speculative: score every child of every current candidate
-      score_children<D, GMAX, TPW>(Kbase, qa, Tp, s.bk_shift, s.G, cand_a[cur], cand_e[cur], 2 * n,
+      score_children<KE, D, GMAX, TPW>(Kbase, qa, Tp, s.bk_shift, s.G, cand_a[cur], cand_e[cur], 2 * n,
                                    true, wave - 1, 3, spec[cur]);
     }
     __syncthreads();
@@ -343,18 +344,18 @@ __global__ __launch_bounds__(256) void mask_decode_pipe(MaskArgs a) {
   if (tid == 0) a.nnz[prob] = Kb;
 }
 
-template <int D, int GMAX>
+template <typename KE, int D, int GMAX>
 void launch_pipe(const MaskArgs &a, hipStream_t st) {
   const int tiles = (4 * a.s.Kb + 15) / 16;  // child tiles per round, over 3 waves
   const int per = (tiles + 2) / 3;
   const dim3 grid((unsigned)a.s.problems), block(256);
-  if (per <= 1) hipLaunchKernelGGL((mask_decode_pipe<D, GMAX, 1>), grid, block, 0, st, a);
-  else if (per <= 2) hipLaunchKernelGGL((mask_decode_pipe<D, GMAX, 2>), grid, block, 0, st, a);
-  else if (per <= 4) hipLaunchKernelGGL((mask_decode_pipe<D, GMAX, 4>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((mask_decode_pipe<D, GMAX, 8>), grid, block, 0, st, a);
+  if (per <= 1) hipLaunchKernelGGL((mask_decode_pipe<KE, D, GMAX, 1>), grid, block, 0, st, a);
+  else if (per <= 2) hipLaunchKernelGGL((mask_decode_pipe<KE, D, GMAX, 2>), grid, block, 0, st, a);
+  else if (per <= 4) hipLaunchKernelGGL((mask_decode_pipe<KE, D, GMAX, 4>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((mask_decode_pipe<KE, D, GMAX, 8>), grid, block, 0, st, a);
 }
 
-template <typename E, int D, int GMAX>
+template <typename E, typename KE, int D, int GMAX>
 void launch_g(const MaskArgs &a, hipStream_t st) {
   constexpr bool kMfma = std::is_same<E, uint16_t>::value;
   constexpr int RPP = 256 / (D / Vec<E>::N);
@@ -363,28 +364,32 @@ void launch_g(const MaskArgs &a, hipStream_t st) {
   // candidate rows per lane (VALU)
   const int per = kMfma ? ((n + 15) / 16 + 3) / 4 : (n + RPP - 1) / RPP;
   const dim3 grid((unsigned)a.s.problems), block(256);
-  if (per <= 1) hipLaunchKernelGGL((mask_decode_kernel<E, D, GMAX, 1>), grid, block, 0, st, a);
-  else if (per <= 2) hipLaunchKernelGGL((mask_decode_kernel<E, D, GMAX, 2>), grid, block, 0, st, a);
-  else if (per <= 4) hipLaunchKernelGGL((mask_decode_kernel<E, D, GMAX, 4>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((mask_decode_kernel<E, D, GMAX, 8>), grid, block, 0, st, a);
+  if (per <= 1) hipLaunchKernelGGL((mask_decode_kernel<E, KE, D, GMAX, 1>), grid, block, 0, st, a);
+  else if (per <= 2) hipLaunchKernelGGL((mask_decode_kernel<E, KE, D, GMAX, 2>), grid, block, 0, st, a);
+  else if (per <= 4) hipLaunchKernelGGL((mask_decode_kernel<E, KE, D, GMAX, 4>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((mask_decode_kernel<E, KE, D, GMAX, 8>), grid, block, 0, st, a);
 }
 
-template <typename E, int D>
+// E: query element type; KE: key element type (E itself, or E5M2 codes
+// under a bf16 query).
+template <typename E, typename KE, int D>
 hipError_t launch_d(const MaskArgs &a, hipStream_t st) {
   const int G = a.s.G;
-  if (std::is_same<E, uint16_t>::value && a.s.Kb <= kPipeMaxKb) {
-    if (G <= 1) launch_pipe<D, 1>(a, st);
-    else if (G <= 2) launch_pipe<D, 2>(a, st);
-    else if (G <= 4) launch_pipe<D, 4>(a, st);
-    else if (G <= 8) launch_pipe<D, 8>(a, st);
-    else launch_pipe<D, 16>(a, st);
-    return hipGetLastError();
+  if constexpr (std::is_same<E, uint16_t>::value) {
+    if (a.s.Kb <= kPipeMaxKb) {
+      if (G <= 1) launch_pipe<KE, D, 1>(a, st);
+      else if (G <= 2) launch_pipe<KE, D, 2>(a, st);
+      else if (G <= 4) launch_pipe<KE, D, 4>(a, st);
+      else if (G <= 8) launch_pipe<KE, D, 8>(a, st);
+      else launch_pipe<KE, D, 16>(a, st);
+      return hipGetLastError();
+    }
   }
-  if (G <= 1) launch_g<E, D, 1>(a, st);
-  else if (G <= 2) launch_g<E, D, 2>(a, st);
-  else if (G <= 4) launch_g<E, D, 4>(a, st);
-  else if (G <= 8) launch_g<E, D, 8>(a, st);
-  else launch_g<E, D, 16>(a, st);
+  if (G <= 1) launch_g<E, KE, D, 1>(a, st);
+  else if (G <= 2) launch_g<E, KE, D, 2>(a, st);
+  else if (G <= 4) launch_g<E, KE, D, 4>(a, st);
+  else if (G <= 8) launch_g<E, KE, D, 8>(a, st);
+  else launch_g<E, KE, D, 16>(a, st);
   return hipGetLastError();
 }
 
@@ -392,8 +397,10 @@ hipError_t launch_d(const MaskArgs &a, hipStream_t st) {
 
 hipError_t launch_mask_decode(const MaskArgs &a, hipStream_t st) {
   if (a.s.dtype == HIPSA_BF16)
-    return a.s.d == 64 ? launch_d<uint16_t, 64>(a, st) : launch_d<uint16_t, 128>(a, st);
-  return a.s.d == 64 ? launch_d<float, 64>(a, st) : launch_d<float, 128>(a, st);
+    return a.s.d == 64 ? launch_d<uint16_t, uint16_t, 64>(a, st) : launch_d<uint16_t, uint16_t, 128>(a, st);
+  if (a.s.dtype == HIPSA_BF16_E5M2)
+    return a.s.d == 64 ? launch_d<uint16_t, uint8_t, 64>(a, st) : launch_d<uint16_t, uint8_t, 128>(a, st);
+  return a.s.d == 64 ? launch_d<float, float, 64>(a, st) : launch_d<float, float, 128>(a, st);
 }
 
 }  // namespace hipsa

@@ -1,5 +1,5 @@
 // Hierarchical top-k key-block selection for query blocks of 64 rows
-// (chunked prefill, bf16).
+// (chunked prefill: bf16 queries, bf16 or fp8 E5M2 keys).
 //
 // Method: rebuttal page "A Training-free Sub-quadratic Cost Transformer Model
 // Serving Framework With Hierarchically Pruned Attention", reviewer RsGC, Q2
@@ -17,7 +17,9 @@
 // and takes the column max in registers; one cross-half exchange finishes the
 // 64-row max, and the per-head results meet in LDS through a 64-bit atomic
 // max on the candidate's ranking key (score above complemented start).
-// Selection and the final ascending write are the same as for decode.
+// Selection and the final ascending write are the same as for decode.  fp8
+// centre rows are loaded as 8-byte slices and widened exactly to bf16 on
+// their way into LDS.
 #include "hipsa_internal.h"
 #include "mask_select.h"
 
@@ -26,7 +28,7 @@ namespace {
 
 // ONEHEAD: the group has at most 4 query heads, so each wave owns one head
 // for the whole search and keeps its query operands in registers.
-template <int D, bool ONEHEAD>
+template <typename KE, int D, bool ONEHEAD>
 __global__ __launch_bounds__(256) void mask_prefill_kernel(MaskArgs a) {
   constexpr int KS = D / 16;  // k-steps of 16 over the head dim
   constexpr int BQ = 64;
@@ -56,14 +58,14 @@ __global__ __launch_bounds__(256) void mask_prefill_kernel(MaskArgs a) {
   __shared__ int32_t flag[2];
 
   const uint16_t *Qb = reinterpret_cast<const uint16_t *>(a.q) + ((int64_t)(b * s.Hq + g * s.G) * Tq + r0) * D;
-  const uint16_t *Kbase = reinterpret_cast<const uint16_t *>(a.K) + (int64_t)(b * Hkv + g) * s.T_cap * D;
+  const KE *Kbase = reinterpret_cast<const KE *>(a.K) + (int64_t)(b * Hkv + g) * s.T_cap * D;
   const int n = 2 * Kb, nct = (n + 31) / 32;
   // staging of 64 candidates' centre rows: SLR lanes per row, SRP rows per
   // pass, SP passes; rows padded to CRS elements (a column read of the 32
   // rows of a tile then falls in distinct banks per 16 lanes)
   constexpr int SLR = D / 8, SRP = 256 / SLR, SP = 64 / SRP, CRS = D + 8;
   __shared__ __attribute__((aligned(16))) uint16_t cst[64 * CRS];
-  uint4 srow[SP];
+  typename Kv8<KE>::raw_t srow[SP];
   const int half = lane >> 5, col = lane & 31;
 
   // A operand: rows rt*32 + col of head h, dims 16*ks + 8*half .. +7
@@ -106,11 +108,11 @@ __global__ __launch_bounds__(256) void mask_prefill_kernel(MaskArgs a) {
         const bool live = c < n && lo_b >= 0;
         const int32_t lo = lo_b << s.bk_shift, hi = min(hi_b << s.bk_shift, Tp);
         const int32_t t = live ? (lo + hi) >> 1 : 0;  // centre token (upper middle)
-        srow[u] = *reinterpret_cast<const uint4 *>(Kbase + (int64_t)t * D + 8 * (tid % SLR));
+        srow[u] = Kv8<KE>::raw(Kbase + (int64_t)t * D + 8 * (tid % SLR));
       }
 #pragma unroll
       for (int u = 0; u < SP; u++)
-        *reinterpret_cast<uint4 *>(&cst[(u * SRP + tid / SLR) * CRS + 8 * (tid % SLR)]) = srow[u];
+        *reinterpret_cast<uint4 *>(&cst[(u * SRP + tid / SLR) * CRS + 8 * (tid % SLR)]) = Kv8<KE>::bf16(srow[u]);
       __syncthreads();
       for (int h = wave; h < s.G; h += 4) {
         if (!ONEHEAD) load_queries(h);
@@ -157,18 +159,24 @@ __global__ __launch_bounds__(256) void mask_prefill_kernel(MaskArgs a) {
   if (tid == 0) a.nnz[prob] = Kb;
 }
 
-}  // namespace
-
-hipError_t launch_mask_prefill(const MaskArgs &a, hipStream_t st) {
+template <typename KE>
+void launch_k(const MaskArgs &a, hipStream_t st) {
   const dim3 grid((unsigned)a.s.problems), block(256);
   const bool one = a.s.G <= 4;
   if (a.s.d == 64) {
-    if (one) hipLaunchKernelGGL((mask_prefill_kernel<64, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((mask_prefill_kernel<64, false>), grid, block, 0, st, a);
+    if (one) hipLaunchKernelGGL((mask_prefill_kernel<KE, 64, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((mask_prefill_kernel<KE, 64, false>), grid, block, 0, st, a);
   } else {
-    if (one) hipLaunchKernelGGL((mask_prefill_kernel<128, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((mask_prefill_kernel<128, false>), grid, block, 0, st, a);
+    if (one) hipLaunchKernelGGL((mask_prefill_kernel<KE, 128, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((mask_prefill_kernel<KE, 128, false>), grid, block, 0, st, a);
   }
+}
+
+}  // namespace
+
+hipError_t launch_mask_prefill(const MaskArgs &a, hipStream_t st) {
+  if (a.s.dtype == HIPSA_BF16_E5M2) launch_k<uint8_t>(a, st);
+  else launch_k<uint16_t>(a, st);
   return hipGetLastError();
 }
 

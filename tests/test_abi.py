@@ -52,7 +52,7 @@ def _mask(desc, k=2048, bk=64, bq=1, ptrs=(FAKE, FAKE, FAKE, FAKE)):
     return hs.lib.hip_mask_estimate(C.byref(desc), q, K, k, bk, bq, idx, nnz, None, 0, None)
 
 
-ERR_NULL, ERR_SHAPE, ERR_BLOCK, ERR_DTYPE, ERR_WS = -1, -2, -3, -4, -5
+ERR_NULL, ERR_SHAPE, ERR_BLOCK, ERR_DTYPE, ERR_WS, ERR_ALIGN = -1, -2, -3, -4, -5, -7
 
 
 @pytest.mark.parametrize("kw,k,bk,bq,code", [
@@ -100,6 +100,46 @@ def test_workspace_query_and_undersized_workspace():
     assert rc == ERR_WS and "too small" in hs.lib.hipsa_last_error().decode()
     bad = _desc(Hq=31)
     assert hs.lib.hipsa_workspace_bytes(C.byref(bad), 2048, 64, 1) == hs.SIZE_MAX
+
+
+def test_fp8_kv_dtype_is_accepted_for_decode_and_prefill():
+    """HIPSA_BF16_E5M2 (bf16 q, E5M2 K/V) passes validation for block_q 1 and 64
+    (checked through the workspace query, which launches nothing); fp32 prefill
+    stays rejected."""
+    import long_context_sparse_mask_amd as hs
+    d = _desc(B=4, T=131072, T_cap=131072, dtype=hs.HIPSA_BF16_E5M2)
+    assert hs.lib.hipsa_workspace_bytes(C.byref(d), 2048, 64, 1) == 32 * 16 * 4 * 130 * 4
+    p = _desc(Tq=4096, dtype=hs.HIPSA_BF16_E5M2)
+    assert hs.lib.hipsa_workspace_bytes(C.byref(p), 2048, 64, 64) == 0
+    assert hs.lib.hipsa_workspace_bytes(C.byref(_desc(Tq=4096, dtype=0)), 2048, 64, 64) == hs.SIZE_MAX
+    assert hs.lib.hipsa_workspace_bytes(C.byref(_desc(dtype=3)), 2048, 64, 1) == hs.SIZE_MAX
+
+
+def test_misaligned_pointers_rejected():
+    import long_context_sparse_mask_amd as hs
+    odd = C.c_void_p(0x1008)
+    for i in range(2):  # q, K
+        ptrs = [FAKE] * 4
+        ptrs[i] = odd
+        assert _mask(_desc(), ptrs=tuple(ptrs)) == ERR_ALIGN
+        assert "aligned" in hs.lib.hipsa_last_error().decode()
+    d = _desc()
+    for i in (0, 1, 2, 9):  # q, K, V, out
+        args = [FAKE, FAKE, FAKE, FAKE, FAKE, 2048, 64, 1, FAKE, FAKE, 1 << 30, None]
+        args[i if i < 5 else 8] = odd
+        assert hs.lib.hip_sparse_attn(C.byref(d), *args) == ERR_ALIGN
+
+
+def test_binding_element_type_pairs():
+    import torch
+    import long_context_sparse_mask_amd as hs
+    q16, q32 = torch.empty(1, dtype=torch.bfloat16), torch.empty(1)
+    k8 = torch.empty(1, dtype=torch.float8_e5m2)
+    assert hs._dtype_code(q16, k8) == hs.HIPSA_BF16_E5M2
+    assert hs._dtype_code(q16, q16) == hs.HIPSA_BF16 and hs._dtype_code(q32, q32) == hs.HIPSA_F32
+    for q, k in ((q32, k8), (q32, q16), (q16, q32), (k8, k8)):
+        with pytest.raises(TypeError):
+            hs._dtype_code(q, k)
 
 
 def test_empty_problem_is_a_no_op():
