@@ -45,16 +45,20 @@ def rounds_of(Np: int, Kb: int) -> int:
     return 0 if Np <= Kb else int(math.ceil(math.log2(Np / Kb)))
 
 
+# bytes per element of (q and out, K and V) for each workload element type
+ELEM_BYTES = {"f32": (4, 4), "bf16": (2, 2), "bf16_e5m2": (2, 1)}
+
+
 def decode_bytes(w) -> dict:
     """Algorithmic HBM bytes of one decode step (what the method must move)."""
-    esz = 2 if w.dtype == "bf16" else 4
-    row = w.d * esz
+    qsz, kvsz = ELEM_BYTES[w.dtype]
+    row = w.d * kvsz
     P = w.B * w.Hkv * w.Tq
     Np = -(-w.T // w.block_k)
     R = rounds_of(Np, w.kb)
     centre = P * R * 2 * w.kb * row
     kv = P * 2 * min(w.kb, Np) * w.block_k * row
-    q = w.B * w.Hq * w.Tq * row
+    q = w.B * w.Hq * w.Tq * w.d * qsz
     idx = P * (w.kb + 1) * 4
     return {"centre": centre, "kv": kv, "q": q, "out": q, "indices": idx, "rounds": R,
             "mask": centre + q + idx, "attn": kv + 2 * q + idx, "step": centre + kv + 3 * q + 2 * idx}
@@ -105,7 +109,22 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kind: str, call: str):
+def kernel_matches(kernel: str, dtype: str) -> bool:
+    """Whether a profiled instantiation (name with template arguments) serves a
+    workload of element type `dtype`: kernels that read K/V by their K/V type
+    (unsigned char = E5M2 codes, unsigned short = bf16, float), the decode
+    combine (which never reads K/V) by its output type."""
+    args = kernel.split("<", 1)[1] if "<" in kernel else ""
+    if kernel.startswith("attn_decode_combine"):
+        return ("float" in args) == (dtype == "f32")
+    if "unsigned char" in args:
+        return dtype == "bf16_e5m2"
+    if "unsigned short" in args:
+        return dtype == "bf16"
+    return dtype == "f32"
+
+
+def measured_traffic(kind: str, call: str, dtype: str = "bf16"):
     """HBM bytes per launch from profiles/hbm_traffic.md (FETCH_SIZE + WRITE_SIZE,
     copy-calibrated), or None when the kernels changed since it was taken."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
@@ -117,7 +136,8 @@ def measured_traffic(kind: str, call: str):
     if blob.get("source_sha") != kernel_source_sha():
         return None
     names = CALL_KERNELS[(kind, call)]
-    hits = [v["traffic_bytes"] for k, v in blob["kernels"].items() if k.startswith(names)]
+    hits = [v["traffic_bytes"] for k, v in blob["kernels"].items()
+            if k.startswith(names) and kernel_matches(k, dtype)]
     return sum(hits) if hits else None
 
 
@@ -197,14 +217,17 @@ def time_graph(g, reps, torch):
 def setup(w, x, torch, dev, n_layers=N_LAYER_COPIES, n_q=N_QUERY_SETS):
     """Device copies: n_layers rolled K/V layers and n_q query sets."""
     K0, V0 = x["K"].to(dev), x["V"].to(dev)
+    kvdt = K0.dtype
+    if K0.element_size() == 1:  # fp8 codes: roll the bytes
+        K0, V0 = K0.view(torch.uint8), V0.view(torch.uint8)
     gen = torch.Generator(device=dev)
     gen.manual_seed(w.seed)
     shifts = [0] + [int(s) for s in torch.randint(1, w.T, (n_layers - 1,), generator=gen,
                                                    device=dev).tolist()]
-    layers = [(torch.roll(K0, s, dims=2).contiguous(), torch.roll(V0, s, dims=2).contiguous())
-              for s in shifts]
+    layers = [(torch.roll(K0, s, dims=2).contiguous().view(kvdt),
+               torch.roll(V0, s, dims=2).contiguous().view(kvdt)) for s in shifts]
     del K0, V0
-    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    tdt = x["q"].dtype
     qs = [x["q"].to(dev)]
     for _ in range(n_q - 1):
         qs.append(torch.randn(x["q"].shape, generator=gen, device=dev, dtype=torch.float32).to(tdt))
@@ -288,6 +311,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_128k_b4")
+    ap.add_argument("--kv", choices=["native", "e5m2"], default="native",
+                    help="e5m2: run the workload with an fp8 (E5M2) KV cache")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 KV cache leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
@@ -308,6 +334,8 @@ def main():
     import synth_inputs as si
 
     w = si.workload(args.workload)
+    if args.kv == "e5m2":
+        w = si.workload(args.workload, dtype="bf16_e5m2")
     is_decode = w.block_q == 1
     r = run_workload(w, args.steps, args.warmup, torch, hs, si, not args.no_cpu_baseline,
                      args.cpu_budget, args.layer_copies, args.query_sets)
@@ -330,7 +358,7 @@ def main():
         ach = byt / (t_ms * 1e-3) / 1e9
         line["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1),
                             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                            "traffic": measured_traffic("decode", dom), "algorithmic_bytes": byt,
+                            "traffic": measured_traffic("decode", dom, w.dtype), "algorithmic_bytes": byt,
                             "launch_us": round(t_ms * 1e3, 3)}
         line["mask_reuse"] = {"r_m": [1] + sorted(r["ms_reuse"]),
                               "us_per_step": [round(us, 3)] + [round(r["ms_reuse"][k] * 1e3, 3)
@@ -355,7 +383,7 @@ def main():
         line["roofline"] = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2),
                             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                             "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
-                            "traffic": measured_traffic("prefill", dom),
+                            "traffic": measured_traffic("prefill", dom, w.dtype),
                             "algorithmic_flops": f, "launch_us": round(t_ms * 1e3, 3)}
         line["step_roofline"] = {"algorithmic_flops": fl["total"], "achieved_tflops": round(tflops, 2),
                                  "mask_us": round(r["ms_mask"] * 1e3, 3),
@@ -371,7 +399,28 @@ def main():
                                 "sample": f"whole {w.name} step on the first query set and layer copy, "
                                           f"median of {len(r['cpu']['times'])} runs, fp64 C + OpenMP",
                                 "cpu_model": host_cpu_model()}
-    if is_decode and not args.no_prefill and args.workload == "decode_128k_b4":
+    headline = is_decode and args.workload == "decode_128k_b4" and args.kv == "native"
+    if headline and not args.no_fp8:
+        # the same step with an fp8 (E5M2) KV cache: half the K/V bytes
+        w8 = si.workload(args.workload, dtype="bf16_e5m2")
+        r8 = run_workload(w8, args.steps, args.warmup, torch, hs, si, False, 0,
+                          args.layer_copies, args.query_sets)
+        nb8 = decode_bytes(w8)
+        a_gbs = nb8["attn"] / (r8["ms_attn"] * 1e-3) / 1e9
+        s_gbs = nb8["step"] / (r8["ms_per_step"] * 1e-3) / 1e9
+        line["fp8_kv"] = {"workload": w8.name, "dtype": w8.dtype,
+                          "us_per_step": round(r8["ms_per_step"] * 1e3, 3),
+                          "mask_us": round(r8["ms_mask"] * 1e3, 3),
+                          "attn_us": round(r8["ms_attn"] * 1e3, 3),
+                          "attn_roofline": {"algorithmic_bytes": nb8["attn"], "achieved": round(a_gbs, 1),
+                                            "frac": round(a_gbs / HBM_PEAK_GBS, 4),
+                                            "traffic": measured_traffic("decode", "hip_sparse_attn",
+                                                                        w8.dtype)},
+                          "step_roofline": {"algorithmic_bytes": nb8["step"], "achieved": round(s_gbs, 1),
+                                            "frac": round(s_gbs / HBM_PEAK_GBS, 4)},
+                          "mask_reuse_us": {str(k): round(v * 1e3, 3)
+                                            for k, v in sorted(r8["ms_reuse"].items())}}
+    if headline and not args.no_prefill:
         wp = si.workload("prefill_32k_chunk4k")
         rp = run_workload(wp, max(4, args.steps // 20), max(1, args.warmup // 10), torch, hs, si,
                           False, 0)
@@ -384,6 +433,13 @@ def main():
                            "mfma_frac": round(fl["total"] / (rp["ms_per_step"] * 1e-3) / 1e12
                                               / MFMA_BF16_PEAK_TFLOPS, 4),
                            "algorithmic_flops": fl["total"]}
+        if not args.no_fp8:
+            wp8 = si.workload("prefill_32k_chunk4k", dtype="bf16_e5m2")
+            rp8 = run_workload(wp8, max(4, args.steps // 20), max(1, args.warmup // 10), torch, hs,
+                               si, False, 0)
+            line["prefill"]["fp8_kv"] = {"tok_per_s": round(wp8.Tq / (rp8["ms_per_step"] * 1e-3), 1),
+                                         "mask_us": round(rp8["ms_mask"] * 1e3, 2),
+                                         "attn_us": round(rp8["ms_attn"] * 1e3, 2)}
         if not args.no_cpu_baseline:
             line["prefill"]["cpu_baseline"] = cpu_baseline_prefill(si, args.cpu_budget)
     if args.copy_calibration:

@@ -94,18 +94,18 @@ template <> struct Vec<uint16_t> {
 };
 
 // ------------------------------------------------------------------ fp8 K/V (OCP E5M2)
-// An E5M2 code is the upper byte of the IEEE binary16 encoding of the same
-// value, and every E5M2 value (2 mantissa bits, magnitudes 2^-16 .. 57344)
-// is also exactly a bf16 value.  So a code widens exactly through binary16
-// to fp32, and that fp32's upper half is its bf16 encoding.
-__device__ inline float e5m2_to_f32(uint32_t code) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)((code & 0xffu) << 8));
+// gfx950 converts OCP E5M2 codes ("bf8" in the ISA) in hardware, two per
+// instruction, taken from the low or the high 16-bit half of a register:
+// v_cvt_pk_f32_bf8 to two fp32, v_cvt_scalef32_pk_bf16_bf8 (scale 1) to two
+// bf16.  Both are exact for every finite code: an E5M2 value has 2 mantissa
+// bits and magnitude 2^-16 .. 57344, so it is also an fp32 and a bf16 value.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+template <bool HI> __device__ inline uint32_t e5m2x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, HI));
 }
-// Codes in bytes 0 and 1 of w -> two bf16 in one word (byte 0 in the low half).
-__device__ inline uint32_t e5m2x2_to_bf16x2(uint32_t w) {
-  const uint32_t lo = __float_as_uint(e5m2_to_f32(w));
-  const uint32_t hi = __float_as_uint(e5m2_to_f32(w >> 8));
-  return (lo >> 16) | (hi & 0xffff0000u);
+template <bool HI> __device__ inline f32x2_t e5m2x2_to_f32x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_bf8(w, HI);
 }
 
 // Eight consecutive elements of a K or V row as one bf16 matrix-core operand
@@ -122,8 +122,8 @@ template <> struct Kv8<uint8_t> {
   using raw_t = uint2;
   __device__ static inline raw_t raw(const uint8_t *p) { return *reinterpret_cast<const uint2 *>(p); }
   __device__ static inline uint4 bf16(raw_t r) {
-    return make_uint4(e5m2x2_to_bf16x2(r.x), e5m2x2_to_bf16x2(r.x >> 16), e5m2x2_to_bf16x2(r.y),
-                      e5m2x2_to_bf16x2(r.y >> 16));
+    return make_uint4(e5m2x2_to_bf16x2<false>(r.x), e5m2x2_to_bf16x2<true>(r.x),
+                      e5m2x2_to_bf16x2<false>(r.y), e5m2x2_to_bf16x2<true>(r.y));
   }
 };
 
@@ -143,9 +143,9 @@ template <> struct KvN<uint8_t, 2> {
   using raw_t = uint32_t;
   __device__ static inline raw_t raw(const uint8_t *p) { return *reinterpret_cast<const uint16_t *>(p); }
   __device__ static inline void widen(raw_t w, bool keep, float (&v)[2]) {
-    w = keep ? w : 0u;
-    v[0] = e5m2_to_f32(w);
-    v[1] = e5m2_to_f32(w >> 8);
+    const f32x2_t a = e5m2x2_to_f32x2<false>(keep ? w : 0u);
+    v[0] = a.x;
+    v[1] = a.y;
   }
 };
 template <> struct KvN<uint8_t, 4> {
@@ -153,10 +153,11 @@ template <> struct KvN<uint8_t, 4> {
   __device__ static inline raw_t raw(const uint8_t *p) { return *reinterpret_cast<const uint32_t *>(p); }
   __device__ static inline void widen(raw_t w, bool keep, float (&v)[4]) {
     w = keep ? w : 0u;
-    v[0] = e5m2_to_f32(w);
-    v[1] = e5m2_to_f32(w >> 8);
-    v[2] = e5m2_to_f32(w >> 16);
-    v[3] = e5m2_to_f32(w >> 24);
+    const f32x2_t a = e5m2x2_to_f32x2<false>(w), b = e5m2x2_to_f32x2<true>(w);
+    v[0] = a.x;
+    v[1] = a.y;
+    v[2] = b.x;
+    v[3] = b.y;
   }
 };
 

@@ -29,6 +29,26 @@ def test_decode_bytes_128k_b4():
     assert nb["step"] == nb["mask"] + nb["attn"] + nb["out"] - nb["q"]
 
 
+def test_decode_bytes_fp8_kv():
+    """An E5M2 KV cache halves the centre-row and K/V bytes; q and out stay bf16."""
+    nb = bench.decode_bytes(si.workload("decode_128k_b4", dtype="bf16_e5m2"))
+    assert nb["centre"] == 3 * 2 ** 19 and nb["kv"] == 16 * 2 ** 20
+    assert nb["q"] == nb["out"] == 4 * 32 * 256
+    assert nb["step"] == 3 * 2 ** 19 + 16 * 2 ** 20 + 3 * 4 * 32 * 256 + 2 * 32 * 33 * 4
+
+
+def test_traffic_lookup_separates_element_types():
+    m = bench.kernel_matches
+    bf = "attn_decode_mfma<unsigned short, 128, 4, 128>"
+    f8 = "attn_decode_mfma<unsigned char, 128, 4, 128>"
+    assert m(bf, "bf16") and not m(bf, "bf16_e5m2") and m(f8, "bf16_e5m2") and not m(f8, "bf16")
+    mk8 = "mask_decode_kernel<unsigned short, unsigned char, 128, 4, 2>"
+    assert m(mk8, "bf16_e5m2") and not m(mk8, "bf16")
+    comb = "attn_decode_combine<unsigned short, 128>"
+    assert m(comb, "bf16") and m(comb, "bf16_e5m2") and not m(comb, "f32")
+    assert m("attn_decode_kernel<float, 64, 1, 64>", "f32")
+
+
 def test_decode_bytes_dense_case():
     """k >= T: no search rounds, every block attended."""
     w = si.workload("tiny_decode", k=1024)
