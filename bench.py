@@ -234,27 +234,67 @@ def setup(w, x, torch, dev, n_layers=N_LAYER_COPIES, n_q=N_QUERY_SETS):
     return layers, qs, shifts
 
 
+def page_pool(K, V, T, page_size, gen, torch):
+    """K, V [B,Hkv,T_cap,d] as a page pool [B*n, Hkv, page_size, d] (n = T/page_size pages per
+    sequence) whose pages are placed in a random order, and the table [B, n] that finds them."""
+    B, Hkv, _, d = K.shape
+    n = T // page_size
+    perm = torch.randperm(B * n, generator=gen, device=K.device)
+
+    def pool(X):
+        X = X[:, :, :n * page_size].reshape(B, Hkv, n, page_size, d).permute(0, 2, 1, 3, 4)
+        X = X.reshape(B * n, Hkv, page_size, d)
+        out = torch.empty_like(X)
+        out[perm] = X  # logical page i of the flattened order lands at physical page perm[i]
+        return out
+    table = perm.view(B, n).to(torch.int32).contiguous()
+    return pool(K), pool(V), table
+
+
 def run_workload(w, steps, warmup, torch, hs, si, with_cpu, cpu_budget,
-                 n_layers=N_LAYER_COPIES, n_q=N_QUERY_SETS):
+                 n_layers=N_LAYER_COPIES, n_q=N_QUERY_SETS, page_size=0):
     dev = torch.device("cuda:0")
     x = si.make_inputs(w)
     layers, qs, shifts = setup(w, x, torch, dev, n_layers, n_q)
+    if page_size:  # the same layer copies held in shuffled page pools
+        assert w.T % page_size == 0
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(w.seed + 1)
+        pooled = []
+        for K, V in layers:
+            if K.element_size() == 1:
+                Kp, Vp, tab = page_pool(K.view(torch.uint8), V.view(torch.uint8), w.T, page_size, gen,
+                                        torch)
+                Kp, Vp = Kp.view(K.dtype), Vp.view(K.dtype)
+            else:
+                Kp, Vp, tab = page_pool(K, V, w.T, page_size, gen, torch)
+            pooled.append((Kp, Vp, tab))
+        del layers
+        layers = pooled
     nqb = -(-w.Tq // w.block_q)
     idx = torch.empty((w.B, w.Hkv, nqb, w.kb), dtype=torch.int32, device=dev)
     nnz = torch.empty((w.B, w.Hkv, nqb), dtype=torch.int32, device=dev)
     out = torch.empty_like(qs[0])
-    K0 = layers[0][0]
-    wsb = hs.hipsa_workspace_bytes(qs[0], K0, w.k, w.block_k, w.block_q, T=w.T)
+    wsb = hs.hipsa_workspace_bytes(qs[0], x["K"], w.k, w.block_k, w.block_q, T=w.T)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
     kw = dict(T=w.T, causal=bool(w.causal))
 
     def mask(j):
-        q, (K, V) = qs[j % len(qs)], layers[j % len(layers)]
-        hs.hip_mask_estimate(q, K, w.k, w.block_k, w.block_q, indices=idx, nnz=nnz, **kw)
+        q, L = qs[j % len(qs)], layers[j % len(layers)]
+        if page_size:
+            hs.hip_mask_estimate_paged(q, L[0], L[2], w.T, w.k, w.block_k, w.block_q, indices=idx,
+                                       nnz=nnz, causal=bool(w.causal))
+        else:
+            hs.hip_mask_estimate(q, L[0], w.k, w.block_k, w.block_q, indices=idx, nnz=nnz, **kw)
 
     def attn(j):
-        q, (K, V) = qs[j % len(qs)], layers[j % len(layers)]
-        hs.hip_sparse_attn(q, K, V, idx, nnz, w.k, w.block_k, w.block_q, out=out, workspace=ws, **kw)
+        q, L = qs[j % len(qs)], layers[j % len(layers)]
+        if page_size:
+            hs.hip_sparse_attn_paged(q, L[0], L[1], L[2], idx, nnz, w.T, w.k, w.block_k, w.block_q,
+                                     causal=bool(w.causal), out=out, workspace=ws)
+        else:
+            hs.hip_sparse_attn(q, L[0], L[1], idx, nnz, w.k, w.block_k, w.block_q, out=out,
+                               workspace=ws, **kw)
 
     def step(j):
         mask(j)
@@ -314,6 +354,8 @@ def main():
     ap.add_argument("--kv", choices=["native", "e5m2"], default="native",
                     help="e5m2: run the workload with an fp8 (E5M2) KV cache")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 KV cache leg")
+    ap.add_argument("--no-paged", action="store_true", help="skip the paged KV cache leg")
+    ap.add_argument("--page-size", type=int, default=64, help="tokens per page of the paged leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
@@ -420,6 +462,14 @@ def main():
                                             "frac": round(s_gbs / HBM_PEAK_GBS, 4)},
                           "mask_reuse_us": {str(k): round(v * 1e3, 3)
                                             for k, v in sorted(r8["ms_reuse"].items())}}
+    if headline and not args.no_paged:
+        # the same step with K/V in a page pool: pages of page_size tokens in a random order
+        rpg = run_workload(w, args.steps, args.warmup, torch, hs, si, False, 0,
+                           args.layer_copies, args.query_sets, page_size=args.page_size)
+        line["paged_kv"] = {"page_size": args.page_size, "pages": "shuffled over the pool",
+                            "us_per_step": round(rpg["ms_per_step"] * 1e3, 3),
+                            "mask_us": round(rpg["ms_mask"] * 1e3, 3),
+                            "attn_us": round(rpg["ms_attn"] * 1e3, 3)}
     if headline and not args.no_prefill:
         wp = si.workload("prefill_32k_chunk4k")
         rp = run_workload(wp, max(4, args.steps // 20), max(1, args.warmup // 10), torch, hs, si,

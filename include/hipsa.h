@@ -77,7 +77,8 @@ typedef enum {
   HIPSA_ERR_DTYPE = -4,     /* unsupported dtype, or dtype/block_q combination      */
   HIPSA_ERR_WORKSPACE = -5, /* workspace smaller than hipsa_workspace_bytes()       */
   HIPSA_ERR_HIP = -6,       /* a HIP runtime call or kernel launch failed           */
-  HIPSA_ERR_ALIGN = -7      /* q, K, V or out is not 16-byte aligned                */
+  HIPSA_ERR_ALIGN = -7,     /* q, K, V or out is not 16-byte aligned                */
+  HIPSA_ERR_PAGES = -8      /* invalid paged-KV description                         */
 } hipsa_status;
 
 typedef struct hipsa_desc {
@@ -135,6 +136,44 @@ int hip_sparse_attn(const hipsa_desc *desc, const void *q, const void *K, const 
                     const int32_t *indices, const int32_t *nnz, int64_t k, int64_t block_k,
                     int64_t block_q, void *out, void *workspace, size_t workspace_bytes,
                     void *stream);
+
+/*
+ * Paged KV cache.  Serving systems keep K and V in a pool of fixed-size pages
+ * and map each sequence's positions to pages through a table (SGLang pull
+ * request "Support Efficient Sparse HiP Attention (InfiniteHiP) ...",
+ * Modifications: a custom KV memory pool; summary page "A Training-Free
+ * Sub-quadratic Cost Transformer Model Serving Framework with Hierarchically
+ * Pruned Attention", the ablation of KV cache indexing by a vector map, i.e.
+ * a table indexed by position, against a hash map).  The *_paged calls take
+ * K and V in that form; everything else (desc, q, indices, nnz, out,
+ * workspace, results) is exactly as in the contiguous calls, with key
+ * position t of sequence b at
+ *     K[table[b * max_pages + t / page_size], g, t % page_size, :]
+ * for K, V laid out [num_pages, Hkv, page_size, d] (one contiguous
+ * page_size x d run per page and KV head).  desc->T_cap is not used.
+ */
+typedef struct hipsa_pages {
+  const int32_t *table; /* DEVICE int32 [B, max_pages]: physical page of each logical page; entries
+                           past ceil(T / page_size) are never read; an entry outside
+                           [0, num_pages) is clamped into it (no fault, unspecified result) */
+  int64_t max_pages;    /* row stride of table; ceil(T / page_size) <= max_pages             */
+  int64_t page_size;    /* tokens per page: a power of two, block_k <= page_size <= 65536     */
+  int64_t num_pages;    /* pages in the pool (K and V each hold num_pages*Hkv*page_size*d)   */
+} hipsa_pages;
+
+/* hip_mask_estimate on a paged KV cache.  Also requires ceil(T / page_size)
+ * <= 16384 (the mask kernels keep a sequence's page numbers on chip). */
+int hip_mask_estimate_paged(const hipsa_desc *desc, const hipsa_pages *pages, const void *q,
+                            const void *K, int64_t k, int64_t block_k, int64_t block_q,
+                            int32_t *indices, int32_t *nnz, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/* hip_sparse_attn on a paged KV cache.  Its workspace is hip_sparse_attn's:
+ * query hipsa_workspace_bytes with the same desc and T_cap = T. */
+int hip_sparse_attn_paged(const hipsa_desc *desc, const hipsa_pages *pages, const void *q,
+                          const void *K, const void *V, const int32_t *indices,
+                          const int32_t *nnz, int64_t k, int64_t block_k, int64_t block_q,
+                          void *out, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Device workspace bytes that hip_sparse_attn (and hip_mask_estimate) need for
  * this shape (0 = none), or SIZE_MAX when the arguments are invalid (see

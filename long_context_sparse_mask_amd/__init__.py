@@ -9,6 +9,9 @@ Layouts (contiguous): q [B,Hq,Tq,d]; K, V [B,Hkv,T_cap,d] with the first T
 rows valid; indices [B,Hkv,NQB,k/block_k] int32; nnz [B,Hkv,NQB] int32.
 Element types (q, K/V): (float32, float32), (bfloat16, bfloat16), or
 (bfloat16, float8_e5m2) for an fp8 KV cache; out has q's type.
+Paged KV cache (the *_paged calls): K, V [num_pages, Hkv, page_size, d] and
+block_table int32 [B, max_pages]; position t of sequence b is row
+t % page_size of page block_table[b, t // page_size].
 """
 from __future__ import annotations
 
@@ -17,8 +20,8 @@ import os
 
 import torch  # loads the HIP runtime first, so libhipsa binds to the same one
 
-__all__ = ["hip_mask_estimate", "hip_sparse_attn", "hipsa_workspace_bytes", "HipsaError",
-           "LIB_PATH", "lib"]
+__all__ = ["hip_mask_estimate", "hip_sparse_attn", "hip_mask_estimate_paged",
+           "hip_sparse_attn_paged", "hipsa_workspace_bytes", "HipsaError", "LIB_PATH", "lib"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhipsa.so")
 if not os.path.exists(LIB_PATH):
@@ -36,12 +39,23 @@ class Desc(C.Structure):
                 ("dtype", C.c_int32)]
 
 
+class Pages(C.Structure):
+    _fields_ = [("table", C.c_void_p), ("max_pages", C.c_int64), ("page_size", C.c_int64),
+                ("num_pages", C.c_int64)]
+
+
 _P, _I64, _SZ = C.c_void_p, C.c_int64, C.c_size_t
 lib.hip_mask_estimate.argtypes = [C.POINTER(Desc), _P, _P, _I64, _I64, _I64, _P, _P, _P, _SZ, _P]
 lib.hip_mask_estimate.restype = C.c_int
 lib.hip_sparse_attn.argtypes = [C.POINTER(Desc), _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P,
                                 _SZ, _P]
 lib.hip_sparse_attn.restype = C.c_int
+lib.hip_mask_estimate_paged.argtypes = [C.POINTER(Desc), C.POINTER(Pages), _P, _P, _I64, _I64, _I64,
+                                        _P, _P, _P, _SZ, _P]
+lib.hip_mask_estimate_paged.restype = C.c_int
+lib.hip_sparse_attn_paged.argtypes = [C.POINTER(Desc), C.POINTER(Pages), _P, _P, _P, _P, _P, _I64,
+                                      _I64, _I64, _P, _P, _SZ, _P]
+lib.hip_sparse_attn_paged.restype = C.c_int
 lib.hipsa_workspace_bytes.argtypes = [C.POINTER(Desc), _I64, _I64, _I64]
 lib.hipsa_workspace_bytes.restype = C.c_size_t
 lib.hipsa_last_error.argtypes = []
@@ -151,4 +165,73 @@ def hip_sparse_attn(q, K, V, indices, nnz, k: int, block_k: int, block_q: int = 
                                _dev_ptr(indices, "indices"), _dev_ptr(nnz, "nnz"), k, block_k,
                                block_q, _dev_ptr(out, "out"), ws_ptr, ws_len,
                                _stream(q.device, stream)))
+    return out
+
+
+# ------------------------------------------------------------------ paged KV cache
+
+def _paged_desc(q, K_pages, block_table, T, causal):
+    if K_pages.dim() != 4 or block_table.dim() != 2 or block_table.dtype != torch.int32:
+        raise ValueError("K, V must be [num_pages, Hkv, page_size, d]; block_table int32 [B, max_pages]")
+    B, Hq, Tq, d = q.shape
+    num_pages, Hkv, page_size, dk = K_pages.shape
+    if dk != d or block_table.shape[0] != B:
+        raise ValueError("K's head dim or block_table's batch does not match q")
+    desc = Desc(B, Hq, Hkv, Tq, T, T, d, int(bool(causal)), _dtype_code(q, K_pages))
+    pages = Pages(_dev_ptr(block_table, "block_table"), block_table.shape[1], page_size, num_pages)
+    return desc, pages
+
+
+def hip_mask_estimate_paged(q, K_pages, block_table, T: int, k: int, block_k: int,
+                            block_q: int = 1, *, causal=True, indices=None, nnz=None, stream=None):
+    """hip_mask_estimate on a paged KV cache.  Returns (indices, nnz)."""
+    desc, pages = _paged_desc(q, K_pages, block_table, T, causal)
+    nqb = -(-desc.Tq // block_q)
+    kb = k // block_k if block_k > 0 else 0
+    if indices is None:
+        indices = torch.empty((desc.B, desc.Hkv, nqb, kb), dtype=torch.int32, device=q.device)
+    if nnz is None:
+        nnz = torch.empty((desc.B, desc.Hkv, nqb), dtype=torch.int32, device=q.device)
+    if tuple(indices.shape) != (desc.B, desc.Hkv, nqb, kb) or indices.dtype != torch.int32:
+        raise ValueError("indices must be int32 [B, Hkv, NQB, k/block_k]")
+    if tuple(nnz.shape) != (desc.B, desc.Hkv, nqb) or nnz.dtype != torch.int32:
+        raise ValueError("nnz must be int32 [B, Hkv, NQB]")
+    if desc.B * desc.Tq == 0:
+        return indices, nnz
+    _check(lib.hip_mask_estimate_paged(C.byref(desc), C.byref(pages), _dev_ptr(q, "q"),
+                                       _dev_ptr(K_pages, "K"), k, block_k, block_q,
+                                       _dev_ptr(indices, "indices"), _dev_ptr(nnz, "nnz"), None, 0,
+                                       _stream(q.device, stream)))
+    return indices, nnz
+
+
+def hip_sparse_attn_paged(q, K_pages, V_pages, block_table, indices, nnz, T: int, k: int,
+                          block_k: int, block_q: int = 1, *, causal=True, out=None, workspace=None,
+                          stream=None):
+    """hip_sparse_attn on a paged KV cache.  Returns out [B,Hq,Tq,d] in q's dtype."""
+    desc, pages = _paged_desc(q, K_pages, block_table, T, causal)
+    if K_pages.dtype != V_pages.dtype or V_pages.shape != K_pages.shape:
+        raise ValueError("V must have K's shape and dtype")
+    nqb = -(-desc.Tq // block_q)
+    kb = k // block_k if block_k > 0 else 0
+    if tuple(indices.shape) != (desc.B, desc.Hkv, nqb, kb) or indices.dtype != torch.int32:
+        raise ValueError("indices must be int32 [B, Hkv, NQB, k/block_k]")
+    if tuple(nnz.shape) != (desc.B, desc.Hkv, nqb) or nnz.dtype != torch.int32:
+        raise ValueError("nnz must be int32 [B, Hkv, NQB]")
+    if out is None:
+        out = torch.empty_like(q)
+    if desc.B * desc.Tq == 0:
+        return out
+    need = lib.hipsa_workspace_bytes(C.byref(desc), k, block_k, block_q)
+    if need == SIZE_MAX:
+        raise HipsaError(-2, lib.hipsa_last_error().decode())
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.hip_sparse_attn_paged(C.byref(desc), C.byref(pages), _dev_ptr(q, "q"),
+                                     _dev_ptr(K_pages, "K"), _dev_ptr(V_pages, "V"),
+                                     _dev_ptr(indices, "indices"), _dev_ptr(nnz, "nnz"), k, block_k,
+                                     block_q, _dev_ptr(out, "out"), ws_ptr, ws_len,
+                                     _stream(q.device, stream)))
     return out

@@ -20,6 +20,10 @@
 // device-scope fence and an arrival counter measured slower on gfx950: the
 // fences serialise across workgroups.)
 //
+// With a paged KV cache each lane also reads the page of its slot's token
+// from the table (one more dependent load, cached: a block's tokens share a
+// page) and addresses its K and V rows through it.
+//
 // After its loads land, a workgroup's remaining time is pure ALU work, which
 // sits in the kernel's tail, so the kernels keep it small: logits on the
 // matrix cores for bf16, no per-head tests inside unrolled loops (heads past
@@ -38,7 +42,7 @@ namespace {
 // lane and is summed across the wave's row groups with DPP/permlane steps.
 // All GMAX heads are computed (the loads of heads past the group repeat the
 // last head); only the stores are limited to the group.
-template <typename E, int D, int GMAX, int TOK>
+template <typename E, int D, int GMAX, int TOK, bool PAGED>
 __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
   constexpr int VEC = Vec<E>::N;
   constexpr int TPR = D / VEC;            // lanes per key row (8, 16 or 32)
@@ -63,9 +67,9 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
   __shared__ float wm[4][GMAX], wl[4][GMAX];
   __shared__ float wo[4][GMAX][D];
 
-  const int64_t kvoff = (int64_t)(b * Hkv + g) * s.T_cap * D;
-  const E *Kp = reinterpret_cast<const E *>(a.K) + kvoff;
-  const E *Vp = reinterpret_cast<const E *>(a.V) + kvoff;
+  const int64_t kvoff = PAGED ? 0 : (int64_t)(b * Hkv + g) * s.T_cap * D;
+  const E *Kp = reinterpret_cast<const E *>(a.K);
+  const E *Vp = reinterpret_cast<const E *>(a.V);
   const E *qbase = reinterpret_cast<const E *>(a.q) + ((int64_t)(b * s.Hq + g * s.G) * Tq + i) * D;
 
   // Token slot u of this lane: wave*TPW + u*RPW + rgl.  A slot past the list,
@@ -81,7 +85,11 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
     const bool ok = n < cnt && blk >= 0 && blk < Np;
     const int32_t t = ((ok ? blk : 0) << s.bk_shift) + (j & (s.bk - 1));
     tk[u] = (ok && t < Tp) ? t : -1;
-    const int64_t row = (int64_t)(tk[u] >= 0 ? tk[u] : 0) * D + cs * VEC;
+    const int32_t ts = tk[u] >= 0 ? tk[u] : 0;
+    int64_t row;
+    if constexpr (PAGED) row = paged_row(page_at(a.pg, b, ts >> a.pg.ps_shift), g, Hkv, ts, a.pg.ps_shift) * D;
+    else row = kvoff + (int64_t)ts * D;
+    row += cs * VEC;
     kr[u] = Vec<E>::raw(Kp + row);
     vr[u] = Vec<E>::raw(Vp + row);
   }
@@ -190,7 +198,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
 // Query loads are issued first: loads complete in order, so the first
 // matrix op then waits for the query and its K rows, not for the V rows
 // issued after them.
-template <typename KE, int D, int GMAX, int TOK>
+template <typename KE, int D, int GMAX, int TOK, bool PAGED>
 __global__ __launch_bounds__(256) void attn_decode_mfma(AttnArgs a) {
   constexpr int KS = D / 32;            // MFMA k-steps over the head dim
   constexpr int TPW = TOK / 4;          // token slots per wave
@@ -216,9 +224,15 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(AttnArgs a) {
   __shared__ float wm[4][GMAX], wl[4][GMAX];
   __shared__ __align__(16) float wo[4][GMAX][D];
 
-  const int64_t kvoff = (int64_t)(b * Hkv + g) * s.T_cap * D;
-  const KE *Kp = reinterpret_cast<const KE *>(a.K) + kvoff;
-  const KE *Vp = reinterpret_cast<const KE *>(a.V) + kvoff;
+  const int64_t kvoff = PAGED ? 0 : (int64_t)(b * Hkv + g) * s.T_cap * D;
+  const KE *Kp = reinterpret_cast<const KE *>(a.K);
+  const KE *Vp = reinterpret_cast<const KE *>(a.V);
+  const int ps = a.pg.ps_shift;
+  // element offset of the K/V row of position t (>= 0) in page pg (paged)
+  auto row_of = [&](int32_t t, int32_t pg) -> int64_t {
+    if constexpr (PAGED) return paged_row(pg, g, Hkv, t, ps) * D;
+    else return kvoff + (int64_t)t * D;
+  };
   const uint16_t *qbase = reinterpret_cast<const uint16_t *>(a.q) + ((int64_t)(b * s.Hq + g * s.G) * Tq + i) * D;
 
   // Token of slot lane % TPW of this wave (row of K/V), or -1 when the slot is
@@ -235,6 +249,8 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(AttnArgs a) {
     const int32_t t = ((ok ? blk : 0) << s.bk_shift) + (j & (s.bk - 1));
     tk_lane = (ok && t < Tp) ? t : -1;
   }
+  int32_t pg_lane = 0;  // paged: page of the slot's token (of position 0 for a masked slot)
+  if constexpr (PAGED) pg_lane = page_at(a.pg, b, (tk_lane >= 0 ? tk_lane : 0) >> ps);
 
   uint4 qa[KS];
   {
@@ -250,16 +266,21 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(AttnArgs a) {
 #pragma unroll
   for (int u = 0; u < NT; u++) {
     kt[u] = __shfl(tk_lane, 16 * u + (lane & 15), 64);
+    const int32_t kpg = PAGED ? __shfl(pg_lane, 16 * u + (lane & 15), 64) : 0;
+    const int64_t krow = row_of(kt[u] >= 0 ? kt[u] : 0, kpg);
 #pragma unroll
     for (int ks = 0; ks < KS; ks++)
-      kr[u][ks] = Kv8<KE>::raw(Kp + (int64_t)(kt[u] >= 0 ? kt[u] : 0) * D + 32 * ks + 8 * (lane >> 4));
+      kr[u][ks] = Kv8<KE>::raw(Kp + krow + 32 * ks + 8 * (lane >> 4));
   }
   int32_t vt[NV];
   typename KvN<KE, EPL>::raw_t vr[NV];
 #pragma unroll
   for (int v = 0; v < NV; v++) {
     vt[v] = RPV == 1 ? __builtin_amdgcn_readlane(tk_lane, v) : __shfl(tk_lane, RPV * v + lane / LPV, 64);
-    vr[v] = KvN<KE, EPL>::raw(Vp + (int64_t)(vt[v] >= 0 ? vt[v] : 0) * D + EPL * (lane % LPV));
+    int32_t vpg = 0;
+    if constexpr (PAGED)
+      vpg = RPV == 1 ? __builtin_amdgcn_readlane(pg_lane, v) : __shfl(pg_lane, RPV * v + lane / LPV, 64);
+    vr[v] = KvN<KE, EPL>::raw(Vp + row_of(vt[v] >= 0 ? vt[v] : 0, vpg) + EPL * (lane % LPV));
   }
 
   // logits on the matrix cores, softmax statistics per head in the
@@ -435,30 +456,30 @@ int tokens_for(const Shape &s) {
 
 // E: query / output element type; KE: K/V element type (E itself, or E5M2
 // codes under a bf16 query).
-template <typename E, typename KE, int D, int GMAX>
+template <typename E, typename KE, int D, int GMAX, bool PAGED>
 void launch_t(const AttnArgs &a, hipStream_t st, int tok) {
   constexpr int kMaxTok = max_tokens<E, D>();
   const dim3 grid((unsigned)(a.s.problems * a.splits)), block(256);
   if constexpr (std::is_same<E, uint16_t>::value) {
-    if (GMAX <= 8 && tok == 128) hipLaunchKernelGGL((attn_decode_mfma<KE, D, (GMAX <= 8 ? GMAX : 8), 128>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((attn_decode_mfma<KE, D, GMAX, 64>), grid, block, 0, st, a);
+    if (GMAX <= 8 && tok == 128) hipLaunchKernelGGL((attn_decode_mfma<KE, D, (GMAX <= 8 ? GMAX : 8), 128, PAGED>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((attn_decode_mfma<KE, D, GMAX, 64, PAGED>), grid, block, 0, st, a);
   } else {
     if (tok == 128) {
-      if constexpr (kMaxTok >= 128) hipLaunchKernelGGL((attn_decode_kernel<E, D, GMAX, 128>), grid, block, 0, st, a);
+      if constexpr (kMaxTok >= 128) hipLaunchKernelGGL((attn_decode_kernel<E, D, GMAX, 128, PAGED>), grid, block, 0, st, a);
     } else {
-      hipLaunchKernelGGL((attn_decode_kernel<E, D, GMAX, 64>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((attn_decode_kernel<E, D, GMAX, 64, PAGED>), grid, block, 0, st, a);
     }
   }
 }
 
-template <typename E, typename KE, int D>
+template <typename E, typename KE, int D, bool PAGED>
 hipError_t launch_d(const AttnArgs &a, hipStream_t st) {
   const int G = a.s.G, tok = tokens_per_split<E, D>(a.s);
-  if (G <= 1) launch_t<E, KE, D, 1>(a, st, tok);
-  else if (G <= 2) launch_t<E, KE, D, 2>(a, st, tok);
-  else if (G <= 4) launch_t<E, KE, D, 4>(a, st, tok);
-  else if (G <= 8) launch_t<E, KE, D, 8>(a, st, tok);
-  else launch_t<E, KE, D, 16>(a, st, tok);
+  if (G <= 1) launch_t<E, KE, D, 1, PAGED>(a, st, tok);
+  else if (G <= 2) launch_t<E, KE, D, 2, PAGED>(a, st, tok);
+  else if (G <= 4) launch_t<E, KE, D, 4, PAGED>(a, st, tok);
+  else if (G <= 8) launch_t<E, KE, D, 8, PAGED>(a, st, tok);
+  else launch_t<E, KE, D, 16, PAGED>(a, st, tok);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_decode_combine<E, D>), dim3((unsigned)(a.s.problems * G)), dim3(128), 0, st, a);
@@ -476,12 +497,20 @@ size_t attn_decode_workspace(const Shape &s) {
   return (size_t)s.problems * attn_decode_splits(s) * s.G * (s.d + 2) * sizeof(float);
 }
 
-hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t st) {
+namespace {
+template <bool PAGED>
+hipError_t launch_layout(const AttnArgs &a, hipStream_t st) {
+  const bool d64 = a.s.d == 64;
   if (a.s.dtype == HIPSA_BF16)
-    return a.s.d == 64 ? launch_d<uint16_t, uint16_t, 64>(a, st) : launch_d<uint16_t, uint16_t, 128>(a, st);
+    return d64 ? launch_d<uint16_t, uint16_t, 64, PAGED>(a, st) : launch_d<uint16_t, uint16_t, 128, PAGED>(a, st);
   if (a.s.dtype == HIPSA_BF16_E5M2)
-    return a.s.d == 64 ? launch_d<uint16_t, uint8_t, 64>(a, st) : launch_d<uint16_t, uint8_t, 128>(a, st);
-  return a.s.d == 64 ? launch_d<float, float, 64>(a, st) : launch_d<float, float, 128>(a, st);
+    return d64 ? launch_d<uint16_t, uint8_t, 64, PAGED>(a, st) : launch_d<uint16_t, uint8_t, 128, PAGED>(a, st);
+  return d64 ? launch_d<float, float, 64, PAGED>(a, st) : launch_d<float, float, 128, PAGED>(a, st);
+}
+}  // namespace
+
+hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t st) {
+  return a.pg.table ? launch_layout<true>(a, st) : launch_layout<false>(a, st);
 }
 
 }  // namespace hipsa

@@ -33,6 +33,9 @@
 //     each 16 lanes, lane i receives element i of the four 4-element row
 //     pieces the group addresses), so V needs no transposing stores;
 //   - the running output is rescaled only when some lane's running max moved.
+// With a paged KV cache the page of every listed block is read once, beside
+// the list itself, and the loader addresses rows through it (a page holds
+// whole key blocks).
 // LDS rows are padded (K: D+8, V: D+32 elements) so that the operand reads
 // of a 256-byte LDS pass fall in distinct banks.
 #include "hipsa_internal.h"
@@ -108,7 +111,7 @@ __device__ inline void online_softmax(const f32x16_t (&sacc)[2], bool masked, co
   }
 }
 
-template <typename KE, int D>
+template <typename KE, int D, bool PAGED>
 __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnArgs a) {
   constexpr int KS = D / 16;   // k-steps of S^T over the head dim
   constexpr int DT = D / 32;   // 32-row tiles of O^T
@@ -145,13 +148,21 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) int32_t tok[2][KT];
   __shared__ int32_t tmask[2];
   __shared__ int32_t lst[kMaxKb];
+  __shared__ int32_t lpg[PAGED ? kMaxKb : 1];  // paged: page of each listed block
 
   const int32_t *list = a.indices + (int64_t)prob * s.Kb;
-  for (int j = tid; j < cnt; j += 512) lst[j] = list[j];
+  for (int j = tid; j < cnt; j += 512) {
+    const int32_t blk = list[j];
+    lst[j] = blk;
+    if constexpr (PAGED) {
+      const bool okb = blk >= 0 && blk < Np;  // other ids are skipped: any page will do
+      lpg[j] = page_at(a.pg, b, ((okb ? blk : 0) << s.bk_shift) >> a.pg.ps_shift);
+    }
+  }
 
-  const int64_t kvoff = (int64_t)(b * Hkv + g) * s.T_cap * D;
-  const KE *Kg = reinterpret_cast<const KE *>(a.K) + kvoff;
-  const KE *Vg = reinterpret_cast<const KE *>(a.V) + kvoff;
+  const int64_t kvoff = PAGED ? 0 : (int64_t)(b * Hkv + g) * s.T_cap * D;
+  const KE *Kg = reinterpret_cast<const KE *>(a.K);
+  const KE *Vg = reinterpret_cast<const KE *>(a.V);
   const int hq = min(h, s.G - 1);
   const uint16_t *Qg = reinterpret_cast<const uint16_t *>(a.q) + ((int64_t)(b * s.Hq + g * s.G + hq) * Tq + r0) * D;
 
@@ -178,12 +189,22 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnArgs a) {
     const int32_t t_ = ((okb_ ? blk_ : 0) << s.bk_shift) + ((J) & (s.bk - 1)); \
     OUT = (okb_ && t_ < Tp) ? t_ : -1;                                       \
   } while (0)
+  // element offset of the K/V row for slot J of tile TL holding token T (or -1)
+  auto row_of = [&](int tl, int j, int32_t t) -> int64_t {
+    const int32_t ts = t >= 0 ? t : 0;
+    if constexpr (PAGED) {
+      const int n = min(tl * bpt + (j >> s.bk_shift), cnt - 1);
+      return paged_row(lpg[n], g, Hkv, ts, a.pg.ps_shift) * D;
+    } else {
+      return kvoff + (int64_t)ts * D;
+    }
+  };
 #define HIPSA_GLOAD(TL)                                                                        \
   do {                                                                                         \
     _Pragma("unroll") for (int u = 0; u < KP; u++) {                                           \
       int32_t t;                                                                               \
       HIPSA_TOKEN(TL, u * RPP + krow0, t);                                                     \
-      const int64_t off_ = (int64_t)(t >= 0 ? t : 0) * D + kcol;                               \
+      const int64_t off_ = row_of(TL, u * RPP + krow0, t) + kcol;                              \
       kreg[u] = Kv8<KE>::raw(Kg + off_);                                                       \
       vreg[u] = Kv8<KE>::raw(Vg + off_);                                                       \
     }                                                                                          \
@@ -277,18 +298,24 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnArgs a) {
     }
 }
 
+template <bool PAGED>
+void launch_kv(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t st) {
+  if (a.s.dtype == HIPSA_BF16_E5M2) {
+    if (a.s.d == 64) hipLaunchKernelGGL((attn_prefill_kernel<uint8_t, 64, PAGED>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((attn_prefill_kernel<uint8_t, 128, PAGED>), grid, block, 0, st, a);
+  } else {
+    if (a.s.d == 64) hipLaunchKernelGGL((attn_prefill_kernel<uint16_t, 64, PAGED>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((attn_prefill_kernel<uint16_t, 128, PAGED>), grid, block, 0, st, a);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_attn_prefill(const AttnArgs &a, hipStream_t st) {
   const unsigned hchunks = (unsigned)(a.s.G + 3) / 4;
   const dim3 grid((unsigned)(a.s.problems * hchunks)), block(512);
-  if (a.s.dtype == HIPSA_BF16_E5M2) {
-    if (a.s.d == 64) hipLaunchKernelGGL((attn_prefill_kernel<uint8_t, 64>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((attn_prefill_kernel<uint8_t, 128>), grid, block, 0, st, a);
-  } else {
-    if (a.s.d == 64) hipLaunchKernelGGL((attn_prefill_kernel<uint16_t, 64>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((attn_prefill_kernel<uint16_t, 128>), grid, block, 0, st, a);
-  }
+  if (a.pg.table) launch_kv<true>(a, grid, block, st);
+  else launch_kv<false>(a, grid, block, st);
   return hipGetLastError();
 }
 

@@ -109,43 +109,65 @@ int hip_fail(hipError_t e, const char *what) {
   return fail(HIPSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-}  // namespace
-
-extern "C" {
-
-int hip_mask_estimate(const hipsa_desc *desc, const void *q, const void *K, int64_t k,
-                      int64_t block_k, int64_t block_q, int32_t *indices, int32_t *nnz,
-                      void *workspace, size_t workspace_bytes, void *stream) {
-  (void)workspace;
-  (void)workspace_bytes;
-  hipsa::Shape s;
-  int rc = check_shape(desc, k, block_k, block_q, &s);
+// Shape checks for a paged call: desc->T_cap is not used, so it is replaced
+// by T before the shared checks.  `mask`: the mask kernels keep a sequence's
+// page numbers on chip, which bounds ceil(T / page_size).
+int check_paged(const hipsa_desc *desc, const hipsa_pages *pg, int64_t k, int64_t block_k,
+                int64_t block_q, bool mask, hipsa::Shape *s, hipsa::Pages *out) {
+  if (!desc || !pg) return fail(HIPSA_ERR_NULL, "desc and pages must be non-NULL");
+  hipsa_desc d = *desc;
+  d.T_cap = d.T;
+  int rc = check_shape(&d, k, block_k, block_q, s);
   if (rc) return rc;
+  if (!pow2_in(pg->page_size, 1, 65536) || pg->page_size < block_k)
+    return fail(HIPSA_ERR_PAGES, "page_size=%lld must be a power of two in [block_k=%lld, 65536]",
+                (long long)pg->page_size, (long long)block_k);
+  const int64_t need = (d.T + pg->page_size - 1) / pg->page_size;
+  if (pg->max_pages < need)
+    return fail(HIPSA_ERR_PAGES, "max_pages=%lld is below ceil(T/page_size)=%lld",
+                (long long)pg->max_pages, (long long)need);
+  if (pg->num_pages < 1 || pg->num_pages > INT32_MAX)
+    return fail(HIPSA_ERR_PAGES, "num_pages=%lld must be in [1, 2^31)", (long long)pg->num_pages);
+  if (mask && need > hipsa::kMaxSeqPagesOnChip)
+    return fail(HIPSA_ERR_PAGES, "ceil(T/page_size)=%lld exceeds %d for mask estimation",
+                (long long)need, hipsa::kMaxSeqPagesOnChip);
+  out->table = pg->table;
+  out->max_pages = pg->max_pages;
+  out->ps_shift = __builtin_ctzll((unsigned long long)pg->page_size);
+  out->last_page = (int32_t)(pg->num_pages - 1);
+  out->seq_pages = (int32_t)(need < INT32_MAX ? need : INT32_MAX);
+  return HIPSA_OK;
+}
+
+int mask_impl(const hipsa::Shape &s, const hipsa::Pages &pg, const void *q, const void *K,
+              int32_t *indices, int32_t *nnz, void *stream) {
   if (s.problems == 0) return ok();
   if (!q || !K || !indices || !nnz)
     return fail(HIPSA_ERR_NULL, "q, K, indices and nnz must be non-NULL");
+  if (pg.max_pages > 0 && !pg.table)  // a paged call (max_pages >= 1) without a table
+    return fail(HIPSA_ERR_NULL, "pages->table must be non-NULL");
+  int rc;
   {
     const void *p[] = {q, K};
     const char *nm[] = {"q", "K"};
     if ((rc = check_aligned(p, nm, 2))) return rc;
   }
-  hipsa::MaskArgs a{q, K, indices, nnz, s};
+  hipsa::MaskArgs a{q, K, indices, nnz, s, pg};
   hipError_t e = s.bq == 1 ? hipsa::launch_mask_decode(a, (hipStream_t)stream)
                            : hipsa::launch_mask_prefill(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "mask estimation launch");
   return ok();
 }
 
-int hip_sparse_attn(const hipsa_desc *desc, const void *q, const void *K, const void *V,
-                    const int32_t *indices, const int32_t *nnz, int64_t k, int64_t block_k,
-                    int64_t block_q, void *out, void *workspace, size_t workspace_bytes,
-                    void *stream) {
-  hipsa::Shape s;
-  int rc = check_shape(desc, k, block_k, block_q, &s);
-  if (rc) return rc;
+int attn_impl(const hipsa::Shape &s, const hipsa::Pages &pg, const void *q, const void *K,
+              const void *V, const int32_t *indices, const int32_t *nnz, void *out,
+              void *workspace, size_t workspace_bytes, void *stream) {
+  int rc;
   if (s.problems == 0) return ok();
   if (!q || !K || !V || !indices || !nnz || !out)
     return fail(HIPSA_ERR_NULL, "q, K, V, indices, nnz and out must be non-NULL");
+  if (pg.max_pages > 0 && !pg.table)  // a paged call (max_pages >= 1) without a table
+    return fail(HIPSA_ERR_NULL, "pages->table must be non-NULL");
   {
     const void *p[] = {q, K, V, out};
     const char *nm[] = {"q", "K", "V", "out"};
@@ -159,6 +181,7 @@ int hip_sparse_attn(const hipsa_desc *desc, const void *q, const void *K, const 
   a.q = q; a.K = K; a.V = V; a.indices = indices; a.nnz = nnz; a.out = out;
   a.ws = static_cast<float *>(workspace);
   a.s = s;
+  a.pg = pg;
   a.scale = (float)(1.0 / __builtin_sqrt((double)s.d));
   hipError_t e;
   if (s.bq == 1) {
@@ -170,6 +193,58 @@ int hip_sparse_attn(const hipsa_desc *desc, const void *q, const void *K, const 
   }
   if (e != hipSuccess) return hip_fail(e, "sparse attention launch");
   return ok();
+}
+
+// The contiguous layout: no table (max_pages 0 marks "not paged").
+constexpr hipsa::Pages kContiguous{nullptr, 0, -1, 0, 0};
+
+}  // namespace
+
+extern "C" {
+
+int hip_mask_estimate(const hipsa_desc *desc, const void *q, const void *K, int64_t k,
+                      int64_t block_k, int64_t block_q, int32_t *indices, int32_t *nnz,
+                      void *workspace, size_t workspace_bytes, void *stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  hipsa::Shape s;
+  int rc = check_shape(desc, k, block_k, block_q, &s);
+  if (rc) return rc;
+  return mask_impl(s, kContiguous, q, K, indices, nnz, stream);
+}
+
+int hip_mask_estimate_paged(const hipsa_desc *desc, const hipsa_pages *pages, const void *q,
+                            const void *K, int64_t k, int64_t block_k, int64_t block_q,
+                            int32_t *indices, int32_t *nnz, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  hipsa::Shape s;
+  hipsa::Pages pg;
+  int rc = check_paged(desc, pages, k, block_k, block_q, true, &s, &pg);
+  if (rc) return rc;
+  return mask_impl(s, pg, q, K, indices, nnz, stream);
+}
+
+int hip_sparse_attn(const hipsa_desc *desc, const void *q, const void *K, const void *V,
+                    const int32_t *indices, const int32_t *nnz, int64_t k, int64_t block_k,
+                    int64_t block_q, void *out, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+  hipsa::Shape s;
+  int rc = check_shape(desc, k, block_k, block_q, &s);
+  if (rc) return rc;
+  return attn_impl(s, kContiguous, q, K, V, indices, nnz, out, workspace, workspace_bytes, stream);
+}
+
+int hip_sparse_attn_paged(const hipsa_desc *desc, const hipsa_pages *pages, const void *q,
+                          const void *K, const void *V, const int32_t *indices,
+                          const int32_t *nnz, int64_t k, int64_t block_k, int64_t block_q,
+                          void *out, void *workspace, size_t workspace_bytes, void *stream) {
+  hipsa::Shape s;
+  hipsa::Pages pg;
+  int rc = check_paged(desc, pages, k, block_k, block_q, false, &s, &pg);
+  if (rc) return rc;
+  return attn_impl(s, pg, q, K, V, indices, nnz, out, workspace, workspace_bytes, stream);
 }
 
 size_t hipsa_workspace_bytes(const hipsa_desc *desc, int64_t k, int64_t block_k,

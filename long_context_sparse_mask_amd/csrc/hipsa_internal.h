@@ -20,10 +20,23 @@ struct Shape {
   int64_t problems; // B * Hkv * nqb
 };
 
+// Paged K/V: K and V are [num_pages, Hkv, page_size, d] and key position t of
+// sequence b lives in page table[b * max_pages + t / page_size].  table ==
+// nullptr means the contiguous [B, Hkv, T_cap, d] layout.
+struct Pages {
+  const int32_t *table;
+  int64_t max_pages;
+  int32_t ps_shift;      // log2(page_size), >= log2(block_k)
+  int32_t last_page;     // num_pages - 1: table entries are clamped to [0, last_page]
+  int32_t seq_pages;     // ceil(T / page_size): the table entries a sequence uses
+};
+constexpr int kMaxSeqPagesOnChip = 16384;  // mask kernels stage a sequence's pages in LDS
+
 struct MaskArgs {
   const void *q, *K;
   int32_t *indices, *nnz;
   Shape s;
+  Pages pg;
 };
 
 struct AttnArgs {
@@ -34,6 +47,7 @@ struct AttnArgs {
   Shape s;
   int32_t splits;  // decode: key splits per problem
   float scale;     // 1 / sqrt(d)
+  Pages pg;
 };
 
 // Decode / per-row problems (block_q == 1).
@@ -47,6 +61,39 @@ hipError_t launch_mask_prefill(const MaskArgs &a, hipStream_t st);
 hipError_t launch_attn_prefill(const AttnArgs &a, hipStream_t st);
 
 // ------------------------------------------------------------------ device helpers
+
+// Paged K/V addressing.  page_at() reads one table entry (clamped into the
+// pool, so a bad table cannot send a load out of bounds); paged_row() is the
+// row, in units of d elements, of position t of KV head g in that page.
+__device__ inline int32_t page_at(const Pages &pg, uint32_t b, int32_t logical_page) {
+  const int32_t p = pg.table[(int64_t)b * pg.max_pages + logical_page];
+  return min(max(p, 0), pg.last_page);
+}
+__device__ inline int64_t paged_row(int32_t page, uint32_t g, uint32_t Hkv, int32_t t, int ps_shift) {
+  return (((int64_t)page * Hkv + g) << ps_shift) + (t & ((1 << ps_shift) - 1));
+}
+// The mask kernels stage the pages of positions 0 .. Tp-1 of sequence b in
+// LDS once (every round then finds a centre row without another memory trip).
+// Each thread issues a batch of 16 loads (addresses clamped, no branches)
+// before storing any, so a batch costs one memory latency, not 16.  The
+// first batch (16 x blockDim pages) is straight-line code: at the head of a
+// loop the compiler waits for every load in flight, the caller's too.
+__device__ inline void stage_pages(const Pages &pg, uint32_t b, int32_t Tp, int32_t *ptab) {
+  constexpr int U = 16;
+  const int32_t n = ((Tp - 1) >> pg.ps_shift) + 1;
+  const int32_t *row = pg.table + (int64_t)b * pg.max_pages;
+  const int32_t stride = (int32_t)blockDim.x;
+  auto batch = [&](int32_t j0) {
+    int32_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) v[u] = row[min(j0 + u * stride, n - 1)];
+#pragma unroll
+    for (int u = 0; u < U; u++)
+      if (j0 + u * stride < n) ptab[j0 + u * stride] = min(max(v[u], 0), pg.last_page);
+  };
+  batch((int32_t)threadIdx.x);
+  for (int32_t j0 = (int32_t)threadIdx.x + U * stride; j0 < n; j0 += U * stride) batch(j0);
+}
 
 // Workgroup -> logical work item, XCD-aware.  gfx950 dispatches the
 // workgroups of a launch round-robin over its 8 XCDs (workgroup x runs on

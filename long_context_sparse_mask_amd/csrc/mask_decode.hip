@@ -27,7 +27,9 @@
 //      sets the flag that runs the next round.
 // Rounds are serially dependent (the next centres depend on this round's
 // top-k), so the kernel is bound by one dependent memory round trip plus the
-// round's LDS work per round, not by bandwidth.
+// round's LDS work per round, not by bandwidth.  With a paged KV cache the
+// problem's page numbers are staged in LDS before the first round, so a
+// centre row costs no extra memory trip.
 #include <type_traits>
 
 #include "hipsa_internal.h"
@@ -36,7 +38,7 @@
 namespace hipsa {
 namespace {
 
-template <typename E, typename KE, int D, int GMAX, int UNROLL>
+template <typename E, typename KE, int D, int GMAX, int UNROLL, bool PAGED>
 __global__ __launch_bounds__(256) void mask_decode_kernel(MaskArgs a) {
   constexpr bool kMfma = std::is_same<E, uint16_t>::value;
   constexpr int VEC = Vec<E>::N;
@@ -64,9 +66,17 @@ __global__ __launch_bounds__(256) void mask_decode_kernel(MaskArgs a) {
   __shared__ uint64_t key[2 * kMaxKb + kSpan];
   __shared__ int32_t rk[2 * kMaxKb];
   __shared__ int32_t flag[2];
+  extern __shared__ int32_t ptab[];  // paged: the sequence's page numbers
 
   const E *qbase = reinterpret_cast<const E *>(a.q) + ((int64_t)(b * s.Hq + g * s.G) * Tq + i) * D;
-  const KE *Kbase = reinterpret_cast<const KE *>(a.K) + (int64_t)(b * Hkv + g) * s.T_cap * D;
+  const KE *Kbase = reinterpret_cast<const KE *>(a.K);
+  const int64_t kvoff = PAGED ? 0 : (int64_t)(b * Hkv + g) * s.T_cap * D;
+  const int ps = a.pg.ps_shift;
+  // element offset of the K row of position t
+  auto row_of = [&](int32_t t) -> int64_t {
+    if constexpr (PAGED) return paged_row(ptab[t >> ps], g, Hkv, t, ps) * D;
+    else return kvoff + (int64_t)t * D;
+  };
 
   // Query operands, loaded once.  MFMA: lane l holds head l%16 (zero when
   // past the group), dims 32*ks + 8*(l/16) .. +7.  VALU: every head, dims
@@ -91,6 +101,9 @@ __global__ __launch_bounds__(256) void mask_decode_kernel(MaskArgs a) {
   }
 
   const int n = 2 * Kb;
+  // paged: page numbers to LDS, issued after the query loads so that both
+  // are in flight together (read after the first barrier)
+  if constexpr (PAGED) stage_pages(a.pg, b, Tp, ptab);
   initial_candidates(Np, Kb, cand_a[0], cand_e[0]);
   if (tid < kSpan) key[n + tid] = 0;  // padding read by the rank batches
   if (tid == 0) flag[0] = 1;          // N_p > K_b: the first round always runs
@@ -118,7 +131,7 @@ __global__ __launch_bounds__(256) void mask_decode_kernel(MaskArgs a) {
           const int32_t t = live[u] ? (lo + hi) >> 1 : 0;  // centre token (upper middle)
 #pragma unroll
           for (int ks = 0; ks < KS; ks++)
-            kr[u][ks] = Kv8<KE>::raw(Kbase + (int64_t)t * D + 32 * ks + 8 * (lane >> 4));
+            kr[u][ks] = Kv8<KE>::raw(Kbase + row_of(t) + 32 * ks + 8 * (lane >> 4));
         }
 #pragma unroll
         for (int u = 0; u < UNROLL; u++) {
@@ -151,7 +164,7 @@ __global__ __launch_bounds__(256) void mask_decode_kernel(MaskArgs a) {
           live[u] = c < n && lo_b >= 0;
           const int32_t lo = lo_b << s.bk_shift, hi = min(hi_b << s.bk_shift, Tp);
           const int32_t t = live[u] ? (lo + hi) >> 1 : 0;  // centre token (upper middle)
-          raw[u] = Vec<E>::raw(Kbase + (int64_t)t * D + cs * VEC);
+          raw[u] = Vec<E>::raw(Kbase + row_of(t) + cs * VEC);
         }
 #pragma unroll
         for (int u = 0; u < UNROLL; u++) {
@@ -193,8 +206,8 @@ __global__ __launch_bounds__(256) void mask_decode_kernel(MaskArgs a) {
 // child slot that holds each candidate's key).
 constexpr int kPipeMaxKb = 64;
 
-template <typename KE, int D, int GMAX, int TPW>
-__device__ inline void score_children(const KE *Kbase, const uint4 *qa, int32_t Tp, int bk_shift,
+template <typename KE, int D, int GMAX, int TPW, typename RowOf>
+__device__ inline void score_children(const KE *Kbase, RowOf row_of, const uint4 *qa, int32_t Tp, int bk_shift,
                                       int G, const int32_t *ca, const int32_t *ce, int nslot,
                                       bool children, int wi, int nw, uint64_t *dst) {
   constexpr int KS = D / 32;
@@ -227,7 +240,7 @@ __device__ inline void score_children(const KE *Kbase, const uint4 *qa, int32_t 
       const int32_t t = ok ? (tlo + thi) >> 1 : 0;  // centre token (upper middle)
 #pragma unroll
       for (int ks = 0; ks < KS; ks++)
-        kr[u][ks] = Kv8<KE>::raw(Kbase + (int64_t)t * D + 32 * ks + 8 * (lane >> 4));
+        kr[u][ks] = Kv8<KE>::raw(Kbase + row_of(t) + 32 * ks + 8 * (lane >> 4));
     }
 #pragma unroll
     for (int u = 0; u < TPW; u++) {
@@ -247,7 +260,7 @@ __device__ inline void score_children(const KE *Kbase, const uint4 *qa, int32_t 
   }
 }
 
-template <typename KE, int D, int GMAX, int TPW>
+template <typename KE, int D, int GMAX, int TPW, bool PAGED>
 __global__ __launch_bounds__(256) void mask_decode_pipe(MaskArgs a) {
   constexpr int KS = D / 32;
   const Shape &s = a.s;
@@ -272,9 +285,16 @@ __global__ __launch_bounds__(256) void mask_decode_pipe(MaskArgs a) {
   __shared__ uint64_t spec[2][4 * kPipeMaxKb];
   __shared__ uint64_t key[2 * kPipeMaxKb + kSpan];
   __shared__ int32_t flag[2];
+  extern __shared__ int32_t ptab[];  // paged: the sequence's page numbers
 
   const uint16_t *qbase = reinterpret_cast<const uint16_t *>(a.q) + ((int64_t)(b * s.Hq + g * s.G) * Tq + i) * D;
-  const KE *Kbase = reinterpret_cast<const KE *>(a.K) + (int64_t)(b * Hkv + g) * s.T_cap * D;
+  const KE *Kbase = reinterpret_cast<const KE *>(a.K);
+  const int64_t kvoff = PAGED ? 0 : (int64_t)(b * Hkv + g) * s.T_cap * D;
+  const int ps = a.pg.ps_shift;
+  auto row_of = [&](int32_t t) -> int64_t {
+    if constexpr (PAGED) return paged_row(ptab[t >> ps], g, Hkv, t, ps) * D;
+    else return kvoff + (int64_t)t * D;
+  };
   uint4 qa[KS];
   {
     const int h = lane & 15;
@@ -286,13 +306,16 @@ __global__ __launch_bounds__(256) void mask_decode_pipe(MaskArgs a) {
   }
 
   const int n = 2 * Kb;
+  // paged: page numbers to LDS, issued after the query loads so that both
+  // are in flight together (read after the first barrier)
+  if constexpr (PAGED) stage_pages(a.pg, b, Tp, ptab);
   initial_candidates(Np, Kb, cand_a[0], cand_e[0]);
   for (int c = tid; c < n; c += 256) srcs[0][c] = c;
   if (tid < kSpan) key[n + tid] = 0;
   if (tid == 0) flag[0] = 1;  // N_p > K_b: the first round always runs
   __syncthreads();
   // keys of the first candidates (all waves), kept where round 0 looks them up
-  score_children<KE, D, GMAX, TPW>(Kbase, qa, Tp, s.bk_shift, s.G, cand_a[0], cand_e[0], n, false,
+  score_children<KE, D, GMAX, TPW>(Kbase, row_of, qa, Tp, s.bk_shift, s.G, cand_a[0], cand_e[0], n, false,
                                wave, 4, spec[1]);
   __syncthreads();
 
@@ -334,7 +357,7 @@ __global__ __launch_bounds__(256) void mask_decode_pipe(MaskArgs a) {
       }
     } else {
       // speculative: score every child of every current candidate
-      score_children<KE, D, GMAX, TPW>(Kbase, qa, Tp, s.bk_shift, s.G, cand_a[cur], cand_e[cur], 2 * n,
+      score_children<KE, D, GMAX, TPW>(Kbase, row_of, qa, Tp, s.bk_shift, s.G, cand_a[cur], cand_e[cur], 2 * n,
                                    true, wave - 1, 3, spec[cur]);
     }
     __syncthreads();
@@ -344,18 +367,22 @@ __global__ __launch_bounds__(256) void mask_decode_pipe(MaskArgs a) {
   if (tid == 0) a.nnz[prob] = Kb;
 }
 
-template <typename KE, int D, int GMAX>
+// dynamic LDS: the page numbers of a whole sequence when paged
+size_t page_lds(const MaskArgs &a) { return a.pg.table ? (size_t)a.pg.seq_pages * sizeof(int32_t) : 0; }
+
+template <typename KE, int D, int GMAX, bool PAGED>
 void launch_pipe(const MaskArgs &a, hipStream_t st) {
   const int tiles = (4 * a.s.Kb + 15) / 16;  // child tiles per round, over 3 waves
   const int per = (tiles + 2) / 3;
   const dim3 grid((unsigned)a.s.problems), block(256);
-  if (per <= 1) hipLaunchKernelGGL((mask_decode_pipe<KE, D, GMAX, 1>), grid, block, 0, st, a);
-  else if (per <= 2) hipLaunchKernelGGL((mask_decode_pipe<KE, D, GMAX, 2>), grid, block, 0, st, a);
-  else if (per <= 4) hipLaunchKernelGGL((mask_decode_pipe<KE, D, GMAX, 4>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((mask_decode_pipe<KE, D, GMAX, 8>), grid, block, 0, st, a);
+  const size_t lds = page_lds(a);
+  if (per <= 1) hipLaunchKernelGGL((mask_decode_pipe<KE, D, GMAX, 1, PAGED>), grid, block, lds, st, a);
+  else if (per <= 2) hipLaunchKernelGGL((mask_decode_pipe<KE, D, GMAX, 2, PAGED>), grid, block, lds, st, a);
+  else if (per <= 4) hipLaunchKernelGGL((mask_decode_pipe<KE, D, GMAX, 4, PAGED>), grid, block, lds, st, a);
+  else hipLaunchKernelGGL((mask_decode_pipe<KE, D, GMAX, 8, PAGED>), grid, block, lds, st, a);
 }
 
-template <typename E, typename KE, int D, int GMAX>
+template <typename E, typename KE, int D, int GMAX, bool PAGED>
 void launch_g(const MaskArgs &a, hipStream_t st) {
   constexpr bool kMfma = std::is_same<E, uint16_t>::value;
   constexpr int RPP = 256 / (D / Vec<E>::N);
@@ -364,43 +391,50 @@ void launch_g(const MaskArgs &a, hipStream_t st) {
   // candidate rows per lane (VALU)
   const int per = kMfma ? ((n + 15) / 16 + 3) / 4 : (n + RPP - 1) / RPP;
   const dim3 grid((unsigned)a.s.problems), block(256);
-  if (per <= 1) hipLaunchKernelGGL((mask_decode_kernel<E, KE, D, GMAX, 1>), grid, block, 0, st, a);
-  else if (per <= 2) hipLaunchKernelGGL((mask_decode_kernel<E, KE, D, GMAX, 2>), grid, block, 0, st, a);
-  else if (per <= 4) hipLaunchKernelGGL((mask_decode_kernel<E, KE, D, GMAX, 4>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((mask_decode_kernel<E, KE, D, GMAX, 8>), grid, block, 0, st, a);
+  const size_t lds = page_lds(a);
+  if (per <= 1) hipLaunchKernelGGL((mask_decode_kernel<E, KE, D, GMAX, 1, PAGED>), grid, block, lds, st, a);
+  else if (per <= 2) hipLaunchKernelGGL((mask_decode_kernel<E, KE, D, GMAX, 2, PAGED>), grid, block, lds, st, a);
+  else if (per <= 4) hipLaunchKernelGGL((mask_decode_kernel<E, KE, D, GMAX, 4, PAGED>), grid, block, lds, st, a);
+  else hipLaunchKernelGGL((mask_decode_kernel<E, KE, D, GMAX, 8, PAGED>), grid, block, lds, st, a);
 }
 
 // E: query element type; KE: key element type (E itself, or E5M2 codes
 // under a bf16 query).
-template <typename E, typename KE, int D>
+template <typename E, typename KE, int D, bool PAGED>
 hipError_t launch_d(const MaskArgs &a, hipStream_t st) {
   const int G = a.s.G;
   if constexpr (std::is_same<E, uint16_t>::value) {
     if (a.s.Kb <= kPipeMaxKb) {
-      if (G <= 1) launch_pipe<KE, D, 1>(a, st);
-      else if (G <= 2) launch_pipe<KE, D, 2>(a, st);
-      else if (G <= 4) launch_pipe<KE, D, 4>(a, st);
-      else if (G <= 8) launch_pipe<KE, D, 8>(a, st);
-      else launch_pipe<KE, D, 16>(a, st);
+      if (G <= 1) launch_pipe<KE, D, 1, PAGED>(a, st);
+      else if (G <= 2) launch_pipe<KE, D, 2, PAGED>(a, st);
+      else if (G <= 4) launch_pipe<KE, D, 4, PAGED>(a, st);
+      else if (G <= 8) launch_pipe<KE, D, 8, PAGED>(a, st);
+      else launch_pipe<KE, D, 16, PAGED>(a, st);
       return hipGetLastError();
     }
   }
-  if (G <= 1) launch_g<E, KE, D, 1>(a, st);
-  else if (G <= 2) launch_g<E, KE, D, 2>(a, st);
-  else if (G <= 4) launch_g<E, KE, D, 4>(a, st);
-  else if (G <= 8) launch_g<E, KE, D, 8>(a, st);
-  else launch_g<E, KE, D, 16>(a, st);
+  if (G <= 1) launch_g<E, KE, D, 1, PAGED>(a, st);
+  else if (G <= 2) launch_g<E, KE, D, 2, PAGED>(a, st);
+  else if (G <= 4) launch_g<E, KE, D, 4, PAGED>(a, st);
+  else if (G <= 8) launch_g<E, KE, D, 8, PAGED>(a, st);
+  else launch_g<E, KE, D, 16, PAGED>(a, st);
   return hipGetLastError();
+}
+
+template <bool PAGED>
+hipError_t launch_layout(const MaskArgs &a, hipStream_t st) {
+  const bool d64 = a.s.d == 64;
+  if (a.s.dtype == HIPSA_BF16)
+    return d64 ? launch_d<uint16_t, uint16_t, 64, PAGED>(a, st) : launch_d<uint16_t, uint16_t, 128, PAGED>(a, st);
+  if (a.s.dtype == HIPSA_BF16_E5M2)
+    return d64 ? launch_d<uint16_t, uint8_t, 64, PAGED>(a, st) : launch_d<uint16_t, uint8_t, 128, PAGED>(a, st);
+  return d64 ? launch_d<float, float, 64, PAGED>(a, st) : launch_d<float, float, 128, PAGED>(a, st);
 }
 
 }  // namespace
 
 hipError_t launch_mask_decode(const MaskArgs &a, hipStream_t st) {
-  if (a.s.dtype == HIPSA_BF16)
-    return a.s.d == 64 ? launch_d<uint16_t, uint16_t, 64>(a, st) : launch_d<uint16_t, uint16_t, 128>(a, st);
-  if (a.s.dtype == HIPSA_BF16_E5M2)
-    return a.s.d == 64 ? launch_d<uint16_t, uint8_t, 64>(a, st) : launch_d<uint16_t, uint8_t, 128>(a, st);
-  return a.s.d == 64 ? launch_d<float, float, 64>(a, st) : launch_d<float, float, 128>(a, st);
+  return a.pg.table ? launch_layout<true>(a, st) : launch_layout<false>(a, st);
 }
 
 }  // namespace hipsa

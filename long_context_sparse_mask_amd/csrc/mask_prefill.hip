@@ -19,7 +19,8 @@
 // max on the candidate's ranking key (score above complemented start).
 // Selection and the final ascending write are the same as for decode.  fp8
 // centre rows are loaded as 8-byte slices and widened exactly to bf16 on
-// their way into LDS.
+// their way into LDS.  With a paged KV cache the sequence's page numbers are
+// staged in LDS before the first round.
 #include "hipsa_internal.h"
 #include "mask_select.h"
 
@@ -28,7 +29,7 @@ namespace {
 
 // ONEHEAD: the group has at most 4 query heads, so each wave owns one head
 // for the whole search and keeps its query operands in registers.
-template <typename KE, int D, bool ONEHEAD>
+template <typename KE, int D, bool ONEHEAD, bool PAGED>
 __global__ __launch_bounds__(256) void mask_prefill_kernel(MaskArgs a) {
   constexpr int KS = D / 16;  // k-steps of 16 over the head dim
   constexpr int BQ = 64;
@@ -58,7 +59,14 @@ __global__ __launch_bounds__(256) void mask_prefill_kernel(MaskArgs a) {
   __shared__ int32_t flag[2];
 
   const uint16_t *Qb = reinterpret_cast<const uint16_t *>(a.q) + ((int64_t)(b * s.Hq + g * s.G) * Tq + r0) * D;
-  const KE *Kbase = reinterpret_cast<const KE *>(a.K) + (int64_t)(b * Hkv + g) * s.T_cap * D;
+  extern __shared__ int32_t ptab[];  // paged: the sequence's page numbers
+  const KE *Kbase = reinterpret_cast<const KE *>(a.K);
+  const int64_t kvoff = PAGED ? 0 : (int64_t)(b * Hkv + g) * s.T_cap * D;
+  const int ps = a.pg.ps_shift;
+  auto row_of = [&](int32_t t) -> int64_t {
+    if constexpr (PAGED) return paged_row(ptab[t >> ps], g, Hkv, t, ps) * D;
+    else return kvoff + (int64_t)t * D;
+  };
   const int n = 2 * Kb, nct = (n + 31) / 32;
   // staging of 64 candidates' centre rows: SLR lanes per row, SRP rows per
   // pass, SP passes; rows padded to CRS elements (a column read of the 32
@@ -81,6 +89,9 @@ __global__ __launch_bounds__(256) void mask_prefill_kernel(MaskArgs a) {
   auto load_queries = [&](int h) { HIPSA_LOAD_QUERIES(h); };
   if (ONEHEAD) HIPSA_LOAD_QUERIES(min(wave, s.G - 1));
 
+  // paged: page numbers to LDS, issued after the query loads so that both
+  // are in flight together (read after the first barrier)
+  if constexpr (PAGED) stage_pages(a.pg, b, Tp, ptab);
   initial_candidates(Np, Kb, cand_a[0], cand_e[0]);
   for (int c = tid; c < n + kSpan; c += 256) key[0][c] = key[1][c] = 0;
   if (tid == 0) flag[0] = 1;
@@ -108,7 +119,7 @@ __global__ __launch_bounds__(256) void mask_prefill_kernel(MaskArgs a) {
         const bool live = c < n && lo_b >= 0;
         const int32_t lo = lo_b << s.bk_shift, hi = min(hi_b << s.bk_shift, Tp);
         const int32_t t = live ? (lo + hi) >> 1 : 0;  // centre token (upper middle)
-        srow[u] = Kv8<KE>::raw(Kbase + (int64_t)t * D + 8 * (tid % SLR));
+        srow[u] = Kv8<KE>::raw(Kbase + row_of(t) + 8 * (tid % SLR));
       }
 #pragma unroll
       for (int u = 0; u < SP; u++)
@@ -159,24 +170,31 @@ __global__ __launch_bounds__(256) void mask_prefill_kernel(MaskArgs a) {
   if (tid == 0) a.nnz[prob] = Kb;
 }
 
-template <typename KE>
+template <typename KE, bool PAGED>
 void launch_k(const MaskArgs &a, hipStream_t st) {
   const dim3 grid((unsigned)a.s.problems), block(256);
+  const size_t lds = PAGED ? (size_t)a.pg.seq_pages * sizeof(int32_t) : 0;
   const bool one = a.s.G <= 4;
   if (a.s.d == 64) {
-    if (one) hipLaunchKernelGGL((mask_prefill_kernel<KE, 64, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((mask_prefill_kernel<KE, 64, false>), grid, block, 0, st, a);
+    if (one) hipLaunchKernelGGL((mask_prefill_kernel<KE, 64, true, PAGED>), grid, block, lds, st, a);
+    else hipLaunchKernelGGL((mask_prefill_kernel<KE, 64, false, PAGED>), grid, block, lds, st, a);
   } else {
-    if (one) hipLaunchKernelGGL((mask_prefill_kernel<KE, 128, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((mask_prefill_kernel<KE, 128, false>), grid, block, 0, st, a);
+    if (one) hipLaunchKernelGGL((mask_prefill_kernel<KE, 128, true, PAGED>), grid, block, lds, st, a);
+    else hipLaunchKernelGGL((mask_prefill_kernel<KE, 128, false, PAGED>), grid, block, lds, st, a);
   }
+}
+
+template <bool PAGED>
+void launch_layout(const MaskArgs &a, hipStream_t st) {
+  if (a.s.dtype == HIPSA_BF16_E5M2) launch_k<uint8_t, PAGED>(a, st);
+  else launch_k<uint16_t, PAGED>(a, st);
 }
 
 }  // namespace
 
 hipError_t launch_mask_prefill(const MaskArgs &a, hipStream_t st) {
-  if (a.s.dtype == HIPSA_BF16_E5M2) launch_k<uint8_t>(a, st);
-  else launch_k<uint16_t>(a, st);
+  if (a.pg.table) launch_layout<true>(a, st);
+  else launch_layout<false>(a, st);
   return hipGetLastError();
 }
 

@@ -20,8 +20,9 @@ def _declared():
 
 
 def test_header_declares_the_boundary():
-    assert _declared() == sorted(["hip_mask_estimate", "hip_sparse_attn",
-                                  "hipsa_workspace_bytes", "hipsa_last_error"])
+    assert _declared() == sorted(["hip_mask_estimate", "hip_sparse_attn", "hip_mask_estimate_paged",
+                                  "hip_sparse_attn_paged", "hipsa_workspace_bytes",
+                                  "hipsa_last_error"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -52,7 +53,7 @@ def _mask(desc, k=2048, bk=64, bq=1, ptrs=(FAKE, FAKE, FAKE, FAKE)):
     return hs.lib.hip_mask_estimate(C.byref(desc), q, K, k, bk, bq, idx, nnz, None, 0, None)
 
 
-ERR_NULL, ERR_SHAPE, ERR_BLOCK, ERR_DTYPE, ERR_WS, ERR_ALIGN = -1, -2, -3, -4, -5, -7
+ERR_NULL, ERR_SHAPE, ERR_BLOCK, ERR_DTYPE, ERR_WS, ERR_ALIGN, ERR_PAGES = -1, -2, -3, -4, -5, -7, -8
 
 
 @pytest.mark.parametrize("kw,k,bk,bq,code", [
@@ -140,6 +141,69 @@ def test_binding_element_type_pairs():
     for q, k in ((q32, k8), (q32, q16), (q16, q32), (k8, k8)):
         with pytest.raises(TypeError):
             hs._dtype_code(q, k)
+
+
+def _pages(**kw):
+    import long_context_sparse_mask_amd as hs
+    base = dict(table=0x2000, max_pages=512, page_size=64, num_pages=4096)
+    base.update(kw)
+    return hs.Pages(**base)
+
+
+def _mask_paged(desc, pages, k=2048, bk=64, bq=1, ptrs=(FAKE, FAKE, FAKE, FAKE)):
+    import long_context_sparse_mask_amd as hs
+    q, K, idx, nnz = ptrs
+    return hs.lib.hip_mask_estimate_paged(C.byref(desc), C.byref(pages) if pages else None, q, K,
+                                          k, bk, bq, idx, nnz, None, 0, None)
+
+
+@pytest.mark.parametrize("pkw,dkw,bk,code", [
+    (dict(page_size=48), {}, 64, ERR_PAGES),               # not a power of two
+    (dict(page_size=32), {}, 64, ERR_PAGES),               # smaller than block_k
+    (dict(page_size=1 << 17), {}, 64, ERR_PAGES),          # too large
+    (dict(max_pages=511), {}, 64, ERR_PAGES),              # 32768 / 64 = 512 pages needed
+    (dict(num_pages=0), {}, 64, ERR_PAGES),
+    (dict(num_pages=1 << 31), {}, 64, ERR_PAGES),
+    (dict(page_size=8, max_pages=20000), dict(T=16385 * 8), 8, ERR_PAGES),  # > 16384 pages on chip
+    (dict(table=None), {}, 64, ERR_NULL),
+    ({}, dict(Hq=30), 64, ERR_SHAPE),                      # the shared shape checks still apply
+])
+def test_paged_mask_rejects_invalid_pages(pkw, dkw, bk, code):
+    import long_context_sparse_mask_amd as hs
+    d = _desc(T_cap=0, **dkw)  # T_cap is not used by the paged calls
+    assert _mask_paged(d, _pages(**pkw), k=32 * bk, bk=bk) == code
+    assert hs.lib.hipsa_last_error().decode() != ""
+
+
+def test_paged_calls_null_and_alignment():
+    import long_context_sparse_mask_amd as hs
+    assert _mask_paged(_desc(), None) == ERR_NULL
+    assert _mask_paged(_desc(), _pages(), ptrs=(FAKE, C.c_void_p(0x1008), FAKE, FAKE)) == ERR_ALIGN
+    d = _desc()
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 2048, 64, 1, FAKE, FAKE, 1 << 30, None]
+    bad = _pages(page_size=12)
+    assert hs.lib.hip_sparse_attn_paged(C.byref(d), C.byref(bad), *args) == ERR_PAGES
+    args_v = list(args)
+    args_v[2] = C.c_void_p(0x1008)  # V
+    assert hs.lib.hip_sparse_attn_paged(C.byref(d), C.byref(_pages()), *args_v) == ERR_ALIGN
+    args_ws = list(args)
+    args_ws[10] = 0  # no workspace
+    assert hs.lib.hip_sparse_attn_paged(C.byref(d), C.byref(_pages()), *args_ws) == ERR_WS
+    # the attention call keeps no page numbers on chip: many pages are fine up to the checks
+    # (exercised here only through the workspace check that precedes any launch)
+    d2 = _desc(T=16385 * 8, T_cap=0)
+    assert hs.lib.hip_sparse_attn_paged(C.byref(d2), C.byref(_pages(page_size=8, max_pages=20000)),
+                                        FAKE, FAKE, FAKE, FAKE, FAKE, 256, 8, 1, FAKE, FAKE, 0,
+                                        None) == ERR_WS
+
+
+def test_paged_empty_problem_is_a_no_op():
+    import long_context_sparse_mask_amd as hs
+    for d in (_desc(B=0, T_cap=0), _desc(Tq=0, T_cap=0)):
+        assert _mask_paged(d, _pages(table=None), ptrs=(None, None, None, None)) == 0
+        assert hs.lib.hip_sparse_attn_paged(C.byref(d), C.byref(_pages(table=None)), None, None,
+                                            None, None, None, 2048, 64, 1, None, None, 0,
+                                            None) == 0
 
 
 def test_empty_problem_is_a_no_op():

@@ -5,6 +5,8 @@ import re
 import subprocess
 import sys
 
+import torch
+
 import bench
 import synth_inputs as si
 
@@ -89,3 +91,18 @@ def test_multi_gpu_request_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_page_pool_addressing():
+    """The bench's page pool: position t of sequence b is row t % page_size of
+    page table[b, t // page_size], pages shuffled over the pool."""
+    g = torch.Generator().manual_seed(0)
+    B, Hkv, T, d, ps = 2, 3, 256, 4, 64
+    K, V = torch.randn(B, Hkv, T, d), torch.randn(B, Hkv, T, d)
+    Kp, Vp, tab = bench.page_pool(K, V, T, ps, g, torch)
+    assert Kp.shape == (B * T // ps, Hkv, ps, d) and tab.dtype == torch.int32
+    assert sorted(tab.flatten().tolist()) == list(range(B * T // ps))
+    t = torch.arange(T)
+    for b in range(B):
+        assert torch.equal(Kp[tab[b, t // ps].long(), :, t % ps].permute(1, 0, 2), K[b])
+        assert torch.equal(Vp[tab[b, t // ps].long(), :, t % ps].permute(1, 0, 2), V[b])
