@@ -208,6 +208,33 @@ template <> struct KvN<uint8_t, 4> {
   }
 };
 
+// Eight consecutive elements of a V row (16 bytes of bf16 or 8 bytes of E5M2
+// codes) widened to fp32; a load that is not kept reads as zeros.
+template <typename KE> struct Kv8f;
+template <> struct Kv8f<uint16_t> {
+  using raw_t = uint4;
+  __device__ static inline raw_t raw(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+  __device__ static inline void widen(raw_t r, bool keep, float (&v)[8]) {
+    const uint32_t w[4] = {keep ? r.x : 0u, keep ? r.y : 0u, keep ? r.z : 0u, keep ? r.w : 0u};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+template <> struct Kv8f<uint8_t> {
+  using raw_t = uint2;
+  __device__ static inline raw_t raw(const uint8_t *p) { return *reinterpret_cast<const uint2 *>(p); }
+  __device__ static inline void widen(raw_t r, bool keep, float (&v)[8]) {
+    const uint32_t x = keep ? r.x : 0u, y = keep ? r.y : 0u;
+    const f32x2_t a = e5m2x2_to_f32x2<false>(x), b = e5m2x2_to_f32x2<true>(x);
+    const f32x2_t c = e5m2x2_to_f32x2<false>(y), d = e5m2x2_to_f32x2<true>(y);
+    v[0] = a.x; v[1] = a.y; v[2] = b.x; v[3] = b.y;
+    v[4] = c.x; v[5] = c.y; v[6] = d.x; v[7] = d.y;
+  }
+};
+
 // MFMA operand / accumulator vectors (gfx950 bf16 matrix cores).
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));

@@ -74,7 +74,7 @@ __device__ inline void select_top(const int32_t *ca, const int32_t *ce, const ui
 // The K_b kept one-block chunks sit at the even slots of `fin`; writes their
 // block ids to out[0..K_b) in ascending order.
 __device__ inline void write_ascending(const int32_t *fin, int Kb, int32_t *out) {
-  for (int c = threadIdx.x; c < Kb; c += 256) {
+  for (int c = threadIdx.x; c < Kb; c += blockDim.x) {
     const int32_t v = fin[2 * c];
     int r = 0;
     for (int j0 = 0; j0 < Kb; j0 += kSpan) {
@@ -91,7 +91,7 @@ __device__ inline void write_ascending(const int32_t *fin, int Kb, int32_t *out)
 // Candidate slots 2c, 2c+1 from the halves of initial chunk c of the uniform
 // partition [floor(c*N_p/K_b), floor((c+1)*N_p/K_b)) (exact in double).
 __device__ inline void initial_candidates(int32_t Np, int Kb, int32_t *ca, int32_t *ce) {
-  for (int c = threadIdx.x; c < Kb; c += 256) {
+  for (int c = threadIdx.x; c < Kb; c += blockDim.x) {
     const int32_t lo = (int32_t)((double)c * Np / Kb), hi = (int32_t)((double)(c + 1) * Np / Kb);
     const bool split = hi - lo >= 2;
     const int32_t m = lo + (hi - lo) / 2;
