@@ -36,7 +36,8 @@ class Shape(C.Structure):
     _fields_ = [("B", C.c_int64), ("Hq", C.c_int64), ("Hkv", C.c_int64), ("Tq", C.c_int64),
                 ("T", C.c_int64), ("T_cap", C.c_int64), ("d", C.c_int64), ("k", C.c_int64),
                 ("block_k", C.c_int64), ("block_q", C.c_int64), ("causal", C.c_int32),
-                ("dtype", C.c_int32), ("kv_dtype", C.c_int32)]
+                ("dtype", C.c_int32), ("kv_dtype", C.c_int32), ("sink", C.c_int64),
+                ("window", C.c_int64)]
 
 
 class Trace(C.Structure):
@@ -90,11 +91,11 @@ def _dtype_code(t: torch.Tensor, kv: bool = False) -> int:
     return code
 
 
-def shape(q, K, *, T, k, block_k, block_q, causal=1) -> Shape:
+def shape(q, K, *, T, k, block_k, block_q, causal=1, sink=0, window=0) -> Shape:
     B, Hq, Tq, d = q.shape
     assert K.shape[0] == B and K.shape[3] == d
     return Shape(B, Hq, K.shape[1], Tq, T, K.shape[2], d, k, block_k, block_q, int(causal),
-                 _dtype_code(q), _dtype_code(K, kv=True))
+                 _dtype_code(q), _dtype_code(K, kv=True), sink, window)
 
 
 def e5m2_values(lib=None) -> np.ndarray:
@@ -112,10 +113,11 @@ def nthreads(n: int | None = None) -> int:
         return os.cpu_count() or 1
 
 
-def mask_all(q, K, *, T, k, block_k, block_q, causal=1, threads=None, lib=None):
+def mask_all(q, K, *, T, k, block_k, block_q, causal=1, sink=0, window=0, threads=None, lib=None):
     """Indices [B,Hkv,NQB,K_b], nnz [B,Hkv,NQB] and the min relative cut margin per problem."""
     lib = lib or load()
-    s = shape(q, K, T=T, k=k, block_k=block_k, block_q=block_q, causal=causal)
+    s = shape(q, K, T=T, k=k, block_k=block_k, block_q=block_q, causal=causal, sink=sink,
+              window=window)
     nqb = -(-s.Tq // block_q)
     kb = k // block_k
     idx = np.full((s.B, s.Hkv, nqb, kb), -1, np.int32)
@@ -127,11 +129,12 @@ def mask_all(q, K, *, T, k, block_k, block_q, causal=1, threads=None, lib=None):
     return idx, nnz, margin
 
 
-def mask_one(q, K, b, g, qb, *, T, k, block_k, block_q, causal=1, trace=False, lib=None,
-             max_rounds=64):
+def mask_one(q, K, b, g, qb, *, T, k, block_k, block_q, causal=1, sink=0, window=0, trace=False,
+             lib=None, max_rounds=64):
     """One problem; with trace=True also the per-round candidates (sorted by rank)."""
     lib = lib or load()
-    s = shape(q, K, T=T, k=k, block_k=block_k, block_q=block_q, causal=causal)
+    s = shape(q, K, T=T, k=k, block_k=block_k, block_q=block_q, causal=causal, sink=sink,
+              window=window)
     kb = k // block_k
     idx = np.full(kb, -1, np.int32)
     nnz = np.zeros(1, np.int32)
@@ -170,11 +173,12 @@ def mask_one(q, K, b, g, qb, *, T, k, block_k, block_q, causal=1, trace=False, l
     return out
 
 
-def attn_all(q, K, V, indices, nnz, *, T, k, block_k, block_q, causal=1, threads=None, lib=None):
+def attn_all(q, K, V, indices, nnz, *, T, k, block_k, block_q, causal=1, sink=0, window=0, threads=None, lib=None):
     """Exact attention over the listed blocks, float64 [B,Hq,Tq,d]."""
     lib = lib or load()
     assert K.dtype == V.dtype and K.shape == V.shape
-    s = shape(q, K, T=T, k=k, block_k=block_k, block_q=block_q, causal=causal)
+    s = shape(q, K, T=T, k=k, block_k=block_k, block_q=block_q, causal=causal, sink=sink,
+              window=window)
     indices = np.ascontiguousarray(indices, np.int32)
     nnz = np.ascontiguousarray(nnz, np.int32)
     out = np.zeros((s.B, s.Hq, s.Tq, s.d), np.float64)
@@ -184,10 +188,11 @@ def attn_all(q, K, V, indices, nnz, *, T, k, block_k, block_q, causal=1, threads
     return out
 
 
-def attn_row(q, K, V, indices, nnz, b, h, i, *, T, k, block_k, block_q, causal=1, lib=None):
+def attn_row(q, K, V, indices, nnz, b, h, i, *, T, k, block_k, block_q, causal=1, sink=0, window=0, lib=None):
     lib = lib or load()
     assert K.dtype == V.dtype and K.shape == V.shape
-    s = shape(q, K, T=T, k=k, block_k=block_k, block_q=block_q, causal=causal)
+    s = shape(q, K, T=T, k=k, block_k=block_k, block_q=block_q, causal=causal, sink=sink,
+              window=window)
     indices = np.ascontiguousarray(indices, np.int32)
     nnz = np.ascontiguousarray(nnz, np.int32)
     out = np.zeros(s.d, np.float64)

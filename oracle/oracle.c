@@ -24,7 +24,10 @@
  *    chunks are represented by their centre tokens; top-k is approximate.
  *  - SGLang pull request "Support Efficient Sparse HiP Attention (InfiniteHiP)
  *    ...", the launch command for the Qwen2.5-VL model: HiP runs with the KV
- *    cache stored as fp8 e5m2.
+ *    cache stored as fp8 e5m2; its layer configuration pairs HiP with a
+ *    sliding window and a "streaming" (attention-sink) dense part.
+ *  - Rebuttal page, reviewer T2wK, Q1: HiP retrieves long-range keys and a
+ *    sliding window the local ones, and the two combine well.
  *
  * Readings taken where the pages are silent (each is pinned by a test):
  *  R1 chunk boundaries live on key-block boundaries; the search stops when
@@ -48,6 +51,13 @@
  *     no scale factor (the launch command names the format and nothing
  *     else); the method then runs unchanged on the decoded values, with the
  *     query in its own element type.
+ *  R10 dense part: `sink` and `window` (tokens, multiples of b_k) make the
+ *     first S_b = sink/b_k blocks and the last W_b = window/b_k of the N_p
+ *     blocks a query block sees (fewer when N_p is small: sink first) part
+ *     of every row's key set.  The search runs over the blocks between them
+ *     only, so the index list holds searched blocks; attention takes the
+ *     union of the dense blocks and the listed ones (a listed id inside a
+ *     dense range adds nothing).
  *
  * Layouts (contiguous, head-major): q [B,Hq,Tq,d]; K, V [B,Hkv,T_cap,d] with
  * rows 0..T-1 valid; indices [B,Hkv,NQB,K_b] (ascending, -1 past nnz);
@@ -68,6 +78,7 @@ typedef struct {
   int32_t causal;
   int32_t dtype;    /* element type of q */
   int32_t kv_dtype; /* element type of K and V */
+  int64_t sink, window; /* R10, in tokens (0 = none) */
 } or_shape;
 
 /* Optional search trace of one problem; arrays hold max_rounds * cap. */
@@ -114,6 +125,16 @@ static int64_t rows_and_tp(const or_shape *s, int64_t qb, int64_t *r0, int64_t *
 
 static int64_t position(const or_shape *s, int64_t i) { return s->T - s->Tq + i; }
 
+/* R10: the dense blocks of a query block that sees Np blocks are [0, *sb)
+ * and [Np - *wb, Np). */
+static void dense_blocks(const or_shape *s, int64_t Np, int64_t *sb, int64_t *wb) {
+  int64_t a = s->sink / s->block_k, w = s->window / s->block_k;
+  if (a > Np) a = Np;
+  if (w > Np - a) w = Np - a;
+  *sb = a;
+  *wb = w;
+}
+
 static double dot_qk(const or_shape *s, const void *q, const void *K, int64_t b, int64_t h,
                      int64_t i, int64_t g, int64_t t) {
   int64_t qo = ((b * s->Hq + h) * s->Tq + i) * s->d;
@@ -148,10 +169,14 @@ int or_mask_one(const or_shape *s, const void *q, const void *K, int64_t b, int6
   const int64_t Np = (Tp + s->block_k - 1) / s->block_k;
   if (tr) tr->rounds = 0;
   for (int64_t j = 0; j < Kb; j++) idx[j] = -1;
+  /* R10: the search covers the blocks [lo, lo + M) between the dense parts */
+  int64_t sb, wb;
+  dense_blocks(s, Np, &sb, &wb);
+  const int64_t lo = sb, M = Np - sb - wb;
 
-  if (Np <= Kb) { /* R7: the block sees few enough keys to attend to all */
-    for (int64_t j = 0; j < Np; j++) idx[j] = (int32_t)j;
-    *nnz = (int32_t)Np;
+  if (M <= Kb) { /* R7: the block sees few enough keys to attend to all */
+    for (int64_t j = 0; j < M; j++) idx[j] = (int32_t)(lo + j);
+    *nnz = (int32_t)M;
     *margin = INFINITY;
     return 0;
   }
@@ -161,8 +186,8 @@ int or_mask_one(const or_shape *s, const void *q, const void *K, int64_t b, int6
   cand_t *cand = malloc(sizeof(cand_t) * 2 * Kb);
   if (!ca || !ce || !cand) { free(ca); free(ce); free(cand); return -1; }
   for (int64_t i = 0; i < Kb; i++) {
-    ca[i] = i * Np / Kb;
-    ce[i] = (i + 1) * Np / Kb;
+    ca[i] = lo + i * M / Kb;
+    ce[i] = lo + (i + 1) * M / Kb;
   }
   double min_rel = INFINITY;
   int32_t round = 0;
@@ -269,14 +294,24 @@ int or_attn_row(const or_shape *s, const void *q, const void *K, const void *V,
   if (cnt < 0) cnt = 0;
   if (cnt > Kb) cnt = Kb;
   const double scale = 1.0 / sqrt((double)s->d);
+  /* R10: the row's blocks are the dense ones, then the listed ones outside
+   * the dense ranges; entry n of this sequence is block blk_at(n) or -1 */
+  int64_t sb, wb;
+  dense_blocks(s, Np, &sb, &wb);
+  const int64_t nd = sb + wb;
+#define BLK_AT(n)                                                                   \
+  ((n) < sb ? (n)                                                                   \
+   : (n) < nd ? Np - wb + ((n) - sb)                                                \
+   : (list[(n) - nd] < 0 || list[(n) - nd] >= Np || list[(n) - nd] < sb ||          \
+      list[(n) - nd] >= Np - wb) ? -1 : list[(n) - nd])
 
   for (int64_t x = 0; x < s->d; x++) out[x] = 0.0;
   /* pass 1: the largest logit, for a stable softmax */
   double mx = -INFINITY;
   int64_t seen = 0;
-  for (int64_t n = 0; n < cnt; n++) {
-    int64_t blk = list[n];
-    if (blk < 0 || blk >= Np) continue;
+  for (int64_t n = 0; n < nd + cnt; n++) {
+    int64_t blk = BLK_AT(n);
+    if (blk < 0) continue;
     for (int64_t t = blk * s->block_k; t < (blk + 1) * s->block_k && t < Tp; t++) {
       if (t > limit) continue;
       double l = dot_qk(s, q, K, b, h, i, g, t) * scale;
@@ -287,9 +322,9 @@ int or_attn_row(const or_shape *s, const void *q, const void *K, const void *V,
   if (seen == 0) return 0;
   /* pass 2: weights and the weighted sum of values */
   double den = 0.0;
-  for (int64_t n = 0; n < cnt; n++) {
-    int64_t blk = list[n];
-    if (blk < 0 || blk >= Np) continue;
+  for (int64_t n = 0; n < nd + cnt; n++) {
+    int64_t blk = BLK_AT(n);
+    if (blk < 0) continue;
     for (int64_t t = blk * s->block_k; t < (blk + 1) * s->block_k && t < Tp; t++) {
       if (t > limit) continue;
       double w = exp(dot_qk(s, q, K, b, h, i, g, t) * scale - mx);
@@ -298,6 +333,7 @@ int or_attn_row(const or_shape *s, const void *q, const void *K, const void *V,
       for (int64_t x = 0; x < s->d; x++) out[x] += w * elem(V, s->kv_dtype, vo + x);
     }
   }
+#undef BLK_AT
   for (int64_t x = 0; x < s->d; x++) out[x] /= den;
   return 0;
 }

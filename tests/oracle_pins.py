@@ -418,10 +418,98 @@ def pin_e5m2_kv(lib):
     assert not np.array_equal(o8, out)  # the sparse result differs from the dense one
 
 
+# ---------------------------------------------------------------- dense part (sink + window)
+
+def pin_dense_part_trace(lib):
+    """Hand-traced search with sink and window blocks, and attention over the
+    union of the dense blocks and the list (softmax over the named tokens)."""
+    g = _golden("dense_part.json")
+    sh = g["shape"]
+    T = sh["T"]
+    q, K, V = _line_inputs(g["s"])
+    kw = dict(T=T, k=sh["k"], block_k=sh["block_k"], block_q=1, causal=1, sink=sh["sink"],
+              window=sh["window"], lib=lib)
+    res = oracle.mask_one(q, K, 0, 0, 0, trace=True, **kw)
+    assert res["indices"].tolist() == g["expected_indices"], res["indices"].tolist()
+    _check_trace(res["rounds"], g["trace"])
+    assert math.isclose(res["margin"], g["expected_margin"], rel_tol=1e-12), res["margin"]
+    idx = res["indices"].reshape(1, 1, 1, -1)
+    nnz = np.array([[[res["nnz"]]]], np.int32)
+    out = oracle.attn_row(q, K, V, idx, nnz, 0, 0, 0, **kw)
+    toks = g["attended_tokens"]
+    logit = np.array([g["s"][t] for t in toks]) / math.sqrt(q.shape[-1])
+    w = np.exp(logit - logit.max())
+    want = (w[:, None] * V[0, 0, toks].double().numpy()).sum(0) / w.sum()
+    assert np.abs(out - want).max() < 1e-12
+
+
+def pin_dense_part_reduction(lib):
+    """sink + window + k covering every visible block: dense attention (torch SDPA)."""
+    rng = torch.Generator().manual_seed(21)
+    for (B, Hq, Hkv, Tq, T, d, bk, bq, sink, window) in [(1, 4, 2, 1, 100, 64, 8, 1, 16, 40),
+                                                         (1, 4, 2, 40, 100, 64, 8, 16, 8, 24)]:
+        q = torch.randn(B, Hq, Tq, d, generator=rng)
+        K = torch.randn(B, Hkv, T, d, generator=rng)
+        V = torch.randn(B, Hkv, T, d, generator=rng)
+        nblk = -(-T // bk)
+        k = (nblk - (sink + window) // bk) * bk  # the search sees every middle block
+        kw = dict(T=T, k=k, block_k=bk, block_q=bq, causal=1, sink=sink, window=window, threads=2,
+                  lib=lib)
+        idx, nnz, margin = oracle.mask_all(q, K, **kw)
+        assert np.isinf(margin).all()
+        out = oracle.attn_all(q, K, V, idx, nnz, **kw)
+        assert np.abs(out - _dense_reference(q, K, V, T, 1)).max() < 1e-10
+
+
+def pin_dense_part_search_range(lib):
+    """For a decode row the search with sink S and window W equals the plain
+    search on the keys between them (same scores, centres and ranking), its
+    block ids shifted by S_b."""
+    import synth_inputs as si
+    w = si.workload("decode_32k", T=3000, Hq=4, Hkv=1, block_k=16, k=256)
+    x = si.make_inputs(w)
+    q, K = x["q"].float(), x["K"].float()
+    S, W = 5 * 16, 9 * 16
+    Np = -(-w.T // 16)
+    hi = (Np - W // 16) * 16  # first token of the window
+    kw = dict(k=w.k, block_k=16, block_q=1, causal=1, threads=2, lib=lib)
+    idx, nnz, m = oracle.mask_all(q, K, T=w.T, sink=S, window=W, **kw)
+    Kc = K[:, :, S:hi].contiguous()
+    idx_c, nnz_c, m_c = oracle.mask_all(q, Kc, T=hi - S, **kw)
+    assert (nnz == nnz_c).all() and np.array_equal(m, m_c)
+    assert (idx == np.where(idx_c >= 0, idx_c + S // 16, -1)).all()
+
+
+def pin_dense_part_union(lib):
+    """Attention with a dense part equals attention over the explicit list of
+    the dense blocks followed by the listed blocks outside them; listed ids
+    inside a dense range add nothing."""
+    rng = torch.Generator().manual_seed(22)
+    T, d, bk, sink, window, kb = 700, 32, 8, 24, 40, 12
+    q = torch.randn(1, 2, 3, d, generator=rng)
+    K = torch.randn(1, 1, T, d, generator=rng)
+    V = torch.randn(1, 1, T, d, generator=rng)
+    Np = -(-T // bk)
+    lst = np.array([0, 2, 5, 40, 41, 41, 80, Np - 1, Np - 3, 500, -1, 63], np.int32)  # dense ids, a repeat, bad ids
+    idx = lst.reshape(1, 1, 1, kb)
+    nnz = np.array([[[kb]]], np.int32)
+    kw = dict(T=T, k=kb * bk, block_k=bk, block_q=3, causal=1, threads=2, lib=lib)
+    out = oracle.attn_all(q, K, V, idx, nnz, sink=sink, window=window, **kw)
+    sb, wb = sink // bk, window // bk
+    dense = list(range(sb)) + list(range(Np - wb, Np))
+    rest = [int(b) for b in lst if 0 <= b < Np and not (b < sb or b >= Np - wb)]
+    full = np.array(dense + rest, np.int32)
+    kb2 = len(full)
+    out2 = oracle.attn_all(q, K, V, full.reshape(1, 1, 1, kb2), np.array([[[kb2]]], np.int32),
+                           T=T, k=kb2 * bk, block_k=bk, block_q=3, causal=1, threads=2, lib=lib)
+    assert np.array_equal(out, out2)
+
+
 ALL_PINS = [
     pin_monotone_counterexample, pin_centre_tokens, pin_centre_blocks, pin_centre_partial_block,
     pin_uneven_partition, pin_causal_vote, pin_group_max, pin_dense_reduction,
     pin_exact_topk_monotone, pin_exact_topk_disjoint_chunks, pin_exact_topk_certified,
     pin_tree_structure, pin_zero_query_ties, pin_attention_invariants, pin_mask_invariances,
-    pin_e5m2_codes, pin_e5m2_kv,
+    pin_e5m2_codes, pin_e5m2_kv, pin_dense_part_trace, pin_dense_part_reduction,
+    pin_dense_part_search_range, pin_dense_part_union,
 ]

@@ -28,14 +28,14 @@ MUTANTS = [
     ("strided_head_group", "for (int64_t h = g * G; h < (g + 1) * G; h++)",
      "for (int64_t h = g; h < s->Hq; h += s->Hkv)"),
     ("first_row_only", "for (int64_t i = r0; i < r1; i++) {", "for (int64_t i = r0; i < r0 + 1; i++) {"),
-    ("ceil_initial_partition", "ca[i] = i * Np / Kb;\n    ce[i] = (i + 1) * Np / Kb;",
-     "ca[i] = (i * Np + Kb - 1) / Kb;\n    ce[i] = ((i + 1) * Np + Kb - 1) / Kb;"),
+    ("ceil_initial_partition", "ca[i] = lo + i * M / Kb;\n    ce[i] = lo + (i + 1) * M / Kb;",
+     "ca[i] = lo + (i * M + Kb - 1) / Kb;\n    ce[i] = lo + ((i + 1) * M + Kb - 1) / Kb;"),
     ("attn_no_scale", "const double scale = 1.0 / sqrt((double)s->d);", "const double scale = 1.0;"),
     ("attn_no_causal_mask", "if (t > limit) continue;\n      double w", "double w"),
     ("attn_value_head_of_query", "int64_t vo = ((b * s->Hkv + g) * s->T_cap + t) * s->d;",
      "int64_t vo = ((b * s->Hkv + h % s->Hkv) * s->T_cap + t) * s->d;"),
     ("margin_not_relative", "rel = den == 0.0 ? 0.0 : (hiS - loS) / den;", "rel = hiS - loS;"),
-    ("dense_case_skipped", "if (Np <= Kb) {", "if (Np < 0) {"),
+    ("dense_case_skipped", "if (M <= Kb) {", "if (M < 0) {"),
     ("score_sum_over_group", "if (v > best) best = v;",
      "best = (best == -INFINITY) ? v : best + v;"),
     ("e5m2_bias_16", "mag = ldexp(1.0 + m / 4.0, e - 15);", "mag = ldexp(1.0 + m / 4.0, e - 16);"),
@@ -47,6 +47,11 @@ MUTANTS = [
     ("e5m2_infinity_as_nan", "if (e == 31) mag = m == 0 ? INFINITY : NAN;", "if (e == 31) mag = NAN;"),
     ("key_type_of_query", "elem(K, s->kv_dtype, ko + x)", "elem(K, s->dtype, ko + x)"),
     ("value_type_of_query", "elem(V, s->kv_dtype, vo + x)", "elem(V, s->dtype, vo + x)"),
+    ("window_searched", "const int64_t lo = sb, M = Np - sb - wb;", "const int64_t lo = sb, M = Np - sb;"),
+    ("sink_searched", "const int64_t lo = sb, M = Np - sb - wb;", "const int64_t lo = 0, M = Np - wb;"),
+    ("sink_not_attended", "((n) < sb ? (n)", "((n) < sb ? -1"),
+    ("window_off_by_one", "Np - wb + ((n) - sb)", "Np - wb - 1 + ((n) - sb)"),
+    ("dense_listed_twice", "list[(n) - nd] < sb ||", "0 ||"),
 ]
 
 
