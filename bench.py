@@ -252,7 +252,7 @@ def page_pool(K, V, T, page_size, gen, torch):
 
 
 def run_workload(w, steps, warmup, torch, hs, si, with_cpu, cpu_budget,
-                 n_layers=N_LAYER_COPIES, n_q=N_QUERY_SETS, page_size=0):
+                 n_layers=N_LAYER_COPIES, n_q=N_QUERY_SETS, page_size=0, dense=(0, 0)):
     dev = torch.device("cuda:0")
     x = si.make_inputs(w)
     layers, qs, shifts = setup(w, x, torch, dev, n_layers, n_q)
@@ -275,13 +275,18 @@ def run_workload(w, steps, warmup, torch, hs, si, with_cpu, cpu_budget,
     idx = torch.empty((w.B, w.Hkv, nqb, w.kb), dtype=torch.int32, device=dev)
     nnz = torch.empty((w.B, w.Hkv, nqb), dtype=torch.int32, device=dev)
     out = torch.empty_like(qs[0])
-    wsb = hs.hipsa_workspace_bytes(qs[0], x["K"], w.k, w.block_k, w.block_q, T=w.T)
+    sink, window = dense
+    wsb = hs.hipsa_workspace_bytes_ex(qs[0], x["K"], w.k, w.block_k, w.block_q, T=w.T, sink=sink,
+                                      window=window)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
     kw = dict(T=w.T, causal=bool(w.causal))
 
     def mask(j):
         q, L = qs[j % len(qs)], layers[j % len(layers)]
-        if page_size:
+        if sink or window:
+            hs.hip_mask_estimate_ex(q, L[0], w.k, w.block_k, w.block_q, T=w.T, causal=bool(w.causal),
+                                    sink=sink, window=window, indices=idx, nnz=nnz)
+        elif page_size:
             hs.hip_mask_estimate_paged(q, L[0], L[2], w.T, w.k, w.block_k, w.block_q, indices=idx,
                                        nnz=nnz, causal=bool(w.causal))
         else:
@@ -289,7 +294,11 @@ def run_workload(w, steps, warmup, torch, hs, si, with_cpu, cpu_budget,
 
     def attn(j):
         q, L = qs[j % len(qs)], layers[j % len(layers)]
-        if page_size:
+        if sink or window:
+            hs.hip_sparse_attn_ex(q, L[0], L[1], idx, nnz, w.k, w.block_k, w.block_q, T=w.T,
+                                  causal=bool(w.causal), sink=sink, window=window, out=out,
+                                  workspace=ws)
+        elif page_size:
             hs.hip_sparse_attn_paged(q, L[0], L[1], L[2], idx, nnz, w.T, w.k, w.block_k, w.block_q,
                                      causal=bool(w.causal), out=out, workspace=ws)
         else:
@@ -356,6 +365,9 @@ def main():
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 KV cache leg")
     ap.add_argument("--no-paged", action="store_true", help="skip the paged KV cache leg")
     ap.add_argument("--page-size", type=int, default=64, help="tokens per page of the paged leg")
+    ap.add_argument("--no-dense", action="store_true", help="skip the sink + window leg")
+    ap.add_argument("--sink", type=int, default=64, help="sink tokens of the dense-part leg")
+    ap.add_argument("--window", type=int, default=4096, help="window tokens of the dense-part leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
@@ -470,6 +482,15 @@ def main():
                             "us_per_step": round(rpg["ms_per_step"] * 1e3, 3),
                             "mask_us": round(rpg["ms_mask"] * 1e3, 3),
                             "attn_us": round(rpg["ms_attn"] * 1e3, 3)}
+    if headline and not args.no_dense:
+        # the same step with a dense part: sink and sliding-window blocks beside the search
+        rd = run_workload(w, args.steps, args.warmup, torch, hs, si, False, 0, args.layer_copies,
+                          args.query_sets, dense=(args.sink, args.window))
+        line["dense_part"] = {"sink": args.sink, "window": args.window,
+                              "keys_per_row": args.sink + args.window + w.k,
+                              "us_per_step": round(rd["ms_per_step"] * 1e3, 3),
+                              "mask_us": round(rd["ms_mask"] * 1e3, 3),
+                              "attn_us": round(rd["ms_attn"] * 1e3, 3)}
     if headline and not args.no_prefill:
         wp = si.workload("prefill_32k_chunk4k")
         rp = run_workload(wp, max(4, args.steps // 20), max(1, args.warmup // 10), torch, hs, si,

@@ -175,6 +175,44 @@ int hip_sparse_attn_paged(const hipsa_desc *desc, const hipsa_pages *pages, cons
                           const int32_t *nnz, int64_t k, int64_t block_k, int64_t block_q,
                           void *out, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Dense part and layout options (the *_ex calls).  HiP is served beside a
+ * sliding window of recent keys and a few always-attended first keys
+ * (PR page, the layer configuration's sliding_window_size and "streaming"
+ * backends; rebuttal page, reviewer T2wK, Q1: HiP retrieves long-range keys,
+ * the sliding window local ones).  With sink = S and window = W tokens, a
+ * query block that sees N_p key blocks always attends to the first
+ * S_b = S / block_k blocks and to the last W_b = W / block_k of its N_p
+ * blocks (fewer when N_p is small; the sink first).  hip_mask_estimate_ex
+ * searches only the blocks between them, so its lists hold searched blocks
+ * (nnz = min(K_b, N_p - S_b - W_b), the dense case when that is <= K_b).
+ * hip_sparse_attn_ex attends to the union of the dense blocks and the listed
+ * ones: a listed id inside the dense part adds nothing.
+ *   sink, window: multiples of block_k, >= 0, (sink + window) / block_k <= 256.
+ *   pages: a paged KV cache as in the *_paged calls, or NULL.
+ * With ext == NULL (or all fields zero) the *_ex calls are the plain calls.
+ * The decode workspace grows with the dense part: size it with
+ * hipsa_workspace_bytes_ex.
+ */
+typedef struct hipsa_ext {
+  const hipsa_pages *pages; /* paged KV cache, or NULL for the contiguous layout */
+  int64_t sink;             /* tokens 0 .. sink-1 attended by every row (0 = none)          */
+  int64_t window;           /* the last window/block_k visible blocks (0 = none)            */
+} hipsa_ext;
+
+int hip_mask_estimate_ex(const hipsa_desc *desc, const hipsa_ext *ext, const void *q,
+                         const void *K, int64_t k, int64_t block_k, int64_t block_q,
+                         int32_t *indices, int32_t *nnz, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+int hip_sparse_attn_ex(const hipsa_desc *desc, const hipsa_ext *ext, const void *q, const void *K,
+                       const void *V, const int32_t *indices, const int32_t *nnz, int64_t k,
+                       int64_t block_k, int64_t block_q, void *out, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+size_t hipsa_workspace_bytes_ex(const hipsa_desc *desc, const hipsa_ext *ext, int64_t k,
+                                int64_t block_k, int64_t block_q);
+
 /* Device workspace bytes that hip_sparse_attn (and hip_mask_estimate) need for
  * this shape (0 = none), or SIZE_MAX when the arguments are invalid (see
  * hipsa_last_error()).  Empty problems (B == 0 or Tq == 0) need none, and

@@ -12,6 +12,8 @@ Element types (q, K/V): (float32, float32), (bfloat16, bfloat16), or
 Paged KV cache (the *_paged calls): K, V [num_pages, Hkv, page_size, d] and
 block_table int32 [B, max_pages]; position t of sequence b is row
 t % page_size of page block_table[b, t // page_size].
+Dense part (the *_ex calls): `sink` first tokens and the last `window`
+tokens' blocks are attended by every row and left out of the search.
 """
 from __future__ import annotations
 
@@ -21,7 +23,8 @@ import os
 import torch  # loads the HIP runtime first, so libhipsa binds to the same one
 
 __all__ = ["hip_mask_estimate", "hip_sparse_attn", "hip_mask_estimate_paged",
-           "hip_sparse_attn_paged", "hipsa_workspace_bytes", "HipsaError", "LIB_PATH", "lib"]
+           "hip_sparse_attn_paged", "hip_mask_estimate_ex", "hip_sparse_attn_ex",
+           "hipsa_workspace_bytes", "hipsa_workspace_bytes_ex", "HipsaError", "LIB_PATH", "lib"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhipsa.so")
 if not os.path.exists(LIB_PATH):
@@ -44,6 +47,10 @@ class Pages(C.Structure):
                 ("num_pages", C.c_int64)]
 
 
+class Ext(C.Structure):
+    _fields_ = [("pages", C.POINTER(Pages)), ("sink", C.c_int64), ("window", C.c_int64)]
+
+
 _P, _I64, _SZ = C.c_void_p, C.c_int64, C.c_size_t
 lib.hip_mask_estimate.argtypes = [C.POINTER(Desc), _P, _P, _I64, _I64, _I64, _P, _P, _P, _SZ, _P]
 lib.hip_mask_estimate.restype = C.c_int
@@ -56,6 +63,14 @@ lib.hip_mask_estimate_paged.restype = C.c_int
 lib.hip_sparse_attn_paged.argtypes = [C.POINTER(Desc), C.POINTER(Pages), _P, _P, _P, _P, _P, _I64,
                                       _I64, _I64, _P, _P, _SZ, _P]
 lib.hip_sparse_attn_paged.restype = C.c_int
+lib.hip_mask_estimate_ex.argtypes = [C.POINTER(Desc), C.POINTER(Ext), _P, _P, _I64, _I64, _I64, _P,
+                                     _P, _P, _SZ, _P]
+lib.hip_mask_estimate_ex.restype = C.c_int
+lib.hip_sparse_attn_ex.argtypes = [C.POINTER(Desc), C.POINTER(Ext), _P, _P, _P, _P, _P, _I64, _I64,
+                                   _I64, _P, _P, _SZ, _P]
+lib.hip_sparse_attn_ex.restype = C.c_int
+lib.hipsa_workspace_bytes_ex.argtypes = [C.POINTER(Desc), C.POINTER(Ext), _I64, _I64, _I64]
+lib.hipsa_workspace_bytes_ex.restype = C.c_size_t
 lib.hipsa_workspace_bytes.argtypes = [C.POINTER(Desc), _I64, _I64, _I64]
 lib.hipsa_workspace_bytes.restype = C.c_size_t
 lib.hipsa_last_error.argtypes = []
@@ -234,4 +249,80 @@ def hip_sparse_attn_paged(q, K_pages, V_pages, block_table, indices, nnz, T: int
                                      _dev_ptr(indices, "indices"), _dev_ptr(nnz, "nnz"), k, block_k,
                                      block_q, _dev_ptr(out, "out"), ws_ptr, ws_len,
                                      _stream(q.device, stream)))
+    return out
+
+
+# ------------------------------------------------------------------ dense part and layout options
+
+def _ext_desc(q, K, T, causal, sink, window, block_table):
+    """(desc, ext, pages): the paged layout when block_table is given (T required)."""
+    if block_table is not None:
+        if T is None:
+            raise ValueError("T is required with a block_table")
+        desc, pages = _paged_desc(q, K, block_table, T, causal)
+        return desc, Ext(C.pointer(pages), sink, window), pages
+    return make_desc(q, K, T, causal), Ext(None, sink, window), None
+
+
+def hipsa_workspace_bytes_ex(q, K, k: int, block_k: int, block_q: int = 1, *, T=None, causal=True,
+                             sink=0, window=0, block_table=None) -> int:
+    desc, ext, _pages = _ext_desc(q, K, T, causal, sink, window, block_table)
+    n = lib.hipsa_workspace_bytes_ex(C.byref(desc), C.byref(ext), k, block_k, block_q)
+    if n == SIZE_MAX:
+        raise HipsaError(-2, lib.hipsa_last_error().decode())
+    return n
+
+
+def hip_mask_estimate_ex(q, K, k: int, block_k: int, block_q: int = 1, *, T=None, causal=True,
+                         sink=0, window=0, block_table=None, indices=None, nnz=None, stream=None):
+    """hip_mask_estimate with a dense part (sink, window tokens) and optionally a
+    paged KV cache (block_table).  Returns (indices, nnz) of the searched blocks."""
+    desc, ext, _pages = _ext_desc(q, K, T, causal, sink, window, block_table)
+    nqb = -(-desc.Tq // block_q)
+    kb = k // block_k if block_k > 0 else 0
+    if indices is None:
+        indices = torch.empty((desc.B, desc.Hkv, nqb, kb), dtype=torch.int32, device=q.device)
+    if nnz is None:
+        nnz = torch.empty((desc.B, desc.Hkv, nqb), dtype=torch.int32, device=q.device)
+    if tuple(indices.shape) != (desc.B, desc.Hkv, nqb, kb) or indices.dtype != torch.int32:
+        raise ValueError("indices must be int32 [B, Hkv, NQB, k/block_k]")
+    if tuple(nnz.shape) != (desc.B, desc.Hkv, nqb) or nnz.dtype != torch.int32:
+        raise ValueError("nnz must be int32 [B, Hkv, NQB]")
+    if desc.B * desc.Tq == 0:
+        return indices, nnz
+    _check(lib.hip_mask_estimate_ex(C.byref(desc), C.byref(ext), _dev_ptr(q, "q"), _dev_ptr(K, "K"),
+                                    k, block_k, block_q, _dev_ptr(indices, "indices"),
+                                    _dev_ptr(nnz, "nnz"), None, 0, _stream(q.device, stream)))
+    return indices, nnz
+
+
+def hip_sparse_attn_ex(q, K, V, indices, nnz, k: int, block_k: int, block_q: int = 1, *, T=None,
+                       causal=True, sink=0, window=0, block_table=None, out=None, workspace=None,
+                       stream=None):
+    """hip_sparse_attn over the dense part and the listed blocks, optionally on a
+    paged KV cache.  Returns out [B,Hq,Tq,d] in q's dtype."""
+    desc, ext, _pages = _ext_desc(q, K, T, causal, sink, window, block_table)
+    if K.dtype != V.dtype or V.shape != K.shape:
+        raise ValueError("V must have K's shape and dtype")
+    nqb = -(-desc.Tq // block_q)
+    kb = k // block_k if block_k > 0 else 0
+    if tuple(indices.shape) != (desc.B, desc.Hkv, nqb, kb) or indices.dtype != torch.int32:
+        raise ValueError("indices must be int32 [B, Hkv, NQB, k/block_k]")
+    if tuple(nnz.shape) != (desc.B, desc.Hkv, nqb) or nnz.dtype != torch.int32:
+        raise ValueError("nnz must be int32 [B, Hkv, NQB]")
+    if out is None:
+        out = torch.empty_like(q)
+    if desc.B * desc.Tq == 0:
+        return out
+    need = lib.hipsa_workspace_bytes_ex(C.byref(desc), C.byref(ext), k, block_k, block_q)
+    if need == SIZE_MAX:
+        raise HipsaError(-2, lib.hipsa_last_error().decode())
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.hip_sparse_attn_ex(C.byref(desc), C.byref(ext), _dev_ptr(q, "q"), _dev_ptr(K, "K"),
+                                  _dev_ptr(V, "V"), _dev_ptr(indices, "indices"),
+                                  _dev_ptr(nnz, "nnz"), k, block_k, block_q, _dev_ptr(out, "out"),
+                                  ws_ptr, ws_len, _stream(q.device, stream)))
     return out

@@ -5,6 +5,9 @@
 // Model Serving Framework With Hierarchically Pruned Attention", reviewer
 // NLBm, W2).  Exact softmax over the listed blocks' visible tokens.
 //
+// A row's key sequence is its dense part (sink and window blocks, if any)
+// followed by the listed blocks; entry_block() maps an entry to its block.
+//
 // Decode attention reads each selected K/V byte once (~4 flops per byte), so
 // it is bound by memory.  The K_b*block_k selected tokens of a problem are
 // split over S workgroups of TOK tokens (TOK chosen so the launch has >= 512
@@ -63,6 +66,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
   const int32_t *list = a.indices + (int64_t)prob * s.Kb;
   const int32_t cnt = min(max(a.nnz[prob], 0), s.Kb);
   const int base_blk = (int)split * (TOK >> s.bk_shift);
+  const Dense dn(s, Np);
 
   __shared__ float wm[4][GMAX], wl[4][GMAX];
   __shared__ float wo[4][GMAX][D];
@@ -80,9 +84,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
 #pragma unroll
   for (int u = 0; u < RPL; u++) {
     const int j = wave * TPW + u * RPW + rgl;
-    const int n = base_blk + (j >> s.bk_shift);
-    const int32_t blk = list[min(n, s.Kb - 1)];
-    const bool ok = n < cnt && blk >= 0 && blk < Np;
+    const int32_t blk = entry_block(base_blk + (j >> s.bk_shift), list, cnt, s, Np, dn);
+    const bool ok = blk >= 0;
     const int32_t t = ((ok ? blk : 0) << s.bk_shift) + (j & (s.bk - 1));
     tk[u] = (ok && t < Tp) ? t : -1;
     const int32_t ts = tk[u] >= 0 ? tk[u] : 0;
@@ -221,6 +224,7 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(AttnArgs a) {
   const int32_t *list = a.indices + (int64_t)prob * s.Kb;
   const int32_t cnt = min(max(a.nnz[prob], 0), s.Kb);
   const int base_blk = (int)split * (TOK >> s.bk_shift);
+  const Dense dn(s, Np);
 
   // probabilities, slot sl of head h at [h][(sl % RPV) * NV + sl / RPV]:
   // the NV slots of one row group are contiguous
@@ -247,9 +251,8 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(AttnArgs a) {
   int32_t tk_lane;
   {
     const int j = wave * TPW + lane % TPW;
-    const int n = base_blk + (j >> s.bk_shift);
-    const int32_t blk = list[min(n, s.Kb - 1)];
-    const bool ok = n < cnt && blk >= 0 && blk < Np;
+    const int32_t blk = entry_block(base_blk + (j >> s.bk_shift), list, cnt, s, Np, dn);
+    const bool ok = blk >= 0;
     const int32_t t = ((ok ? blk : 0) << s.bk_shift) + (j & (s.bk - 1));
     tk_lane = (ok && t < Tp) ? t : -1;
   }
@@ -450,7 +453,7 @@ constexpr int max_tokens() { return (std::is_same<E, float>::value && D == 128) 
 
 template <typename E, int D>
 int tokens_per_split(const Shape &s) {
-  const int64_t total = (int64_t)s.Kb * s.bk;
+  const int64_t total = entry_tokens(s);
   if (max_tokens<E, D>() >= 128 && s.G <= 8 && s.problems * ((total + 127) / 128) >= 512) return 128;
   return 64;
 }
@@ -497,7 +500,7 @@ hipError_t launch_d(const AttnArgs &a, hipStream_t st) {
 
 int32_t attn_decode_splits(const Shape &s) {
   const int tok = tokens_for(s);
-  return (int32_t)(((int64_t)s.Kb * s.bk + tok - 1) / tok);
+  return (int32_t)((entry_tokens(s) + tok - 1) / tok);
 }
 
 size_t attn_decode_workspace(const Shape &s) {

@@ -33,9 +33,10 @@
 //     each 16 lanes, lane i receives element i of the four 4-element row
 //     pieces the group addresses), so V needs no transposing stores;
 //   - the running output is rescaled only when some lane's running max moved.
-// With a paged KV cache the page of every listed block is read once, beside
-// the list itself, and the loader addresses rows through it (a page holds
-// whole key blocks).
+// The tiles walk a row's key sequence: its dense part (sink and window
+// blocks, if any) followed by the listed blocks (entry_block()).  With a
+// paged KV cache the page of every entry is read once, beside the list, and
+// the loader addresses rows through it (a page holds whole key blocks).
 // LDS rows are padded (K: D+8, V: D+32 elements) so that the operand reads
 // of a 256-byte LDS pass fall in distinct banks.
 #include "hipsa_internal.h"
@@ -140,23 +141,24 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnArgs a) {
   const int32_t Tp = s.causal ? pos0 + (r1 - r0) : (int32_t)s.T;
   const int32_t Np = (Tp + s.bk - 1) >> s.bk_shift;
   const int32_t cnt = min(max(a.nnz[prob], 0), s.Kb);
+  const Dense dn(s, Np);
+  const int nent = s.sink_b + s.window_b + cnt;  // entries of the key sequence
   const int bpt = KT >> s.bk_shift;  // key blocks per tile
-  const int ntiles = (cnt + bpt - 1) / bpt;
+  const int ntiles = (nent + bpt - 1) / bpt;
 
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * KPAD];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][KT * VPAD];
   __shared__ __attribute__((aligned(16))) int32_t tok[2][KT];
   __shared__ int32_t tmask[2];
   __shared__ int32_t lst[kMaxKb];
-  __shared__ int32_t lpg[PAGED ? kMaxKb : 1];  // paged: page of each listed block
+  __shared__ int32_t lpg[PAGED ? kMaxKb + kMaxDenseBlocks : 1];  // paged: page of each entry
 
   const int32_t *list = a.indices + (int64_t)prob * s.Kb;
-  for (int j = tid; j < cnt; j += 512) {
-    const int32_t blk = list[j];
-    lst[j] = blk;
-    if constexpr (PAGED) {
-      const bool okb = blk >= 0 && blk < Np;  // other ids are skipped: any page will do
-      lpg[j] = page_at(a.pg, b, ((okb ? blk : 0) << s.bk_shift) >> a.pg.ps_shift);
+  for (int j = tid; j < cnt; j += 512) lst[j] = list[j];
+  if constexpr (PAGED) {
+    for (int j = tid; j < nent; j += 512) {
+      const int32_t blk = entry_block(j, list, cnt, s, Np, dn);  // -1: skipped, any page will do
+      lpg[j] = page_at(a.pg, b, ((blk >= 0 ? blk : 0) << s.bk_shift) >> a.pg.ps_shift);
     }
   }
 
@@ -183,9 +185,8 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnArgs a) {
   // token of slot J of tile TL, or -1 (branch-free so the loads stay in flight)
 #define HIPSA_TOKEN(TL, J, OUT)                                              \
   do {                                                                       \
-    const int n_ = (TL) * bpt + ((J) >> s.bk_shift);                         \
-    const int32_t blk_ = lst[min(n_, cnt - 1)];                              \
-    const bool okb_ = n_ < cnt && blk_ >= 0 && blk_ < Np;                    \
+    const int32_t blk_ = entry_block((TL) * bpt + ((J) >> s.bk_shift), lst, cnt, s, Np, dn); \
+    const bool okb_ = blk_ >= 0;                                             \
     const int32_t t_ = ((okb_ ? blk_ : 0) << s.bk_shift) + ((J) & (s.bk - 1)); \
     OUT = (okb_ && t_ < Tp) ? t_ : -1;                                       \
   } while (0)
@@ -193,7 +194,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnArgs a) {
   auto row_of = [&](int tl, int j, int32_t t) -> int64_t {
     const int32_t ts = t >= 0 ? t : 0;
     if constexpr (PAGED) {
-      const int n = min(tl * bpt + (j >> s.bk_shift), cnt - 1);
+      const int n = min(tl * bpt + (j >> s.bk_shift), nent - 1);
       return paged_row(lpg[n], g, Hkv, ts, a.pg.ps_shift) * D;
     } else {
       return kvoff + (int64_t)ts * D;

@@ -83,6 +83,7 @@ int check_shape(const hipsa_desc *d, int64_t k, int64_t block_k, int64_t block_q
   s->dtype = d->dtype;
   s->nqb = (d->Tq + block_q - 1) / block_q;
   s->problems = d->B * d->Hkv * s->nqb;
+  s->sink_b = s->window_b = 0;
   // largest grid: decode attention launches problems x splits x G workgroups at most
   const int64_t splits = ((int64_t)s->Kb * s->bk + 63) / 64;
   if (s->problems * splits * s->G >= (int64_t(1) << 31))
@@ -136,6 +137,35 @@ int check_paged(const hipsa_desc *desc, const hipsa_pages *pg, int64_t k, int64_
   out->ps_shift = __builtin_ctzll((unsigned long long)pg->page_size);
   out->last_page = (int32_t)(pg->num_pages - 1);
   out->seq_pages = (int32_t)(need < INT32_MAX ? need : INT32_MAX);
+  return HIPSA_OK;
+}
+
+// The contiguous layout: no table (max_pages 0 marks "not paged").
+constexpr hipsa::Pages kContiguous{nullptr, 0, -1, 0, 0};
+
+// Checks of every call: the shape, the paged layout when ext->pages is set,
+// and the dense part (sink, window).
+int prepare(const hipsa_desc *desc, const hipsa_ext *ext, int64_t k, int64_t block_k,
+            int64_t block_q, bool mask, hipsa::Shape *s, hipsa::Pages *pg) {
+  int rc;
+  if (ext && ext->pages) {
+    rc = check_paged(desc, ext->pages, k, block_k, block_q, mask, s, pg);
+  } else {
+    rc = check_shape(desc, k, block_k, block_q, s);
+    *pg = kContiguous;
+  }
+  if (rc || !ext) return rc;
+  if (ext->sink < 0 || ext->window < 0 || ext->sink % block_k != 0 || ext->window % block_k != 0)
+    return fail(HIPSA_ERR_BLOCK, "sink=%lld and window=%lld must be non-negative multiples of "
+                "block_k=%lld", (long long)ext->sink, (long long)ext->window, (long long)block_k);
+  if ((ext->sink + ext->window) / block_k > hipsa::kMaxDenseBlocks)
+    return fail(HIPSA_ERR_BLOCK, "(sink + window) / block_k = %lld exceeds %d",
+                (long long)((ext->sink + ext->window) / block_k), hipsa::kMaxDenseBlocks);
+  s->sink_b = (int32_t)(ext->sink / block_k);
+  s->window_b = (int32_t)(ext->window / block_k);
+  // largest grid: decode attention launches problems x splits x G workgroups at most
+  if (s->problems * ((hipsa::entry_tokens(*s) + 63) / 64) * s->G >= (int64_t(1) << 31))
+    return fail(HIPSA_ERR_SHAPE, "too many problems (%lld) for one launch", (long long)s->problems);
   return HIPSA_OK;
 }
 
@@ -195,9 +225,6 @@ int attn_impl(const hipsa::Shape &s, const hipsa::Pages &pg, const void *q, cons
   return ok();
 }
 
-// The contiguous layout: no table (max_pages 0 marks "not paged").
-constexpr hipsa::Pages kContiguous{nullptr, 0, -1, 0, 0};
-
 }  // namespace
 
 extern "C" {
@@ -213,17 +240,27 @@ int hip_mask_estimate(const hipsa_desc *desc, const void *q, const void *K, int6
   return mask_impl(s, kContiguous, q, K, indices, nnz, stream);
 }
 
-int hip_mask_estimate_paged(const hipsa_desc *desc, const hipsa_pages *pages, const void *q,
-                            const void *K, int64_t k, int64_t block_k, int64_t block_q,
-                            int32_t *indices, int32_t *nnz, void *workspace,
-                            size_t workspace_bytes, void *stream) {
+int hip_mask_estimate_ex(const hipsa_desc *desc, const hipsa_ext *ext, const void *q,
+                         const void *K, int64_t k, int64_t block_k, int64_t block_q,
+                         int32_t *indices, int32_t *nnz, void *workspace, size_t workspace_bytes,
+                         void *stream) {
   (void)workspace;
   (void)workspace_bytes;
   hipsa::Shape s;
   hipsa::Pages pg;
-  int rc = check_paged(desc, pages, k, block_k, block_q, true, &s, &pg);
+  int rc = prepare(desc, ext, k, block_k, block_q, true, &s, &pg);
   if (rc) return rc;
   return mask_impl(s, pg, q, K, indices, nnz, stream);
+}
+
+int hip_mask_estimate_paged(const hipsa_desc *desc, const hipsa_pages *pages, const void *q,
+                            const void *K, int64_t k, int64_t block_k, int64_t block_q,
+                            int32_t *indices, int32_t *nnz, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+  if (!pages) return fail(HIPSA_ERR_NULL, "desc and pages must be non-NULL");
+  const hipsa_ext ext{pages, 0, 0};
+  return hip_mask_estimate_ex(desc, &ext, q, K, k, block_k, block_q, indices, nnz, workspace,
+                              workspace_bytes, stream);
 }
 
 int hip_sparse_attn(const hipsa_desc *desc, const void *q, const void *K, const void *V,
@@ -236,21 +273,37 @@ int hip_sparse_attn(const hipsa_desc *desc, const void *q, const void *K, const 
   return attn_impl(s, kContiguous, q, K, V, indices, nnz, out, workspace, workspace_bytes, stream);
 }
 
-int hip_sparse_attn_paged(const hipsa_desc *desc, const hipsa_pages *pages, const void *q,
-                          const void *K, const void *V, const int32_t *indices,
-                          const int32_t *nnz, int64_t k, int64_t block_k, int64_t block_q,
-                          void *out, void *workspace, size_t workspace_bytes, void *stream) {
+int hip_sparse_attn_ex(const hipsa_desc *desc, const hipsa_ext *ext, const void *q, const void *K,
+                       const void *V, const int32_t *indices, const int32_t *nnz, int64_t k,
+                       int64_t block_k, int64_t block_q, void *out, void *workspace,
+                       size_t workspace_bytes, void *stream) {
   hipsa::Shape s;
   hipsa::Pages pg;
-  int rc = check_paged(desc, pages, k, block_k, block_q, false, &s, &pg);
+  int rc = prepare(desc, ext, k, block_k, block_q, false, &s, &pg);
   if (rc) return rc;
   return attn_impl(s, pg, q, K, V, indices, nnz, out, workspace, workspace_bytes, stream);
 }
 
+int hip_sparse_attn_paged(const hipsa_desc *desc, const hipsa_pages *pages, const void *q,
+                          const void *K, const void *V, const int32_t *indices,
+                          const int32_t *nnz, int64_t k, int64_t block_k, int64_t block_q,
+                          void *out, void *workspace, size_t workspace_bytes, void *stream) {
+  if (!pages) return fail(HIPSA_ERR_NULL, "desc and pages must be non-NULL");
+  const hipsa_ext ext{pages, 0, 0};
+  return hip_sparse_attn_ex(desc, &ext, q, K, V, indices, nnz, k, block_k, block_q, out,
+                            workspace, workspace_bytes, stream);
+}
+
 size_t hipsa_workspace_bytes(const hipsa_desc *desc, int64_t k, int64_t block_k,
                              int64_t block_q) {
+  return hipsa_workspace_bytes_ex(desc, nullptr, k, block_k, block_q);
+}
+
+size_t hipsa_workspace_bytes_ex(const hipsa_desc *desc, const hipsa_ext *ext, int64_t k,
+                                int64_t block_k, int64_t block_q) {
   hipsa::Shape s;
-  if (check_shape(desc, k, block_k, block_q, &s)) return SIZE_MAX;
+  hipsa::Pages pg;
+  if (prepare(desc, ext, k, block_k, block_q, false, &s, &pg)) return SIZE_MAX;
   g_err.clear();
   return workspace_for(s);
 }

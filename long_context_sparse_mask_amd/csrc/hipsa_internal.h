@@ -10,6 +10,7 @@ namespace hipsa {
 
 constexpr int kMaxKb = 512;   // largest K_b = k / block_k the kernels accept
 constexpr int kMaxGroup = 16; // largest Hq / Hkv
+constexpr int kMaxDenseBlocks = 256;  // largest (sink + window) / block_k
 
 // Validated shape of one call, in the units the kernels use.
 struct Shape {
@@ -18,6 +19,7 @@ struct Shape {
   int32_t bk_shift;  // log2(bk)
   int64_t nqb;     // query blocks per (b, kv head)
   int64_t problems; // B * Hkv * nqb
+  int32_t sink_b, window_b;  // dense part, in blocks (0 = none)
 };
 
 // Paged K/V: K and V are [num_pages, Hkv, page_size, d] and key position t of
@@ -61,6 +63,38 @@ hipError_t launch_mask_prefill(const MaskArgs &a, hipStream_t st);
 hipError_t launch_attn_prefill(const AttnArgs &a, hipStream_t st);
 
 // ------------------------------------------------------------------ device helpers
+
+// Tokens in a row's key sequence: the dense entries and the list.
+inline int64_t entry_tokens(const Shape &s) {
+  return (int64_t)(s.Kb + s.sink_b + s.window_b) * s.bk;
+}
+
+// Dense part of a query block that sees Np key blocks: sink blocks [0, Sb)
+// and window blocks [Np - Wb, Np), the sink first when they overlap.  The
+// search covers the blocks between them.
+struct Dense {
+  int32_t Sb, Wb;
+  __device__ Dense(const Shape &s, int32_t Np) {
+    Sb = min(s.sink_b, Np);
+    Wb = min(s.window_b, Np - Sb);
+  }
+};
+
+// Block of entry n of a row's key sequence, or -1 if the entry holds none.
+// The sequence is the dense part, at fixed entries (sink: 0 .. sink_b-1,
+// window: sink_b .. sink_b+window_b-1, unused when the row sees fewer
+// blocks), then the list: an id past nnz (cnt), outside [0, Np) or inside
+// the dense part adds nothing.  Branch-free: the list entry is always read.
+__device__ inline int32_t entry_block(int n, const int32_t *list, int cnt, const Shape &s,
+                                      int32_t Np, const Dense &dn) {
+  const int nd = s.sink_b + s.window_b;
+  const int m = n - nd;
+  const int32_t lb = list[min(max(m, 0), s.Kb - 1)];
+  const int j = n - s.sink_b;
+  const int32_t db = n < s.sink_b ? (n < dn.Sb ? n : -1) : (j < dn.Wb ? Np - dn.Wb + j : -1);
+  const bool lok = m < cnt && lb >= dn.Sb && lb < Np - dn.Wb;
+  return m < 0 ? db : (lok ? lb : -1);
+}
 
 // Paged K/V addressing.  page_at() reads one table entry (clamped into the
 // pool, so a bad table cannot send a load out of bounds); paged_row() is the

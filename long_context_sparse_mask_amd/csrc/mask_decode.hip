@@ -56,9 +56,13 @@ __global__ __launch_bounds__(256) void mask_decode_kernel(MaskArgs a) {
   const int32_t Kb = s.Kb;
   int32_t *out = a.indices + (int64_t)prob * Kb;
 
-  if (Np <= Kb) {  // the row sees few enough blocks to keep them all
-    for (int j = tid; j < Kb; j += 256) out[j] = j < Np ? j : -1;
-    if (tid == 0) a.nnz[prob] = Np;
+  // the search covers the M blocks from `first` between the dense sink and
+  // window blocks (none of either by default)
+  const Dense dn(s, Np);
+  const int32_t first = dn.Sb, M = Np - dn.Sb - dn.Wb;
+  if (M <= Kb) {  // the row sees few enough blocks to keep them all
+    for (int j = tid; j < Kb; j += 256) out[j] = j < M ? first + j : -1;
+    if (tid == 0) a.nnz[prob] = M;
     return;
   }
 
@@ -104,9 +108,9 @@ __global__ __launch_bounds__(256) void mask_decode_kernel(MaskArgs a) {
   // paged: page numbers to LDS, issued after the query loads so that both
   // are in flight together (read after the first barrier)
   if constexpr (PAGED) stage_pages(a.pg, b, Tp, ptab);
-  initial_candidates(Np, Kb, cand_a[0], cand_e[0]);
+  initial_candidates(first, M, Kb, cand_a[0], cand_e[0]);
   if (tid < kSpan) key[n + tid] = 0;  // padding read by the rank batches
-  if (tid == 0) flag[0] = 1;          // N_p > K_b: the first round always runs
+  if (tid == 0) flag[0] = 1;          // M > K_b: the first round always runs
   __syncthreads();
 
   int cur = 0;
@@ -274,9 +278,11 @@ __global__ __launch_bounds__(256) void mask_decode_pipe(MaskArgs a) {
   const int32_t Kb = s.Kb;
   int32_t *out = a.indices + (int64_t)prob * Kb;
 
-  if (Np <= Kb) {
-    for (int j = tid; j < Kb; j += 256) out[j] = j < Np ? j : -1;
-    if (tid == 0) a.nnz[prob] = Np;
+  const Dense dn(s, Np);  // the search covers the M blocks from `first` between the dense parts
+  const int32_t first = dn.Sb, M = Np - dn.Sb - dn.Wb;
+  if (M <= Kb) {
+    for (int j = tid; j < Kb; j += 256) out[j] = j < M ? first + j : -1;
+    if (tid == 0) a.nnz[prob] = M;
     return;
   }
 
@@ -309,10 +315,10 @@ __global__ __launch_bounds__(256) void mask_decode_pipe(MaskArgs a) {
   // paged: page numbers to LDS, issued after the query loads so that both
   // are in flight together (read after the first barrier)
   if constexpr (PAGED) stage_pages(a.pg, b, Tp, ptab);
-  initial_candidates(Np, Kb, cand_a[0], cand_e[0]);
+  initial_candidates(first, M, Kb, cand_a[0], cand_e[0]);
   for (int c = tid; c < n; c += 256) srcs[0][c] = c;
   if (tid < kSpan) key[n + tid] = 0;
-  if (tid == 0) flag[0] = 1;  // N_p > K_b: the first round always runs
+  if (tid == 0) flag[0] = 1;  // M > K_b: the first round always runs
   __syncthreads();
   // keys of the first candidates (all waves), kept where round 0 looks them up
   score_children<KE, D, GMAX, TPW>(Kbase, row_of, qa, Tp, s.bk_shift, s.G, cand_a[0], cand_e[0], n, false,

@@ -47,9 +47,11 @@ __global__ __launch_bounds__(256) void mask_prefill_kernel(MaskArgs a) {
   const int32_t Kb = s.Kb;
   int32_t *out = a.indices + (int64_t)prob * Kb;
 
-  if (Np <= Kb) {
-    for (int j = tid; j < Kb; j += 256) out[j] = j < Np ? j : -1;
-    if (tid == 0) a.nnz[prob] = Np;
+  const Dense dn(s, Np);  // the search covers the M blocks from `first` between the dense parts
+  const int32_t first = dn.Sb, M = Np - dn.Sb - dn.Wb;
+  if (M <= Kb) {
+    for (int j = tid; j < Kb; j += 256) out[j] = j < M ? first + j : -1;
+    if (tid == 0) a.nnz[prob] = M;
     return;
   }
 
@@ -92,7 +94,7 @@ __global__ __launch_bounds__(256) void mask_prefill_kernel(MaskArgs a) {
   // paged: page numbers to LDS, issued after the query loads so that both
   // are in flight together (read after the first barrier)
   if constexpr (PAGED) stage_pages(a.pg, b, Tp, ptab);
-  initial_candidates(Np, Kb, cand_a[0], cand_e[0]);
+  initial_candidates(first, M, Kb, cand_a[0], cand_e[0]);
   for (int c = tid; c < n + kSpan; c += 256) key[0][c] = key[1][c] = 0;
   if (tid == 0) flag[0] = 1;
   __syncthreads();

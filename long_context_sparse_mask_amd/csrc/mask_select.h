@@ -89,10 +89,12 @@ __device__ inline void write_ascending(const int32_t *fin, int Kb, int32_t *out)
 }
 
 // Candidate slots 2c, 2c+1 from the halves of initial chunk c of the uniform
-// partition [floor(c*N_p/K_b), floor((c+1)*N_p/K_b)) (exact in double).
-__device__ inline void initial_candidates(int32_t Np, int Kb, int32_t *ca, int32_t *ce) {
+// partition of the M searched blocks from block `first`:
+// first + [floor(c*M/K_b), floor((c+1)*M/K_b)) (exact in double).
+__device__ inline void initial_candidates(int32_t first, int32_t M, int Kb, int32_t *ca, int32_t *ce) {
   for (int c = threadIdx.x; c < Kb; c += blockDim.x) {
-    const int32_t lo = (int32_t)((double)c * Np / Kb), hi = (int32_t)((double)(c + 1) * Np / Kb);
+    const int32_t lo = first + (int32_t)((double)c * M / Kb);
+    const int32_t hi = first + (int32_t)((double)(c + 1) * M / Kb);
     const bool split = hi - lo >= 2;
     const int32_t m = lo + (hi - lo) / 2;
     ca[2 * c] = lo;

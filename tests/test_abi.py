@@ -21,8 +21,9 @@ def _declared():
 
 def test_header_declares_the_boundary():
     assert _declared() == sorted(["hip_mask_estimate", "hip_sparse_attn", "hip_mask_estimate_paged",
-                                  "hip_sparse_attn_paged", "hipsa_workspace_bytes",
-                                  "hipsa_last_error"])
+                                  "hip_sparse_attn_paged", "hip_mask_estimate_ex",
+                                  "hip_sparse_attn_ex", "hipsa_workspace_bytes",
+                                  "hipsa_workspace_bytes_ex", "hipsa_last_error"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -195,6 +196,28 @@ def test_paged_calls_null_and_alignment():
     assert hs.lib.hip_sparse_attn_paged(C.byref(d2), C.byref(_pages(page_size=8, max_pages=20000)),
                                         FAKE, FAKE, FAKE, FAKE, FAKE, 256, 8, 1, FAKE, FAKE, 0,
                                         None) == ERR_WS
+
+
+def test_dense_part_validation_and_workspace():
+    """sink / window: non-negative multiples of block_k, at most 256 blocks
+    together; the decode workspace grows with the dense entries."""
+    import long_context_sparse_mask_amd as hs
+    d = _desc(B=4, T=131072, T_cap=131072)
+
+    def ws(sink, window, bk=64, k=2048):
+        return hs.lib.hipsa_workspace_bytes_ex(C.byref(d), C.byref(hs.Ext(None, sink, window)), k,
+                                               bk, 1)
+    plain = hs.lib.hipsa_workspace_bytes(C.byref(d), 2048, 64, 1)
+    assert ws(0, 0) == plain == 32 * 16 * 4 * 130 * 4
+    # 1 sink + 64 window + 32 listed blocks = 6208 tokens: 49 splits of 128 tokens
+    assert ws(64, 4096) == 32 * 49 * 4 * 130 * 4
+    for sink, window in ((-64, 0), (32, 0), (0, 100), (64 * 200, 64 * 57)):
+        assert ws(sink, window) == hs.SIZE_MAX
+    assert ws(64 * 200, 64 * 56) != hs.SIZE_MAX  # exactly 256 blocks
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 2048, 64, 1, FAKE, FAKE, 0, None]
+    assert hs.lib.hip_sparse_attn_ex(C.byref(d), C.byref(hs.Ext(None, 32, 0)), *args) == ERR_BLOCK
+    assert hs.lib.hip_mask_estimate_ex(C.byref(d), C.byref(hs.Ext(None, 0, 64 * 300)), FAKE, FAKE,
+                                       2048, 64, 1, FAKE, FAKE, None, 0, None) == ERR_BLOCK
 
 
 def test_paged_empty_problem_is_a_no_op():
