@@ -191,13 +191,11 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
 //     accumulators: lane l, register r -> head 4*(l/16) + r, slot 16u + l%16;
 //   * softmax statistics are taken in that layout (DPP within 16-lane rows)
 //     and the probabilities go to a per-wave LDS table;
-//   * P.V runs with lanes owning output dimensions: a lane loads 8
-//     consecutive elements of a V row (16 bytes of bf16, 8 of fp8), so one
-//     wave-wide load covers RPV = 4 rows (d = 128) or 8 (d = 64) and each
-//     row group of lanes takes every RPV-th slot.  A lane's probabilities are
-//     contiguous in the LDS table (vector reads), it accumulates its
-//     dimensions over its slots, and the row groups are summed once at the
-//     end with DPP / permlane steps.
+//   * P.V runs with lanes owning output dimensions: a lane loads EPL
+//     consecutive elements of a V row (4 bytes, or 2 for fp8 at d = 64), the
+//     probabilities are LDS broadcasts, and each lane accumulates its
+//     dimensions over every slot of the wave; when a row takes half a wave
+//     the two halves take alternate rows and are summed once at the end.
 // fp8 K rows are loaded as 8-byte slices and widened to bf16 operands in
 // registers (exact: every E5M2 value is a bf16 value).
 // Query loads are issued first: loads complete in order, so the first
@@ -208,11 +206,11 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(AttnArgs a) {
   constexpr int KS = D / 32;            // MFMA k-steps over the head dim
   constexpr int TPW = TOK / 4;          // token slots per wave
   constexpr int NT = TPW / 16;          // 16-slot tiles per wave
-  constexpr int VE = 8;                 // V elements per lane per load
-  constexpr int LPV = D / VE;           // lanes per V row (16 or 8)
-  constexpr int RPV = 64 / LPV;         // V rows per wave-wide load (4 or 8)
+  constexpr int EPL = (sizeof(KE) == 1 && D == 128) ? 4 : 2;  // V elements per lane
+  constexpr int LPV = D / EPL < 64 ? D / EPL : 64;  // lanes per V row
+  constexpr int RPV = 64 / LPV;         // V rows per wave-wide load
   constexpr int NV = TPW / RPV;         // V loads per lane
-  static_assert(NT >= 1 && TPW % RPV == 0 && NV >= 1, "split too small");
+  static_assert(NT >= 1 && TPW % RPV == 0 && RPV <= 2, "split too small");
   const Shape &s = a.s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t S = (uint32_t)a.splits;
@@ -226,8 +224,6 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(AttnArgs a) {
   const int base_blk = (int)split * (TOK >> s.bk_shift);
   const Dense dn(s, Np);
 
-  // probabilities, slot sl of head h at [h][(sl % RPV) * NV + sl / RPV]:
-  // the NV slots of one row group are contiguous
   __shared__ __align__(16) float pw[4][GMAX][TPW];
   __shared__ float wm[4][GMAX], wl[4][GMAX];
   __shared__ __align__(16) float wo[4][GMAX][D];
@@ -279,14 +275,15 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(AttnArgs a) {
     for (int ks = 0; ks < KS; ks++)
       kr[u][ks] = Kv8<KE>::raw(Kp + krow + 32 * ks + 8 * (lane >> 4));
   }
-  const int rg = lane / LPV;  // row group: this lane takes slots RPV * v + rg
   int32_t vt[NV];
-  typename Kv8f<KE>::raw_t vr[NV];
+  typename KvN<KE, EPL>::raw_t vr[NV];
 #pragma unroll
   for (int v = 0; v < NV; v++) {
-    vt[v] = __shfl(tk_lane, RPV * v + rg, 64);
-    const int32_t vpg = PAGED ? __shfl(pg_lane, RPV * v + rg, 64) : 0;
-    vr[v] = Kv8f<KE>::raw(Vp + row_of(vt[v] >= 0 ? vt[v] : 0, vpg) + VE * (lane % LPV));
+    vt[v] = RPV == 1 ? __builtin_amdgcn_readlane(tk_lane, v) : __shfl(tk_lane, RPV * v + lane / LPV, 64);
+    int32_t vpg = 0;
+    if constexpr (PAGED)
+      vpg = RPV == 1 ? __builtin_amdgcn_readlane(pg_lane, v) : __shfl(pg_lane, RPV * v + lane / LPV, 64);
+    vr[v] = KvN<KE, EPL>::raw(Vp + row_of(vt[v] >= 0 ? vt[v] : 0, vpg) + EPL * (lane % LPV));
   }
 
   // logits on the matrix cores, softmax statistics per head in the
@@ -318,8 +315,7 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(AttnArgs a) {
     for (int u = 0; u < NT; u++) {
       const float e = sc[u] == -INFINITY ? 0.f : __expf(sc[u] - m);
       l += e;
-      const int sl = 16 * u + (lane & 15);
-      if (h < GMAX) pw[wave][h][(sl % RPV) * NV + sl / RPV] = e;
+      if (h < GMAX) pw[wave][h][16 * u + (lane & 15)] = e;
     }
     l = group_sum<16>(l);
     if ((lane & 15) == 0 && h < s.G) { wm[wave][h] = m; wl[wave][h] = l; }
@@ -328,55 +324,52 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(AttnArgs a) {
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // P.V: lane owns dimensions VE*(lane % LPV) .. +VE-1 of its row group's
-  // slots; probabilities read up to 4 slots at a time.  Every one of the
-  // GMAX heads is computed (heads past the group have finite probabilities
-  // and are never stored): a per-head test inside this loop would become a
-  // select on every accumulator update.
-  constexpr int C = NV < 4 ? NV : 4;  // slots per probability read
-  float o[GMAX][VE];
+  // P.V: lane owns dimensions EPL*(lane % LPV) .. +EPL-1 over the wave's
+  // slots; probabilities read 4 slots at a time (an LDS broadcast)
+  constexpr int VPG = 4 / RPV;  // V loads per group of 4 slots
+  const int half = lane / LPV;  // RPV = 2: which of the two rows of a load
+  float o[GMAX][EPL];
 #pragma unroll
   for (int h = 0; h < GMAX; h++)
 #pragma unroll
-    for (int e = 0; e < VE; e++) o[h][e] = 0.f;
+    for (int e = 0; e < EPL; e++) o[h][e] = 0.f;
 #pragma unroll
-  for (int v0 = 0; v0 < NV; v0 += C) {
-    float pv[GMAX][C];
+  for (int g4 = 0; g4 < TPW / 4; g4++) {
+    // every one of the GMAX heads is computed (heads past the group have
+    // finite probabilities and are never stored): a per-head test inside
+    // this loop would become a select on every accumulator update
+    float4 p4[GMAX];
 #pragma unroll
-    for (int h = 0; h < GMAX; h++) {
-      const float *src = &pw[wave][h][rg * NV + v0];
-      if constexpr (C == 4) {
-        const float4 t = *reinterpret_cast<const float4 *>(src);
-        pv[h][0] = t.x; pv[h][1] = t.y; pv[h][2] = t.z; pv[h][3] = t.w;
-      } else if constexpr (C == 2) {
-        const float2 t = *reinterpret_cast<const float2 *>(src);
-        pv[h][0] = t.x; pv[h][1] = t.y;
-      } else {
-        pv[h][0] = *src;
+    for (int h = 0; h < GMAX; h++) p4[h] = *reinterpret_cast<const float4 *>(&pw[wave][h][4 * g4]);
+#pragma unroll
+    for (int vv = 0; vv < VPG; vv++) {
+      const int v = g4 * VPG + vv;
+      float vx[EPL];
+      KvN<KE, EPL>::widen(vr[v], vt[v] >= 0, vx);
+#pragma unroll
+      for (int h = 0; h < GMAX; h++) {
+        float pj;
+        if (RPV == 1) pj = vv == 0 ? p4[h].x : vv == 1 ? p4[h].y : vv == 2 ? p4[h].z : p4[h].w;
+        else pj = vv == 0 ? (half ? p4[h].y : p4[h].x) : (half ? p4[h].w : p4[h].z);
+#pragma unroll
+        for (int e = 0; e < EPL; e++) o[h][e] = fmaf(pj, vx[e], o[h][e]);
       }
     }
-#pragma unroll
-    for (int c = 0; c < C; c++) {
-      float vx[VE];
-      Kv8f<KE>::widen(vr[v0 + c], vt[v0 + c] >= 0, vx);
-#pragma unroll
-      for (int h = 0; h < GMAX; h++)
-#pragma unroll
-        for (int e = 0; e < VE; e++) o[h][e] = fmaf(pv[h][c], vx[e], o[h][e]);
-    }
   }
-  // sum over the row groups (lanes that share lane % LPV)
+  if (RPV == 2) {  // the two halves of the wave took alternate rows
 #pragma unroll
-  for (int h = 0; h < GMAX; h++)
+    for (int h = 0; h < GMAX; h++)
 #pragma unroll
-    for (int e = 0; e < VE; e++) o[h][e] = across_sum<LPV>(o[h][e]);
+      for (int e = 0; e < EPL; e++) o[h][e] = xor32_sum(o[h][e]);
+  }
   if (lane < LPV) {
 #pragma unroll
     for (int h = 0; h < GMAX; h++) {
       if (h >= s.G) continue;
-      float *dst = &wo[wave][h][VE * lane];
-      *reinterpret_cast<float4 *>(dst) = make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
-      *reinterpret_cast<float4 *>(dst + 4) = make_float4(o[h][4], o[h][5], o[h][6], o[h][7]);
+      if constexpr (EPL == 4)
+        *reinterpret_cast<float4 *>(&wo[wave][h][4 * lane]) = make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
+      else
+        *reinterpret_cast<float2 *>(&wo[wave][h][2 * lane]) = make_float2(o[h][0], o[h][1]);
     }
   }
   __syncthreads();

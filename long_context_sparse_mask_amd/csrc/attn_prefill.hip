@@ -17,8 +17,9 @@
 // and measured slower.)  Per tile of 64 keys:
 //   - the workgroup stages K and V row-major in a double-buffered LDS slot
 //     (16-byte stores of bf16; fp8 slices are loaded as 8 bytes and widened
-//     exactly to bf16 on the way in); the global loads of the next tile are
-//     issued before this tile's math, and one barrier per tile suffices;
+//     exactly to bf16 on the way in); the global loads run two tiles ahead
+//     (two register sets), so a tile's rows have a whole tile of math to
+//     arrive before they are stored to LDS, and one barrier per tile suffices;
 //   - each wave forms S^T = K . Q^T (keys down the rows, its 32 queries
 //     across the columns), so a query's 64 scores sit in one lane pair and
 //     the online-softmax max and sum need one cross-half exchange; the two
@@ -178,9 +179,9 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnArgs a) {
   }
   __syncthreads();  // lst ready
 
-  // loader state: this lane's K and V rows of the tile in flight
-  typename Kv8<KE>::raw_t kreg[KP], vreg[KP];
-  int32_t vtok = -1;
+  // loader state: this lane's K and V rows of two tiles in flight (sets 0, 1)
+  typename Kv8<KE>::raw_t kreg0[KP], vreg0[KP], kreg1[KP], vreg1[KP];
+  int32_t vtok0 = -1, vtok1 = -1;
   const int krow0 = tid / TPR, kcol = (tid % TPR) * 8;
   // token of slot J of tile TL, or -1 (branch-free so the loads stay in flight)
 #define HIPSA_TOKEN(TL, J, OUT)                                              \
@@ -200,24 +201,25 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnArgs a) {
       return kvoff + (int64_t)ts * D;
     }
   };
-#define HIPSA_GLOAD(TL)                                                                        \
+#define HIPSA_GLOAD(TL, KREG, VREG, VTOK)                                                      \
   do {                                                                                         \
     _Pragma("unroll") for (int u = 0; u < KP; u++) {                                           \
       int32_t t;                                                                               \
       HIPSA_TOKEN(TL, u * RPP + krow0, t);                                                     \
       const int64_t off_ = row_of(TL, u * RPP + krow0, t) + kcol;                              \
-      kreg[u] = Kv8<KE>::raw(Kg + off_);                                                       \
-      vreg[u] = Kv8<KE>::raw(Vg + off_);                                                       \
+      KREG[u] = Kv8<KE>::raw(Kg + off_);                                                       \
+      VREG[u] = Kv8<KE>::raw(Vg + off_);                                                       \
     }                                                                                          \
-    HIPSA_TOKEN(TL, lane, vtok);                                                               \
+    HIPSA_TOKEN(TL, lane, VTOK);                                                               \
   } while (0)
-#define HIPSA_LSTORE(BUF)                                                                      \
+#define HIPSA_LSTORE(BUF, KREG, VREG, VTOK)                                                    \
   do {                                                                                         \
     _Pragma("unroll") for (int u = 0; u < KP; u++) {                                           \
-      *reinterpret_cast<uint4 *>(&Ks[BUF][(u * RPP + krow0) * KPAD + kcol]) = Kv8<KE>::bf16(kreg[u]); \
-      *reinterpret_cast<uint4 *>(&Vs[BUF][(u * RPP + krow0) * VPAD + kcol]) = Kv8<KE>::bf16(vreg[u]); \
+      *reinterpret_cast<uint4 *>(&Ks[BUF][(u * RPP + krow0) * KPAD + kcol]) = Kv8<KE>::bf16(KREG[u]); \
+      *reinterpret_cast<uint4 *>(&Vs[BUF][(u * RPP + krow0) * VPAD + kcol]) = Kv8<KE>::bf16(VREG[u]); \
     }                                                                                          \
     if (wave == 0) {                                                                           \
+      const int32_t vtok = VTOK;                                                               \
       tok[BUF][lane] = vtok;                                                                   \
       const bool bad_ = vtok < 0 || (s.causal && vtok > pos0);                                 \
       const uint64_t any_ = __builtin_amdgcn_ballot_w64(bad_);                                 \
@@ -234,17 +236,8 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnArgs a) {
   const bool qvalid = r0 + qq < r1;
   const int32_t qpos = pos0 + qq;
 
-  if (ntiles > 0) {
-    HIPSA_GLOAD(0);
-    HIPSA_LSTORE(0);
-  }
-  __syncthreads();
-
-  for (int tl = 0; tl < ntiles; tl++) {
-    const int buf = tl & 1;
-    // next tile's loads (the last iteration reloads a valid tile it never uses,
-    // which keeps this code free of branches)
-    HIPSA_GLOAD(min(tl + 1, ntiles - 1));
+  // the math of one tile, held in LDS slot BUF_
+  auto tile = [&](const int BUF_) {
     if (active) {
       // S^T: keys kt*32 + 8*(r/4) + 4*half + r%4, queries qt*32 + col; the two
       // key halves are independent accumulation chains, interleaved
@@ -253,12 +246,12 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnArgs a) {
       for (int ks = 0; ks < KS; ks++) {
 #pragma unroll
         for (int kt = 0; kt < 2; kt++) {
-          const uint4 kf = *reinterpret_cast<const uint4 *>(&Ks[buf][(kt * 32 + col) * KPAD + 16 * ks + 8 * half]);
+          const uint4 kf = *reinterpret_cast<const uint4 *>(&Ks[BUF_][(kt * 32 + col) * KPAD + 16 * ks + 8 * half]);
           sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[ks]), sacc[kt], 0, 0, 0);
         }
       }
       bf16x8_t pf[4];
-      online_softmax<DT>(sacc, tmask[buf] != 0, tok[buf], qvalid, qpos, s.causal != 0, half, sl2, m, l, o, pf);
+      online_softmax<DT>(sacc, tmask[BUF_] != 0, tok[BUF_], qvalid, qpos, s.causal != 0, half, sl2, m, l, o, pf);
       // O^T += V^T . P^T over 4 k-steps of 16 keys.  Lane l (group g = l/16,
       // L = l%16) names V row 16ks + 4*(g/2) + L/4 (+8 for the upper half of
       // the fragment), columns dt*32 + 16*(g%2) + 4*(L%4) .. +3, and receives
@@ -268,14 +261,36 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnArgs a) {
       for (int ks = 0; ks < 4; ks++)
 #pragma unroll
         for (int dt = 0; dt < DT; dt++) {
-          const uint16_t *vp = &Vs[buf][(16 * ks + 4 * (vg >> 1) + (vl >> 2)) * VPAD + dt * 32 + 16 * (vg & 1) + 4 * (vl & 3)];
+          const uint16_t *vp = &Vs[BUF_][(16 * ks + 4 * (vg >> 1) + (vl >> 2)) * VPAD + dt * 32 + 16 * (vg & 1) + 4 * (vl & 3)];
           const uint2 lo = lds_read_tr16(vp);
           const uint2 hi = lds_read_tr16(vp + 8 * VPAD);
           o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)),
                                                           pf[ks], o[dt], 0, 0, 0);
         }
     }
-    HIPSA_LSTORE(buf ^ 1);
+  };
+
+  const int last = ntiles - 1;
+  if (ntiles > 0) {
+    HIPSA_GLOAD(0, kreg0, vreg0, vtok0);
+    HIPSA_LSTORE(0, kreg0, vreg0, vtok0);
+    HIPSA_GLOAD(min(1, last), kreg1, vreg1, vtok1);
+  }
+  __syncthreads();
+
+  // tile tl sits in LDS slot tl & 1; register set (tl + 1) & 1 holds tile
+  // tl + 1 (in flight since the previous tile), and set tl & 1, free again,
+  // takes tile tl + 2.  Tiles past the last reload the last one, unused,
+  // which keeps this code free of branches.
+  for (int tl = 0; tl < ntiles; tl += 2) {
+    HIPSA_GLOAD(min(tl + 2, last), kreg0, vreg0, vtok0);
+    tile(0);
+    HIPSA_LSTORE(1, kreg1, vreg1, vtok1);
+    __syncthreads();
+    if (tl + 1 >= ntiles) break;  // uniform
+    HIPSA_GLOAD(min(tl + 3, last), kreg1, vreg1, vtok1);
+    tile(1);
+    HIPSA_LSTORE(0, kreg0, vreg0, vtok0);
     __syncthreads();
   }
 #undef HIPSA_LSTORE

@@ -108,15 +108,16 @@ __device__ inline int64_t paged_row(int32_t page, uint32_t g, uint32_t Hkv, int3
 }
 // The mask kernels stage the pages of positions 0 .. Tp-1 of sequence b in
 // LDS once (every round then finds a centre row without another memory trip).
-// Each thread issues a batch of 16 loads (addresses clamped, no branches)
-// before storing any, so a batch costs one memory latency, not 16.  The
-// first batch (16 x blockDim pages) is straight-line code: at the head of a
-// loop the compiler waits for every load in flight, the caller's too.
+// Called by the 256 threads of a mask workgroup.  Each thread issues a batch
+// of 16 loads (addresses clamped, no branches) before storing any, so a batch
+// costs one memory latency, not 16.  The first batch (4096 pages) is
+// straight-line code: at the head of a loop the compiler waits for every load
+// in flight, the caller's too.
 __device__ inline void stage_pages(const Pages &pg, uint32_t b, int32_t Tp, int32_t *ptab) {
   constexpr int U = 16;
   const int32_t n = ((Tp - 1) >> pg.ps_shift) + 1;
   const int32_t *row = pg.table + (int64_t)b * pg.max_pages;
-  const int32_t stride = (int32_t)blockDim.x;
+  constexpr int32_t stride = 256;
   auto batch = [&](int32_t j0) {
     int32_t v[U];
 #pragma unroll
@@ -239,33 +240,6 @@ template <> struct KvN<uint8_t, 4> {
     v[1] = a.y;
     v[2] = b.x;
     v[3] = b.y;
-  }
-};
-
-// Eight consecutive elements of a V row (16 bytes of bf16 or 8 bytes of E5M2
-// codes) widened to fp32; a load that is not kept reads as zeros.
-template <typename KE> struct Kv8f;
-template <> struct Kv8f<uint16_t> {
-  using raw_t = uint4;
-  __device__ static inline raw_t raw(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
-  __device__ static inline void widen(raw_t r, bool keep, float (&v)[8]) {
-    const uint32_t w[4] = {keep ? r.x : 0u, keep ? r.y : 0u, keep ? r.z : 0u, keep ? r.w : 0u};
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      v[2 * i] = __uint_as_float(w[i] << 16);
-      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-    }
-  }
-};
-template <> struct Kv8f<uint8_t> {
-  using raw_t = uint2;
-  __device__ static inline raw_t raw(const uint8_t *p) { return *reinterpret_cast<const uint2 *>(p); }
-  __device__ static inline void widen(raw_t r, bool keep, float (&v)[8]) {
-    const uint32_t x = keep ? r.x : 0u, y = keep ? r.y : 0u;
-    const f32x2_t a = e5m2x2_to_f32x2<false>(x), b = e5m2x2_to_f32x2<true>(x);
-    const f32x2_t c = e5m2x2_to_f32x2<false>(y), d = e5m2x2_to_f32x2<true>(y);
-    v[0] = a.x; v[1] = a.y; v[2] = b.x; v[3] = b.y;
-    v[4] = c.x; v[5] = c.y; v[6] = d.x; v[7] = d.y;
   }
 };
 

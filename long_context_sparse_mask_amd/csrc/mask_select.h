@@ -74,7 +74,7 @@ __device__ inline void select_top(const int32_t *ca, const int32_t *ce, const ui
 // The K_b kept one-block chunks sit at the even slots of `fin`; writes their
 // block ids to out[0..K_b) in ascending order.
 __device__ inline void write_ascending(const int32_t *fin, int Kb, int32_t *out) {
-  for (int c = threadIdx.x; c < Kb; c += blockDim.x) {
+  for (int c = threadIdx.x; c < Kb; c += 256) {
     const int32_t v = fin[2 * c];
     int r = 0;
     for (int j0 = 0; j0 < Kb; j0 += kSpan) {
@@ -92,7 +92,7 @@ __device__ inline void write_ascending(const int32_t *fin, int Kb, int32_t *out)
 // partition of the M searched blocks from block `first`:
 // first + [floor(c*M/K_b), floor((c+1)*M/K_b)) (exact in double).
 __device__ inline void initial_candidates(int32_t first, int32_t M, int Kb, int32_t *ca, int32_t *ce) {
-  for (int c = threadIdx.x; c < Kb; c += blockDim.x) {
+  for (int c = threadIdx.x; c < Kb; c += 256) {
     const int32_t lo = first + (int32_t)((double)c * M / Kb);
     const int32_t hi = first + (int32_t)((double)(c + 1) * M / Kb);
     const bool split = hi - lo >= 2;
