@@ -395,7 +395,9 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(AttnArgs a) {
 }
 
 // Merge the S partials of one (problem, query head): one workgroup of D lanes,
-// every load of a batch issued before any is used.
+// every load of a batch issued before any is used.  Per batch of CH partials
+// the maximum is a tree and the weights are independent exponentials, so the
+// dependent chain is one step per batch rather than one per partial.
 template <typename E, int D>
 __global__ __launch_bounds__(128) void attn_decode_combine(AttnArgs a) {
   constexpr int CH = 16;  // partials in flight per lane
@@ -416,20 +418,30 @@ __global__ __launch_bounds__(128) void attn_decode_combine(AttnArgs a) {
 #pragma unroll
     for (int u = 0; u < CH; u++) {
       const int sp = min(s0 + u, S - 1);
-      mm[u] = ph_[sp * sstride];
+      mm[u] = s0 + u < S ? ph_[sp * sstride] : -INFINITY;
       ll[u] = ph_[sp * sstride + 1];
       oo[u] = ph_[sp * sstride + 2 + x];
     }
+    // batch max as a tree, then independent weights
+    float bm[CH];
+#pragma unroll
+    for (int u = 0; u < CH; u++) bm[u] = mm[u];
+#pragma unroll
+    for (int w = CH / 2; w >= 1; w /= 2)
+#pragma unroll
+      for (int u = 0; u < w; u++) bm[u] = fmaxf(bm[u], bm[u + w]);
+    const float Mn = fmaxf(M, bm[0]);
+    const float c0 = M == -INFINITY ? 0.f : __expf(M - Mn);
+    float Lb = 0.f, Ab = 0.f;
 #pragma unroll
     for (int u = 0; u < CH; u++) {
-      const float mu = s0 + u < S ? mm[u] : -INFINITY;
-      const float Mn = fmaxf(M, mu);
-      const float c0 = M == -INFINITY ? 0.f : __expf(M - Mn);
-      const float c1 = mu == -INFINITY ? 0.f : __expf(mu - Mn);
-      L = L * c0 + ll[u] * c1;
-      acc = acc * c0 + oo[u] * c1;
-      M = Mn;
+      const float c = mm[u] == -INFINITY ? 0.f : __expf(mm[u] - Mn);
+      Lb = fmaf(c, ll[u], Lb);
+      Ab = fmaf(c, oo[u], Ab);
     }
+    L = fmaf(L, c0, Lb);
+    acc = fmaf(acc, c0, Ab);
+    M = Mn;
   }
   const float v = L > 0.f ? acc / L : 0.f;
   E *out = reinterpret_cast<E *>(a.out) + ((int64_t)(b * s.Hq + g * s.G + h) * Tq + i) * D;
