@@ -118,6 +118,7 @@ __global__ __launch_bounds__(256) void mask_decode_kernel(MaskArgs a) {
     if (!flag[round & 1]) break;  // uniform: read after a barrier
     if (tid == 0) flag[(round + 1) & 1] = 0;  // its last readers are two barriers back
     const int32_t *ca = cand_a[cur], *ce = cand_e[cur];
+    for (int c = tid; c < n; c += 256) rk[c] = 0;  // rank counts of this round
 
     // ---- 1. scoring
     if constexpr (kMfma) {

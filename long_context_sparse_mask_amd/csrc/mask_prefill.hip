@@ -106,6 +106,7 @@ __global__ __launch_bounds__(256) void mask_prefill_kernel(MaskArgs a) {
     const int32_t *ca = cand_a[cur], *ce = cand_e[cur];
     uint64_t *kcur = key[cur];
     for (int c = tid; c < n + kSpan; c += 256) key[cur ^ 1][c] = 0;  // read last round; free now
+    for (int c = tid; c < n; c += 256) rk[c] = 0;                     // rank counts of this round
 
     // ---- 1. scoring, 64 candidates at a time: the workgroup loads their
     // centre rows once (whole rows, D/8 lanes each) into LDS, then every wave
@@ -138,21 +139,44 @@ __global__ __launch_bounds__(256) void mask_prefill_kernel(MaskArgs a) {
           const bool live = c < n && lo_b >= 0;
           const int32_t lo = lo_b << s.bk_shift, hi = min(hi_b << s.bk_shift, Tp);
           const int32_t t = live ? (lo + hi) >> 1 : 0;
+          // the tile's B operands are read from LDS together (one latency), and
+          // the two row tiles are independent accumulation chains, interleaved
+          uint4 kb[KS];
+#pragma unroll
+          for (int ks = 0; ks < KS; ks++)
+            kb[ks] = *reinterpret_cast<const uint4 *>(&cst[(32 * u + col) * CRS + 16 * ks + 8 * half]);
+          f32x16_t acc[2] = {f32x16_t{}, f32x16_t{}};
+#pragma unroll
+          for (int ks = 0; ks < KS; ks++)
+#pragma unroll
+            for (int rt = 0; rt < 2; rt++)
+              acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa[rt][ks]), as_bf16x8(kb[ks]), acc[rt], 0, 0, 0);
+          // acc[rt][r]: row rt*32 + 8*(r/4) + 4*half + r%4, candidate column col.
+          // When every lane's centre is at or before the block's first row and
+          // the block is full, every row votes (the common case: only chunks
+          // near the diagonal need the per-row test).
           float best = -INFINITY;
+          const bool all_vote = r1 - r0 == BQ && (!s.causal || t <= pos0);
+          if (__builtin_amdgcn_ballot_w64(!all_vote) == 0) {  // uniform
+            float mx[4];
 #pragma unroll
-          for (int rt = 0; rt < 2; rt++) {
-            f32x16_t acc = {};
+            for (int j = 0; j < 4; j++)
+              mx[j] = fmaxf(fmaxf(acc[j >> 1][8 * (j & 1)], acc[j >> 1][8 * (j & 1) + 1]),
+                            fmaxf(acc[j >> 1][8 * (j & 1) + 2], acc[j >> 1][8 * (j & 1) + 3]));
 #pragma unroll
-            for (int ks = 0; ks < KS; ks++) {
-              const uint4 kb = *reinterpret_cast<const uint4 *>(&cst[(32 * u + col) * CRS + 16 * ks + 8 * half]);
-              acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa[rt][ks]), as_bf16x8(kb), acc, 0, 0, 0);
-            }
-            // acc[r]: row rt*32 + 8*(r/4) + 4*half + r%4, candidate column col
+            for (int r = 4; r < 8; r++)
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-              const int ri = rt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-              const bool votes = r0 + ri < r1 && (!s.causal || pos0 + ri >= t);
-              best = votes ? fmaxf(best, acc[r]) : best;
+              for (int j = 0; j < 4; j++) mx[j] = fmaxf(mx[j], acc[j >> 1][8 * (j & 1) + r]);
+            best = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
+          } else {
+#pragma unroll
+            for (int rt = 0; rt < 2; rt++) {
+#pragma unroll
+              for (int r = 0; r < 16; r++) {
+                const int ri = rt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                const bool votes = r0 + ri < r1 && (!s.causal || pos0 + ri >= t);
+                best = votes ? fmaxf(best, acc[rt][r]) : best;
+              }
             }
           }
           best = xor32_max(best);

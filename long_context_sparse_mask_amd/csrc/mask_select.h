@@ -21,13 +21,30 @@ constexpr int kSpan = 16;  // keys compared per batch of LDS reads
 // the K_b best into buffer (na, ne) at slots 2*rank and 2*rank+1 (a one-block
 // chunk is copied to 2*rank with an empty slot after it).  Sets *more when a
 // kept chunk still spans several blocks.  `key` must hold n valid entries
-// followed by kSpan zeros; `rk` is n ints of scratch (used when n > 256).
-// Called by all 256 threads; contains barriers only when n > 256.
+// followed by kSpan zeros; `rk` must hold n zeros on entry (the caller clears
+// it before the barrier that ends scoring).  A candidate's rank is the number
+// of keys above its own: all 256 threads share the comparisons, thread t
+// counting for candidate t % n over the kSpan keys of batch t / n, and the
+// counts meet in `rk`.  Called by all 256 threads; contains one barrier.
 __device__ inline void select_top(const int32_t *ca, const int32_t *ce, const uint64_t *key,
                                   int32_t *rk, int n, int Kb, int32_t *na, int32_t *ne,
                                   int32_t *more) {
-  const int tid = threadIdx.x;
-  auto emit = [&](int c, int r) {
+  const int parts = (n + kSpan - 1) / kSpan;
+  for (int t = threadIdx.x; t < n * parts; t += 256) {
+    const int c = t % n, j0 = (t / n) * kSpan;
+    const uint64_t kc = key[c];
+    uint64_t kk[kSpan];
+#pragma unroll
+    for (int u = 0; u < kSpan; u++) kk[u] = key[j0 + u];
+    int r = 0;
+#pragma unroll
+    for (int u = 0; u < kSpan; u++) r += kk[u] > kc;
+    if (r && kc) atomicAdd(&rk[c], r);
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < n; c += 256) {
+    const int r = rk[c];
+    if (key[c] == 0 || r >= Kb) continue;
     const int32_t lo = ca[c], hi = ce[c];
     const bool split = hi - lo >= 2;
     const int32_t m = lo + (hi - lo) / 2;
@@ -36,38 +53,6 @@ __device__ inline void select_top(const int32_t *ca, const int32_t *ce, const ui
     na[2 * r + 1] = split ? m : -1;
     ne[2 * r + 1] = split ? hi : -1;
     if (split) *more = 1;
-  };
-  if (n <= 256) {
-    if (tid < n) {
-      const uint64_t kc = key[tid];
-      int r = 0;
-      for (int j0 = 0; j0 < n; j0 += kSpan) {
-        uint64_t kk[kSpan];
-#pragma unroll
-        for (int u = 0; u < kSpan; u++) kk[u] = key[j0 + u];
-#pragma unroll
-        for (int u = 0; u < kSpan; u++) r += kk[u] > kc;
-      }
-      if (kc != 0 && r < Kb) emit(tid, r);
-    }
-  } else {  // large K_b: several lanes per candidate, counts summed in LDS
-    for (int c = tid; c < n; c += 256) rk[c] = 0;
-    __syncthreads();
-    const int parts = (n + kSpan - 1) / kSpan;
-    for (int t = tid; t < n * parts; t += 256) {
-      const int c = t % n, j0 = (t / n) * kSpan;
-      const uint64_t kc = key[c];
-      uint64_t kk[kSpan];
-#pragma unroll
-      for (int u = 0; u < kSpan; u++) kk[u] = key[j0 + u];
-      int r = 0;
-#pragma unroll
-      for (int u = 0; u < kSpan; u++) r += kk[u] > kc;
-      if (r && kc) atomicAdd(&rk[c], r);
-    }
-    __syncthreads();
-    for (int c = tid; c < n; c += 256)
-      if (key[c] != 0 && rk[c] < Kb) emit(c, rk[c]);
   }
 }
 
