@@ -46,6 +46,7 @@ namespace hipsa {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.f;  // log2 of the largest weight before the running max moves
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
@@ -82,7 +83,7 @@ __device__ inline void online_softmax(const f32x16_t (&sacc)[2], bool masked, co
         const int32_t tt[4] = {t4.x, t4.y, t4.z, t4.w};
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-          const bool ok = qvalid && tt[e] >= 0 && (!causal || tt[e] <= qpos);
+          const bool ok = qvalid & (tt[e] >= 0) & (!causal | (tt[e] <= qpos));
           sv[kt][4 * gq + e] = ok ? sv[kt][4 * gq + e] : -INFINITY;
         }
       }
@@ -93,21 +94,27 @@ __device__ inline void online_softmax(const f32x16_t (&sacc)[2], bool masked, co
 #pragma unroll
     for (int r = 0; r < 16; r++) mx = fmaxf(mx, sv[kt][r]);
   mx = xor32_max(mx) * sl2;  // scale > 0: max commutes
-  const float mnew = fmaxf(m, mx);
-  const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
+  // The reference max m moves only when a tile's max exceeds it by more than
+  // kLazy (log2 units): until then the weights exp2(s - m) stay <= 2^kLazy,
+  // harmless in fp32 and in bf16, and since l and o always share the same m
+  // the normalised result is the same, while the rescale of o (DT*16
+  // multiplies) runs on few tiles.  m = -inf: any finite max moves it.
+  const bool upd = mx > m + kLazy;
+  const float mnew = upd ? mx : m;
+  const float alpha = upd ? __builtin_amdgcn_exp2f(m - mnew) : 1.f;  // exp2(-inf) = 0
   const float msub = mnew == -INFINITY ? 0.f : mnew;
-  float ps = 0.f;
+  float ps4[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums: short dependency chains
 #pragma unroll
   for (int kt = 0; kt < 2; kt++)
 #pragma unroll
     for (int r = 0; r < 16; r++) {
       const float p = __builtin_amdgcn_exp2f(fmaf(sv[kt][r], sl2, -msub));  // exp2(-inf) = 0
-      ps += p;
+      ps4[r & 3] += p;
       pf[kt * 2 + (r >> 3)][r & 7] = (__bf16)p;
     }
-  l = fmaf(l, alpha, ps);
+  l = fmaf(l, alpha, (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]));
   m = mnew;
-  if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+  if (__builtin_amdgcn_ballot_w64(upd)) {
 #pragma unroll
     for (int dt = 0; dt < DT; dt++) o[dt] *= alpha;
   }
@@ -151,16 +158,16 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][KT * VPAD];
   __shared__ __attribute__((aligned(16))) int32_t tok[2][KT];
   __shared__ int32_t tmask[2];
-  __shared__ int32_t lst[kMaxKb];
-  __shared__ int32_t lpg[PAGED ? kMaxKb + kMaxDenseBlocks : 1];  // paged: page of each entry
+  // block of every entry of the tiles (-1: none), and with a paged cache its page
+  __shared__ int32_t ent[kMaxKb + kMaxDenseBlocks + 8];
+  __shared__ int32_t lpg[PAGED ? kMaxKb + kMaxDenseBlocks : 1];
 
   const int32_t *list = a.indices + (int64_t)prob * s.Kb;
-  for (int j = tid; j < cnt; j += 512) lst[j] = list[j];
-  if constexpr (PAGED) {
-    for (int j = tid; j < nent; j += 512) {
-      const int32_t blk = entry_block(j, list, cnt, s, Np, dn);  // -1: skipped, any page will do
-      lpg[j] = page_at(a.pg, b, ((blk >= 0 ? blk : 0) << s.bk_shift) >> a.pg.ps_shift);
-    }
+  for (int j = tid; j < ntiles * bpt; j += 512) {  // < nent + bpt entries
+    const int32_t blk = j < nent ? entry_block(j, list, cnt, s, Np, dn) : -1;
+    ent[j] = blk;
+    if constexpr (PAGED)  // a skipped entry: any page will do
+      if (j < nent) lpg[j] = page_at(a.pg, b, ((blk >= 0 ? blk : 0) << s.bk_shift) >> a.pg.ps_shift);
   }
 
   const int64_t kvoff = PAGED ? 0 : (int64_t)(b * Hkv + g) * s.T_cap * D;
@@ -177,7 +184,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnArgs a) {
     for (int ks = 0; ks < KS; ks++)
       qf[ks] = *reinterpret_cast<const uint4 *>(Qg + (int64_t)row * D + 16 * ks + 8 * half);
   }
-  __syncthreads();  // lst ready
+  __syncthreads();  // ent ready
 
   // loader state: this lane's K and V rows of two tiles in flight (sets 0, 1)
   typename Kv8<KE>::raw_t kreg0[KP], vreg0[KP], kreg1[KP], vreg1[KP];
@@ -186,7 +193,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnArgs a) {
   // token of slot J of tile TL, or -1 (branch-free so the loads stay in flight)
 #define HIPSA_TOKEN(TL, J, OUT)                                              \
   do {                                                                       \
-    const int32_t blk_ = entry_block((TL) * bpt + ((J) >> s.bk_shift), lst, cnt, s, Np, dn); \
+    const int32_t blk_ = ent[(TL) * bpt + ((J) >> s.bk_shift)];              \
     const bool okb_ = blk_ >= 0;                                             \
     const int32_t t_ = ((okb_ ? blk_ : 0) << s.bk_shift) + ((J) & (s.bk - 1)); \
     OUT = (okb_ && t_ < Tp) ? t_ : -1;                                       \
