@@ -409,13 +409,16 @@ def main():
         nb = decode_bytes(w)
         kern = {"hip_mask_estimate": (r["ms_mask"], nb["mask"]),
                 "hip_sparse_attn": (r["ms_attn"], nb["attn"])}
-        dom = max(kern, key=lambda k: kern[k][0])
-        t_ms, byt = kern[dom]
-        ach = byt / (t_ms * 1e-3) / 1e9
-        line["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1),
-                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                            "traffic": measured_traffic("decode", dom, w.dtype), "algorithmic_bytes": byt,
-                            "launch_us": round(t_ms * 1e3, 3)}
+        def hbm_roof(k):
+            t_ms, byt = kern[k]
+            ach = byt / (t_ms * 1e-3) / 1e9
+            return {"bound": "hbm", "kernel": k, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                    "traffic": measured_traffic("decode", k, w.dtype), "algorithmic_bytes": byt,
+                    "launch_us": round(t_ms * 1e3, 3)}
+        dom = max(kern, key=lambda k: kern[k][0])  # the longer launch
+        line["roofline"] = hbm_roof(dom)
+        line["roofline_other"] = hbm_roof(min(kern, key=lambda k: kern[k][0]))
         line["mask_reuse"] = {"r_m": [1] + sorted(r["ms_reuse"]),
                               "us_per_step": [round(us, 3)] + [round(r["ms_reuse"][k] * 1e3, 3)
                                                                for k in sorted(r["ms_reuse"])],
@@ -433,14 +436,17 @@ def main():
         line["higher_is_better"] = True
         kern = {"hip_mask_estimate": (r["ms_mask"], fl["mask"]),
                 "hip_sparse_attn": (r["ms_attn"], fl["attn"])}
-        dom = max(kern, key=lambda k: kern[k][0])
-        t_ms, f = kern[dom]
-        ach = f / (t_ms * 1e-3) / 1e12
-        line["roofline"] = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2),
-                            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                            "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
-                            "traffic": measured_traffic("prefill", dom, w.dtype),
-                            "algorithmic_flops": f, "launch_us": round(t_ms * 1e3, 3)}
+        def mfma_roof(k):
+            t_ms, f = kern[k]
+            ach = f / (t_ms * 1e-3) / 1e12
+            return {"bound": "mfma", "kernel": k, "achieved": round(ach, 2),
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "traffic": measured_traffic("prefill", k, w.dtype),
+                    "algorithmic_flops": f, "launch_us": round(t_ms * 1e3, 3)}
+        dom = max(kern, key=lambda k: kern[k][0])  # the longer launch
+        line["roofline"] = mfma_roof(dom)
+        line["roofline_other"] = mfma_roof(min(kern, key=lambda k: kern[k][0]))
         line["step_roofline"] = {"algorithmic_flops": fl["total"], "achieved_tflops": round(tflops, 2),
                                  "mask_us": round(r["ms_mask"] * 1e3, 3),
                                  "attn_us": round(r["ms_attn"] * 1e3, 3)}
