@@ -196,21 +196,28 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
 //     probabilities are LDS broadcasts, and each lane accumulates its
 //     dimensions over every slot of the wave; when a row takes half a wave
 //     the two halves take alternate rows and are summed once at the end.
+//   * WIDE: a lane loads 8 consecutive elements (16 bytes of bf16, 8 of
+//     fp8), so one wave-wide load covers RPV = 4 rows (d = 128) or 8 (d = 64)
+//     and each row group of lanes takes every RPV-th slot; the probabilities
+//     of a row group's slots are contiguous in the LDS table (vector reads),
+//     and the row groups are summed once at the end.  Fewer, wider loads
+//     pay when the grid is large (several workgroups per CU); on a grid of
+//     about two workgroups per CU the narrow form measured faster.
 // fp8 K rows are loaded as 8-byte slices and widened to bf16 operands in
 // registers (exact: every E5M2 value is a bf16 value).
 // Query loads are issued first: loads complete in order, so the first
 // matrix op then waits for the query and its K rows, not for the V rows
 // issued after them.
-template <typename KE, int D, int GMAX, int TOK, bool PAGED>
+template <typename KE, int D, int GMAX, int TOK, bool PAGED, bool WIDE>
 __global__ __launch_bounds__(256) void attn_decode_mfma(AttnArgs a) {
   constexpr int KS = D / 32;            // MFMA k-steps over the head dim
   constexpr int TPW = TOK / 4;          // token slots per wave
   constexpr int NT = TPW / 16;          // 16-slot tiles per wave
-  constexpr int EPL = (sizeof(KE) == 1 && D == 128) ? 4 : 2;  // V elements per lane
+  constexpr int EPL = WIDE ? 8 : (sizeof(KE) == 1 && D == 128) ? 4 : 2;  // V elements per lane
   constexpr int LPV = D / EPL < 64 ? D / EPL : 64;  // lanes per V row
   constexpr int RPV = 64 / LPV;         // V rows per wave-wide load
   constexpr int NV = TPW / RPV;         // V loads per lane
-  static_assert(NT >= 1 && TPW % RPV == 0 && RPV <= 2, "split too small");
+  static_assert(NT >= 1 && TPW % RPV == 0 && NV >= 1 && (WIDE || RPV <= 2), "split too small");
   const Shape &s = a.s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t S = (uint32_t)a.splits;
@@ -279,6 +286,7 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(AttnArgs a) {
   typename KvN<KE, EPL>::raw_t vr[NV];
 #pragma unroll
   for (int v = 0; v < NV; v++) {
+    // WIDE: row group lane / LPV takes slots RPV * v + lane / LPV
     vt[v] = RPV == 1 ? __builtin_amdgcn_readlane(tk_lane, v) : __shfl(tk_lane, RPV * v + lane / LPV, 64);
     int32_t vpg = 0;
     if constexpr (PAGED)
@@ -315,7 +323,9 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(AttnArgs a) {
     for (int u = 0; u < NT; u++) {
       const float e = sc[u] == -INFINITY ? 0.f : __expf(sc[u] - m);
       l += e;
-      if (h < GMAX) pw[wave][h][16 * u + (lane & 15)] = e;
+      const int sl = 16 * u + (lane & 15);
+      // WIDE: slot sl at (sl % RPV) * NV + sl / RPV, a row group's slots contiguous
+      if (h < GMAX) pw[wave][h][WIDE ? (sl % RPV) * NV + sl / RPV : sl] = e;
     }
     l = group_sum<16>(l);
     if ((lane & 15) == 0 && h < s.G) { wm[wave][h] = m; wl[wave][h] = l; }
@@ -325,14 +335,49 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(AttnArgs a) {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
   // P.V: lane owns dimensions EPL*(lane % LPV) .. +EPL-1 over the wave's
-  // slots; probabilities read 4 slots at a time (an LDS broadcast)
-  constexpr int VPG = 4 / RPV;  // V loads per group of 4 slots
-  const int half = lane / LPV;  // RPV = 2: which of the two rows of a load
+  // slots (WIDE: over its row group's slots)
   float o[GMAX][EPL];
 #pragma unroll
   for (int h = 0; h < GMAX; h++)
 #pragma unroll
     for (int e = 0; e < EPL; e++) o[h][e] = 0.f;
+  if constexpr (WIDE) {
+    constexpr int C = NV < 4 ? NV : 4;  // slots per probability read
+    const int rg = lane / LPV;
+#pragma unroll
+    for (int v0 = 0; v0 < NV; v0 += C) {
+      float pv[GMAX][C];
+#pragma unroll
+      for (int h = 0; h < GMAX; h++) {
+        const float *src = &pw[wave][h][rg * NV + v0];
+        if constexpr (C == 4) {
+          const float4 t = *reinterpret_cast<const float4 *>(src);
+          pv[h][0] = t.x; pv[h][1] = t.y; pv[h][2] = t.z; pv[h][3] = t.w;
+        } else if constexpr (C == 2) {
+          const float2 t = *reinterpret_cast<const float2 *>(src);
+          pv[h][0] = t.x; pv[h][1] = t.y;
+        } else {
+          pv[h][0] = *src;
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < C; c++) {
+        float vx[EPL];
+        KvN<KE, EPL>::widen(vr[v0 + c], vt[v0 + c] >= 0, vx);
+        // every one of the GMAX heads is computed (see below)
+#pragma unroll
+        for (int h = 0; h < GMAX; h++)
+#pragma unroll
+          for (int e = 0; e < EPL; e++) o[h][e] = fmaf(pv[h][c], vx[e], o[h][e]);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < GMAX; h++)
+#pragma unroll
+      for (int e = 0; e < EPL; e++) o[h][e] = across_sum<LPV>(o[h][e]);
+  } else {
+  constexpr int VPG = 4 / RPV;  // V loads per group of 4 slots
+  const int half = lane / LPV;  // RPV = 2: which of the two rows of a load
 #pragma unroll
   for (int g4 = 0; g4 < TPW / 4; g4++) {
     // every one of the GMAX heads is computed (heads past the group have
@@ -362,11 +407,15 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < EPL; e++) o[h][e] = xor32_sum(o[h][e]);
   }
+  }
   if (lane < LPV) {
 #pragma unroll
     for (int h = 0; h < GMAX; h++) {
       if (h >= s.G) continue;
-      if constexpr (EPL == 4)
+      if constexpr (EPL == 8) {
+        *reinterpret_cast<float4 *>(&wo[wave][h][8 * lane]) = make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
+        *reinterpret_cast<float4 *>(&wo[wave][h][8 * lane + 4]) = make_float4(o[h][4], o[h][5], o[h][6], o[h][7]);
+      } else if constexpr (EPL == 4)
         *reinterpret_cast<float4 *>(&wo[wave][h][4 * lane]) = make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
       else
         *reinterpret_cast<float2 *>(&wo[wave][h][2 * lane]) = make_float2(o[h][0], o[h][1]);
@@ -471,13 +520,23 @@ int tokens_for(const Shape &s) {
 
 // E: query / output element type; KE: K/V element type (E itself, or E5M2
 // codes under a bf16 query).
+// Split workgroups from which the bf16 kernel reads V rows 16 bytes per lane
+// (about four per CU and more); below, 2-4 bytes per lane.
+constexpr int64_t kWideGrid = 1024;
+
+template <typename KE, int D, int GMAX, bool PAGED, bool WIDE>
+void launch_mfma(const AttnArgs &a, dim3 grid, hipStream_t st, int tok) {
+  if (GMAX <= 8 && tok == 128) hipLaunchKernelGGL((attn_decode_mfma<KE, D, (GMAX <= 8 ? GMAX : 8), 128, PAGED, WIDE>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((attn_decode_mfma<KE, D, GMAX, 64, PAGED, WIDE>), grid, dim3(256), 0, st, a);
+}
+
 template <typename E, typename KE, int D, int GMAX, bool PAGED>
 void launch_t(const AttnArgs &a, hipStream_t st, int tok) {
   constexpr int kMaxTok = max_tokens<E, D>();
   const dim3 grid((unsigned)(a.s.problems * a.splits)), block(256);
   if constexpr (std::is_same<E, uint16_t>::value) {
-    if (GMAX <= 8 && tok == 128) hipLaunchKernelGGL((attn_decode_mfma<KE, D, (GMAX <= 8 ? GMAX : 8), 128, PAGED>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((attn_decode_mfma<KE, D, GMAX, 64, PAGED>), grid, block, 0, st, a);
+    if ((int64_t)a.s.problems * a.splits >= kWideGrid) launch_mfma<KE, D, GMAX, PAGED, true>(a, grid, st, tok);
+    else launch_mfma<KE, D, GMAX, PAGED, false>(a, grid, st, tok);
   } else {
     if (tok == 128) {
       if constexpr (kMaxTok >= 128) hipLaunchKernelGGL((attn_decode_kernel<E, D, GMAX, 128, PAGED>), grid, block, 0, st, a);

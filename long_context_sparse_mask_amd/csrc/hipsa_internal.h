@@ -209,8 +209,8 @@ template <> struct Kv8<uint8_t> {
   }
 };
 
-// N consecutive elements of a V row (N*sizeof(KE) = 2 or 4 bytes) widened to
-// fp32; a load that is not kept reads as zeros.
+// N consecutive elements of a V row (N*sizeof(KE) = 2, 4, 8 or 16 bytes)
+// widened to fp32; a load that is not kept reads as zeros.
 template <typename KE, int N> struct KvN;
 template <> struct KvN<uint16_t, 2> {
   using raw_t = uint32_t;
@@ -240,6 +240,29 @@ template <> struct KvN<uint8_t, 4> {
     v[1] = a.y;
     v[2] = b.x;
     v[3] = b.y;
+  }
+};
+template <> struct KvN<uint16_t, 8> {
+  using raw_t = uint4;
+  __device__ static inline raw_t raw(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+  __device__ static inline void widen(raw_t r, bool keep, float (&v)[8]) {
+    const uint32_t w[4] = {keep ? r.x : 0u, keep ? r.y : 0u, keep ? r.z : 0u, keep ? r.w : 0u};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+template <> struct KvN<uint8_t, 8> {
+  using raw_t = uint2;
+  __device__ static inline raw_t raw(const uint8_t *p) { return *reinterpret_cast<const uint2 *>(p); }
+  __device__ static inline void widen(raw_t r, bool keep, float (&v)[8]) {
+    const uint32_t x = keep ? r.x : 0u, y = keep ? r.y : 0u;
+    const f32x2_t a = e5m2x2_to_f32x2<false>(x), b = e5m2x2_to_f32x2<true>(x);
+    const f32x2_t c = e5m2x2_to_f32x2<false>(y), d = e5m2x2_to_f32x2<true>(y);
+    v[0] = a.x; v[1] = a.y; v[2] = b.x; v[3] = b.y;
+    v[4] = c.x; v[5] = c.y; v[6] = d.x; v[7] = d.y;
   }
 };
 

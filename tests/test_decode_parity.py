@@ -77,6 +77,40 @@ def test_edge(case):
     assert r["exempt"] <= max(1, r["problems"] // 10)
 
 
+# Grids of >= 1024 split workgroups, where the bf16-query split kernel reads
+# V rows 16 bytes per lane (many query rows make many problems).
+WIDE = {
+    "wide_bf16_d128": dict(base="decode_32k", Hq=32, Hkv=8, Tq=16, T=4096, k=1024),
+    "wide_e5m2_d128": dict(base="decode_32k", Hq=32, Hkv=8, Tq=16, T=4096, k=1024, dtype="bf16_e5m2"),
+    "wide_bf16_d64_g2": dict(base="decode_32k", Hq=16, Hkv=8, Tq=16, T=4096, d=64, k=1024),
+    "wide_e5m2_d64_ragged": dict(base="decode_32k", Hq=16, Hkv=8, Tq=16, T=4001, d=64, k=1024,
+                                 dtype="bf16_e5m2"),
+    "wide_group8": dict(base="decode_32k", Hq=64, Hkv=8, Tq=16, T=4096, k=1024),
+    "wide_group16_noncausal": dict(base="decode_32k", Hq=32, Hkv=2, Tq=32, T=4096, k=1024, causal=0),
+}
+
+
+def split_workgroups(w):
+    """Split workgroups of the decode attention launch, from the workspace size
+    (problems x splits x G x (d + 2) floats)."""
+    import long_context_sparse_mask_amd as hs
+    q = torch.empty((w.B, w.Hq, w.Tq, w.d), dtype=torch.bfloat16)
+    K = torch.empty((w.B, w.Hkv, w.T, w.d), dtype=q.dtype)
+    ws = hs.hipsa_workspace_bytes_ex(q, K, w.k, w.block_k, w.block_q, T=w.T, causal=bool(w.causal))
+    return ws // ((w.Hq // w.Hkv) * (w.d + 2) * 4)
+
+
+@pytest.mark.parametrize("case", sorted(WIDE))
+def test_wide_grid(case):
+    kw = dict(WIDE[case])
+    w = si.workload(kw.pop("base"), **kw)
+    assert split_workgroups(w) >= 1024
+    print(f"[case] {case} {w}", flush=True)
+    r = full_parity(_inputs(w), w)
+    _report(case, r)
+    assert r["exempt"] <= max(1, r["problems"] // 10)
+
+
 def test_spare_capacity_rows():
     w = si.workload("decode_32k", Hq=8, Hkv=2, T=3000, k=512)
     x = _inputs(w, T_cap=3333)
