@@ -27,6 +27,7 @@ import argparse
 import json
 import math
 import os
+import re
 import statistics
 import sys
 import time
@@ -100,12 +101,24 @@ CALL_KERNELS = {
 }
 
 
-def kernel_source_sha() -> str:
+# string and character literals (kept) or comments (dropped), in source order
+_LITERAL_OR_COMMENT = re.compile(r'"(?:\\.|[^"\\])*"|\'(?:\\.|[^\'\\])*\'|//[^\n]*|/\*.*?\*/', re.S)
+
+
+def code_text(src: str) -> str:
+    """The code of a C/C++/HIP source without comments, whitespace runs collapsed."""
+    src = _LITERAL_OR_COMMENT.sub(lambda m: m.group(0) if m.group(0)[0] in "\"'" else " ", src)
+    return re.sub(r"\s+", " ", src).strip()
+
+
+def kernel_source_sha(d: str | None = None) -> str:
+    """Hash of the library's sources, comments and layout aside: the measured
+    traffic stays valid across comment edits and is dropped on any code change."""
     import hashlib
-    d = os.path.join(ROOT, "long_context_sparse_mask_amd", "csrc")
+    d = d or os.path.join(ROOT, "long_context_sparse_mask_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(os.listdir(d)):
-        h.update(open(os.path.join(d, f), "rb").read())
+        h.update(f.encode() + b"\0" + code_text(open(os.path.join(d, f)).read()).encode() + b"\0")
     return h.hexdigest()[:16]
 
 

@@ -10,7 +10,7 @@
 // on the matrix cores (v_mfma_f32_32x32x16_bf16).  One workgroup of 8 wave64s
 // serves one (b, kv head, query block) and four query heads of the group:
 // wave w takes head w/2 and query rows 32*(w%2) .. +31, so every K/V tile
-// fetched from memory feeds four heads, and at ~190 registers per lane two
+// fetched from memory feeds four heads, and at ~210 registers per lane two
 // waves share each SIMD (one's softmax VALU work overlaps the other's
 // MFMAs).  (Giving each wave both query tiles of its head halves the LDS
 // operand reads per MFMA, but needs ~500 registers, leaves one wave per SIMD

@@ -106,3 +106,17 @@ def test_page_pool_addressing():
     for b in range(B):
         assert torch.equal(Kp[tab[b, t // ps].long(), :, t % ps].permute(1, 0, 2), K[b])
         assert torch.equal(Vp[tab[b, t // ps].long(), :, t % ps].permute(1, 0, 2), V[b])
+
+
+def test_source_hash_ignores_comments_only(tmp_path):
+    """The hash that gates the measured traffic survives comment and layout
+    edits and changes with any code edit."""
+    src = 'int f(int a) { // add one\n  return a + 1; /* done */ }\nconst char *s = "// kept";\n'
+    (tmp_path / "k.hip").write_text(src)
+    base = bench.kernel_source_sha(str(tmp_path))
+    (tmp_path / "k.hip").write_text(src.replace("// add one", "// increment").replace("  return", "return"))
+    assert bench.kernel_source_sha(str(tmp_path)) == base
+    (tmp_path / "k.hip").write_text(src.replace('"// kept"', '"// changed"'))
+    assert bench.kernel_source_sha(str(tmp_path)) != base
+    (tmp_path / "k.hip").write_text(src.replace("a + 1", "a + 2"))
+    assert bench.kernel_source_sha(str(tmp_path)) != base
