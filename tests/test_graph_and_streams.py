@@ -40,6 +40,8 @@ CASES = {
     "prefill": (dict(name="prefill_32k_chunk4k", T=3000, Tq=200, Hq=8, Hkv=2, k=512), None),
     "decode_e5m2_dense": (dict(name="decode_32k", Hq=8, Hkv=2, T=12000, dtype="bf16_e5m2"),
                           dict(sink=64, window=1024)),
+    # 1024 split workgroups: the 16-byte V reads of the split kernel
+    "decode_wide_grid": (dict(name="decode_32k", Hq=32, Hkv=8, Tq=16, T=4096, k=1024), None),
 }
 
 
