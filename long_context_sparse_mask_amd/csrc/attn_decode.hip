@@ -446,10 +446,10 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(AttnArgs a) {
 // Merge the S partials of one (problem, query head): one workgroup of D lanes,
 // every load of a batch issued before any is used.  Per batch of CH partials
 // the maximum is a tree and the weights are independent exponentials, so the
-// dependent chain is one step per batch rather than one per partial.
-template <typename E, int D>
+// dependent chain is one step per batch rather than one per partial.  CH is
+// 16 or 32, chosen so that up to 32 partials take one memory round trip.
+template <typename E, int D, int CH>
 __global__ __launch_bounds__(128) void attn_decode_combine(AttnArgs a) {
-  constexpr int CH = 16;  // partials in flight per lane
   const Shape &s = a.s;
   const int S = a.splits;
   const uint32_t ph = blockIdx.x;
@@ -556,7 +556,9 @@ hipError_t launch_d(const AttnArgs &a, hipStream_t st) {
   else launch_t<E, KE, D, 16, PAGED>(a, st, tok);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_decode_combine<E, D>), dim3((unsigned)(a.s.problems * G)), dim3(128), 0, st, a);
+  const dim3 cgrid((unsigned)(a.s.problems * G));
+  if (a.splits <= 16) hipLaunchKernelGGL((attn_decode_combine<E, D, 16>), cgrid, dim3(128), 0, st, a);
+  else hipLaunchKernelGGL((attn_decode_combine<E, D, 32>), cgrid, dim3(128), 0, st, a);
   return hipGetLastError();
 }
 
