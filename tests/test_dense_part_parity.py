@@ -80,6 +80,10 @@ CASES = {
     "prefill_bk16": ("prefill_32k_chunk4k", 32, 256, dict(T=4096, Tq=128, Hq=4, Hkv=1, block_k=16, k=256)),
     "prefill_e5m2_d64": ("prefill_32k_chunk4k", 64, 1024, dict(T=4500, Tq=128, Hq=8, Hkv=2, d=64, k=512,
                                                              dtype="bf16_e5m2")),
+    # the largest dense part the calls accept: (sink + window) / block_k = 256 blocks
+    "decode_dense_256_blocks": ("decode_32k", 64, 16320, dict(Hq=8, Hkv=2, T=32768, k=2048)),
+    "prefill_dense_256_blocks": ("prefill_32k_chunk4k", 64, 16320, dict(T=20000, Tq=128, Hq=4, Hkv=1,
+                                                                     k=512)),
 }
 
 

@@ -122,6 +122,13 @@ def test_paged(case):
 
 
 @pytest.mark.timeout(900)
+def test_paged_max_pages_per_sequence():
+    """A 1M-token sequence in 64-token pages: 16384 pages, the most a sequence
+    may have in the mask calls (its page numbers fill 64 KiB of LDS)."""
+    check_paged(si.workload("decode_32k", Hq=4, Hkv=1, T=1 << 20, k=4096), 64, seed=13)
+
+
+@pytest.mark.timeout(900)
 def test_paged_decode_128k_b4_full():
     """The 128k x4 decode at full size, pages of one key block, shuffled."""
     check_paged(si.workload("decode_128k_b4"), 64, seed=11)
