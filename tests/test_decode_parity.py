@@ -62,6 +62,10 @@ EDGE = {
     "group1": dict(base="decode_32k", Hq=4, Hkv=4, T=4096, k=1024),
     "group8": dict(base="decode_32k", Hq=16, Hkv=2, T=4096, k=1024),
     "group16": dict(base="decode_32k", Hq=16, Hkv=1, T=4096, k=1024),
+    # groups that are not a power of two (padded head rows in the matrix ops)
+    "group3": dict(base="decode_32k", Hq=6, Hkv=2, T=4096, k=1024),
+    "group5": dict(base="decode_32k", Hq=5, Hkv=1, T=4096, k=1024),
+    "group12_f32": dict(base="decode_32k", dtype="f32", Hq=12, Hkv=1, T=3000, k=512),
     # fp32 at d=128, batch 3
     "f32_d128_b3": dict(base="decode_32k", dtype="f32", B=3, Hq=4, Hkv=2, T=6000, k=1024),
 }

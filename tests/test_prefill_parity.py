@@ -36,6 +36,10 @@ SMALL = {
     "group2": dict(T=4096, Tq=128, Hq=4, Hkv=2, k=512),
     "group8": dict(T=4096, Tq=128, Hq=8, Hkv=1, k=512),
     "group16": dict(T=4096, Tq=64, Hq=16, Hkv=1, k=512),
+    # groups that are not a power of two: idle waves in the last 4-head chunk
+    "group3": dict(T=4096, Tq=128, Hq=6, Hkv=2, k=512),
+    "group6": dict(T=4096, Tq=128, Hq=6, Hkv=1, k=512),
+    "group12_ragged": dict(T=3001, Tq=100, Hq=12, Hkv=1, k=512),
     "noncausal": dict(T=4096, Tq=130, Hq=4, Hkv=1, k=512, causal=0),
     "batch2": dict(B=2, T=2048, Tq=128, Hq=4, Hkv=2, k=512),
     "kb_odd": dict(T=4096, Tq=128, Hq=4, Hkv=1, k=7 * 64),
