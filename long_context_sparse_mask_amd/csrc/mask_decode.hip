@@ -17,14 +17,15 @@
 //      (zero-padded to 16 rows), then takes the max over the valid head rows
 //      of the accumulator; fp32 inputs use 16-byte VALU dot products with DPP
 //      reductions instead.  fp8 (E5M2) keys are loaded as 8-byte slices and
-//      widened exactly to bf16 operands in registers.  Every load of a round is issued before any is used
-//      (an empty slot reads row 0 and discards it), so a round pays one memory
-//      latency;
+//      widened exactly to bf16 operands in registers.  Every load of a round
+//      is issued before any is used (an empty slot reads row 0 and discards
+//      it), so a round pays one memory latency;
 //   2. selection.  A candidate's rank is the number of keys above its own
-//      (key = score, then lower start, packed in one 64-bit integer); a
-//      kept candidate writes its two halves (or itself and an empty slot)
-//      straight into the other buffer, and a kept chunk wider than one block
-//      sets the flag that runs the next round.
+//      (key = score, then lower start, packed in one 64-bit integer), the
+//      comparisons shared by all 256 threads; a kept candidate writes its
+//      two halves (or itself and an empty slot) straight into the other
+//      buffer, and a kept chunk wider than one block sets the flag that runs
+//      the next round.
 // Rounds are serially dependent (the next centres depend on this round's
 // top-k), so the kernel is bound by one dependent memory round trip plus the
 // round's LDS work per round, not by bandwidth.  With a paged KV cache the
