@@ -3,7 +3,7 @@
 Argument marshalling only.  Every step of the computation runs in the HIP
 kernels of libhipsa.so; torch supplies device memory and the current stream.
 There is no fallback: importing this package fails if the library is not
-built (``python -m long_context_sparse_mask_amd.build``).
+built (``python long_context_sparse_mask_amd/build.py``).
 
 Layouts (contiguous): q [B,Hq,Tq,d]; K, V [B,Hkv,T_cap,d] with the first T
 rows valid; indices [B,Hkv,NQB,k/block_k] int32; nnz [B,Hkv,NQB] int32.
@@ -28,7 +28,7 @@ __all__ = ["hip_mask_estimate", "hip_sparse_attn", "hip_mask_estimate_paged",
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhipsa.so")
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m long_context_sparse_mask_amd.build`")
+    raise ImportError(f"{LIB_PATH} is not built; run `python long_context_sparse_mask_amd/build.py`")
 
 lib = C.CDLL(LIB_PATH)
 

@@ -257,3 +257,11 @@ def test_binding_fails_loudly_without_the_library(tmp_path):
     code = "import sys; sys.path.insert(0, %r); import long_context_sparse_mask_amd" % str(tmp_path)
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True)
     assert r.returncode != 0 and "not built" in r.stderr
+    # the command the message names runs the build script by path, which
+    # loads without the library (loaded here without building)
+    shutil.copy(os.path.join(ROOT, "long_context_sparse_mask_amd", "build.py"), pkg)
+    hint = r.stderr.strip().splitlines()[-1]
+    assert "long_context_sparse_mask_amd/build.py" in hint
+    code = "import runpy; runpy.run_path(%r, run_name='check')" % str(pkg / "build.py")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
