@@ -348,13 +348,5 @@ template <int W> __device__ inline float across_max(float v) {
   if (W <= 32) v = xor32_max(v);
   return v;
 }
-__device__ inline float wave_max(float v) {
-  v = fmaxf(v, dpp_mov<kDppXor1>(v));
-  v = fmaxf(v, dpp_mov<kDppXor2>(v));
-  v = fmaxf(v, dpp_mov<kDppHalfMirror>(v));
-  v = fmaxf(v, dpp_mov<kDppMirror>(v));
-  return across_max<16>(v);
-}
-__device__ inline float wave_sum(float v) { return group_sum<64>(v); }
 
 }  // namespace hipsa
