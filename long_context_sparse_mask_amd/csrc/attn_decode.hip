@@ -58,7 +58,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rgl = lane / TPR, cs = lane % TPR;
   const uint32_t S = (uint32_t)a.splits;
-  const uint32_t split = blockIdx.x % S, prob = blockIdx.x / S;
+  const uint32_t wgi = xcd_swizzle(blockIdx.x, gridDim.x);
+  const uint32_t split = wgi % S, prob = wgi / S;
   const uint32_t Tq = (uint32_t)s.Tq, Hkv = (uint32_t)s.Hkv;
   const uint32_t i = prob % Tq, g = (prob / Tq) % Hkv, b = prob / (Tq * Hkv);
   const int32_t Tp = s.causal ? (int32_t)(s.T - s.Tq + i + 1) : (int32_t)s.T;
@@ -221,7 +222,8 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(AttnArgs a) {
   const Shape &s = a.s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t S = (uint32_t)a.splits;
-  const uint32_t split = blockIdx.x % S, prob = blockIdx.x / S;
+  const uint32_t wgi = xcd_swizzle(blockIdx.x, gridDim.x);
+  const uint32_t split = wgi % S, prob = wgi / S;
   const uint32_t Tq = (uint32_t)s.Tq, Hkv = (uint32_t)s.Hkv;
   const uint32_t i = prob % Tq, g = (prob / Tq) % Hkv, b = prob / (Tq * Hkv);
   const int32_t Tp = s.causal ? (int32_t)(s.T - s.Tq + i + 1) : (int32_t)s.T;
@@ -452,7 +454,7 @@ template <typename E, int D, int CH>
 __global__ __launch_bounds__(128) void attn_decode_combine(AttnArgs a) {
   const Shape &s = a.s;
   const int S = a.splits;
-  const uint32_t ph = blockIdx.x;
+  const uint32_t ph = xcd_swizzle(blockIdx.x, gridDim.x);
   const uint32_t prob = ph / (uint32_t)s.G;
   const int h = (int)(ph % (uint32_t)s.G);
   const uint32_t Tq = (uint32_t)s.Tq, Hkv = (uint32_t)s.Hkv;

@@ -162,14 +162,6 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnArgs a) {
   __shared__ int32_t ent[kMaxKb + kMaxDenseBlocks + 8];
   __shared__ int32_t lpg[PAGED ? kMaxKb + kMaxDenseBlocks : 1];
 
-  const int32_t *list = a.indices + (int64_t)prob * s.Kb;
-  for (int j = tid; j < ntiles * bpt; j += 512) {  // < nent + bpt entries
-    const int32_t blk = j < nent ? entry_block(j, list, cnt, s, Np, dn) : -1;
-    ent[j] = blk;
-    if constexpr (PAGED)  // a skipped entry: any page will do
-      if (j < nent) lpg[j] = page_at(a.pg, b, ((blk >= 0 ? blk : 0) << s.bk_shift) >> a.pg.ps_shift);
-  }
-
   const int64_t kvoff = PAGED ? 0 : (int64_t)(b * Hkv + g) * s.T_cap * D;
   const KE *Kg = reinterpret_cast<const KE *>(a.K);
   const KE *Vg = reinterpret_cast<const KE *>(a.V);
@@ -183,6 +175,18 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(AttnArgs a) {
 #pragma unroll
     for (int ks = 0; ks < KS; ks++)
       qf[ks] = *reinterpret_cast<const uint4 *>(Qg + (int64_t)row * D + 16 * ks + 8 * half);
+  }
+
+  // The entries are read up to the largest possible count, not up to nent,
+  // so the list loads do not wait for nnz: q, nnz and the list arrive in one
+  // memory round trip.  Entries past nent come out as -1.
+  const int32_t *list = a.indices + (int64_t)prob * s.Kb;
+  const int nmax = ((s.sink_b + s.window_b + s.Kb + bpt - 1) / bpt) * bpt;  // >= ntiles * bpt
+  for (int j = tid; j < nmax; j += 512) {
+    const int32_t blk = entry_block(j, list, cnt, s, Np, dn);
+    ent[j] = blk;
+    if constexpr (PAGED)  // a skipped entry: any page will do
+      if (j < nent) lpg[j] = page_at(a.pg, b, ((blk >= 0 ? blk : 0) << s.bk_shift) >> a.pg.ps_shift);
   }
   __syncthreads();  // ent ready
 

@@ -135,7 +135,11 @@ __device__ inline void stage_pages(const Pages &pg, uint32_t b, int32_t Tp, int3
 // XCD x % 8), and each XCD has its own L2.  This bijection on [0, P) gives
 // XCD j a contiguous range of logical items (ceil or floor of P/8), so items
 // that are adjacent in logical order (the query blocks of one KV head, which
-// select overlapping key blocks) share an L2.
+// select overlapping key blocks) share an L2.  The decode kernels use it on
+// (problem, split) and (problem, head) items numbered problem-major, so a
+// problem's mask, its split workgroups and its merge all run on the same XCD
+// (for P a multiple of 8; otherwise on neighbouring ones), and the list and
+// the partials are read on the XCD that wrote them.
 __device__ inline uint32_t xcd_swizzle(uint32_t x, uint32_t P) {
   constexpr uint32_t kXcd = 8;
   const uint32_t q = P / kXcd, r = P % kXcd, xcd = x % kXcd, i = x / kXcd;

@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256) void mask_decode_kernel(MaskArgs a) {
   const Shape &s = a.s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  const uint32_t prob = blockIdx.x;
+  const uint32_t prob = xcd_swizzle(blockIdx.x, gridDim.x);
   const uint32_t Tq = (uint32_t)s.Tq, Hkv = (uint32_t)s.Hkv;
   const uint32_t i = prob % Tq, g = (prob / Tq) % Hkv, b = prob / (Tq * Hkv);
   const int32_t Tp = s.causal ? (int32_t)(s.T - s.Tq + i + 1) : (int32_t)s.T;
@@ -272,7 +272,7 @@ __global__ __launch_bounds__(256) void mask_decode_pipe(MaskArgs a) {
   const Shape &s = a.s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  const uint32_t prob = blockIdx.x;
+  const uint32_t prob = xcd_swizzle(blockIdx.x, gridDim.x);
   const uint32_t Tq = (uint32_t)s.Tq, Hkv = (uint32_t)s.Hkv;
   const uint32_t i = prob % Tq, g = (prob / Tq) % Hkv, b = prob / (Tq * Hkv);
   const int32_t Tp = s.causal ? (int32_t)(s.T - s.Tq + i + 1) : (int32_t)s.T;
