@@ -29,7 +29,7 @@ from parity_util import compare_attention, compare_masks
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 24
+N_CASES = 48
 
 
 def draw(seed):
