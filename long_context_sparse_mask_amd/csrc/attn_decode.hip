@@ -163,7 +163,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  // merge the four waves (log-sum-exp weights); partials to the workspace
+  // merge the four waves (log-sum-exp weights); partials to the workspace, or
+  // with a single split the normalised output itself (no merge launch follows)
   float *mine = a.ws + ((int64_t)(prob * S + split) * s.G) * (D + 2);
   for (int o = tid; o < s.G * D; o += 256) {
     const int h = o / D, x = o % D;
@@ -177,9 +178,14 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
       L = fmaf(c, wl[w][h], L);
       O = fmaf(c, wo[w][h][x], O);
     }
-    float *dst = mine + (int64_t)h * (D + 2);
-    dst[2 + x] = O;
-    if (x == 0) { dst[0] = M; dst[1] = L; }
+    if (S == 1) {
+      E *out = reinterpret_cast<E *>(a.out) + ((int64_t)(b * s.Hq + g * s.G + h) * Tq + i) * D;
+      store_elem(out + x, L > 0.f ? O / L : 0.f);
+    } else {
+      float *dst = mine + (int64_t)h * (D + 2);
+      dst[2 + x] = O;
+      if (x == 0) { dst[0] = M; dst[1] = L; }
+    }
   }
 }
 
@@ -425,7 +431,8 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(AttnArgs a) {
   }
   __syncthreads();
 
-  // merge the four waves (log-sum-exp weights); partials to the workspace
+  // merge the four waves (log-sum-exp weights); partials to the workspace, or
+  // with a single split the normalised bf16 output itself (no merge launch)
   float *mine = a.ws + ((int64_t)(prob * S + split) * s.G) * (D + 2);
   for (int oi = tid; oi < s.G * D; oi += 256) {
     const int h = oi / D, x = oi % D;
@@ -439,9 +446,14 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(AttnArgs a) {
       L = fmaf(c, wl[w][h], L);
       O = fmaf(c, wo[w][h][x], O);
     }
-    float *dst = mine + (int64_t)h * (D + 2);
-    dst[2 + x] = O;
-    if (x == 0) { dst[0] = M; dst[1] = L; }
+    if (S == 1) {
+      uint16_t *out = reinterpret_cast<uint16_t *>(a.out) + ((int64_t)(b * s.Hq + g * s.G + h) * Tq + i) * D;
+      store_elem(out + x, L > 0.f ? O / L : 0.f);
+    } else {
+      float *dst = mine + (int64_t)h * (D + 2);
+      dst[2 + x] = O;
+      if (x == 0) { dst[0] = M; dst[1] = L; }
+    }
   }
 }
 
@@ -500,17 +512,20 @@ __global__ __launch_bounds__(128) void attn_decode_combine(AttnArgs a) {
 }
 
 // Tokens per split workgroup: 128 or 64, the larger when it still gives
-// >= 512 workgroups.  64 for fp32 at d = 128 (a lane's K and V rows must fit
-// in registers) and for groups of more than 8 query heads (the per-head
-// probabilities and outputs of a lane must fit); a bf16 wave also has at
-// most 63 loads in flight, which caps its slots at 32.
+// >= 512 workgroups, or when it covers a row's whole key sequence (one split:
+// the split workgroup then writes the output and no merge is launched).  64
+// for fp32 at d = 128 (a lane's K and V rows must fit in registers) and for
+// groups of more than 8 query heads (the per-head probabilities and outputs
+// of a lane must fit); a bf16 wave also has at most 63 loads in flight, which
+// caps its slots at 32.
 template <typename E, int D>
 constexpr int max_tokens() { return (std::is_same<E, float>::value && D == 128) ? 64 : 128; }
 
 template <typename E, int D>
 int tokens_per_split(const Shape &s) {
   const int64_t total = entry_tokens(s);
-  if (max_tokens<E, D>() >= 128 && s.G <= 8 && s.problems * ((total + 127) / 128) >= 512) return 128;
+  if (max_tokens<E, D>() >= 128 && s.G <= 8 && (total <= 128 || s.problems * ((total + 127) / 128) >= 512))
+    return 128;
   return 64;
 }
 
@@ -557,7 +572,7 @@ hipError_t launch_d(const AttnArgs &a, hipStream_t st) {
   else if (G <= 8) launch_t<E, KE, D, 8, PAGED>(a, st, tok);
   else launch_t<E, KE, D, 16, PAGED>(a, st, tok);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || a.splits == 1) return e;  // one split wrote the output itself
   const dim3 cgrid((unsigned)(a.s.problems * G));
   if (a.splits <= 16) hipLaunchKernelGGL((attn_decode_combine<E, D, 16>), cgrid, dim3(128), 0, st, a);
   else hipLaunchKernelGGL((attn_decode_combine<E, D, 32>), cgrid, dim3(128), 0, st, a);

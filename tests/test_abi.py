@@ -117,6 +117,23 @@ def test_fp8_kv_dtype_is_accepted_for_decode_and_prefill():
     assert hs.lib.hipsa_workspace_bytes(C.byref(_desc(dtype=3)), 2048, 64, 1) == hs.SIZE_MAX
 
 
+def test_one_split_when_it_covers_the_key_sequence():
+    """Decode splits a row's key sequence over workgroups of 64 or 128 tokens;
+    a sequence that one workgroup covers gets a single split (its workgroup
+    writes the output, no merge is launched).  Seen through the workspace size,
+    problems x splits x G x (d + 2) floats."""
+    import long_context_sparse_mask_amd as hs
+    # bf16, 128 listed tokens, 32 problems of G = 4: one split each
+    d = _desc(B=1, T=8192, T_cap=8192)
+    assert hs.lib.hipsa_workspace_bytes(C.byref(d), 128, 64, 1) == 8 * 1 * 4 * 130 * 4
+    # 256 tokens on few problems: 64-token splits
+    assert hs.lib.hipsa_workspace_bytes(C.byref(d), 256, 64, 1) == 8 * 4 * 4 * 130 * 4
+    # fp32 at d = 128 takes at most 64 tokens per split
+    d32 = _desc(B=1, T=8192, T_cap=8192, dtype=0)
+    assert hs.lib.hipsa_workspace_bytes(C.byref(d32), 64, 64, 1) == 8 * 1 * 4 * 130 * 4
+    assert hs.lib.hipsa_workspace_bytes(C.byref(d32), 128, 64, 1) == 8 * 2 * 4 * 130 * 4
+
+
 def test_misaligned_pointers_rejected():
     import long_context_sparse_mask_amd as hs
     odd = C.c_void_p(0x1008)

@@ -68,6 +68,9 @@ EDGE = {
     "group12_f32": dict(base="decode_32k", dtype="f32", Hq=12, Hkv=1, T=3000, k=512),
     # fp32 at d=128, batch 3
     "f32_d128_b3": dict(base="decode_32k", dtype="f32", B=3, Hq=4, Hkv=2, T=6000, k=1024),
+    # 128 listed tokens: one split workgroup writes the output, no merge launch
+    "one_split_bf16": dict(base="decode_32k", Hq=8, Hkv=2, Tq=2, T=3000, k=128),
+    "one_split_f32_d128": dict(base="decode_32k", dtype="f32", Hq=4, Hkv=2, T=3000, k=64),
 }
 
 
