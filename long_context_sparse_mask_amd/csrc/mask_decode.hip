@@ -202,15 +202,18 @@ __global__ __launch_bounds__(256) void mask_decode_kernel(MaskArgs a) {
   if (tid == 0) a.nnz[prob] = Kb;
 }
 
-// Pipelined variant for bf16 and K_b <= 64 (the decode workloads).  The
-// children of every current candidate are a superset of the next round's
-// candidates, so in round r waves 1-3 load and score all 4*K_b children of
-// C_r on the matrix cores while wave 0 ranks C_r with the keys the other
-// waves produced in round r-1.  The dependent memory latency then overlaps
-// the selection instead of following it, and a round needs one barrier.
-// Keys of the next round's candidates are looked up through `srcs` (the
-// child slot that holds each candidate's key).
-constexpr int kPipeMaxKb = 64;
+// Pipelined variant for bf16 and K_b <= 32.  The children of every current
+// candidate are a superset of the next round's candidates, so in round r
+// waves 1-3 load and score all 4*K_b children of C_r on the matrix cores
+// while wave 0 ranks C_r with the keys the other waves produced in round r-1.
+// The dependent memory latency then overlaps the selection instead of
+// following it, and a round needs one barrier.  Keys of the next round's
+// candidates are looked up through `srcs` (the child slot that holds each
+// candidate's key).  The speculation doubles the rows gathered per round,
+// which pays while a round's gather costs mostly latency (up to 128 rows);
+// at K_b = 64 (256 rows per round, and a 128-candidate ranking on one wave)
+// the plain kernel is faster.
+constexpr int kPipeMaxKb = 32;
 
 template <typename KE, int D, int GMAX, int TPW, typename RowOf>
 __device__ inline void score_children(const KE *Kbase, RowOf row_of, const uint4 *qa, int32_t Tp, int bk_shift,
@@ -384,10 +387,10 @@ void launch_pipe(const MaskArgs &a, hipStream_t st) {
   const int per = (tiles + 2) / 3;
   const dim3 grid((unsigned)a.s.problems), block(256);
   const size_t lds = page_lds(a);
+  static_assert(((4 * kPipeMaxKb + 15) / 16 + 2) / 3 <= 4, "child tiles per wave exceed the largest TPW");
   if (per <= 1) hipLaunchKernelGGL((mask_decode_pipe<KE, D, GMAX, 1, PAGED>), grid, block, lds, st, a);
   else if (per <= 2) hipLaunchKernelGGL((mask_decode_pipe<KE, D, GMAX, 2, PAGED>), grid, block, lds, st, a);
-  else if (per <= 4) hipLaunchKernelGGL((mask_decode_pipe<KE, D, GMAX, 4, PAGED>), grid, block, lds, st, a);
-  else hipLaunchKernelGGL((mask_decode_pipe<KE, D, GMAX, 8, PAGED>), grid, block, lds, st, a);
+  else hipLaunchKernelGGL((mask_decode_pipe<KE, D, GMAX, 4, PAGED>), grid, block, lds, st, a);
 }
 
 template <typename E, typename KE, int D, int GMAX, bool PAGED>
