@@ -202,7 +202,7 @@ __global__ __launch_bounds__(256) void mask_decode_kernel(MaskArgs a) {
   if (tid == 0) a.nnz[prob] = Kb;
 }
 
-// Pipelined variant for bf16 and K_b <= 32.  The children of every current
+// Pipelined variant for bf16 queries and keys, contiguous layout, K_b <= 32.  The children of every current
 // candidate are a superset of the next round's candidates, so in round r
 // waves 1-3 load and score all 4*K_b children of C_r on the matrix cores
 // while wave 0 ranks C_r with the keys the other waves produced in round r-1.
@@ -414,7 +414,10 @@ void launch_g(const MaskArgs &a, hipStream_t st) {
 template <typename E, typename KE, int D, bool PAGED>
 hipError_t launch_d(const MaskArgs &a, hipStream_t st) {
   const int G = a.s.G;
-  if constexpr (std::is_same<E, uint16_t>::value) {
+  // The pipelined kernel for bf16 keys in the contiguous layout only: with
+  // fp8 keys (half the bytes per row) or a paged cache the plain kernel
+  // measured faster per step at K_b = 32.
+  if constexpr (std::is_same<E, uint16_t>::value && std::is_same<KE, uint16_t>::value && !PAGED) {
     if (a.s.Kb <= kPipeMaxKb) {
       if (G <= 1) launch_pipe<KE, D, 1, PAGED>(a, st);
       else if (G <= 2) launch_pipe<KE, D, 2, PAGED>(a, st);
