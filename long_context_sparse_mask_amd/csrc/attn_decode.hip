@@ -457,26 +457,36 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(AttnArgs a) {
   }
 }
 
+// The merge's arguments, kept within one 64-byte line of the kernel-argument
+// segment: they are read with one scalar-cache miss, where the fields spread
+// over the full argument block took two or three misses one after another.
+struct CombineArgs {
+  const float *ws;
+  void *out;
+  int32_t S, G, Tq, Hkv, Hq;
+};
+
 // Merge the S partials of one (problem, query head): one workgroup of D lanes,
 // every load of a batch issued before any is used.  Per batch of CH partials
 // the maximum is a tree and the weights are independent exponentials, so the
 // dependent chain is one step per batch rather than one per partial.  CH is
 // 16 or 32, chosen so that up to 32 partials take one memory round trip.
 template <typename E, int D, int CH>
-__global__ __launch_bounds__(128) void attn_decode_combine(AttnArgs a) {
-  const Shape &s = a.s;
-  const int S = a.splits;
+__global__ __launch_bounds__(128) void attn_decode_combine(CombineArgs a) {
+  const int S = a.S;
+  const uint32_t G = (uint32_t)a.G;
   const uint32_t ph = xcd_swizzle(blockIdx.x, gridDim.x);
-  const uint32_t prob = ph / (uint32_t)s.G;
-  const int h = (int)(ph % (uint32_t)s.G);
-  const uint32_t Tq = (uint32_t)s.Tq, Hkv = (uint32_t)s.Hkv;
+  const uint32_t prob = ph / G;
+  const int h = (int)(ph % G);
+  const uint32_t Tq = (uint32_t)a.Tq, Hkv = (uint32_t)a.Hkv;
   const uint32_t i = prob % Tq, g = (prob / Tq) % Hkv, b = prob / (Tq * Hkv);
-  const int x = threadIdx.x;
-  if (x >= D) return;
-  const float *ph_ = a.ws + ((int64_t)prob * S * s.G + h) * (int64_t)(D + 2);
-  const int64_t sstride = (int64_t)s.G * (D + 2);
+  const int x = threadIdx.x;  // launched with D lanes
+  const float *ph_ = a.ws + ((int64_t)prob * S * G + h) * (int64_t)(D + 2);
+  const int64_t sstride = (int64_t)G * (D + 2);
+  E *out = reinterpret_cast<E *>(a.out) + ((int64_t)(b * (uint32_t)a.Hq + g * G + h) * Tq + i) * D;
   float M = -INFINITY, L = 0.f, acc = 0.f;
-  for (int s0 = 0; s0 < S; s0 += CH) {
+  int s0 = 0;
+  do {  // S >= 2: launched only for several splits
     float mm[CH], ll[CH], oo[CH];
 #pragma unroll
     for (int u = 0; u < CH; u++) {
@@ -505,9 +515,9 @@ __global__ __launch_bounds__(128) void attn_decode_combine(AttnArgs a) {
     L = fmaf(L, c0, Lb);
     acc = fmaf(acc, c0, Ab);
     M = Mn;
-  }
+    s0 += CH;
+  } while (s0 < S);
   const float v = L > 0.f ? acc / L : 0.f;
-  E *out = reinterpret_cast<E *>(a.out) + ((int64_t)(b * s.Hq + g * s.G + h) * Tq + i) * D;
   store_elem(out + x, v);
 }
 
@@ -574,8 +584,9 @@ hipError_t launch_d(const AttnArgs &a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;  // one split wrote the output itself
   const dim3 cgrid((unsigned)(a.s.problems * G));
-  if (a.splits <= 16) hipLaunchKernelGGL((attn_decode_combine<E, D, 16>), cgrid, dim3(128), 0, st, a);
-  else hipLaunchKernelGGL((attn_decode_combine<E, D, 32>), cgrid, dim3(128), 0, st, a);
+  const CombineArgs c{a.ws, a.out, a.splits, a.s.G, (int32_t)a.s.Tq, (int32_t)a.s.Hkv, (int32_t)a.s.Hq};
+  if (a.splits <= 16) hipLaunchKernelGGL((attn_decode_combine<E, D, 16>), cgrid, dim3(D), 0, st, c);
+  else hipLaunchKernelGGL((attn_decode_combine<E, D, 32>), cgrid, dim3(D), 0, st, c);
   return hipGetLastError();
 }
 

@@ -140,10 +140,12 @@ __device__ inline void stage_pages(const Pages &pg, uint32_t b, int32_t Tp, int3
 // problem's mask, its split workgroups and its merge all run on the same XCD
 // (for P a multiple of 8; otherwise on neighbouring ones), and the list and
 // the partials are read on the XCD that wrote them.
+// XCD j's range starts at j*q + min(j, r): the first r XCDs take q + 1 items.
+// Written without a branch, so the scalar code around it stays one block.
 __device__ inline uint32_t xcd_swizzle(uint32_t x, uint32_t P) {
   constexpr uint32_t kXcd = 8;
   const uint32_t q = P / kXcd, r = P % kXcd, xcd = x % kXcd, i = x / kXcd;
-  return xcd < r ? xcd * (q + 1) + i : r * (q + 1) + (xcd - r) * q + i;
+  return xcd * q + min(xcd, r) + i;
 }
 
 
