@@ -457,33 +457,30 @@ __global__ __launch_bounds__(256) void attn_decode_mfma(AttnArgs a) {
   }
 }
 
-// The merge's arguments, kept within one 64-byte line of the kernel-argument
-// segment: they are read with one scalar-cache miss, where the fields spread
-// over the full argument block took two or three misses one after another.
-struct CombineArgs {
-  const float *ws;
-  void *out;
-  int32_t S, G, Tq, Hkv, Hq;
-};
-
 // Merge the S partials of one (problem, query head): one workgroup of D lanes,
 // every load of a batch issued before any is used.  Per batch of CH partials
 // the maximum is a tree and the weights are independent exponentials, so the
 // dependent chain is one step per batch rather than one per partial.  CH is
 // 16 or 32, chosen so that up to 32 partials take one memory round trip.
+// The merge takes its arguments one by one, 36 bytes in all: the library is
+// built with kernel-argument preloading (gfx950's dispatcher writes the first
+// argument dwords into scalar registers before the first instruction), so
+// they need no scalar-cache read.  Fields spread over the full argument block
+// took two or three cache misses one after another.
 template <typename E, int D, int CH>
-__global__ __launch_bounds__(128) void attn_decode_combine(CombineArgs a) {
-  const int S = a.S;
-  const uint32_t G = (uint32_t)a.G;
+__global__ __launch_bounds__(128) void attn_decode_combine(const float *ws, void *outp, int32_t S_,
+                                                           int32_t G_, int32_t Tq_, int32_t Hkv_, int32_t Hq_) {
+  const int S = S_;
+  const uint32_t G = (uint32_t)G_;
   const uint32_t ph = xcd_swizzle(blockIdx.x, gridDim.x);
   const uint32_t prob = ph / G;
   const int h = (int)(ph % G);
-  const uint32_t Tq = (uint32_t)a.Tq, Hkv = (uint32_t)a.Hkv;
+  const uint32_t Tq = (uint32_t)Tq_, Hkv = (uint32_t)Hkv_;
   const uint32_t i = prob % Tq, g = (prob / Tq) % Hkv, b = prob / (Tq * Hkv);
   const int x = threadIdx.x;  // launched with D lanes
-  const float *ph_ = a.ws + ((int64_t)prob * S * G + h) * (int64_t)(D + 2);
+  const float *ph_ = ws + ((int64_t)prob * S * G + h) * (int64_t)(D + 2);
   const int64_t sstride = (int64_t)G * (D + 2);
-  E *out = reinterpret_cast<E *>(a.out) + ((int64_t)(b * (uint32_t)a.Hq + g * G + h) * Tq + i) * D;
+  E *out = reinterpret_cast<E *>(outp) + ((int64_t)(b * (uint32_t)Hq_ + g * G + h) * Tq + i) * D;
   float M = -INFINITY, L = 0.f, acc = 0.f;
   int s0 = 0;
   do {  // S >= 2: launched only for several splits
@@ -584,9 +581,11 @@ hipError_t launch_d(const AttnArgs &a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;  // one split wrote the output itself
   const dim3 cgrid((unsigned)(a.s.problems * G));
-  const CombineArgs c{a.ws, a.out, a.splits, a.s.G, (int32_t)a.s.Tq, (int32_t)a.s.Hkv, (int32_t)a.s.Hq};
-  if (a.splits <= 16) hipLaunchKernelGGL((attn_decode_combine<E, D, 16>), cgrid, dim3(D), 0, st, c);
-  else hipLaunchKernelGGL((attn_decode_combine<E, D, 32>), cgrid, dim3(D), 0, st, c);
+  const int32_t Tq = (int32_t)a.s.Tq, Hkv = (int32_t)a.s.Hkv, Hq = (int32_t)a.s.Hq;
+  if (a.splits <= 16)
+    hipLaunchKernelGGL((attn_decode_combine<E, D, 16>), cgrid, dim3(D), 0, st, a.ws, a.out, a.splits, a.s.G, Tq, Hkv, Hq);
+  else
+    hipLaunchKernelGGL((attn_decode_combine<E, D, 32>), cgrid, dim3(D), 0, st, a.ws, a.out, a.splits, a.s.G, Tq, Hkv, Hq);
   return hipGetLastError();
 }
 
