@@ -29,7 +29,7 @@ from parity_util import compare_attention, compare_masks
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 48
+N_CASES = 64
 
 
 def draw(seed):
