@@ -19,9 +19,12 @@
 // The four waves are merged with log-sum-exp weights through LDS after one
 // barrier, and the workgroup writes (max, sum, output) per head to the
 // workspace.  A second kernel merges the S partials of each (problem, head)
-// and writes the output.  (Merging inside the split kernel through a
-// device-scope fence and an arrival counter measured slower on gfx950: the
-// fences serialise across workgroups.)
+// and writes the output; with a single split the split workgroup writes the
+// normalised output itself and no merge is launched.  (Merging inside the
+// split kernel through a device-scope fence and an arrival counter measured
+// slower on gfx950: the fences serialise across workgroups.)  Workgroups map
+// to (problem, split) and (problem, head) through xcd_swizzle(), so a
+// problem's splits and merge run on the XCD that ran its mask.
 //
 // With a paged KV cache each lane also reads the page of its slot's token
 // from the table (one more dependent load, cached: a block's tokens share a
