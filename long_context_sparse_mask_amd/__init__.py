@@ -101,10 +101,42 @@ def _dtype_code(q: torch.Tensor, K: torch.Tensor) -> int:
 
 
 def make_desc(q: torch.Tensor, K: torch.Tensor, T: int | None = None, causal: bool = True) -> Desc:
+    if q.dim() != 4 or K.dim() != 4:
+        raise ValueError("q must be [B, Hq, Tq, d] and K [B, Hkv, T_cap, d]")
     B, Hq, Tq, d = q.shape
-    _, Hkv, T_cap, _ = K.shape
+    Bk, Hkv, T_cap, dk = K.shape
+    if Bk != B or dk != d:
+        raise ValueError(f"K {tuple(K.shape)} does not match q {tuple(q.shape)} in batch or head dim")
+    if K.device != q.device:
+        raise ValueError("q and K must be on the same device")
     return Desc(B, Hq, Hkv, Tq, T_cap if T is None else T, T_cap, d, int(bool(causal)),
                 _dtype_code(q, K))
+
+
+def _check_v(K: torch.Tensor, V: torch.Tensor):
+    """V must match K exactly (shape, element type, device): the kernels read
+    both through one row layout."""
+    if V.dtype != K.dtype or V.shape != K.shape or V.device != K.device:
+        raise ValueError(f"V {tuple(V.shape)} {V.dtype} must have K's shape, dtype and device "
+                         f"({tuple(K.shape)} {K.dtype})")
+
+
+def _check_out(out: torch.Tensor, q: torch.Tensor):
+    """A caller-supplied output must be exactly what the kernels write: q's
+    shape, element type and device (a smaller buffer would be overrun)."""
+    if out.shape != q.shape or out.dtype != q.dtype or out.device != q.device:
+        raise ValueError(f"out {tuple(out.shape)} {out.dtype} on {out.device} must have q's shape, "
+                         f"dtype and device ({tuple(q.shape)} {q.dtype} on {q.device})")
+
+
+def _check_lists(indices: torch.Tensor, nnz: torch.Tensor, desc: Desc, nqb: int, kb: int,
+                 dev: torch.device):
+    if tuple(indices.shape) != (desc.B, desc.Hkv, nqb, kb) or indices.dtype != torch.int32:
+        raise ValueError("indices must be int32 [B, Hkv, NQB, k/block_k]")
+    if tuple(nnz.shape) != (desc.B, desc.Hkv, nqb) or nnz.dtype != torch.int32:
+        raise ValueError("nnz must be int32 [B, Hkv, NQB]")
+    if indices.device != dev or nnz.device != dev:
+        raise ValueError("indices and nnz must be on q's device")
 
 
 def _stream(dev: torch.device, stream) -> int:
@@ -140,10 +172,7 @@ def hip_mask_estimate(q, K, k: int, block_k: int, block_q: int = 1, *, T=None, c
         indices = torch.empty((desc.B, desc.Hkv, nqb, kb), dtype=torch.int32, device=q.device)
     if nnz is None:
         nnz = torch.empty((desc.B, desc.Hkv, nqb), dtype=torch.int32, device=q.device)
-    if tuple(indices.shape) != (desc.B, desc.Hkv, nqb, kb) or indices.dtype != torch.int32:
-        raise ValueError("indices must be int32 [B, Hkv, NQB, k/block_k]")
-    if tuple(nnz.shape) != (desc.B, desc.Hkv, nqb) or nnz.dtype != torch.int32:
-        raise ValueError("nnz must be int32 [B, Hkv, NQB]")
+    _check_lists(indices, nnz, desc, nqb, kb, q.device)
     if desc.B * desc.Tq == 0:
         return indices, nnz
     _check(lib.hip_mask_estimate(C.byref(desc), _dev_ptr(q, "q"), _dev_ptr(K, "K"), k, block_k,
@@ -157,18 +186,13 @@ def hip_sparse_attn(q, K, V, indices, nnz, k: int, block_k: int, block_q: int = 
     """Softmax attention of every query row over the tokens of its listed key
     blocks.  Returns out [B,Hq,Tq,d] in q's dtype."""
     desc = make_desc(q, K, T, causal)
-    if K.dtype != V.dtype:
-        raise TypeError("K and V must share a dtype")
-    if V.shape != K.shape:
-        raise ValueError("V must have K's shape")
+    _check_v(K, V)
     nqb = -(-desc.Tq // block_q)
     kb = k // block_k if block_k > 0 else 0
-    if tuple(indices.shape) != (desc.B, desc.Hkv, nqb, kb) or indices.dtype != torch.int32:
-        raise ValueError("indices must be int32 [B, Hkv, NQB, k/block_k]")
-    if tuple(nnz.shape) != (desc.B, desc.Hkv, nqb) or nnz.dtype != torch.int32:
-        raise ValueError("nnz must be int32 [B, Hkv, NQB]")
+    _check_lists(indices, nnz, desc, nqb, kb, q.device)
     if out is None:
         out = torch.empty_like(q)
+    _check_out(out, q)
     if desc.B * desc.Tq == 0:
         return out
     need = hipsa_workspace_bytes(q, K, k, block_k, block_q, T=T, causal=causal)
@@ -186,12 +210,16 @@ def hip_sparse_attn(q, K, V, indices, nnz, k: int, block_k: int, block_q: int = 
 # ------------------------------------------------------------------ paged KV cache
 
 def _paged_desc(q, K_pages, block_table, T, causal):
-    if K_pages.dim() != 4 or block_table.dim() != 2 or block_table.dtype != torch.int32:
-        raise ValueError("K, V must be [num_pages, Hkv, page_size, d]; block_table int32 [B, max_pages]")
+    if (q.dim() != 4 or K_pages.dim() != 4 or block_table.dim() != 2
+            or block_table.dtype != torch.int32):
+        raise ValueError("q must be [B, Hq, Tq, d], K and V [num_pages, Hkv, page_size, d] and "
+                         "block_table int32 [B, max_pages]")
     B, Hq, Tq, d = q.shape
     num_pages, Hkv, page_size, dk = K_pages.shape
     if dk != d or block_table.shape[0] != B:
         raise ValueError("K's head dim or block_table's batch does not match q")
+    if K_pages.device != q.device or block_table.device != q.device:
+        raise ValueError("q, K and block_table must be on the same device")
     desc = Desc(B, Hq, Hkv, Tq, T, T, d, int(bool(causal)), _dtype_code(q, K_pages))
     pages = Pages(_dev_ptr(block_table, "block_table"), block_table.shape[1], page_size, num_pages)
     return desc, pages
@@ -207,10 +235,7 @@ def hip_mask_estimate_paged(q, K_pages, block_table, T: int, k: int, block_k: in
         indices = torch.empty((desc.B, desc.Hkv, nqb, kb), dtype=torch.int32, device=q.device)
     if nnz is None:
         nnz = torch.empty((desc.B, desc.Hkv, nqb), dtype=torch.int32, device=q.device)
-    if tuple(indices.shape) != (desc.B, desc.Hkv, nqb, kb) or indices.dtype != torch.int32:
-        raise ValueError("indices must be int32 [B, Hkv, NQB, k/block_k]")
-    if tuple(nnz.shape) != (desc.B, desc.Hkv, nqb) or nnz.dtype != torch.int32:
-        raise ValueError("nnz must be int32 [B, Hkv, NQB]")
+    _check_lists(indices, nnz, desc, nqb, kb, q.device)
     if desc.B * desc.Tq == 0:
         return indices, nnz
     _check(lib.hip_mask_estimate_paged(C.byref(desc), C.byref(pages), _dev_ptr(q, "q"),
@@ -225,16 +250,13 @@ def hip_sparse_attn_paged(q, K_pages, V_pages, block_table, indices, nnz, T: int
                           stream=None):
     """hip_sparse_attn on a paged KV cache.  Returns out [B,Hq,Tq,d] in q's dtype."""
     desc, pages = _paged_desc(q, K_pages, block_table, T, causal)
-    if K_pages.dtype != V_pages.dtype or V_pages.shape != K_pages.shape:
-        raise ValueError("V must have K's shape and dtype")
+    _check_v(K_pages, V_pages)
     nqb = -(-desc.Tq // block_q)
     kb = k // block_k if block_k > 0 else 0
-    if tuple(indices.shape) != (desc.B, desc.Hkv, nqb, kb) or indices.dtype != torch.int32:
-        raise ValueError("indices must be int32 [B, Hkv, NQB, k/block_k]")
-    if tuple(nnz.shape) != (desc.B, desc.Hkv, nqb) or nnz.dtype != torch.int32:
-        raise ValueError("nnz must be int32 [B, Hkv, NQB]")
+    _check_lists(indices, nnz, desc, nqb, kb, q.device)
     if out is None:
         out = torch.empty_like(q)
+    _check_out(out, q)
     if desc.B * desc.Tq == 0:
         return out
     need = lib.hipsa_workspace_bytes(C.byref(desc), k, block_k, block_q)
@@ -284,10 +306,7 @@ def hip_mask_estimate_ex(q, K, k: int, block_k: int, block_q: int = 1, *, T=None
         indices = torch.empty((desc.B, desc.Hkv, nqb, kb), dtype=torch.int32, device=q.device)
     if nnz is None:
         nnz = torch.empty((desc.B, desc.Hkv, nqb), dtype=torch.int32, device=q.device)
-    if tuple(indices.shape) != (desc.B, desc.Hkv, nqb, kb) or indices.dtype != torch.int32:
-        raise ValueError("indices must be int32 [B, Hkv, NQB, k/block_k]")
-    if tuple(nnz.shape) != (desc.B, desc.Hkv, nqb) or nnz.dtype != torch.int32:
-        raise ValueError("nnz must be int32 [B, Hkv, NQB]")
+    _check_lists(indices, nnz, desc, nqb, kb, q.device)
     if desc.B * desc.Tq == 0:
         return indices, nnz
     _check(lib.hip_mask_estimate_ex(C.byref(desc), C.byref(ext), _dev_ptr(q, "q"), _dev_ptr(K, "K"),
@@ -302,16 +321,13 @@ def hip_sparse_attn_ex(q, K, V, indices, nnz, k: int, block_k: int, block_q: int
     """hip_sparse_attn over the dense part and the listed blocks, optionally on a
     paged KV cache.  Returns out [B,Hq,Tq,d] in q's dtype."""
     desc, ext, _pages = _ext_desc(q, K, T, causal, sink, window, block_table)
-    if K.dtype != V.dtype or V.shape != K.shape:
-        raise ValueError("V must have K's shape and dtype")
+    _check_v(K, V)
     nqb = -(-desc.Tq // block_q)
     kb = k // block_k if block_k > 0 else 0
-    if tuple(indices.shape) != (desc.B, desc.Hkv, nqb, kb) or indices.dtype != torch.int32:
-        raise ValueError("indices must be int32 [B, Hkv, NQB, k/block_k]")
-    if tuple(nnz.shape) != (desc.B, desc.Hkv, nqb) or nnz.dtype != torch.int32:
-        raise ValueError("nnz must be int32 [B, Hkv, NQB]")
+    _check_lists(indices, nnz, desc, nqb, kb, q.device)
     if out is None:
         out = torch.empty_like(q)
+    _check_out(out, q)
     if desc.B * desc.Tq == 0:
         return out
     need = lib.hipsa_workspace_bytes_ex(C.byref(desc), C.byref(ext), k, block_k, block_q)

@@ -282,3 +282,66 @@ def test_binding_fails_loudly_without_the_library(tmp_path):
     code = "import runpy; runpy.run_path(%r, run_name='check')" % str(pkg / "build.py")
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+def _cpu(shape, dtype=None):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.bfloat16)
+
+
+@pytest.mark.parametrize("case", ["K_batch", "K_dim", "V_shape", "V_dtype", "out_shape", "out_dtype",
+                                  "idx_shape", "nnz_dtype", "q_rank"])
+def test_binding_rejects_mismatched_tensors(case):
+    """Shape, element-type and device mismatches are caught in the binding
+    before any pointer reaches the library: a K with another batch or head
+    dim, a V unlike K, or a caller's `out` unlike q would otherwise send the
+    kernels past the end of an allocation."""
+    import torch
+    import long_context_sparse_mask_amd as hs
+    B, Hq, Hkv, T, d = 2, 8, 2, 256, 128
+    q, K, V = _cpu((B, Hq, 1, d)), _cpu((B, Hkv, T, d)), _cpu((B, Hkv, T, d))
+    idx = torch.zeros((B, Hkv, 1, 2), dtype=torch.int32)
+    nnz = torch.zeros((B, Hkv, 1), dtype=torch.int32)
+    out = _cpu((B, Hq, 1, d))
+    if case == "K_batch":
+        K = _cpu((B + 1, Hkv, T, d))
+    elif case == "K_dim":
+        K = _cpu((B, Hkv, T, 64))
+    elif case == "V_shape":
+        V = _cpu((B, Hkv, T - 1, d))
+    elif case == "V_dtype":
+        V = _cpu((B, Hkv, T, d), torch.float8_e5m2)
+    elif case == "out_shape":
+        out = _cpu((B, Hq, 1, 64))
+    elif case == "out_dtype":
+        out = _cpu((B, Hq, 1, d), torch.float32)
+    elif case == "idx_shape":
+        idx = torch.zeros((B, Hkv, 1, 3), dtype=torch.int32)
+    elif case == "nnz_dtype":
+        nnz = torch.zeros((B, Hkv, 1), dtype=torch.int64)
+    elif case == "q_rank":
+        q = _cpu((B, Hq, d))
+    with pytest.raises(ValueError):
+        hs.hip_sparse_attn(q, K, V, idx, nnz, 128, 64, 1, out=out)
+    with pytest.raises(ValueError):
+        hs.hip_sparse_attn_ex(q, K, V, idx, nnz, 128, 64, 1, out=out, sink=64)
+    if case in ("K_batch", "K_dim", "idx_shape", "nnz_dtype", "q_rank"):
+        with pytest.raises(ValueError):
+            hs.hip_mask_estimate(q, K, 128, 64, 1, indices=idx, nnz=nnz)
+
+
+def test_binding_rejects_mismatched_paged_tensors():
+    import torch
+    import long_context_sparse_mask_amd as hs
+    B, Hq, Hkv, d, ps = 2, 8, 2, 128, 64
+    q = _cpu((B, Hq, 1, d))
+    Kp, Vp = _cpu((8, Hkv, ps, d)), _cpu((8, Hkv, ps, d))
+    table = torch.zeros((B, 4), dtype=torch.int32)
+    idx = torch.zeros((B, Hkv, 1, 2), dtype=torch.int32)
+    nnz = torch.zeros((B, Hkv, 1), dtype=torch.int32)
+    with pytest.raises(ValueError):  # V pool unlike K's
+        hs.hip_sparse_attn_paged(q, Kp, _cpu((8, Hkv, ps, 64)), table, idx, nnz, 256, 128, 64)
+    with pytest.raises(ValueError):  # out unlike q
+        hs.hip_sparse_attn_paged(q, Kp, Vp, table, idx, nnz, 256, 128, 64, out=_cpu((B, Hq, 2, d)))
+    with pytest.raises(ValueError):  # table for another batch
+        hs.hip_mask_estimate_paged(q, Kp, torch.zeros((B + 1, 4), dtype=torch.int32), 256, 128, 64)
