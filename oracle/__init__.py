@@ -66,6 +66,8 @@ def load(path: str | None = None):
     lib.or_attn_all.argtypes = [C.POINTER(Shape), P, P, P, P, P, P, I32]
     for f in (lib.or_mask_one, lib.or_mask_all, lib.or_attn_row, lib.or_attn_all):
         f.restype = C.c_int
+    lib.or_mask_reach.argtypes = [C.POINTER(Shape), P, P, I64, I64, I64, C.c_double, P, P, I64, I64]
+    lib.or_mask_reach.restype = C.c_int64
     lib.or_e5m2_value.argtypes = [C.c_uint8]
     lib.or_e5m2_value.restype = C.c_double
     if path is None:
@@ -200,3 +202,29 @@ def attn_row(q, K, V, indices, nnz, b, h, i, *, T, k, block_k, block_q, causal=1
                          nnz.ctypes.data, b, h, i, out.ctypes.data)
     assert rc == 0
     return out
+
+
+def mask_reach(q, K, b, g, qb, *, T, k, block_k, block_q, causal=1, sink=0, window=0, tol=1e-4,
+               target=None, max_leaves=256, max_nodes=200000, lib=None):
+    """Final lists the search reaches when every candidate score may move by
+    (tol/2)*|score| (near ties at a cut resolved either way).
+
+    Without `target`: (count, lists) with every distinct reachable list
+    (ascending block ids, [count, K_b]; at most max_leaves stored).  With
+    `target` (K_b ascending ids): (1 or 0, lists) -- whether the target is
+    reachable.  Raises if the node budget runs out."""
+    lib = lib or load()
+    s = shape(q, K, T=T, k=k, block_k=block_k, block_q=block_q, causal=causal, sink=sink,
+              window=window)
+    kb = k // block_k
+    leaves = np.full((max_leaves, kb), -1, np.int32)
+    tgt = None
+    if target is not None:
+        tgt = np.ascontiguousarray(target, np.int32)
+        assert tgt.shape == (kb,)
+    n = lib.or_mask_reach(C.byref(s), _ptr(q), _ptr(K), b, g, qb, tol,
+                          None if tgt is None else tgt.ctypes.data, leaves.ctypes.data, max_leaves,
+                          max_nodes)
+    if n < 0:
+        raise RuntimeError(f"or_mask_reach failed ({n}: {'node budget' if n == -1 else 'memory'})")
+    return int(n), leaves[:min(n, max_leaves)]

@@ -59,6 +59,11 @@
  *     union of the dense blocks and the listed ones (a listed id inside a
  *     dense range adds nothing).
  *
+ * or_mask_reach (near-tie-tolerant search) follows the same steps but lets
+ * every score move by half a relative tolerance, branching at each cut the
+ * tolerance makes ambiguous; it lists every final result the search can then
+ * reach.  A GPU that ranks fp32 scores may legitimately take any of them.
+ *
  * Layouts (contiguous, head-major): q [B,Hq,Tq,d]; K, V [B,Hkv,T_cap,d] with
  * rows 0..T-1 valid; indices [B,Hkv,NQB,K_b] (ascending, -1 past nnz);
  * nnz [B,Hkv,NQB]; query head h belongs to KV head h / (Hq/Hkv).
@@ -149,6 +154,51 @@ typedef struct {
   double score;
 } cand_t;
 
+/* R2: the K_b initial chunks of the M searched blocks from block `first`. */
+static void initial_chunks(int64_t first, int64_t M, int64_t Kb, int64_t *ca, int64_t *ce) {
+  for (int64_t i = 0; i < Kb; i++) {
+    ca[i] = first + i * M / Kb;
+    ce[i] = first + (i + 1) * M / Kb;
+  }
+}
+
+/* R3: the candidates of a round, the halves of every kept chunk of >= 2
+ * blocks and every one-block chunk unchanged; returns their number. */
+static int64_t halve_all(const int64_t *ca, const int64_t *ce, int64_t Kb, int64_t *a, int64_t *e) {
+  int64_t n = 0;
+  for (int64_t i = 0; i < Kb; i++) {
+    if (ce[i] - ca[i] >= 2) {
+      int64_t m = ca[i] + (ce[i] - ca[i]) / 2;
+      a[n] = ca[i]; e[n] = m; n++;
+      a[n] = m; e[n] = ce[i]; n++;
+    } else {
+      a[n] = ca[i]; e[n] = ce[i]; n++;
+    }
+  }
+  return n;
+}
+
+/* R4, R5: the score of candidate chunk [a, e) (in blocks) for the query
+ * rows [r0, r1) of KV head g: the largest q . K[t] over the group's query
+ * heads and the rows allowed to vote, t the chunk's centre token (*t_out). */
+static double chunk_score(const or_shape *s, const void *q, const void *K, int64_t b, int64_t g,
+                          int64_t r0, int64_t r1, int64_t Tp, int64_t a, int64_t e,
+                          int64_t *t_out) {
+  const int64_t G = s->Hq / s->Hkv;
+  int64_t lo = a * s->block_k;
+  int64_t hi = e * s->block_k < Tp ? e * s->block_k : Tp;
+  int64_t t = (lo + hi) / 2;
+  double best = -INFINITY;
+  for (int64_t h = g * G; h < (g + 1) * G; h++)
+    for (int64_t i = r0; i < r1; i++) {
+      if (s->causal && position(s, i) < t) continue;
+      double v = dot_qk(s, q, K, b, h, i, g, t);
+      if (v > best) best = v;
+    }
+  *t_out = t;
+  return best;
+}
+
 /* R6: true when x ranks before y. */
 static int ranks_before(const cand_t *x, const cand_t *y) {
   if (x->score != y->score) return x->score > y->score;
@@ -162,7 +212,6 @@ static int cmp_i32(const void *x, const void *y) {
 
 int or_mask_one(const or_shape *s, const void *q, const void *K, int64_t b, int64_t g, int64_t qb,
                 int32_t *idx, int32_t *nnz, double *margin, or_trace *tr) {
-  const int64_t G = s->Hq / s->Hkv;
   const int64_t Kb = s->k / s->block_k;
   int64_t r0, r1;
   const int64_t Tp = rows_and_tp(s, qb, &r0, &r1);
@@ -183,12 +232,13 @@ int or_mask_one(const or_shape *s, const void *q, const void *K, int64_t b, int6
 
   /* Step 1: uniform split into K_b chunks (R2). */
   int64_t *ca = malloc(sizeof(int64_t) * Kb), *ce = malloc(sizeof(int64_t) * Kb);
+  int64_t *ha = malloc(sizeof(int64_t) * 2 * Kb), *he = malloc(sizeof(int64_t) * 2 * Kb);
   cand_t *cand = malloc(sizeof(cand_t) * 2 * Kb);
-  if (!ca || !ce || !cand) { free(ca); free(ce); free(cand); return -1; }
-  for (int64_t i = 0; i < Kb; i++) {
-    ca[i] = lo + i * M / Kb;
-    ce[i] = lo + (i + 1) * M / Kb;
+  if (!ca || !ce || !ha || !he || !cand) {
+    free(ca); free(ce); free(ha); free(he); free(cand);
+    return -1;
   }
+  initial_chunks(lo, M, Kb, ca, ce);
   double min_rel = INFINITY;
   int32_t round = 0;
 
@@ -198,32 +248,12 @@ int or_mask_one(const or_shape *s, const void *q, const void *K, int64_t b, int6
     if (!wide) break; /* Step 4 exit: every chunk is a single block */
 
     /* Step 2: halve every chunk (R3). */
-    int64_t n = 0;
-    for (int64_t i = 0; i < Kb; i++) {
-      if (ce[i] - ca[i] >= 2) {
-        int64_t m = ca[i] + (ce[i] - ca[i]) / 2;
-        cand[n].a = ca[i]; cand[n].e = m; n++;
-        cand[n].a = m; cand[n].e = ce[i]; n++;
-      } else {
-        cand[n].a = ca[i]; cand[n].e = ce[i]; n++;
-      }
-    }
+    const int64_t n = halve_all(ca, ce, Kb, ha, he);
+    for (int64_t c = 0; c < n; c++) { cand[c].a = ha[c]; cand[c].e = he[c]; }
 
     /* Step 3: score each candidate by its centre key (R4, R5). */
-    for (int64_t c = 0; c < n; c++) {
-      int64_t lo = cand[c].a * s->block_k;
-      int64_t hi = cand[c].e * s->block_k < Tp ? cand[c].e * s->block_k : Tp;
-      int64_t t = (lo + hi) / 2;
-      double best = -INFINITY;
-      for (int64_t h = g * G; h < (g + 1) * G; h++)
-        for (int64_t i = r0; i < r1; i++) {
-          if (s->causal && position(s, i) < t) continue;
-          double v = dot_qk(s, q, K, b, h, i, g, t);
-          if (v > best) best = v;
-        }
-      cand[c].t = t;
-      cand[c].score = best;
-    }
+    for (int64_t c = 0; c < n; c++)
+      cand[c].score = chunk_score(s, q, K, b, g, r0, r1, Tp, cand[c].a, cand[c].e, &cand[c].t);
 
     /* Step 4: global top-K_b by (score desc, start asc): a stable insertion sort. */
     for (int64_t c = 1; c < n; c++) {
@@ -261,7 +291,7 @@ int or_mask_one(const or_shape *s, const void *q, const void *K, int64_t b, int6
   qsort(idx, (size_t)Kb, sizeof(int32_t), cmp_i32);
   *nnz = (int32_t)Kb;
   *margin = min_rel;
-  free(ca); free(ce); free(cand);
+  free(ca); free(ce); free(ha); free(he); free(cand);
   return 0;
 }
 
@@ -276,6 +306,190 @@ int or_mask_all(const or_shape *s, const void *q, const void *K, int32_t *indice
     err |= or_mask_one(s, q, K, b, g, qb, indices + p * Kb, nnz + p, margin + p, NULL);
   }
   return err ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------------
+ * Near-tie-tolerant search (checks results where the cut is ambiguous).
+ *
+ * The search is a discrete decision on floating-point scores: when two
+ * candidates at a top-k cut score within rounding of each other, a GPU that
+ * accumulates in fp32 may keep the other one and, from there, follow another
+ * subtree (rebuttal page, reviewer RsGC, Q2: the kept set of each round
+ * decides the next round's candidates).  This enumerates every final list
+ * the search can reach when each candidate's score may move by up to
+ * delta = (tol / 2) * |score|: at every round, a kept set S of K_b
+ * candidates is allowed when
+ *     min over S of (score + delta) >= max over the rest of (score - delta).
+ * At a round whose relative cut gap (the margin of or_mask_one) is at least
+ * tol, only the exact top-K_b satisfies this (up to exact equality of the
+ * two bounds), so a problem without near-ties reaches exactly the list
+ * or_mask_one returns.
+ *
+ * With `target` (K_b ascending block ids), only paths that can still end at
+ * the target are followed: a candidate holding a target block must be kept.
+ * Returns the number of distinct final lists reached (1 or 0 with a target),
+ * storing up to max_leaves of them (K_b ids each, ascending) in `leaves`
+ * (may be NULL); -1 if more than max_nodes kept sets were visited, -2 on an
+ * allocation failure.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  const or_shape *s;
+  const void *q, *K;
+  int64_t b, g, r0, r1, Tp, Kb;
+  double tol;
+  const int32_t *target;
+  int32_t *leaves;
+  int64_t max_leaves, n_leaves, n_found;
+  int64_t nodes, max_nodes;
+  int32_t *leaf_buf; /* K_b scratch */
+  int status;
+} reach_ctx;
+
+static int contains_target(const reach_ctx *c, int64_t a, int64_t e) {
+  for (int64_t j = 0; j < c->Kb; j++)
+    if (c->target[j] >= a && c->target[j] < e) return 1;
+  return 0;
+}
+
+static void reach_leaf(reach_ctx *c, const int64_t *ca) {
+  for (int64_t i = 0; i < c->Kb; i++) c->leaf_buf[i] = (int32_t)ca[i];
+  qsort(c->leaf_buf, (size_t)c->Kb, sizeof(int32_t), cmp_i32);
+  if (c->target) {
+    if (c->n_found == 0 && memcmp(c->leaf_buf, c->target, sizeof(int32_t) * c->Kb) == 0) {
+      c->n_found = 1;
+      if (c->leaves && c->max_leaves > 0) memcpy(c->leaves, c->leaf_buf, sizeof(int32_t) * c->Kb);
+    }
+    return;
+  }
+  /* distinct lists only: a list is compared with the stored ones, so past
+   * max_leaves stored lists the count becomes an upper bound */
+  const int64_t stored = c->n_found < c->max_leaves ? c->n_found : c->max_leaves;
+  for (int64_t l = 0; c->leaves && l < stored; l++)
+    if (memcmp(c->leaves + l * c->Kb, c->leaf_buf, sizeof(int32_t) * c->Kb) == 0) return;
+  if (c->leaves && c->n_found < c->max_leaves)
+    memcpy(c->leaves + c->n_found * c->Kb, c->leaf_buf, sizeof(int32_t) * c->Kb);
+  c->n_found++;
+}
+
+/* Visits every allowed kept set of the round whose chunks are (ca, ce). */
+static void reach_round(reach_ctx *c, const int64_t *ca, const int64_t *ce) {
+  const int64_t Kb = c->Kb;
+  if (c->status || (c->target && c->n_found)) return;
+  int wide = 0;
+  for (int64_t i = 0; i < Kb; i++) wide |= (ce[i] - ca[i] >= 2);
+  if (!wide) { reach_leaf(c, ca); return; }
+  if (++c->nodes > c->max_nodes) { c->status = -1; return; }
+
+  /* halve (R3) and score (R4, R5) every chunk */
+  int64_t n = 0;
+  int64_t *a = malloc(sizeof(int64_t) * 2 * Kb), *e = malloc(sizeof(int64_t) * 2 * Kb);
+  double *lo = malloc(sizeof(double) * 2 * Kb), *hi = malloc(sizeof(double) * 2 * Kb);
+  double *th = malloc(sizeof(double) * 4 * Kb);
+  char *req = malloc((size_t)(2 * Kb)), *in = malloc((size_t)(2 * Kb));
+  int64_t *pool = malloc(sizeof(int64_t) * 2 * Kb), *pick = malloc(sizeof(int64_t) * 2 * Kb);
+  int64_t *na = malloc(sizeof(int64_t) * Kb), *ne = malloc(sizeof(int64_t) * Kb);
+  /* kept sets already visited this round (as candidate membership strings) */
+  int64_t seen_cap = 16, n_seen = 0;
+  char *seen = malloc((size_t)(seen_cap * 2 * Kb));
+  if (!a || !e || !lo || !hi || !th || !req || !in || !pool || !pick || !na || !ne || !seen) {
+    c->status = -2;
+    goto done;
+  }
+  n = halve_all(ca, ce, Kb, a, e);
+  int64_t n_req = 0;
+  for (int64_t j = 0; j < n; j++) {
+    int64_t t;
+    double sc = chunk_score(c->s, c->q, c->K, c->b, c->g, c->r0, c->r1, c->Tp, a[j], e[j], &t);
+    double dl = isfinite(sc) ? 0.5 * c->tol * fabs(sc) : 0.0;
+    lo[j] = sc - dl;
+    hi[j] = sc + dl;
+    th[2 * j] = lo[j];
+    th[2 * j + 1] = hi[j];
+    req[j] = c->target ? (char)contains_target(c, a[j], e[j]) : 0;
+    n_req += req[j];
+  }
+  if (n_req > Kb) goto done; /* the target's blocks cannot all survive */
+
+  /* A kept set S is allowed iff some threshold th has every member with
+   * hi >= th and every other candidate with lo <= th; it suffices to try
+   * the bounds themselves as th.  For each: candidates with lo > th must be
+   * kept, those with hi < th dropped, the others are free. */
+  for (int64_t k = 0; k < 2 * n && !c->status; k++) {
+    const double t0 = th[k];
+    int64_t base = 0, np = 0, bad = 0;
+    for (int64_t j = 0; j < n; j++) {
+      const int must_in = lo[j] > t0, must_out = hi[j] < t0;
+      if (must_in || req[j]) {
+        if (must_out) bad = 1;
+        in[j] = 1;
+        base++;
+      } else {
+        in[j] = 0;
+        if (!must_out) pool[np++] = j;
+      }
+    }
+    const int64_t need = Kb - base;
+    if (bad || need < 0 || need > np) continue;
+    /* every choice of `need` free candidates, in lexicographic order */
+    for (int64_t i = 0; i < need; i++) pick[i] = i;
+    for (;;) {
+      for (int64_t i = 0; i < need; i++) in[pool[pick[i]]] = 1;
+      int dup = 0;
+      for (int64_t v = 0; v < n_seen && !dup; v++) dup = memcmp(seen + v * 2 * Kb, in, (size_t)n) == 0;
+      if (!dup) {
+        if (n_seen == seen_cap) {
+          char *grown = realloc(seen, (size_t)(2 * seen_cap * 2 * Kb));
+          if (!grown) { c->status = -2; break; }
+          seen = grown;
+          seen_cap *= 2;
+        }
+        memcpy(seen + n_seen * 2 * Kb, in, (size_t)n);
+        n_seen++;
+        int64_t m = 0;
+        for (int64_t j = 0; j < n; j++)
+          if (in[j]) { na[m] = a[j]; ne[m] = e[j]; m++; }
+        reach_round(c, na, ne);
+        if (c->status || (c->target && c->n_found)) break;
+      }
+      for (int64_t i = 0; i < need; i++) in[pool[pick[i]]] = 0;
+      int64_t i = need - 1;
+      while (i >= 0 && pick[i] == np - need + i) i--;
+      if (i < 0) break;
+      pick[i]++;
+      for (int64_t j = i + 1; j < need; j++) pick[j] = pick[j - 1] + 1;
+    }
+  }
+done:
+  free(a); free(e); free(lo); free(hi); free(th); free(req); free(in); free(pool); free(pick);
+  free(na); free(ne); free(seen);
+}
+
+int64_t or_mask_reach(const or_shape *s, const void *q, const void *K, int64_t b, int64_t g,
+                      int64_t qb, double tol, const int32_t *target, int32_t *leaves,
+                      int64_t max_leaves, int64_t max_nodes) {
+  const int64_t Kb = s->k / s->block_k;
+  int64_t r0, r1;
+  const int64_t Tp = rows_and_tp(s, qb, &r0, &r1);
+  const int64_t Np = (Tp + s->block_k - 1) / s->block_k;
+  int64_t sb, wb;
+  dense_blocks(s, Np, &sb, &wb);
+  const int64_t first = sb, M = Np - sb - wb;
+  reach_ctx c = {s, q, K, b, g, r0, r1, Tp, Kb, tol, target, leaves, max_leaves, 0, 0,
+                 0, max_nodes, NULL, 0};
+  if (Kb >= M) { /* R7: one possible result */
+    int ok = 1;
+    for (int64_t j = 0; j < Kb && target; j++) ok &= target[j] == (j < M ? first + j : -1);
+    if (leaves && max_leaves > 0 && ok)
+      for (int64_t j = 0; j < Kb; j++) leaves[j] = (int32_t)(j < M ? first + j : -1);
+    return ok;
+  }
+  int64_t *ca = malloc(sizeof(int64_t) * Kb), *ce = malloc(sizeof(int64_t) * Kb);
+  c.leaf_buf = malloc(sizeof(int32_t) * Kb);
+  if (!ca || !ce || !c.leaf_buf) { free(ca); free(ce); free(c.leaf_buf); return -2; }
+  initial_chunks(first, M, Kb, ca, ce);
+  reach_round(&c, ca, ce);
+  free(ca); free(ce); free(c.leaf_buf);
+  return c.status ? c.status : c.n_found;
 }
 
 /* R8: one output row in fp64. */

@@ -505,11 +505,75 @@ def pin_dense_part_union(lib):
     assert np.array_equal(out, out2)
 
 
+
+# ---------------------------------------------------------------- near-tie-tolerant search
+
+def pin_reach_branch_golden(lib):
+    """Hand-traced: a near tie at the first cut branches into two final lists."""
+    g = _golden("near_tie_branch.json")
+    sh = g["shape"]
+    q, K, _ = _line_inputs(_s_from(g, sh["T"]))
+    kw = dict(T=sh["T"], k=sh["k"], block_k=sh["block_k"], block_q=sh["block_q"], causal=sh["causal"])
+    r = oracle.mask_one(q, K, 0, 0, 0, lib=lib, **kw)
+    assert r["indices"].tolist() == g["exact_indices"]
+    n, lists = oracle.mask_reach(q, K, 0, 0, 0, tol=g["tol"], lib=lib, **kw)
+    assert n == len(g["reachable"]) and sorted(l.tolist() for l in lists) == g["reachable"], lists
+    for t in g["reachable"]:
+        assert oracle.mask_reach(q, K, 0, 0, 0, tol=g["tol"], target=t, lib=lib, **kw)[0] == 1, t
+    for t in g["unreachable"]:
+        assert oracle.mask_reach(q, K, 0, 0, 0, tol=g["tol"], target=t, lib=lib, **kw)[0] == 0, t
+    n, lists = oracle.mask_reach(q, K, 0, 0, 0, tol=g["tol_below_gap"], lib=lib, **kw)
+    assert n == 1 and [l.tolist() for l in lists] == g["reachable_below_gap"]
+
+
+def pin_reach_identity(lib):
+    """Without near ties the tolerant search has exactly one result, the exact
+    search's; with them the exact search's result is always among its results.
+    Seeded AR(1) decode and prefill problems, several group sizes."""
+    import synth_inputs as si
+    cases = [si.workload("decode_32k", T=6000, Hq=8, Hkv=2, Tq=8, k=512, seed=77),
+             si.workload("decode_32k", T=3000, Hq=16, Hkv=1, Tq=8, block_k=16, k=256, seed=78),
+             si.workload("prefill_32k_chunk4k", T=1500, Tq=640, Hq=8, Hkv=2, k=256, block_k=32,
+                         seed=79)]
+    tol = 1e-4
+    seen_exempt = seen_safe = 0
+    for w in cases:
+        x = si.make_inputs(w)
+        kw = dict(T=w.T, k=w.k, block_k=w.block_k, block_q=w.block_q, causal=w.causal)
+        idx, _, margin = oracle.mask_all(x["q"], x["K"], lib=lib, **kw)
+        for b, g, qb in np.ndindex(*margin.shape):
+            n, lists = oracle.mask_reach(x["q"], x["K"], b, g, qb, tol=tol, lib=lib, **kw)
+            exact = idx[b, g, qb].tolist()
+            if margin[b, g, qb] > tol:
+                seen_safe += 1
+                assert n == 1 and lists[0].tolist() == exact, (w.name, b, g, qb, n)
+            elif margin[b, g, qb] < tol:
+                seen_exempt += 1
+                assert exact in [l.tolist() for l in lists], (w.name, b, g, qb)
+    assert seen_safe >= 30, seen_safe
+
+
+def pin_reach_target_agrees(lib):
+    """Target mode answers exactly the membership question of the enumeration."""
+    g = _golden("near_tie_branch.json")
+    sh = g["shape"]
+    q, K, _ = _line_inputs(_s_from(g, sh["T"]))
+    kw = dict(T=sh["T"], k=sh["k"], block_k=sh["block_k"], block_q=sh["block_q"], causal=sh["causal"])
+    n, lists = oracle.mask_reach(q, K, 0, 0, 0, tol=g["tol"], lib=lib, **kw)
+    reach = {tuple(l.tolist()) for l in lists}
+    T = sh["T"]
+    for a in range(T):
+        for b in range(a + 1, T):
+            got = oracle.mask_reach(q, K, 0, 0, 0, tol=g["tol"], target=[a, b], lib=lib, **kw)[0]
+            assert got == ((a, b) in reach), (a, b)
+
+
 ALL_PINS = [
     pin_monotone_counterexample, pin_centre_tokens, pin_centre_blocks, pin_centre_partial_block,
     pin_uneven_partition, pin_causal_vote, pin_group_max, pin_dense_reduction,
     pin_exact_topk_monotone, pin_exact_topk_disjoint_chunks, pin_exact_topk_certified,
     pin_tree_structure, pin_zero_query_ties, pin_attention_invariants, pin_mask_invariances,
     pin_e5m2_codes, pin_e5m2_kv, pin_dense_part_trace, pin_dense_part_reduction,
-    pin_dense_part_search_range, pin_dense_part_union,
+    pin_dense_part_search_range, pin_dense_part_union, pin_reach_branch_golden,
+    pin_reach_identity, pin_reach_target_agrees,
 ]

@@ -15,8 +15,8 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 MUTANTS = [
     ("centre_lower_middle", "int64_t t = (lo + hi) / 2;", "int64_t t = (lo + hi - 1) / 2;"),
     ("centre_ignores_partial_block",
-     "int64_t hi = cand[c].e * s->block_k < Tp ? cand[c].e * s->block_k : Tp;",
-     "int64_t hi = cand[c].e * s->block_k;"),
+     "int64_t hi = e * s->block_k < Tp ? e * s->block_k : Tp;",
+     "int64_t hi = e * s->block_k;"),
     ("split_ceil_midpoint", "int64_t m = ca[i] + (ce[i] - ca[i]) / 2;",
      "int64_t m = ca[i] + (ce[i] - ca[i] + 1) / 2;"),
     ("tie_prefers_higher_start", "return x->a < y->a;", "return x->a > y->a;"),
@@ -28,8 +28,8 @@ MUTANTS = [
     ("strided_head_group", "for (int64_t h = g * G; h < (g + 1) * G; h++)",
      "for (int64_t h = g; h < s->Hq; h += s->Hkv)"),
     ("first_row_only", "for (int64_t i = r0; i < r1; i++) {", "for (int64_t i = r0; i < r0 + 1; i++) {"),
-    ("ceil_initial_partition", "ca[i] = lo + i * M / Kb;\n    ce[i] = lo + (i + 1) * M / Kb;",
-     "ca[i] = lo + (i * M + Kb - 1) / Kb;\n    ce[i] = lo + ((i + 1) * M + Kb - 1) / Kb;"),
+    ("ceil_initial_partition", "ca[i] = first + i * M / Kb;\n    ce[i] = first + (i + 1) * M / Kb;",
+     "ca[i] = first + (i * M + Kb - 1) / Kb;\n    ce[i] = first + ((i + 1) * M + Kb - 1) / Kb;"),
     ("attn_no_scale", "const double scale = 1.0 / sqrt((double)s->d);", "const double scale = 1.0;"),
     ("attn_no_causal_mask", "if (t > limit) continue;\n      double w", "double w"),
     ("attn_value_head_of_query", "int64_t vo = ((b * s->Hkv + g) * s->T_cap + t) * s->d;",
@@ -52,6 +52,16 @@ MUTANTS = [
     ("sink_not_attended", "((n) < sb ? (n)", "((n) < sb ? -1"),
     ("window_off_by_one", "Np - wb + ((n) - sb)", "Np - wb - 1 + ((n) - sb)"),
     ("dense_listed_twice", "list[(n) - nd] < sb ||", "0 ||"),
+    # near-tie-tolerant search
+    ("reach_band_not_halved", "double dl = isfinite(sc) ? 0.5 * c->tol * fabs(sc) : 0.0;",
+     "double dl = isfinite(sc) ? c->tol * fabs(sc) : 0.0;"),
+    ("reach_tolerance_ignored", "double dl = isfinite(sc) ? 0.5 * c->tol * fabs(sc) : 0.0;",
+     "double dl = 0.0;"),
+    ("reach_band_inverted", "lo[j] = sc - dl;\n    hi[j] = sc + dl;", "lo[j] = sc + dl;\n    hi[j] = sc - dl;"),
+    ("reach_one_threshold_only", "for (int64_t k = 0; k < 2 * n && !c->status; k++) {",
+     "for (int64_t k = 0; k < 1 && !c->status; k++) {"),
+    ("reach_required_dropped", "req[j] = c->target ? (char)contains_target(c, a[j], e[j]) : 0;",
+     "req[j] = c->target ? (char)!contains_target(c, a[j], e[j]) : 0;"),
 ]
 
 
