@@ -4,8 +4,13 @@ run the CPU oracle on the same bits, and compare.
 Acceptance (per query block problem):
   * index lists equal exactly, unless the oracle's smallest relative score gap
     at a top-k cut (its `margin`) is below 1e-4: fp32 accumulation on the GPU
-    against fp64 in the oracle may then legitimately reorder the cut; such
-    problems are counted and their GPU lists only checked for validity;
+    against fp64 in the oracle may then legitimately reorder the cut.  Such a
+    problem is counted as exempt, and its GPU list must be one that the
+    oracle's near-tie-tolerant search reaches when every score may move by
+    half of that relative tolerance (oracle.mask_reach); for a problem
+    without near ties that search reaches the oracle's list only;
+  * exempt problems stay below 10% of a workload's problems (at least one is
+    allowed);
   * attention outputs within max |err| <= 2e-2 (bf16 in, fp32 accumulate),
     against the oracle run on the very index lists the GPU produced.
 """
@@ -47,14 +52,28 @@ def check_valid_lists(idx, nnz, w):
                 assert (np.diff(row[:n]) > 0).all() and row[0] >= 0 and row[n - 1] < Np
 
 
-def compare_masks(idx, nnz, o_idx, o_nnz, o_margin):
-    """Exact equality where the oracle's cut margin is safe; returns the count
-    of exempt problems."""
+def compare_masks(idx, nnz, o_idx, o_nnz, o_margin, x, w, sink=0, window=0):
+    """Exact equality where the oracle's cut margin is safe; elsewhere the GPU
+    list must be reachable by the oracle's near-tie-tolerant search on the
+    same inputs (x, workload w, dense part).  Returns the count of exempt
+    problems."""
     safe = o_margin >= MARGIN
     assert (nnz == o_nnz).all()
     bad = np.argwhere(safe & (idx != o_idx).any(axis=-1))
     assert len(bad) == 0, f"index mismatch at problems {bad[:8].tolist()}"
+    kw = dict(T=w.T, k=w.k, block_k=w.block_k, block_q=w.block_q, causal=w.causal, sink=sink,
+              window=window)
+    for b, g, qb in np.argwhere(~safe).tolist():
+        if (idx[b, g, qb] == o_idx[b, g, qb]).all():
+            continue  # the oracle's own list: always reachable
+        n, _ = oracle.mask_reach(x["q"], x["K"], b, g, qb, tol=MARGIN, target=idx[b, g, qb], **kw)
+        assert n == 1, f"problem {(b, g, qb)}: GPU list {idx[b, g, qb].tolist()} is not reachable"
     return int((~safe).sum())
+
+
+def exempt_cap(problems: int) -> int:
+    """Largest allowed count of exempt problems: 10%, at least one."""
+    return max(1, problems // 10)
 
 
 def compare_attention(out_gpu, ref, atol=ATOL):
@@ -71,7 +90,8 @@ def full_parity(x, w, threads=None):
     check_valid_lists(idx, nnz, w)
     kw = dict(T=w.T, k=w.k, block_k=w.block_k, block_q=w.block_q, causal=w.causal)
     o_idx, o_nnz, o_margin = oracle.mask_all(x["q"], x["K"], threads=threads, **kw)
-    exempt = compare_masks(idx, nnz, o_idx, o_nnz, o_margin)
+    exempt = compare_masks(idx, nnz, o_idx, o_nnz, o_margin, x, w)
+    assert exempt <= exempt_cap(o_margin.size), (exempt, o_margin.size)
     ref = oracle.attn_all(x["q"], x["K"], x["V"], idx, nnz, threads=threads, **kw)
     err = compare_attention(out, ref)
     return {"exempt": exempt, "problems": int(o_margin.size), "max_err": err}

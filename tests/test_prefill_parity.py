@@ -1,10 +1,8 @@
 """GPU parity of the chunked-prefill path (block_q = 64, bf16) against the CPU oracle.
 
-Small cases compare every problem and every output row.  The 4096-token chunk
-at the end of a 32k sequence runs at full size in the bench's launch
-configuration and is compared on sampled query blocks (the oracle's search)
-and sampled output rows (the oracle's attention), which the oracle computes
-one at a time.
+Every case compares every problem and every output row, the 4096-token
+chunk at the end of a 32k sequence included (at full size, in the bench's
+launch configuration).
 """
 import numpy as np
 import pytest
@@ -12,8 +10,7 @@ import torch
 
 import oracle
 import synth_inputs as si
-from parity_util import (MARGIN, check_valid_lists, compare_attention, compare_masks, full_parity,
-                         run_gpu)
+from parity_util import compare_attention, full_parity, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -53,7 +50,6 @@ def test_small_full(case):
     x = si.make_inputs(w)
     r = full_parity(x, w)
     _report(case, r)
-    assert r["exempt"] <= max(1, r["problems"] // 10)
 
 
 def test_spare_capacity_rows():
@@ -65,7 +61,6 @@ def test_spare_capacity_rows():
     x["V"][:, :, w.T:] = 1e4
     r = full_parity(x, w)
     _report("spare_capacity", r)
-    assert r["exempt"] <= max(1, r["problems"] // 10)
 
 
 def test_chunk_is_whole_sequence():
@@ -74,7 +69,6 @@ def test_chunk_is_whole_sequence():
     w = si.workload("prefill_32k_chunk4k", T=1536, Tq=1536, Hq=4, Hkv=1, k=512)
     r = full_parity(si.make_inputs(w), w)
     _report("whole_sequence", r)
-    assert r["exempt"] <= max(1, r["problems"] // 10)
 
 
 def test_zero_query_ties_exact():
@@ -114,32 +108,13 @@ def test_determinism():
 
 
 @pytest.mark.timeout(900)
-def test_full_size_chunk_sampled():
-    """The 4096-token chunk at the end of a 32k sequence, 32/8 heads, k=2048:
-    all index lists checked for validity; 24 query blocks against the
-    oracle's search; 96 output rows against the oracle's attention."""
+def test_full_size_chunk():
+    """The 4096-token chunk at the end of a 32k sequence, 32/8 heads, k=2048,
+    in the bench's launch configuration: every one of the 512 index lists
+    against the oracle's search (or, for a near tie, its tolerant search) and
+    every one of the 131072 output rows against the oracle's attention."""
     w = si.workload("prefill_32k_chunk4k")
-    x = si.make_inputs(w)
-    idx, nnz, out = run_gpu(x, w)
-    check_valid_lists(idx, nnz, w)
-    kw = dict(T=w.T, k=w.k, block_k=w.block_k, block_q=w.block_q, causal=w.causal)
-    rng = np.random.default_rng(17)
-    probs = [(0, 0, 0), (0, w.Hkv - 1, w.nqb - 1)] + [
-        (0, int(rng.integers(w.Hkv)), int(rng.integers(w.nqb))) for _ in range(22)]
-    exempt = 0
-    for (b, g, qb) in probs:
-        r = oracle.mask_one(x["q"], x["K"], b, g, qb, **kw)
-        if r["margin"] < MARGIN:
-            exempt += 1
-            continue
-        assert r["nnz"] == nnz[b, g, qb]
-        assert (r["indices"] == idx[b, g, qb]).all(), (b, g, qb)
-    assert exempt <= 4
-    got = out.float().cpu().numpy()
-    err = 0.0
-    for _ in range(96):
-        h, i = int(rng.integers(w.Hq)), int(rng.integers(w.Tq))
-        ref = oracle.attn_row(x["q"], x["K"], x["V"], idx, nnz, 0, h, i, **kw)
-        err = max(err, float(np.abs(got[0, h, i] - ref).max()))
-    print(f"[parity] prefill_32k_chunk4k sampled: exempt={exempt}/24 max_err={err:.3e}", flush=True)
-    assert err <= 2e-2
+    print(f"[case] prefill_32k_chunk4k full {w}", flush=True)
+    r = full_parity(si.make_inputs(w), w)
+    _report("prefill_32k_chunk4k", r)
+    assert r["problems"] == 512

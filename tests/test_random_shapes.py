@@ -10,14 +10,16 @@ Each case draws, from its own seed:
 
 It is checked against the oracle with the usual bar: index sets exact where
 the oracle's cut margin is at least 1e-4; outputs within 2e-2, against the
-oracle run on the lists the GPU produced.  Every list, exempt or not, must be
-a valid selection (ascending, in the searched range, the right count).  A
+oracle run on the lists the GPU produced.  Every list must be a valid
+selection (ascending, in the searched range, the right count).  A
 paged case must also equal the contiguous call bit for bit.
 
-The share of exempt problems is a property of the inputs, not of the GPU:
-a chunk's score is a maximum over up to 16 heads x 64 rows, and such maxima
-lie close together, so with few problems per case the usual 10% cap rounds
-to one.  Here at least half of a case's problems must be compared exactly.
+An exempt problem (a near tie at some cut) must still produce a list that
+the oracle's near-tie-tolerant search reaches.  The share of exempt problems
+is a property of the inputs, not of the GPU: a chunk's score is a maximum
+over up to 16 heads x 64 rows, and such maxima lie close together.  Over the
+64 cases 14 of 579 problems (2.4%) are exempt, but a case has only 1 to 30
+problems, so the usual cap (10%, at least one) becomes at least two here.
 """
 import numpy as np
 import pytest
@@ -87,8 +89,8 @@ def test_random_configuration(seed):
     o_idx, o_nnz, o_margin = oracle.mask_all(x["q"], x["K"], **okw)
     from test_dense_part_parity import check_lists
     check_lists(idx, nnz, w, sink, window)
-    exempt = compare_masks(idx, nnz, o_idx, o_nnz, o_margin)
-    assert exempt <= o_margin.size // 2
+    exempt = compare_masks(idx, nnz, o_idx, o_nnz, o_margin, x, w, sink, window)
+    assert exempt <= max(2, o_margin.size // 10), (exempt, o_margin.size)
     ref = oracle.attn_all(x["q"], x["K"], x["V"], idx, nnz, **okw)
     err = compare_attention(out, ref)
     if page:
