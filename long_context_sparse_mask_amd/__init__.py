@@ -106,9 +106,8 @@ def make_desc(q: torch.Tensor, K: torch.Tensor, T: int | None = None, causal: bo
     B, Hq, Tq, d = q.shape
     Bk, Hkv, T_cap, dk = K.shape
     if Bk != B or dk != d:
-        raise ValueError(f"K {tuple(K.shape)} does not match q {tuple(q.shape)} in batch or head dim")
-    if K.device != q.device:
-        raise ValueError("q and K must be on the same device")
+        raise ValueError(f"K {tuple(K.shape)} does not match q {tuple(q.shape)} in batch or "
+                         "head dim")
     return Desc(B, Hq, Hkv, Tq, T_cap if T is None else T, T_cap, d, int(bool(causal)),
                 _dtype_code(q, K))
 
@@ -139,15 +138,23 @@ def _check_lists(indices: torch.Tensor, nnz: torch.Tensor, desc: Desc, nqb: int,
         raise ValueError("indices and nnz must be on q's device")
 
 
+def _on(dev: torch.device):
+    """Marshaller of device pointers for one call: every tensor must sit on `dev`."""
+    return lambda t, name: _dev_ptr(t, name, dev)
+
+
 def _stream(dev: torch.device, stream) -> int:
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _dev_ptr(t: torch.Tensor, name: str) -> int:
+def _dev_ptr(t: torch.Tensor, name: str, dev: torch.device | None = None) -> int:
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be a device tensor")
+    if dev is not None and t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, q on {dev}: every tensor of a call must be on "
+                         "one device")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t.data_ptr()
@@ -165,6 +172,7 @@ def hip_mask_estimate(q, K, k: int, block_k: int, block_q: int = 1, *, T=None, c
                       indices=None, nnz=None, stream=None):
     """Per (batch, kv head, query block): the ids of the selected key blocks
     (ascending, -1 padded) and their count.  Returns (indices, nnz)."""
+    p = _on(q.device)  # device pointer of a tensor on q's device
     desc = make_desc(q, K, T, causal)
     nqb = -(-desc.Tq // block_q)
     kb = k // block_k if block_k > 0 else 0
@@ -175,9 +183,9 @@ def hip_mask_estimate(q, K, k: int, block_k: int, block_q: int = 1, *, T=None, c
     _check_lists(indices, nnz, desc, nqb, kb, q.device)
     if desc.B * desc.Tq == 0:
         return indices, nnz
-    _check(lib.hip_mask_estimate(C.byref(desc), _dev_ptr(q, "q"), _dev_ptr(K, "K"), k, block_k,
-                                 block_q, _dev_ptr(indices, "indices"), _dev_ptr(nnz, "nnz"),
-                                 None, 0, _stream(q.device, stream)))
+    _check(lib.hip_mask_estimate(C.byref(desc), p(q, "q"), p(K, "K"), k, block_k, block_q,
+                                 p(indices, "indices"), p(nnz, "nnz"), None, 0,
+                                 _stream(q.device, stream)))
     return indices, nnz
 
 
@@ -185,6 +193,7 @@ def hip_sparse_attn(q, K, V, indices, nnz, k: int, block_k: int, block_q: int = 
                     causal=True, out=None, workspace=None, stream=None):
     """Softmax attention of every query row over the tokens of its listed key
     blocks.  Returns out [B,Hq,Tq,d] in q's dtype."""
+    p = _on(q.device)  # device pointer of a tensor on q's device
     desc = make_desc(q, K, T, causal)
     _check_v(K, V)
     nqb = -(-desc.Tq // block_q)
@@ -198,18 +207,18 @@ def hip_sparse_attn(q, K, V, indices, nnz, k: int, block_k: int, block_q: int = 
     need = hipsa_workspace_bytes(q, K, k, block_k, block_q, T=T, causal=causal)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None
+    ws_ptr = p(workspace, "workspace") if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib.hip_sparse_attn(C.byref(desc), _dev_ptr(q, "q"), _dev_ptr(K, "K"), _dev_ptr(V, "V"),
-                               _dev_ptr(indices, "indices"), _dev_ptr(nnz, "nnz"), k, block_k,
-                               block_q, _dev_ptr(out, "out"), ws_ptr, ws_len,
-                               _stream(q.device, stream)))
+    _check(lib.hip_sparse_attn(C.byref(desc), p(q, "q"), p(K, "K"), p(V, "V"),
+                               p(indices, "indices"), p(nnz, "nnz"), k, block_k, block_q,
+                               p(out, "out"), ws_ptr, ws_len, _stream(q.device, stream)))
     return out
 
 
 # ------------------------------------------------------------------ paged KV cache
 
 def _paged_desc(q, K_pages, block_table, T, causal):
+    p = _on(q.device)  # device pointer of a tensor on q's device
     if (q.dim() != 4 or K_pages.dim() != 4 or block_table.dim() != 2
             or block_table.dtype != torch.int32):
         raise ValueError("q must be [B, Hq, Tq, d], K and V [num_pages, Hkv, page_size, d] and "
@@ -218,16 +227,16 @@ def _paged_desc(q, K_pages, block_table, T, causal):
     num_pages, Hkv, page_size, dk = K_pages.shape
     if dk != d or block_table.shape[0] != B:
         raise ValueError("K's head dim or block_table's batch does not match q")
-    if K_pages.device != q.device or block_table.device != q.device:
-        raise ValueError("q, K and block_table must be on the same device")
     desc = Desc(B, Hq, Hkv, Tq, T, T, d, int(bool(causal)), _dtype_code(q, K_pages))
-    pages = Pages(_dev_ptr(block_table, "block_table"), block_table.shape[1], page_size, num_pages)
+    pages = Pages(p(block_table, "block_table"), block_table.shape[1], page_size,
+                  num_pages)
     return desc, pages
 
 
 def hip_mask_estimate_paged(q, K_pages, block_table, T: int, k: int, block_k: int,
                             block_q: int = 1, *, causal=True, indices=None, nnz=None, stream=None):
     """hip_mask_estimate on a paged KV cache.  Returns (indices, nnz)."""
+    p = _on(q.device)  # device pointer of a tensor on q's device
     desc, pages = _paged_desc(q, K_pages, block_table, T, causal)
     nqb = -(-desc.Tq // block_q)
     kb = k // block_k if block_k > 0 else 0
@@ -238,9 +247,9 @@ def hip_mask_estimate_paged(q, K_pages, block_table, T: int, k: int, block_k: in
     _check_lists(indices, nnz, desc, nqb, kb, q.device)
     if desc.B * desc.Tq == 0:
         return indices, nnz
-    _check(lib.hip_mask_estimate_paged(C.byref(desc), C.byref(pages), _dev_ptr(q, "q"),
-                                       _dev_ptr(K_pages, "K"), k, block_k, block_q,
-                                       _dev_ptr(indices, "indices"), _dev_ptr(nnz, "nnz"), None, 0,
+    _check(lib.hip_mask_estimate_paged(C.byref(desc), C.byref(pages), p(q, "q"),
+                                       p(K_pages, "K"), k, block_k, block_q,
+                                       p(indices, "indices"), p(nnz, "nnz"), None, 0,
                                        _stream(q.device, stream)))
     return indices, nnz
 
@@ -249,6 +258,7 @@ def hip_sparse_attn_paged(q, K_pages, V_pages, block_table, indices, nnz, T: int
                           block_k: int, block_q: int = 1, *, causal=True, out=None, workspace=None,
                           stream=None):
     """hip_sparse_attn on a paged KV cache.  Returns out [B,Hq,Tq,d] in q's dtype."""
+    p = _on(q.device)  # device pointer of a tensor on q's device
     desc, pages = _paged_desc(q, K_pages, block_table, T, causal)
     _check_v(K_pages, V_pages)
     nqb = -(-desc.Tq // block_q)
@@ -264,12 +274,13 @@ def hip_sparse_attn_paged(q, K_pages, V_pages, block_table, indices, nnz, T: int
         raise HipsaError(-2, lib.hipsa_last_error().decode())
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None
+    ws_ptr = p(workspace, "workspace") if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib.hip_sparse_attn_paged(C.byref(desc), C.byref(pages), _dev_ptr(q, "q"),
-                                     _dev_ptr(K_pages, "K"), _dev_ptr(V_pages, "V"),
-                                     _dev_ptr(indices, "indices"), _dev_ptr(nnz, "nnz"), k, block_k,
-                                     block_q, _dev_ptr(out, "out"), ws_ptr, ws_len,
+    _check(lib.hip_sparse_attn_paged(C.byref(desc), C.byref(pages), p(q, "q"),
+                                     p(K_pages, "K"),
+                                     p(V_pages, "V"),
+                                     p(indices, "indices"), p(nnz, "nnz"), k, block_k,
+                                     block_q, p(out, "out"), ws_ptr, ws_len,
                                      _stream(q.device, stream)))
     return out
 
@@ -299,6 +310,7 @@ def hip_mask_estimate_ex(q, K, k: int, block_k: int, block_q: int = 1, *, T=None
                          sink=0, window=0, block_table=None, indices=None, nnz=None, stream=None):
     """hip_mask_estimate with a dense part (sink, window tokens) and optionally a
     paged KV cache (block_table).  Returns (indices, nnz) of the searched blocks."""
+    p = _on(q.device)  # device pointer of a tensor on q's device
     desc, ext, _pages = _ext_desc(q, K, T, causal, sink, window, block_table)
     nqb = -(-desc.Tq // block_q)
     kb = k // block_k if block_k > 0 else 0
@@ -309,9 +321,10 @@ def hip_mask_estimate_ex(q, K, k: int, block_k: int, block_q: int = 1, *, T=None
     _check_lists(indices, nnz, desc, nqb, kb, q.device)
     if desc.B * desc.Tq == 0:
         return indices, nnz
-    _check(lib.hip_mask_estimate_ex(C.byref(desc), C.byref(ext), _dev_ptr(q, "q"), _dev_ptr(K, "K"),
-                                    k, block_k, block_q, _dev_ptr(indices, "indices"),
-                                    _dev_ptr(nnz, "nnz"), None, 0, _stream(q.device, stream)))
+    _check(lib.hip_mask_estimate_ex(C.byref(desc), C.byref(ext), p(q, "q"),
+                                    p(K, "K"),
+                                    k, block_k, block_q, p(indices, "indices"),
+                                    p(nnz, "nnz"), None, 0, _stream(q.device, stream)))
     return indices, nnz
 
 
@@ -320,6 +333,7 @@ def hip_sparse_attn_ex(q, K, V, indices, nnz, k: int, block_k: int, block_q: int
                        stream=None):
     """hip_sparse_attn over the dense part and the listed blocks, optionally on a
     paged KV cache.  Returns out [B,Hq,Tq,d] in q's dtype."""
+    p = _on(q.device)  # device pointer of a tensor on q's device
     desc, ext, _pages = _ext_desc(q, K, T, causal, sink, window, block_table)
     _check_v(K, V)
     nqb = -(-desc.Tq // block_q)
@@ -335,10 +349,11 @@ def hip_sparse_attn_ex(q, K, V, indices, nnz, k: int, block_k: int, block_q: int
         raise HipsaError(-2, lib.hipsa_last_error().decode())
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None
+    ws_ptr = p(workspace, "workspace") if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib.hip_sparse_attn_ex(C.byref(desc), C.byref(ext), _dev_ptr(q, "q"), _dev_ptr(K, "K"),
-                                  _dev_ptr(V, "V"), _dev_ptr(indices, "indices"),
-                                  _dev_ptr(nnz, "nnz"), k, block_k, block_q, _dev_ptr(out, "out"),
+    _check(lib.hip_sparse_attn_ex(C.byref(desc), C.byref(ext), p(q, "q"),
+                                  p(K, "K"),
+                                  p(V, "V"), p(indices, "indices"),
+                                  p(nnz, "nnz"), k, block_k, block_q, p(out, "out"),
                                   ws_ptr, ws_len, _stream(q.device, stream)))
     return out
