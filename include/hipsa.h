@@ -213,6 +213,28 @@ int hip_sparse_attn_ex(const hipsa_desc *desc, const hipsa_ext *ext, const void 
 size_t hipsa_workspace_bytes_ex(const hipsa_desc *desc, const hipsa_ext *ext, int64_t k,
                                 int64_t block_k, int64_t block_q);
 
+/*
+ * hip_sparse_attn without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Arguments, checks and results are those
+ * of hip_sparse_attn; the split partials of decode (block_q == 1) go to a
+ * scratch array of HIPSA_NOALLOC_SCRATCH_BYTES in the library's own device
+ * memory, one per GPU, which each GPU the library runs on holds until the
+ * process ends.  The call allocates and frees nothing.
+ *   - A shape whose workspace need (hipsa_workspace_bytes) exceeds the
+ *     scratch returns HIPSA_ERR_WORKSPACE before any HIP call.
+ *   - The scratch needs no initialisation and keeps the last call's partials.
+ *   - Every call on one GPU shares that GPU's scratch: calls that overlap in
+ *     time on one GPU (several streams or host threads) race and give wrong
+ *     outputs.  Order them on one stream.
+ *   - The first call on a device looks the scratch up on the device that
+ *     runs `stream` (HIPSA_ERR_HIP if that fails).
+ */
+#define HIPSA_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int hip_sparse_attn_noalloc(const hipsa_desc *desc, const void *q, const void *K, const void *V,
+                            const int32_t *indices, const int32_t *nnz, int64_t k,
+                            int64_t block_k, int64_t block_q, void *out, void *stream);
+
 /* Device workspace bytes that hip_sparse_attn (and hip_mask_estimate) need for
  * this shape (0 = none), or SIZE_MAX when the arguments are invalid (see
  * hipsa_last_error()).  Empty problems (B == 0 or Tq == 0) need none, and

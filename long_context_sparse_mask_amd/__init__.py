@@ -24,7 +24,8 @@ import torch  # loads the HIP runtime first, so libhipsa binds to the same one
 
 __all__ = ["hip_mask_estimate", "hip_sparse_attn", "hip_mask_estimate_paged",
            "hip_sparse_attn_paged", "hip_mask_estimate_ex", "hip_sparse_attn_ex",
-           "hipsa_workspace_bytes", "hipsa_workspace_bytes_ex", "HipsaError", "LIB_PATH", "lib"]
+           "hip_sparse_attn_noalloc", "hipsa_workspace_bytes", "hipsa_workspace_bytes_ex",
+           "HipsaError", "LIB_PATH", "lib", "NOALLOC_SCRATCH_BYTES"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhipsa.so")
 if not os.path.exists(LIB_PATH):
@@ -34,6 +35,7 @@ lib = C.CDLL(LIB_PATH)
 
 HIPSA_F32, HIPSA_BF16, HIPSA_BF16_E5M2 = 0, 1, 2
 SIZE_MAX = (1 << (8 * C.sizeof(C.c_size_t))) - 1
+NOALLOC_SCRATCH_BYTES = 8 << 20  # HIPSA_NOALLOC_SCRATCH_BYTES
 
 
 class Desc(C.Structure):
@@ -69,6 +71,9 @@ lib.hip_mask_estimate_ex.restype = C.c_int
 lib.hip_sparse_attn_ex.argtypes = [C.POINTER(Desc), C.POINTER(Ext), _P, _P, _P, _P, _P, _I64, _I64,
                                    _I64, _P, _P, _SZ, _P]
 lib.hip_sparse_attn_ex.restype = C.c_int
+lib.hip_sparse_attn_noalloc.argtypes = [C.POINTER(Desc), _P, _P, _P, _P, _P, _I64, _I64, _I64, _P,
+                                        _P]
+lib.hip_sparse_attn_noalloc.restype = C.c_int
 lib.hipsa_workspace_bytes_ex.argtypes = [C.POINTER(Desc), C.POINTER(Ext), _I64, _I64, _I64]
 lib.hipsa_workspace_bytes_ex.restype = C.c_size_t
 lib.hipsa_workspace_bytes.argtypes = [C.POINTER(Desc), _I64, _I64, _I64]
@@ -212,6 +217,29 @@ def hip_sparse_attn(q, K, V, indices, nnz, k: int, block_k: int, block_q: int = 
     _check(lib.hip_sparse_attn(C.byref(desc), p(q, "q"), p(K, "K"), p(V, "V"),
                                p(indices, "indices"), p(nnz, "nnz"), k, block_k, block_q,
                                p(out, "out"), ws_ptr, ws_len, _stream(q.device, stream)))
+    return out
+
+
+def hip_sparse_attn_noalloc(q, K, V, indices, nnz, k: int, block_k: int, block_q: int = 1, *,
+                            T=None, causal=True, out=None, stream=None):
+    """hip_sparse_attn with the split partials in the library's own per-GPU
+    scratch (no workspace).  `out` must be given (the call allocates nothing;
+    pass out=None only outside graph capture, to let torch allocate it here).
+    Calls on one GPU must be ordered on one stream."""
+    p = _on(q.device)  # device pointer of a tensor on q's device
+    desc = make_desc(q, K, T, causal)
+    _check_v(K, V)
+    nqb = -(-desc.Tq // block_q)
+    kb = k // block_k if block_k > 0 else 0
+    _check_lists(indices, nnz, desc, nqb, kb, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_out(out, q)
+    if desc.B * desc.Tq == 0:
+        return out
+    _check(lib.hip_sparse_attn_noalloc(C.byref(desc), p(q, "q"), p(K, "K"), p(V, "V"),
+                                       p(indices, "indices"), p(nnz, "nnz"), k, block_k, block_q,
+                                       p(out, "out"), _stream(q.device, stream)))
     return out
 
 

@@ -294,6 +294,32 @@ int hip_sparse_attn_paged(const hipsa_desc *desc, const hipsa_pages *pages, cons
                             workspace, workspace_bytes, stream);
 }
 
+int hip_sparse_attn_noalloc(const hipsa_desc *desc, const void *q, const void *K, const void *V,
+                            const int32_t *indices, const int32_t *nnz, int64_t k, int64_t block_k,
+                            int64_t block_q, void *out, void *stream) {
+  hipsa::Shape s;
+  int rc = check_shape(desc, k, block_k, block_q, &s);
+  if (rc) return rc;
+  if (s.problems == 0) return ok();
+  if (!q || !K || !V || !indices || !nnz || !out)
+    return fail(HIPSA_ERR_NULL, "q, K, V, indices, nnz and out must be non-NULL");
+  {
+    const void *p[] = {q, K, V, out};
+    const char *nm[] = {"q", "K", "V", "out"};
+    if ((rc = check_aligned(p, nm, 4))) return rc;
+  }
+  const size_t need = workspace_for(s);
+  if (need > hipsa::kNoAllocScratchBytes)
+    return fail(HIPSA_ERR_WORKSPACE, "this shape needs %zu bytes of split partials; the "
+                "library's scratch holds %zu (use hip_sparse_attn with a workspace)", need,
+                hipsa::kNoAllocScratchBytes);
+  void *scratch = nullptr;
+  hipError_t e = hipsa::noalloc_scratch((hipStream_t)stream, &scratch);
+  if (e != hipSuccess) return hip_fail(e, "scratch lookup");
+  return attn_impl(s, kContiguous, q, K, V, indices, nnz, out, scratch,
+                   hipsa::kNoAllocScratchBytes, stream);
+}
+
 size_t hipsa_workspace_bytes(const hipsa_desc *desc, int64_t k, int64_t block_k,
                              int64_t block_q) {
   return hipsa_workspace_bytes_ex(desc, nullptr, k, block_k, block_q);

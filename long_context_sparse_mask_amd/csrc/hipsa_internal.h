@@ -11,6 +11,10 @@ namespace hipsa {
 constexpr int kMaxKb = 512;   // largest K_b = k / block_k the kernels accept
 constexpr int kMaxGroup = 16; // largest Hq / Hkv
 constexpr int kMaxDenseBlocks = 256;  // largest (sink + window) / block_k
+// Scratch array of hip_sparse_attn_noalloc (per GPU, library-owned).
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+// Its address on the device that runs `stream` (looked up once per device).
+hipError_t noalloc_scratch(hipStream_t stream, void **ptr);
 
 // Validated shape of one call, in the units the kernels use.
 struct Shape {

@@ -22,8 +22,9 @@ def _declared():
 def test_header_declares_the_boundary():
     assert _declared() == sorted(["hip_mask_estimate", "hip_sparse_attn", "hip_mask_estimate_paged",
                                   "hip_sparse_attn_paged", "hip_mask_estimate_ex",
-                                  "hip_sparse_attn_ex", "hipsa_workspace_bytes",
-                                  "hipsa_workspace_bytes_ex", "hipsa_last_error"])
+                                  "hip_sparse_attn_ex", "hip_sparse_attn_noalloc",
+                                  "hipsa_workspace_bytes", "hipsa_workspace_bytes_ex",
+                                  "hipsa_last_error"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -345,3 +346,32 @@ def test_binding_rejects_mismatched_paged_tensors():
         hs.hip_sparse_attn_paged(q, Kp, Vp, table, idx, nnz, 256, 128, 64, out=_cpu((B, Hq, 2, d)))
     with pytest.raises(ValueError):  # table for another batch
         hs.hip_mask_estimate_paged(q, Kp, torch.zeros((B + 1, 4), dtype=torch.int32), 256, 128, 64)
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch():
+    """hip_sparse_attn_noalloc keeps split partials in an 8 MiB library
+    scratch: a shape needing more is refused before any HIP call, with the
+    same argument checks as hip_sparse_attn before that."""
+    import long_context_sparse_mask_amd as hs
+    assert hs.NOALLOC_SCRATCH_BYTES == 8 << 20
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 2048, 64, 1, FAKE, None]
+    # 128k x 4 decode: 32 problems x 16 splits x 4 heads x 130 floats = 1 MiB: fits, but the
+    # invalid variants below fail first
+    assert hs.lib.hip_sparse_attn_noalloc(C.byref(_desc(Hq=30)), *args) == ERR_SHAPE
+    bad = list(args)
+    bad[0] = None
+    assert hs.lib.hip_sparse_attn_noalloc(C.byref(_desc()), *bad) == ERR_NULL
+    bad = list(args)
+    bad[8] = C.c_void_p(0x1008)  # out
+    assert hs.lib.hip_sparse_attn_noalloc(C.byref(_desc()), *bad) == ERR_ALIGN
+    # 64 query rows x 8 KV heads x 64 splits (k = 8192 keys) x 4 heads x 130 floats: 68 MB
+    big = _desc(Tq=64, T=65536, T_cap=65536)
+    need = hs.lib.hipsa_workspace_bytes(C.byref(big), 8192, 64, 1)
+    assert need > hs.NOALLOC_SCRATCH_BYTES
+    big_args = list(args)
+    big_args[5] = 8192
+    assert hs.lib.hip_sparse_attn_noalloc(C.byref(big), *big_args) == ERR_WS
+    assert "scratch" in hs.lib.hipsa_last_error().decode()
+    # empty problems: no pointer is read
+    assert hs.lib.hip_sparse_attn_noalloc(C.byref(_desc(B=0)), None, None, None, None, None, 2048,
+                                          64, 1, None, None) == 0
