@@ -6,20 +6,22 @@ attention per step, on seeded synthetic Llama-3.1-8B-shaped inputs.
 
 Prints ONE JSON line.  Default workload: decode at 128k context, batch 4,
 32 query / 8 KV heads, d=128, bf16, block_k=64, k=2048 (decode_128k_b4).
-A step = hip_mask_estimate + hip_sparse_attn for the whole batch; the value
-is microseconds per step (lower is better).  With the default workload the
-line also carries the chunked-prefill throughput (4096-token chunk at the end
-of a 32k sequence) as `prefill`.
+A step = one hip_decode_step call (mask estimation then sparse attention) for
+the whole batch; the value is microseconds per step (lower is better).  With
+the default workload the line also carries the 32k and 1M-token decodes
+(`decode_32k`, `decode_1m_needles`, the latter with needle recall), the step
+as two calls, the chunked-prefill throughput (4096-token chunk at the end of
+a 32k sequence, `prefill`) and the fp8, paged and dense-part variants.
 
 Timing: the K timed steps (and the W warm-up steps) are captured as HIP
 graphs of C-ABI launches on torch's capture stream and replayed, so host
-call overhead is not in the figure.  Consecutive steps rotate over 4 rolled
-copies of the layer's K/V and 16 query sets, so selected blocks differ from
-step to step and the selected bytes come from HBM, not from the 256 MB
-last-level cache.  Per-kernel launch durations for the roofline are taken the
-same way from graphs of one kernel each, with HIP events on the stream that
-the kernels run on.  Decode lines also carry `mask_reuse`: µs per step when
-the mask is re-estimated only every r_m steps (attention every step).
+call overhead is not in the figure; HIP events on that stream bracket the
+replay.  Consecutive steps rotate over 8 rolled copies of the layer's K/V
+and 16 query sets, so the selected blocks differ from step to step and come
+from HBM, not from the 256 MB last-level cache.  The attention-only and
+mask-reuse legs (`mask_reuse`: the mask re-estimated every r_m steps,
+attention every step) attend each step over the lists that step's own mask
+selected, so they read as many distinct bytes as full steps do.
 """
 from __future__ import annotations
 
@@ -37,7 +39,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
-N_LAYER_COPIES = 4   # defaults; --layer-copies / --query-sets override
+N_LAYER_COPIES = 8   # defaults; --layer-copies / --query-sets override
 N_QUERY_SETS = 16
 
 
@@ -94,11 +96,16 @@ def prefill_flops(w) -> dict:
 
 # kernels behind each call, for matching the committed HBM counter summary
 CALL_KERNELS = {
+    ("decode", "hip_decode_step"): ("decode_step_kernel", "attn_decode_combine"),
     ("decode", "hip_sparse_attn"): ("attn_decode_mfma", "attn_decode_kernel", "attn_decode_combine"),
     ("decode", "hip_mask_estimate"): ("mask_decode",),
     ("prefill", "hip_sparse_attn"): ("attn_prefill_kernel",),
     ("prefill", "hip_mask_estimate"): ("mask_prefill_kernel",),
 }
+# hip_decode_step runs the one-launch kernel for bf16 K/V; for fp8 K/V it runs
+# the two calls' kernels in turn
+CALL_KERNELS[("decode", "hip_decode_step", "bf16_e5m2")] = (
+    "mask_decode_kernel", "attn_decode_mfma", "attn_decode_combine")
 
 
 # string and character literals (kept) or comments (dropped), in source order
@@ -128,6 +135,8 @@ def kernel_matches(kernel: str, dtype: str) -> bool:
     (unsigned char = E5M2 codes, unsigned short = bf16, float), the decode
     combine (which never reads K/V) by its output type."""
     args = kernel.split("<", 1)[1] if "<" in kernel else ""
+    if kernel.startswith("decode_step_kernel"):  # bf16 query and K/V only
+        return dtype == "bf16"
     if kernel.startswith("attn_decode_combine"):
         return ("float" in args) == (dtype == "f32")
     if "unsigned char" in args:
@@ -148,56 +157,76 @@ def measured_traffic(kind: str, call: str, dtype: str = "bf16"):
         return None
     if blob.get("source_sha") != kernel_source_sha():
         return None
-    names = CALL_KERNELS[(kind, call)]
+    names = CALL_KERNELS.get((kind, call, dtype), CALL_KERNELS[(kind, call)])
     hits = [v["traffic_bytes"] for k, v in blob["kernels"].items()
             if k.startswith(names) and kernel_matches(k, dtype)]
     return sum(hits) if hits else None
 
 
+def _time_oracle(fn, budget_s: float, min_runs: int, max_runs: int) -> list:
+    """Wall-clock seconds of repeated fn() calls: at least min_runs, then
+    until budget_s is spent (at most max_runs)."""
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < min_runs or (time.perf_counter() - t_start < budget_s
+                                    and len(times) < max_runs):
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+    return times
+
+
 def cpu_baseline(x, w, budget_s: float) -> dict:
-    """The CPU oracle on the same seeded step, all host threads."""
+    """The CPU oracle (mask + attention) on one whole decode step of the
+    workload (the first query set and layer copy): with every host thread,
+    and with one thread."""
     import oracle
     kw = dict(T=w.T, k=w.k, block_k=w.block_k, block_q=w.block_q, causal=w.causal)
     nt = oracle.nthreads()
-    times = []
-    t_start = time.perf_counter()
-    # whole steps, repeated until about budget_s of CPU time is spent (at least 3)
-    while len(times) < 3 or (time.perf_counter() - t_start < budget_s and len(times) < 2000):
-        t0 = time.perf_counter()
-        idx, nnz, _ = oracle.mask_all(x["q"], x["K"], threads=nt, **kw)
-        oracle.attn_all(x["q"], x["K"], x["V"], idx, nnz, threads=nt, **kw)
-        times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_start > 4 * budget_s:
-            break
-    return times, nt
+
+    def step(threads):
+        idx, nnz, _ = oracle.mask_all(x["q"], x["K"], threads=threads, **kw)
+        oracle.attn_all(x["q"], x["K"], x["V"], idx, nnz, threads=threads, **kw)
+    all_t = _time_oracle(lambda: step(nt), budget_s, 3, 2000)
+    one_t = _time_oracle(lambda: step(1), budget_s / 2, 1, 200)
+    med, med1 = statistics.median(all_t), statistics.median(one_t)
+    return {"value": round(med * 1e6, 1), "unit": "us/step", "cores": nt, "kind": "oracle",
+            "sample": f"whole {w.name} step (first query set and layer copy), median of "
+                      f"{len(all_t)} runs ({sum(all_t):.1f} s), fp64 C + OpenMP",
+            "single_thread": {"value": round(med1 * 1e6, 1), "unit": "us/step", "cores": 1,
+                              "sample": f"the same step, median of {len(one_t)} runs "
+                                        f"({sum(one_t):.1f} s)"},
+            "cpu_model": host_cpu_model()}
 
 
 def cpu_baseline_prefill(si, budget_s: float) -> dict:
-    """The CPU oracle on a bounded sample of the prefill chunk: the last 1024
-    query rows (16 of the 64 query blocks, each seeing 32 selected blocks like
-    every block of the chunk) at the same T, same shapes and distributions,
-    repeated until about budget_s of CPU time is spent; the time is scaled to
-    the 4096-row chunk."""
+    """The CPU oracle (mask + attention) on the whole 4096-row prefill chunk
+    with every host thread; with one thread on its last 256 rows (4 of its 64
+    query blocks, each with the same 32 selected blocks per KV head as every
+    block of the chunk), the time scaled by 16."""
     import oracle
-    ws = si.workload("prefill_32k_chunk4k", Tq=1024)
-    xs = si.make_inputs(ws)
-    kw = dict(T=ws.T, k=ws.k, block_k=ws.block_k, block_q=ws.block_q, causal=ws.causal)
-    nt = oracle.nthreads()
-    times = []
-    t_start = time.perf_counter()
-    while len(times) < 1 or (time.perf_counter() - t_start < budget_s and len(times) < 50):
-        t0 = time.perf_counter()
-        idx, nnz, _ = oracle.mask_all(xs["q"], xs["K"], threads=nt, **kw)
-        oracle.attn_all(xs["q"], xs["K"], xs["V"], idx, nnz, threads=nt, **kw)
-        times.append(time.perf_counter() - t0)
     full = si.workload("prefill_32k_chunk4k")
-    scale = full.Tq / ws.Tq
-    t = statistics.median(times) * scale
-    return {"value": round(full.Tq / t, 1), "unit": "tok/s", "cores": nt, "kind": "oracle",
-            "sample": f"last {ws.Tq} query rows of the 4096-row chunk at T={ws.T} "
-                      f"({ws.Tq // ws.block_q} of 64 query blocks, 32 heads), fp64 C + OpenMP, "
-                      f"median of {len(times)} runs ({sum(times):.1f} s in all), time scaled x{scale:g}",
-            "s_per_chunk": round(t, 2)}
+    xf = si.make_inputs(full)
+    nt = oracle.nthreads()
+
+    def chunk(w, x, threads):
+        kw = dict(T=w.T, k=w.k, block_k=w.block_k, block_q=w.block_q, causal=w.causal)
+        idx, nnz, _ = oracle.mask_all(x["q"], x["K"], threads=threads, **kw)
+        oracle.attn_all(x["q"], x["K"], x["V"], idx, nnz, threads=threads, **kw)
+    all_t = _time_oracle(lambda: chunk(full, xf, nt), budget_s, 2, 5)
+    part = si.workload("prefill_32k_chunk4k", Tq=256)
+    xp = si.make_inputs(part)
+    one_t = _time_oracle(lambda: chunk(part, xp, 1), budget_s / 2, 1, 5)
+    med = statistics.median(all_t)
+    scale = full.Tq / part.Tq
+    med1 = statistics.median(one_t) * scale
+    return {"value": round(full.Tq / med, 1), "unit": "tok/s", "cores": nt, "kind": "oracle",
+            "sample": f"whole 4096-row chunk at T={full.T}, fp64 C + OpenMP, median of "
+                      f"{len(all_t)} runs ({sum(all_t):.1f} s)", "s_per_chunk": round(med, 2),
+            "single_thread": {"value": round(full.Tq / med1, 1), "unit": "tok/s", "cores": 1,
+                              "sample": f"last {part.Tq} rows of the chunk, median of "
+                                        f"{len(one_t)} runs, time scaled x{scale:g}",
+                              "s_per_chunk": round(med1, 1)}}
 
 
 def host_cpu_model() -> str:
@@ -266,10 +295,18 @@ def page_pool(K, V, T, page_size, gen, torch):
     return pool(K), pool(V), table
 
 
-def run_workload(w, steps, warmup, torch, hs, si, with_cpu, cpu_budget,
-                 n_layers=N_LAYER_COPIES, n_q=N_QUERY_SETS, page_size=0, dense=(0, 0)):
+def run_workload(w, steps, warmup, torch, hs, si, n_layers=N_LAYER_COPIES, n_q=N_QUERY_SETS,
+                 page_size=0, dense=(0, 0), legs=True, x=None):
+    """Times one workload on cuda:0.
+
+    Decode (block_q 1): the timed step is one hip_decode_step call.  With
+    `legs`: also the step as two calls (hip_mask_estimate + hip_sparse_attn),
+    the mask call alone, the attention call alone on each step's own lists,
+    and mask reuse every r_m steps.  Prefill: the step is the two calls; with
+    `legs` each call alone as well.  Returns milliseconds per step of each
+    and the lists of the eager step on the first query set and layer copy."""
     dev = torch.device("cuda:0")
-    x = si.make_inputs(w)
+    x = x if x is not None else si.make_inputs(w)
     layers, qs, shifts = setup(w, x, torch, dev, n_layers, n_q)
     if page_size:  # the same layer copies held in shuffled page pools
         assert w.T % page_size == 0
@@ -286,6 +323,7 @@ def run_workload(w, steps, warmup, torch, hs, si, with_cpu, cpu_budget,
             pooled.append((Kp, Vp, tab))
         del layers
         layers = pooled
+    decode = w.block_q == 1
     nqb = -(-w.Tq // w.block_q)
     idx = torch.empty((w.B, w.Hkv, nqb, w.kb), dtype=torch.int32, device=dev)
     nnz = torch.empty((w.B, w.Hkv, nqb), dtype=torch.int32, device=dev)
@@ -293,37 +331,44 @@ def run_workload(w, steps, warmup, torch, hs, si, with_cpu, cpu_budget,
     sink, window = dense
     wsb = hs.hipsa_workspace_bytes_ex(qs[0], x["K"], w.k, w.block_k, w.block_q, T=w.T, sink=sink,
                                       window=window)
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
-    kw = dict(T=w.T, causal=bool(w.causal))
+    if decode:  # the step's workspace (partials, then its zeroed arrival counters) covers both
+        wsb = max(wsb, hs.hipsa_decode_step_workspace_bytes(qs[0], x["K"], w.k, w.block_k, T=w.T,
+                                                            sink=sink, window=window))
+    ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device=dev)
+    ckw = dict(T=w.T, causal=bool(w.causal), sink=sink, window=window)
 
-    def mask(j):
+    def table(L):
+        return L[2] if page_size else None
+
+    def mask(j, idx=idx, nnz=nnz):
         q, L = qs[j % len(qs)], layers[j % len(layers)]
-        if sink or window:
-            hs.hip_mask_estimate_ex(q, L[0], w.k, w.block_k, w.block_q, T=w.T, causal=bool(w.causal),
-                                    sink=sink, window=window, indices=idx, nnz=nnz)
-        elif page_size:
-            hs.hip_mask_estimate_paged(q, L[0], L[2], w.T, w.k, w.block_k, w.block_q, indices=idx,
-                                       nnz=nnz, causal=bool(w.causal))
-        else:
-            hs.hip_mask_estimate(q, L[0], w.k, w.block_k, w.block_q, indices=idx, nnz=nnz, **kw)
+        hs.hip_mask_estimate_ex(q, L[0], w.k, w.block_k, w.block_q, block_table=table(L),
+                                indices=idx, nnz=nnz, **ckw)
 
-    def attn(j):
+    def attn(j, idx=idx, nnz=nnz):
         q, L = qs[j % len(qs)], layers[j % len(layers)]
-        if sink or window:
-            hs.hip_sparse_attn_ex(q, L[0], L[1], idx, nnz, w.k, w.block_k, w.block_q, T=w.T,
-                                  causal=bool(w.causal), sink=sink, window=window, out=out,
-                                  workspace=ws)
-        elif page_size:
-            hs.hip_sparse_attn_paged(q, L[0], L[1], L[2], idx, nnz, w.T, w.k, w.block_k, w.block_q,
-                                     causal=bool(w.causal), out=out, workspace=ws)
-        else:
-            hs.hip_sparse_attn(q, L[0], L[1], idx, nnz, w.k, w.block_k, w.block_q, out=out,
-                               workspace=ws, **kw)
+        hs.hip_sparse_attn_ex(q, L[0], L[1], idx, nnz, w.k, w.block_k, w.block_q,
+                              block_table=table(L), out=out, workspace=ws, **ckw)
 
-    def step(j):
+    def fused(j):
+        q, L = qs[j % len(qs)], layers[j % len(layers)]
+        hs.hip_decode_step(q, L[0], L[1], w.k, w.block_k, block_table=table(L), indices=idx,
+                           nnz=nnz, out=out, workspace=ws, **ckw)
+
+    def two_calls(j):
         mask(j)
         attn(j)
 
+    step = fused if decode else two_calls
+    # the lists and output of the eager step on the first query set and layer copy
+    step(0)
+    torch.cuda.synchronize()
+    first = {"indices": idx.cpu().numpy(), "nnz": nnz.cpu().numpy(), "out": out.float().cpu()}
+    if decode:  # the one-call step equals the two calls bit for bit
+        two_calls(0)
+        torch.cuda.synchronize()
+        assert (idx.cpu().numpy() == first["indices"]).all() and torch.equal(out.float().cpu(),
+                                                                              first["out"])
     # eager reference of the last timed step, to check the graph replays against
     step(steps - 1)
     torch.cuda.synchronize()
@@ -338,35 +383,71 @@ def run_workload(w, steps, warmup, torch, hs, si, with_cpu, cpu_budget,
     ms = time_graph(g_step, 1, torch)
     wall = time.perf_counter() - t0
     assert torch.equal(idx, eager[0]) and torch.equal(out, eager[1]), "graph replay differs from eager"
+    del g_warm, g_step
+    res = {"ms_per_step": ms / steps, "wall_s": wall, "shifts": shifts, "first": first}
+    if not legs:
+        return res
 
-    # per-kernel launch durations (graphs of one kernel kind)
-    g_mask = graph_of(mask, steps, torch)
-    g_attn = graph_of(attn, steps, torch)
-    g_mask.replay(); g_attn.replay()
-    ms_mask = time_graph(g_mask, 1, torch) / steps
-    ms_attn = time_graph(g_attn, 1, torch) / steps
+    def timed(fn, n):
+        g = graph_of(fn, n, torch)
+        g.replay()  # warm-up replay
+        t = time_graph(g, 1, torch) / n
+        del g
+        return t
 
-    res = {"ms_per_step": ms / steps, "wall_s": wall, "ms_mask": ms_mask, "ms_attn": ms_attn,
-           "shifts": shifts}
-    if w.block_q == 1:
-        # mask reuse: the mask estimated every r_m steps, attention every step
+    res["ms_mask"] = timed(mask, steps)
+    # attention alone, each step over the lists its own mask selected
+    lists = []
+    for j in range(steps):
+        mask(j)
+        lists.append((idx.clone(), nnz.clone()))
+    torch.cuda.synchronize()
+    res["ms_attn"] = timed(lambda j: attn(j, *lists[j]), steps)
+    if decode:
+        res["ms_two_calls"] = timed(two_calls, steps)
         reuse = {}
         for r_m in (2, 4, 8):
             def step_r(j, r_m=r_m):
                 if j % r_m == 0:
-                    mask(j)
-                attn(j)
-            g_r = graph_of(step_r, steps, torch)
-            g_r.replay()
-            reuse[r_m] = time_graph(g_r, 1, torch) / steps
-            del g_r
+                    fused(j)  # new lists, and the attention over them
+                else:
+                    attn(j)   # the lists of the last refresh
+            reuse[r_m] = timed(step_r, steps)
         res["ms_reuse"] = reuse
-    if with_cpu:
-        times, nt = cpu_baseline(x, w, cpu_budget)
-        res["cpu"] = {"times": times, "threads": nt}
-    del layers, qs
+    del layers, qs, lists
     torch.cuda.empty_cache()
     return res
+
+
+def needle_recall(w, x, indices):
+    """Share of (problem, needle block) pairs whose needle block is in the
+    problem's list: the GPU's lists (`indices`) and the oracle's, on the first
+    query set and layer copy (no roll, so the needles sit where drawn)."""
+    import numpy as np
+    import oracle
+    kw = dict(T=w.T, k=w.k, block_k=w.block_k, block_q=w.block_q, causal=w.causal)
+    o_idx, _, _ = oracle.mask_all(x["q"], x["K"], **kw)
+    needles = np.array(x["needles"])
+
+    def share(lists):
+        hits = [np.isin(needles, lists[b, g, 0]).sum() for b in range(w.B) for g in range(w.Hkv)]
+        return round(float(sum(hits)) / (len(hits) * len(needles)), 4)
+    return {"gpu": share(indices), "oracle": share(o_idx), "needles": len(needles),
+            "lists_equal": bool((indices == o_idx).all())}
+
+
+def decode_line(w, r) -> dict:
+    """Figures of one decode workload: µs per step and the step's roofline."""
+    nb = decode_bytes(w)
+    us = r["ms_per_step"] * 1e3
+    gbs = nb["step"] / (r["ms_per_step"] * 1e-3) / 1e9
+    d = {"workload": w.name, "us_per_step": round(us, 3), "algorithmic_bytes": nb["step"],
+         "achieved_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4), "rounds": nb["rounds"]}
+    for key, name in (("ms_two_calls", "two_calls_us"), ("ms_mask", "mask_us"),
+                      ("ms_attn", "attn_us")):
+        if key in r:
+            d[name] = round(r[key] * 1e3, 3)
+    return d
 
 
 def main():
@@ -383,9 +464,13 @@ def main():
     ap.add_argument("--no-dense", action="store_true", help="skip the sink + window leg")
     ap.add_argument("--sink", type=int, default=64, help="sink tokens of the dense-part leg")
     ap.add_argument("--window", type=int, default=4096, help="window tokens of the dense-part leg")
+    ap.add_argument("--no-other-decodes", action="store_true",
+                    help="skip the 32k and 1M-token decode legs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--only-step", action="store_true",
+                    help="time the headline step only (no legs): for kernel profiles of the step")
+    ap.add_argument("--cpu-budget", type=float, default=8.0)
     ap.add_argument("--layer-copies", type=int, default=N_LAYER_COPIES,
                     help="rolled K/V copies rotated over the steps (1 = one layer, cache-warm)")
     ap.add_argument("--query-sets", type=int, default=N_QUERY_SETS,
@@ -397,6 +482,9 @@ def main():
         print("bench.py: the library runs on exactly one GPU (no multi-GPU path); use --gpus 1",
               file=sys.stderr)
         sys.exit(2)
+    if args.only_step:
+        args.no_fp8 = args.no_paged = args.no_dense = args.no_other_decodes = True
+        args.no_prefill = args.no_cpu_baseline = True
 
     import torch
     import long_context_sparse_mask_amd as hs
@@ -406,8 +494,9 @@ def main():
     if args.kv == "e5m2":
         w = si.workload(args.workload, dtype="bf16_e5m2")
     is_decode = w.block_q == 1
-    r = run_workload(w, args.steps, args.warmup, torch, hs, si, not args.no_cpu_baseline,
-                     args.cpu_budget, args.layer_copies, args.query_sets)
+    x = si.make_inputs(w)
+    r = run_workload(w, args.steps, args.warmup, torch, hs, si, args.layer_copies,
+                     args.query_sets, legs=not args.only_step, x=x)
     us = r["ms_per_step"] * 1e3
     line = {"metric": "decode attn us/step/layer at 128k (mask+sparse) & % HBM peak; prefill tok/s",
             "value": round(us, 3) if is_decode else None, "unit": "us/step",
@@ -420,103 +509,99 @@ def main():
                        "query_sets": args.query_sets}}
     if is_decode:
         nb = decode_bytes(w)
-        kern = {"hip_mask_estimate": (r["ms_mask"], nb["mask"]),
-                "hip_sparse_attn": (r["ms_attn"], nb["attn"])}
-        def hbm_roof(k):
-            t_ms, byt = kern[k]
+
+        def hbm_roof(call, t_ms, byt, kernels):
             ach = byt / (t_ms * 1e-3) / 1e9
-            return {"bound": "hbm", "kernel": k, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                    "traffic": measured_traffic("decode", k, w.dtype), "algorithmic_bytes": byt,
+            return {"bound": "hbm", "kernel": call, "launches": kernels, "achieved": round(ach, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                    "traffic": measured_traffic("decode", call, w.dtype), "algorithmic_bytes": byt,
                     "launch_us": round(t_ms * 1e3, 3)}
-        dom = max(kern, key=lambda k: kern[k][0])  # the longer launch
-        line["roofline"] = hbm_roof(dom)
-        line["roofline_other"] = hbm_roof(min(kern, key=lambda k: kern[k][0]))
-        line["mask_reuse"] = {"r_m": [1] + sorted(r["ms_reuse"]),
-                              "us_per_step": [round(us, 3)] + [round(r["ms_reuse"][k] * 1e3, 3)
-                                                               for k in sorted(r["ms_reuse"])],
-                              "attention_only_us": round(r["ms_attn"] * 1e3, 3)}
-        step_gbs = nb["step"] / (r["ms_per_step"] * 1e-3) / 1e9
-        line["step_roofline"] = {"algorithmic_bytes": nb["step"], "achieved": round(step_gbs, 1),
-                                 "frac": round(step_gbs / HBM_PEAK_GBS, 4),
-                                 "mask_us": round(r["ms_mask"] * 1e3, 3),
-                                 "attn_us": round(r["ms_attn"] * 1e3, 3), "rounds": nb["rounds"]}
+        # the step is one call: its kernels (the one-launch search + attention, then the
+        # merge of the splits) carry every byte of the step
+        line["roofline"] = hbm_roof("hip_decode_step", r["ms_per_step"], nb["step"],
+                                    list(CALL_KERNELS.get(("decode", "hip_decode_step", w.dtype),
+                                                          CALL_KERNELS[("decode", "hip_decode_step")])))
+        if "ms_attn" in r:
+            line["roofline_other"] = {
+                "hip_sparse_attn": hbm_roof("hip_sparse_attn", r["ms_attn"], nb["attn"],
+                                            list(CALL_KERNELS[("decode", "hip_sparse_attn")])),
+                "hip_mask_estimate": hbm_roof("hip_mask_estimate", r["ms_mask"], nb["mask"],
+                                              list(CALL_KERNELS[("decode", "hip_mask_estimate")]))}
+            line["mask_reuse"] = {"r_m": [1] + sorted(r["ms_reuse"]),
+                                  "us_per_step": [round(us, 3)] + [round(r["ms_reuse"][k] * 1e3, 3)
+                                                                   for k in sorted(r["ms_reuse"])],
+                                  "attention_only_us": round(r["ms_attn"] * 1e3, 3)}
+        line["step_roofline"] = decode_line(w, r)
     else:
         fl = prefill_flops(w)
         tflops = fl["total"] / (r["ms_per_step"] * 1e-3) / 1e12
         line["value"] = round(w.B * w.Tq / (r["ms_per_step"] * 1e-3), 1)
         line["unit"] = "tok/s"
         line["higher_is_better"] = True
-        kern = {"hip_mask_estimate": (r["ms_mask"], fl["mask"]),
-                "hip_sparse_attn": (r["ms_attn"], fl["attn"])}
-        def mfma_roof(k):
-            t_ms, f = kern[k]
-            ach = f / (t_ms * 1e-3) / 1e12
-            return {"bound": "mfma", "kernel": k, "achieved": round(ach, 2),
-                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
-                    "traffic": measured_traffic("prefill", k, w.dtype),
-                    "algorithmic_flops": f, "launch_us": round(t_ms * 1e3, 3)}
-        dom = max(kern, key=lambda k: kern[k][0])  # the longer launch
-        line["roofline"] = mfma_roof(dom)
-        line["roofline_other"] = mfma_roof(min(kern, key=lambda k: kern[k][0]))
+        if "ms_attn" in r:
+            kern = {"hip_mask_estimate": (r["ms_mask"], fl["mask"]),
+                    "hip_sparse_attn": (r["ms_attn"], fl["attn"])}
+
+            def mfma_roof(k):
+                t_ms, f = kern[k]
+                ach = f / (t_ms * 1e-3) / 1e12
+                return {"bound": "mfma", "kernel": k, "achieved": round(ach, 2),
+                        "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
+                        "traffic": measured_traffic("prefill", k, w.dtype),
+                        "algorithmic_flops": f, "launch_us": round(t_ms * 1e3, 3)}
+            line["roofline"] = mfma_roof("hip_sparse_attn")
+            line["roofline_other"] = mfma_roof("hip_mask_estimate")
         line["step_roofline"] = {"algorithmic_flops": fl["total"], "achieved_tflops": round(tflops, 2),
-                                 "mask_us": round(r["ms_mask"] * 1e3, 3),
-                                 "attn_us": round(r["ms_attn"] * 1e3, 3)}
-    if "cpu" in r:
-        med = statistics.median(r["cpu"]["times"])
-        if is_decode:
-            cv, cu = med * 1e6, "us/step"
-        else:
-            cv, cu = w.B * w.Tq / med, "tok/s"
-        line["cpu_baseline"] = {"value": round(cv, 1), "unit": cu, "cores": r["cpu"]["threads"],
-                                "kind": "oracle",
-                                "sample": f"whole {w.name} step on the first query set and layer copy, "
-                                          f"median of {len(r['cpu']['times'])} runs "
-                                          f"({sum(r['cpu']['times']):.1f} s in all), fp64 C + OpenMP",
-                                "cpu_model": host_cpu_model()}
+                                 "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = (cpu_baseline(x, w, args.cpu_budget) if is_decode
+                                else cpu_baseline_prefill(si, args.cpu_budget))
+    del x
     headline = is_decode and args.workload == "decode_128k_b4" and args.kv == "native"
+    small = dict(steps=max(10, args.steps // 2), warmup=max(2, args.warmup // 2))
+    if headline and not args.no_other_decodes:
+        w1 = si.workload("decode_32k")
+        r1 = run_workload(w1, small["steps"], small["warmup"], torch, hs, si, args.layer_copies,
+                          args.query_sets)
+        line["decode_32k"] = decode_line(w1, r1)
+        w4 = si.workload("decode_1m_needles")
+        x4 = si.make_inputs(w4)
+        r4 = run_workload(w4, small["steps"], small["warmup"], torch, hs, si, 4, args.query_sets,
+                          x=x4)
+        line["decode_1m_needles"] = decode_line(w4, r4)
+        line["decode_1m_needles"]["needle_recall"] = needle_recall(w4, x4, r4["first"]["indices"])
+        del x4
     if headline and not args.no_fp8:
         # the same step with an fp8 (E5M2) KV cache: half the K/V bytes
         w8 = si.workload(args.workload, dtype="bf16_e5m2")
-        r8 = run_workload(w8, args.steps, args.warmup, torch, hs, si, False, 0,
-                          args.layer_copies, args.query_sets)
+        r8 = run_workload(w8, args.steps, args.warmup, torch, hs, si, args.layer_copies,
+                          args.query_sets)
         nb8 = decode_bytes(w8)
         a_gbs = nb8["attn"] / (r8["ms_attn"] * 1e-3) / 1e9
-        s_gbs = nb8["step"] / (r8["ms_per_step"] * 1e-3) / 1e9
-        line["fp8_kv"] = {"workload": w8.name, "dtype": w8.dtype,
-                          "us_per_step": round(r8["ms_per_step"] * 1e3, 3),
-                          "mask_us": round(r8["ms_mask"] * 1e3, 3),
-                          "attn_us": round(r8["ms_attn"] * 1e3, 3),
-                          "attn_roofline": {"algorithmic_bytes": nb8["attn"], "achieved": round(a_gbs, 1),
-                                            "frac": round(a_gbs / HBM_PEAK_GBS, 4),
-                                            "traffic": measured_traffic("decode", "hip_sparse_attn",
-                                                                        w8.dtype)},
-                          "step_roofline": {"algorithmic_bytes": nb8["step"], "achieved": round(s_gbs, 1),
-                                            "frac": round(s_gbs / HBM_PEAK_GBS, 4)},
-                          "mask_reuse_us": {str(k): round(v * 1e3, 3)
-                                            for k, v in sorted(r8["ms_reuse"].items())}}
+        line["fp8_kv"] = decode_line(w8, r8)
+        line["fp8_kv"]["attn_roofline"] = {
+            "algorithmic_bytes": nb8["attn"], "achieved": round(a_gbs, 1),
+            "frac": round(a_gbs / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic("decode", "hip_sparse_attn", w8.dtype)}
+        line["fp8_kv"]["mask_reuse_us"] = {str(k): round(v * 1e3, 3)
+                                           for k, v in sorted(r8["ms_reuse"].items())}
     if headline and not args.no_paged:
         # the same step with K/V in a page pool: pages of page_size tokens in a random order
-        rpg = run_workload(w, args.steps, args.warmup, torch, hs, si, False, 0,
-                           args.layer_copies, args.query_sets, page_size=args.page_size)
-        line["paged_kv"] = {"page_size": args.page_size, "pages": "shuffled over the pool",
-                            "us_per_step": round(rpg["ms_per_step"] * 1e3, 3),
-                            "mask_us": round(rpg["ms_mask"] * 1e3, 3),
-                            "attn_us": round(rpg["ms_attn"] * 1e3, 3)}
+        rpg = run_workload(w, small["steps"], small["warmup"], torch, hs, si, args.layer_copies,
+                           args.query_sets, page_size=args.page_size)
+        line["paged_kv"] = dict(decode_line(w, rpg), page_size=args.page_size,
+                                pages="shuffled over the pool")
     if headline and not args.no_dense:
         # the same step with a dense part: sink and sliding-window blocks beside the search
-        rd = run_workload(w, args.steps, args.warmup, torch, hs, si, False, 0, args.layer_copies,
+        rd = run_workload(w, small["steps"], small["warmup"], torch, hs, si, args.layer_copies,
                           args.query_sets, dense=(args.sink, args.window))
-        line["dense_part"] = {"sink": args.sink, "window": args.window,
-                              "keys_per_row": args.sink + args.window + w.k,
-                              "us_per_step": round(rd["ms_per_step"] * 1e3, 3),
-                              "mask_us": round(rd["ms_mask"] * 1e3, 3),
-                              "attn_us": round(rd["ms_attn"] * 1e3, 3)}
+        line["dense_part"] = dict(decode_line(w, rd), sink=args.sink, window=args.window,
+                                  keys_per_row=args.sink + args.window + w.k)
     if headline and not args.no_prefill:
         wp = si.workload("prefill_32k_chunk4k")
-        rp = run_workload(wp, max(4, args.steps // 20), max(1, args.warmup // 10), torch, hs, si,
-                          False, 0)
+        psteps, pwarm = max(4, args.steps // 20), max(1, args.warmup // 10)
+        rp = run_workload(wp, psteps, pwarm, torch, hs, si, 4)
         fl = prefill_flops(wp)
         line["prefill"] = {"workload": wp.name,
                            "tok_per_s": round(wp.Tq / (rp["ms_per_step"] * 1e-3), 1),
@@ -525,11 +610,12 @@ def main():
                            "attn_us": round(rp["ms_attn"] * 1e3, 2),
                            "mfma_frac": round(fl["total"] / (rp["ms_per_step"] * 1e-3) / 1e12
                                               / MFMA_BF16_PEAK_TFLOPS, 4),
+                           "attn_mfma_frac": round(fl["attn"] / (rp["ms_attn"] * 1e-3) / 1e12
+                                                   / MFMA_BF16_PEAK_TFLOPS, 4),
                            "algorithmic_flops": fl["total"]}
         if not args.no_fp8:
             wp8 = si.workload("prefill_32k_chunk4k", dtype="bf16_e5m2")
-            rp8 = run_workload(wp8, max(4, args.steps // 20), max(1, args.warmup // 10), torch, hs,
-                               si, False, 0)
+            rp8 = run_workload(wp8, psteps, pwarm, torch, hs, si, 4)
             line["prefill"]["fp8_kv"] = {"tok_per_s": round(wp8.Tq / (rp8["ms_per_step"] * 1e-3), 1),
                                          "mask_us": round(rp8["ms_mask"] * 1e3, 2),
                                          "attn_us": round(rp8["ms_attn"] * 1e3, 2)}

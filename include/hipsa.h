@@ -214,6 +214,35 @@ size_t hipsa_workspace_bytes_ex(const hipsa_desc *desc, const hipsa_ext *ext, in
                                 int64_t block_k, int64_t block_q);
 
 /*
+ * One decode step (block_q = 1): hip_mask_estimate followed by hip_sparse_attn
+ * on the lists it writes, in one call (rebuttal page, reviewer KprR, W2: the
+ * reported latency is masking plus sparse attention).  Results are bit for
+ * bit those of the two calls: indices/nnz as hip_mask_estimate writes them
+ * (so later steps may reuse the mask with hip_sparse_attn), out as
+ * hip_sparse_attn computes it.  For bf16 K/V in the contiguous layout with
+ * k / block_k <= 32 the search and the attention of a problem run in one
+ * launch (each split workgroup runs the problem's search itself and attends
+ * its share of the kept blocks) followed by the merge of the splits; other
+ * cases run the two calls' kernels in turn.  In the one-launch form the last
+ * split workgroup of each problem to finish merges the splits, so a step is
+ * a single kernel launch.
+ *   ext: dense part and paged layout as in the *_ex calls, or NULL.
+ *   workspace: hipsa_decode_step_workspace_bytes() bytes, 16-byte aligned,
+ *     zero-filled before its first use (it holds one arrival counter per
+ *     problem; every call leaves them at zero, so a workspace serves any
+ *     number of later calls).  Calls sharing a workspace must be ordered on
+ *     one stream.
+ */
+int hip_decode_step(const hipsa_desc *desc, const hipsa_ext *ext, const void *q, const void *K,
+                    const void *V, int64_t k, int64_t block_k, int32_t *indices, int32_t *nnz,
+                    void *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes of hip_decode_step for this shape (SIZE_MAX when the
+ * arguments are invalid; 0 for empty problems). */
+size_t hipsa_decode_step_workspace_bytes(const hipsa_desc *desc, const hipsa_ext *ext, int64_t k,
+                                         int64_t block_k);
+
+/*
  * hip_sparse_attn without a workspace argument, for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation.  Arguments, checks and results are those

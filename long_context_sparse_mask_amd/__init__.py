@@ -24,7 +24,8 @@ import torch  # loads the HIP runtime first, so libhipsa binds to the same one
 
 __all__ = ["hip_mask_estimate", "hip_sparse_attn", "hip_mask_estimate_paged",
            "hip_sparse_attn_paged", "hip_mask_estimate_ex", "hip_sparse_attn_ex",
-           "hip_sparse_attn_noalloc", "hipsa_workspace_bytes", "hipsa_workspace_bytes_ex",
+           "hip_sparse_attn_noalloc", "hip_decode_step", "hipsa_decode_step_workspace_bytes",
+           "hipsa_workspace_bytes", "hipsa_workspace_bytes_ex",
            "HipsaError", "LIB_PATH", "lib", "NOALLOC_SCRATCH_BYTES"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhipsa.so")
@@ -71,6 +72,11 @@ lib.hip_mask_estimate_ex.restype = C.c_int
 lib.hip_sparse_attn_ex.argtypes = [C.POINTER(Desc), C.POINTER(Ext), _P, _P, _P, _P, _P, _I64, _I64,
                                    _I64, _P, _P, _SZ, _P]
 lib.hip_sparse_attn_ex.restype = C.c_int
+lib.hip_decode_step.argtypes = [C.POINTER(Desc), C.POINTER(Ext), _P, _P, _P, _I64, _I64, _P, _P, _P,
+                                _P, _SZ, _P]
+lib.hip_decode_step.restype = C.c_int
+lib.hipsa_decode_step_workspace_bytes.argtypes = [C.POINTER(Desc), C.POINTER(Ext), _I64, _I64]
+lib.hipsa_decode_step_workspace_bytes.restype = C.c_size_t
 lib.hip_sparse_attn_noalloc.argtypes = [C.POINTER(Desc), _P, _P, _P, _P, _P, _I64, _I64, _I64, _P,
                                         _P]
 lib.hip_sparse_attn_noalloc.restype = C.c_int
@@ -385,3 +391,47 @@ def hip_sparse_attn_ex(q, K, V, indices, nnz, k: int, block_k: int, block_q: int
                                   p(nnz, "nnz"), k, block_k, block_q, p(out, "out"),
                                   ws_ptr, ws_len, _stream(q.device, stream)))
     return out
+
+
+# ------------------------------------------------------------------ one decode step
+
+def hipsa_decode_step_workspace_bytes(q, K, k: int, block_k: int, *, T=None, causal=True, sink=0,
+                                      window=0, block_table=None) -> int:
+    desc, ext, _pages = _ext_desc(q, K, T, causal, sink, window, block_table)
+    n = lib.hipsa_decode_step_workspace_bytes(C.byref(desc), C.byref(ext), k, block_k)
+    if n == SIZE_MAX:
+        raise HipsaError(-2, lib.hipsa_last_error().decode())
+    return n
+
+
+def hip_decode_step(q, K, V, k: int, block_k: int, *, T=None, causal=True, sink=0, window=0,
+                    block_table=None, indices=None, nnz=None, out=None, workspace=None,
+                    stream=None):
+    """hip_mask_estimate then hip_sparse_attn (block_q = 1) in one call.
+    Returns (out, indices, nnz), bit for bit the two calls' results.  A
+    caller's `workspace` (hipsa_decode_step_workspace_bytes bytes) must be
+    zero-filled before its first use; every call leaves it reusable."""
+    p = _on(q.device)  # device pointer of a tensor on q's device
+    desc, ext, _pages = _ext_desc(q, K, T, causal, sink, window, block_table)
+    _check_v(K, V)
+    kb = k // block_k if block_k > 0 else 0
+    if indices is None:
+        indices = torch.empty((desc.B, desc.Hkv, desc.Tq, kb), dtype=torch.int32, device=q.device)
+    if nnz is None:
+        nnz = torch.empty((desc.B, desc.Hkv, desc.Tq), dtype=torch.int32, device=q.device)
+    _check_lists(indices, nnz, desc, desc.Tq, kb, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_out(out, q)
+    if desc.B * desc.Tq == 0:
+        return out, indices, nnz
+    if workspace is None:  # zero-filled: it holds the arrival counters
+        workspace = torch.zeros(hipsa_decode_step_workspace_bytes(
+            q, K, k, block_k, T=T, causal=causal, sink=sink, window=window,
+            block_table=block_table), dtype=torch.uint8, device=q.device)
+    ws_ptr = p(workspace, "workspace")
+    ws_len = workspace.numel() * workspace.element_size()
+    _check(lib.hip_decode_step(C.byref(desc), C.byref(ext), p(q, "q"), p(K, "K"), p(V, "V"), k,
+                               block_k, p(indices, "indices"), p(nnz, "nnz"), p(out, "out"),
+                               ws_ptr, ws_len, _stream(q.device, stream)))
+    return out, indices, nnz

@@ -1,0 +1,163 @@
+// One decode step in one launch: the hierarchical top-k search of a problem
+// and its block-sparse attention, followed by the merge of the split partials.
+//
+// The pages report decode latency as masking plus sparse attention (rebuttal
+// page "A Training-free Sub-quadratic Cost Transformer Model Serving Framework
+// With Hierarchically Pruned Attention", reviewer KprR, W2), and the mask is
+// consumed by the attention right away unless it is reused across steps
+// (summary page, Limitations: the mask refresh interval).  Run as two
+// launches, the attention kernel waits for the mask kernel to end and then
+// reads the lists back from memory.  Here every split workgroup of a problem
+// runs the problem's search itself (search_pipe), holds the kept blocks in
+// LDS and attends its share of them (attend_split); no workgroup waits for
+// another.  The search is latency-bound (serially dependent rounds of row
+// gathers) and cheap, so running it once per split costs little time: the
+// splits of a problem run on one XCD (xcd_swizzle), where they read the
+// same centre rows through its L2.  Split 0 also writes the lists, so a
+// later step can reuse the mask through hip_sparse_attn.
+//
+// The last split workgroup of a problem to finish merges the splits'
+// partials (no second launch).  Results are bit for bit those of
+// hip_mask_estimate followed by hip_sparse_attn: the same search, the same
+// split assignment of the same ascending list, the same merge arithmetic
+// (merge_partials).
+#include "decode_search.h"
+#include "decode_split.h"
+#include "hipsa_internal.h"
+#include "mask_select.h"
+
+namespace hipsa {
+namespace {
+
+// bf16 query and keys, contiguous layout, K_b <= kPipeMaxKb.
+template <int D, int GMAX, int TPW, int TOK, bool WIDE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void decode_step_kernel(StepArgs a) {
+  const Shape &s = a.at.s;
+  const int tid = threadIdx.x;
+  const uint32_t S = (uint32_t)a.at.splits;
+  const uint32_t wgi = xcd_swizzle(blockIdx.x, gridDim.x);
+  const uint32_t split = wgi % S, prob = wgi / S;
+  const uint32_t Tq = (uint32_t)s.Tq, Hkv = (uint32_t)s.Hkv;
+  const uint32_t i = prob % Tq, g = (prob / Tq) % Hkv, b = prob / (Tq * Hkv);
+  const int32_t Tp = s.causal ? (int32_t)(s.T - s.Tq + i + 1) : (int32_t)s.T;
+  const int32_t Np = (Tp + s.bk - 1) >> s.bk_shift;
+  const int32_t Kb = s.Kb;
+  const Dense dn(s, Np);  // the search covers the M blocks from `first` between the dense parts
+  const int32_t first = dn.Sb, M = Np - dn.Sb - dn.Wb;
+
+  __shared__ int32_t list[kPipeMaxKb];
+  __shared__ int32_t cnt;
+  if (M <= Kb) {  // the row sees few enough blocks to keep them all
+    for (int j = tid; j < Kb; j += 256) list[j] = j < M ? first + j : -1;
+    if (tid == 0) cnt = M;
+  } else {
+    search_pipe<uint16_t, D, GMAX, TPW, false>(a.at.q, a.at.K, s, a.at.pg, b, g, i, Tp, first, M, list);
+    if (tid == 0) cnt = Kb;
+  }
+  __syncthreads();
+  if (split == 0) {  // the mask, for later steps that reuse it
+    int32_t *out = a.indices + (int64_t)prob * Kb;
+    for (int j = tid; j < Kb; j += 256) out[j] = list[j];
+    if (tid == 0) a.nnz[prob] = cnt;
+  }
+  attend_split<uint16_t, D, GMAX, TOK, false, WIDE, true>(a.at, prob, split, list, &cnt);
+  if (S == 1) return;  // the only split wrote the output
+
+  // Arrival: the last split workgroup of the problem to finish merges the S
+  // partials.  The partials, the arrival counter and the merger's reads of
+  // the partials are all agent-scope atomic accesses: gfx950 performs such
+  // stores and loads at the device's coherence point (the stores write
+  // through, the loads bypass non-coherent caches), so once every thread's
+  // partial stores have completed (the explicit wait: a workgroup barrier
+  // does not wait for stores) and the counter has been incremented, the
+  // workgroup that sees S - 1 earlier arrivals reads every partial as
+  // written.  No cache write-back or invalidation is needed.  (Agent-scope
+  // release/acquire fences around the counter, which write back and
+  // invalidate the L2, measured 3.8 us slower per 128k x 4 step.)
+  __shared__ uint32_t before;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0)
+    before = __hip_atomic_fetch_add(a.arrived + prob, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (before != S - 1) return;
+  if (tid == 0) __hip_atomic_store(a.arrived + prob, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t G = (uint32_t)s.G;
+  const int64_t sstride = (int64_t)G * (D + 2);
+  auto load = [](const float *p) {
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  uint16_t *out = reinterpret_cast<uint16_t *>(a.at.out);
+  for (int oi = tid; oi < (int)G * D; oi += 256) {
+    const int h = oi / D, x = oi % D;
+    const float *ph = a.at.ws + ((int64_t)prob * S * G + h) * (D + 2);
+    const float v = S <= 16 ? merge_partials<16>(ph, (int)S, sstride, x, load)
+                            : merge_partials<32>(ph, (int)S, sstride, x, load);
+    store_elem(out + ((int64_t)(b * s.Hq + g * G + h) * Tq + i) * D + x, v);
+  }
+}
+
+template <int D, int GMAX, int TPW>
+void launch_tok(const StepArgs &a, hipStream_t st) {
+  const dim3 grid((unsigned)(a.at.s.problems * a.at.splits)), block(256);
+  const bool wide = (int64_t)a.at.s.problems * a.at.splits >= kWideGrid;
+  const int tok = attn_decode_tokens(a.at.s);
+  constexpr int G8 = GMAX <= 8 ? GMAX : 8;
+  if (GMAX <= 8 && tok == 256) {
+    hipLaunchKernelGGL((decode_step_kernel<D, G8, TPW, 256, true>), grid, block, 0, st, a);
+  } else if (GMAX <= 8 && tok == 128) {
+    if (wide) hipLaunchKernelGGL((decode_step_kernel<D, G8, TPW, 128, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((decode_step_kernel<D, G8, TPW, 128, false>), grid, block, 0, st, a);
+  } else {
+    if (wide) hipLaunchKernelGGL((decode_step_kernel<D, GMAX, TPW, 64, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((decode_step_kernel<D, GMAX, TPW, 64, false>), grid, block, 0, st, a);
+  }
+}
+
+template <int D, int GMAX>
+void launch_g(const StepArgs &a, hipStream_t st) {
+  const int tiles = (4 * a.at.s.Kb + 15) / 16;  // child tiles per round, over 3 waves
+  const int per = (tiles + 2) / 3;
+  if (per <= 1) launch_tok<D, GMAX, 1>(a, st);
+  else if (per <= 2) launch_tok<D, GMAX, 2>(a, st);
+  else launch_tok<D, GMAX, 4>(a, st);
+}
+
+template <int D>
+void launch_d(const StepArgs &a, hipStream_t st) {
+  const int G = a.at.s.G;
+  if (G <= 1) launch_g<D, 1>(a, st);
+  else if (G <= 2) launch_g<D, 2>(a, st);
+  else if (G <= 4) launch_g<D, 4>(a, st);
+  else if (G <= 8) launch_g<D, 8>(a, st);
+  else launch_g<D, 16>(a, st);
+}
+
+}  // namespace
+
+hipError_t launch_decode_step(const StepArgs &a, hipStream_t st) {
+  const Shape &s = a.at.s;
+  // The one-launch form covers what the pipelined search covers (bf16 keys in
+  // the contiguous layout, K_b <= kPipeMaxKb); otherwise the two calls' kernels
+  // run in turn on the same lists.
+  if (s.dtype != HIPSA_BF16 || a.at.pg.table || s.Kb > kPipeMaxKb) {
+    MaskArgs m{a.at.q, a.at.K, a.indices, a.nnz, s, a.at.pg};
+    hipError_t e = launch_mask_decode(m, st);
+    if (e != hipSuccess) return e;
+    AttnArgs at = a.at;
+    at.indices = a.indices;
+    at.nnz = a.nnz;
+    return launch_attn_decode(at, st);
+  }
+  if (s.d == 64) launch_d<64>(a, st);
+  else launch_d<128>(a, st);
+  return hipGetLastError();  // the last split workgroup of each problem merged the partials
+}
+
+size_t decode_step_workspace(const Shape &s) {
+  if (s.problems == 0) return 0;
+  const size_t partials = (attn_decode_workspace(s) + 255) / 256 * 256;
+  return partials + (size_t)s.problems * sizeof(uint32_t);
+}
+
+}  // namespace hipsa

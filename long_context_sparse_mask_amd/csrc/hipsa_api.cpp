@@ -294,6 +294,45 @@ int hip_sparse_attn_paged(const hipsa_desc *desc, const hipsa_pages *pages, cons
                             workspace, workspace_bytes, stream);
 }
 
+int hip_decode_step(const hipsa_desc *desc, const hipsa_ext *ext, const void *q, const void *K,
+                    const void *V, int64_t k, int64_t block_k, int32_t *indices, int32_t *nnz,
+                    void *out, void *workspace, size_t workspace_bytes, void *stream) {
+  hipsa::Shape s;
+  hipsa::Pages pg;
+  int rc = prepare(desc, ext, k, block_k, 1, true, &s, &pg);
+  if (rc) return rc;
+  if (s.problems == 0) return ok();
+  if (!q || !K || !V || !indices || !nnz || !out)
+    return fail(HIPSA_ERR_NULL, "q, K, V, indices, nnz and out must be non-NULL");
+  if (pg.max_pages > 0 && !pg.table)
+    return fail(HIPSA_ERR_NULL, "pages->table must be non-NULL");
+  {
+    const void *p[] = {q, K, V, out};
+    const char *nm[] = {"q", "K", "V", "out"};
+    if ((rc = check_aligned(p, nm, 4))) return rc;
+  }
+  const size_t need = hipsa::decode_step_workspace(s);
+  if (!workspace || workspace_bytes < need)
+    return fail(HIPSA_ERR_WORKSPACE, "workspace of %zu bytes at %p is too small: need %zu",
+                workspace_bytes, workspace, need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+    return fail(HIPSA_ERR_ALIGN, "workspace at %p is not 16-byte aligned", workspace);
+  hipsa::StepArgs a{};
+  a.at.q = q; a.at.K = K; a.at.V = V; a.at.out = out;
+  a.at.ws = static_cast<float *>(workspace);
+  a.at.s = s;
+  a.at.pg = pg;
+  a.at.scale = (float)(1.0 / __builtin_sqrt((double)s.d));
+  a.at.splits = hipsa::attn_decode_splits(s);
+  a.indices = indices;
+  a.nnz = nnz;
+  a.arrived = reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) + need -
+                                           (size_t)s.problems * sizeof(uint32_t));
+  hipError_t e = hipsa::launch_decode_step(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "decode step launch");
+  return ok();
+}
+
 int hip_sparse_attn_noalloc(const hipsa_desc *desc, const void *q, const void *K, const void *V,
                             const int32_t *indices, const int32_t *nnz, int64_t k, int64_t block_k,
                             int64_t block_q, void *out, void *stream) {
@@ -318,6 +357,15 @@ int hip_sparse_attn_noalloc(const hipsa_desc *desc, const void *q, const void *K
   if (e != hipSuccess) return hip_fail(e, "scratch lookup");
   return attn_impl(s, kContiguous, q, K, V, indices, nnz, out, scratch,
                    hipsa::kNoAllocScratchBytes, stream);
+}
+
+size_t hipsa_decode_step_workspace_bytes(const hipsa_desc *desc, const hipsa_ext *ext, int64_t k,
+                                         int64_t block_k) {
+  hipsa::Shape s;
+  hipsa::Pages pg;
+  if (prepare(desc, ext, k, block_k, 1, true, &s, &pg)) return SIZE_MAX;
+  g_err.clear();
+  return hipsa::decode_step_workspace(s);
 }
 
 size_t hipsa_workspace_bytes(const hipsa_desc *desc, int64_t k, int64_t block_k,

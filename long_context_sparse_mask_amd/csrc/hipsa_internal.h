@@ -56,11 +56,24 @@ struct AttnArgs {
   Pages pg;
 };
 
+// One decode step: the search and the split attention of a problem in one
+// launch, then the merge; indices/nnz receive the mask like hip_mask_estimate.
+struct StepArgs {
+  AttnArgs at;  // at.indices, at.nnz unused: the lists stay on chip
+  int32_t *indices, *nnz;
+  uint32_t *arrived;  // per problem: split workgroups done (zero between calls)
+};
+
 // Decode / per-row problems (block_q == 1).
 hipError_t launch_mask_decode(const MaskArgs &a, hipStream_t st);
 hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t st);
+hipError_t launch_attn_combine(const AttnArgs &a, hipStream_t st);  // merge of the split partials
+hipError_t launch_decode_step(const StepArgs &a, hipStream_t st);
 size_t attn_decode_workspace(const Shape &s);
+size_t decode_step_workspace(const Shape &s);  // partials, then one arrival counter per problem
 int32_t attn_decode_splits(const Shape &s);
+int attn_decode_tokens(const Shape &s);  // tokens per split workgroup
+constexpr int64_t kWideGrid = 1024;  // split workgroups from which V rows are read 16 bytes per lane
 
 // Chunked prefill (block_q == 64, bf16).
 hipError_t launch_mask_prefill(const MaskArgs &a, hipStream_t st);

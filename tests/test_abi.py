@@ -22,7 +22,8 @@ def _declared():
 def test_header_declares_the_boundary():
     assert _declared() == sorted(["hip_mask_estimate", "hip_sparse_attn", "hip_mask_estimate_paged",
                                   "hip_sparse_attn_paged", "hip_mask_estimate_ex",
-                                  "hip_sparse_attn_ex", "hip_sparse_attn_noalloc",
+                                  "hip_sparse_attn_ex", "hip_sparse_attn_noalloc", "hip_decode_step",
+                                  "hipsa_decode_step_workspace_bytes",
                                   "hipsa_workspace_bytes", "hipsa_workspace_bytes_ex",
                                   "hipsa_last_error"])
 
@@ -96,8 +97,8 @@ def test_workspace_query_and_undersized_workspace():
     import long_context_sparse_mask_amd as hs
     d = _desc(B=4, T=131072, T_cap=131072)
     need = hs.lib.hipsa_workspace_bytes(C.byref(d), 2048, 64, 1)
-    # 32 problems x 16 splits of 128 tokens x 4 heads x (d + 2) floats
-    assert need == 32 * 16 * 4 * 130 * 4
+    # 32 problems x 8 splits of 256 tokens x 4 heads x (d + 2) floats
+    assert need == 32 * 8 * 4 * 130 * 4
     rc = hs.lib.hip_sparse_attn(C.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 2048, 64, 1, FAKE,
                                 FAKE, need - 1, None)
     assert rc == ERR_WS and "too small" in hs.lib.hipsa_last_error().decode()
@@ -111,7 +112,7 @@ def test_fp8_kv_dtype_is_accepted_for_decode_and_prefill():
     stays rejected."""
     import long_context_sparse_mask_amd as hs
     d = _desc(B=4, T=131072, T_cap=131072, dtype=hs.HIPSA_BF16_E5M2)
-    assert hs.lib.hipsa_workspace_bytes(C.byref(d), 2048, 64, 1) == 32 * 16 * 4 * 130 * 4
+    assert hs.lib.hipsa_workspace_bytes(C.byref(d), 2048, 64, 1) == 32 * 8 * 4 * 130 * 4
     p = _desc(Tq=4096, dtype=hs.HIPSA_BF16_E5M2)
     assert hs.lib.hipsa_workspace_bytes(C.byref(p), 2048, 64, 64) == 0
     assert hs.lib.hipsa_workspace_bytes(C.byref(_desc(Tq=4096, dtype=0)), 2048, 64, 64) == hs.SIZE_MAX
@@ -119,16 +120,25 @@ def test_fp8_kv_dtype_is_accepted_for_decode_and_prefill():
 
 
 def test_one_split_when_it_covers_the_key_sequence():
-    """Decode splits a row's key sequence over workgroups of 64 or 128 tokens;
-    a sequence that one workgroup covers gets a single split (its workgroup
-    writes the output, no merge is launched).  Seen through the workspace size,
-    problems x splits x G x (d + 2) floats."""
+    """Decode splits a row's key sequence over workgroups of 64 to 256 tokens
+    (the largest giving one workgroup per CU); a sequence that one workgroup
+    covers gets a single split (its workgroup writes the output, no merge
+    follows).  Seen through the workspace size, problems x splits x G x
+    (d + 2) floats."""
     import long_context_sparse_mask_amd as hs
     # bf16, 128 listed tokens, 32 problems of G = 4: one split each
     d = _desc(B=1, T=8192, T_cap=8192)
     assert hs.lib.hipsa_workspace_bytes(C.byref(d), 128, 64, 1) == 8 * 1 * 4 * 130 * 4
-    # 256 tokens on few problems: 64-token splits
-    assert hs.lib.hipsa_workspace_bytes(C.byref(d), 256, 64, 1) == 8 * 4 * 4 * 130 * 4
+    # 256 tokens: one split of 256
+    assert hs.lib.hipsa_workspace_bytes(C.byref(d), 256, 64, 1) == 8 * 1 * 4 * 130 * 4
+    # 512 tokens on 8 problems: 64-token splits give 64 workgroups (larger ones fewer)
+    assert hs.lib.hipsa_workspace_bytes(C.byref(d), 512, 64, 1) == 8 * 8 * 4 * 130 * 4
+    # 128k x 4 (32 problems, 2048 tokens): 256-token splits already give 256 workgroups
+    d4 = _desc(B=4, T=131072, T_cap=131072)
+    assert hs.lib.hipsa_workspace_bytes(C.byref(d4), 2048, 64, 1) == 32 * 8 * 4 * 130 * 4
+    # groups of more than 8 query heads: 64-token splits
+    d16 = _desc(B=4, Hq=32, Hkv=2, T=131072, T_cap=131072)
+    assert hs.lib.hipsa_workspace_bytes(C.byref(d16), 2048, 64, 1) == 8 * 32 * 16 * 130 * 4
     # fp32 at d = 128 takes at most 64 tokens per split
     d32 = _desc(B=1, T=8192, T_cap=8192, dtype=0)
     assert hs.lib.hipsa_workspace_bytes(C.byref(d32), 64, 64, 1) == 8 * 1 * 4 * 130 * 4
@@ -226,9 +236,9 @@ def test_dense_part_validation_and_workspace():
         return hs.lib.hipsa_workspace_bytes_ex(C.byref(d), C.byref(hs.Ext(None, sink, window)), k,
                                                bk, 1)
     plain = hs.lib.hipsa_workspace_bytes(C.byref(d), 2048, 64, 1)
-    assert ws(0, 0) == plain == 32 * 16 * 4 * 130 * 4
-    # 1 sink + 64 window + 32 listed blocks = 6208 tokens: 49 splits of 128 tokens
-    assert ws(64, 4096) == 32 * 49 * 4 * 130 * 4
+    assert ws(0, 0) == plain == 32 * 8 * 4 * 130 * 4
+    # 1 sink + 64 window + 32 listed blocks = 6208 tokens: 25 splits of 256 tokens
+    assert ws(64, 4096) == 32 * 25 * 4 * 130 * 4
     for sink, window in ((-64, 0), (32, 0), (0, 100), (64 * 200, 64 * 57)):
         assert ws(sink, window) == hs.SIZE_MAX
     assert ws(64 * 200, 64 * 56) != hs.SIZE_MAX  # exactly 256 blocks
@@ -375,3 +385,33 @@ def test_noalloc_rejects_shapes_beyond_its_scratch():
     # empty problems: no pointer is read
     assert hs.lib.hip_sparse_attn_noalloc(C.byref(_desc(B=0)), None, None, None, None, None, 2048,
                                           64, 1, None, None) == 0
+
+
+def test_decode_step_rejects_invalid_arguments():
+    """hip_decode_step runs the checks of both calls before any HIP call."""
+    import long_context_sparse_mask_amd as hs
+
+    def step(desc, ext=None, k=2048, bk=64, ptrs=None, ws=1 << 30):
+        q, K, V, idx, nnz, out, wsp = ptrs or (FAKE,) * 7
+        return hs.lib.hip_decode_step(C.byref(desc), C.byref(ext) if ext else None, q, K, V, k, bk,
+                                      idx, nnz, out, wsp, ws, None)
+    assert step(_desc(Hq=30)) == ERR_SHAPE
+    assert step(_desc(), k=2000) == ERR_BLOCK
+    assert step(_desc(dtype=9)) == ERR_DTYPE
+    assert step(_desc(), ext=hs.Ext(None, 32, 0)) == ERR_BLOCK  # sink not a multiple of block_k
+    assert step(_desc(), ptrs=(FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE)) == ERR_NULL
+    assert step(_desc(), ptrs=(FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE)) == ERR_NULL
+    odd = C.c_void_p(0x1008)
+    assert step(_desc(), ptrs=(FAKE, FAKE, FAKE, FAKE, FAKE, odd, FAKE)) == ERR_ALIGN
+    assert step(_desc(), ws=0) == ERR_WS
+    big = _desc(B=4, T=131072, T_cap=131072)
+    need = hs.lib.hipsa_decode_step_workspace_bytes(C.byref(big), None, 2048, 64)
+    # 32 problems x 8 splits x 4 heads x 130 floats of partials, then 32 arrival counters
+    assert need == 32 * 8 * 4 * 130 * 4 + 32 * 4
+    assert step(big, ws=need - 1) == ERR_WS
+    assert step(_desc(), ptrs=(FAKE,) * 6 + (C.c_void_p(0x1008),)) == ERR_ALIGN  # workspace
+    pages = _pages(page_size=48)
+    assert step(_desc(T_cap=0), ext=hs.Ext(C.pointer(pages), 0, 0)) == ERR_PAGES
+    # empty problems read no pointer
+    assert hs.lib.hip_decode_step(C.byref(_desc(B=0)), None, None, None, None, 2048, 64, None,
+                                  None, None, None, 0, None) == 0

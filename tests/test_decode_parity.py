@@ -82,8 +82,9 @@ def test_edge(case):
     _report(case, r)
 
 
-# Grids of >= 1024 split workgroups, where the bf16-query split kernel reads
-# V rows 16 bytes per lane (many query rows make many problems).
+# Cases where the bf16-query split kernel reads V rows 16 bytes per lane:
+# 256-token splits, or grids of >= 1024 split workgroups (many query rows
+# make many problems; with groups of more than 8 heads, 64-token splits).
 WIDE = {
     "wide_bf16_d128": dict(base="decode_32k", Hq=32, Hkv=8, Tq=16, T=4096, k=1024),
     "wide_e5m2_d128": dict(base="decode_32k", Hq=32, Hkv=8, Tq=16, T=4096, k=1024, dtype="bf16_e5m2"),
@@ -105,11 +106,19 @@ def split_workgroups(w):
     return ws // ((w.Hq // w.Hkv) * (w.d + 2) * 4)
 
 
+def wide_v_reads(w):
+    """Whether the split kernel takes 16-byte V reads for this (bf16 query)
+    workload: 256-token splits, or at least 1024 split workgroups."""
+    grid = split_workgroups(w)
+    splits = grid // (w.B * w.Hkv * w.Tq)
+    return grid >= 1024 or (w.k > 256 and splits == -(-w.k // 256))
+
+
 @pytest.mark.parametrize("case", sorted(WIDE))
 def test_wide_grid(case):
     kw = dict(WIDE[case])
     w = si.workload(kw.pop("base"), **kw)
-    assert split_workgroups(w) >= 1024
+    assert wide_v_reads(w)
     print(f"[case] {case} {w}", flush=True)
     r = full_parity(_inputs(w), w)
     _report(case, r)

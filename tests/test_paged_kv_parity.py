@@ -100,7 +100,7 @@ CASES = {
     "decode_multi_row": ("decode_32k", 64, dict(Hq=8, Hkv=2, Tq=5, T=3000, k=512)),
     # fp32 path, d = 64
     "decode_f32_d64": ("tiny_decode", 16, dict(T=1000)),
-    # >= 1024 split workgroups (16-byte V reads), pages of 2 blocks
+    # 256-token splits (16-byte V reads), pages of 2 blocks
     "decode_wide_grid_ps128": ("decode_32k", 128, dict(Hq=32, Hkv=8, Tq=16, T=4096, k=1024)),
     # fp8 KV cache, paged
     "decode_e5m2_ps128": ("decode_32k", 128, dict(B=2, Hq=8, Hkv=2, T=20000, dtype="bf16_e5m2")),
