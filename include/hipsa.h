@@ -220,12 +220,11 @@ size_t hipsa_workspace_bytes_ex(const hipsa_desc *desc, const hipsa_ext *ext, in
  * bit those of the two calls: indices/nnz as hip_mask_estimate writes them
  * (so later steps may reuse the mask with hip_sparse_attn), out as
  * hip_sparse_attn computes it.  For bf16 K/V in the contiguous layout with
- * k / block_k <= 32 the search and the attention of a problem run in one
- * launch (each split workgroup runs the problem's search itself and attends
- * its share of the kept blocks) followed by the merge of the splits; other
- * cases run the two calls' kernels in turn.  In the one-launch form the last
- * split workgroup of each problem to finish merges the splits, so a step is
- * a single kernel launch.
+ * k / block_k <= 32, when the attention's split workgroups number at most one
+ * per CU (256) and at most 16 per problem, the search and the attention run
+ * in one launch: each split workgroup runs the problem's search itself,
+ * attends its share of the kept blocks, and the last one of each problem to
+ * finish merges the splits.  Other cases run the two calls' kernels in turn.
  *   ext: dense part and paged layout as in the *_ex calls, or NULL.
  *   workspace: hipsa_decode_step_workspace_bytes() bytes, 16-byte aligned,
  *     zero-filled before its first use (it holds one arrival counter per

@@ -135,12 +135,28 @@ void launch_d(const StepArgs &a, hipStream_t st) {
 
 }  // namespace
 
+// The one-launch form runs a problem's search once per split workgroup.  It
+// pays while the grid has at most one workgroup per CU and a problem few
+// splits: measured against the two calls, it saves 1.1 us per 128k x 4 step
+// (32 problems x 8 splits) but costs 2.0 us at 32k (8 problems x 32 splits:
+// 32 searches of the same rows and a 32-way merge in one workgroup) and
+// 19.7 us with a 4096-token window (32 problems x 25 splits: about three
+// searches per CU).
+constexpr int64_t kMaxStepGrid = 256;
+constexpr int32_t kMaxStepSplits = 16;
+
+bool one_launch(const Shape &s, int32_t splits) {
+  return s.dtype == HIPSA_BF16 && s.Kb <= kPipeMaxKb && splits <= kMaxStepSplits &&
+         s.problems * splits <= kMaxStepGrid;
+}
+
 hipError_t launch_decode_step(const StepArgs &a, hipStream_t st) {
   const Shape &s = a.at.s;
-  // The one-launch form covers what the pipelined search covers (bf16 keys in
-  // the contiguous layout, K_b <= kPipeMaxKb); otherwise the two calls' kernels
-  // run in turn on the same lists.
-  if (s.dtype != HIPSA_BF16 || a.at.pg.table || s.Kb > kPipeMaxKb) {
+  // The one-launch form needs the pipelined search (bf16 keys in the
+  // contiguous layout, K_b <= kPipeMaxKb); otherwise, or when its redundant
+  // searches would cost more than the launch they save, the two calls'
+  // kernels run in turn on the same lists.
+  if (a.at.pg.table || !one_launch(s, a.at.splits)) {
     MaskArgs m{a.at.q, a.at.K, a.indices, a.nnz, s, a.at.pg};
     hipError_t e = launch_mask_decode(m, st);
     if (e != hipSuccess) return e;
