@@ -40,6 +40,10 @@ class Shape(C.Structure):
                 ("window", C.c_int64)]
 
 
+class Stage(C.Structure):
+    _fields_ = [("chunk", C.c_int64), ("keep", C.c_int64)]
+
+
 class Trace(C.Structure):
     _fields_ = [("max_rounds", C.c_int32), ("cap", C.c_int32), ("rounds", C.c_int32),
                 ("n_cand", C.c_void_p), ("cand_start", C.c_void_p), ("cand_end", C.c_void_p),
@@ -68,6 +72,15 @@ def load(path: str | None = None):
         f.restype = C.c_int
     lib.or_mask_reach.argtypes = [C.POINTER(Shape), P, P, I64, I64, I64, C.c_double, P, P, I64, I64]
     lib.or_mask_reach.restype = C.c_int64
+    SP = C.POINTER(Stage)
+    lib.or_mask_stages_one.argtypes = [C.POINTER(Shape), SP, I32, P, P, I64, I64, I64, P, P, P,
+                                       C.POINTER(Trace)]
+    lib.or_mask_stages_one.restype = C.c_int
+    lib.or_mask_stages_all.argtypes = [C.POINTER(Shape), SP, I32, P, P, P, P, P, I32]
+    lib.or_mask_stages_all.restype = C.c_int
+    lib.or_mask_stages_reach.argtypes = [C.POINTER(Shape), SP, I32, P, P, I64, I64, I64, C.c_double,
+                                         P, P, I64, I64]
+    lib.or_mask_stages_reach.restype = C.c_int64
     lib.or_e5m2_value.argtypes = [C.c_uint8]
     lib.or_e5m2_value.restype = C.c_double
     if path is None:
@@ -228,3 +241,93 @@ def mask_reach(q, K, b, g, qb, *, T, k, block_k, block_q, causal=1, sink=0, wind
     if n < 0:
         raise RuntimeError(f"or_mask_reach failed ({n}: {'node budget' if n == -1 else 'memory'})")
     return int(n), leaves[:min(n, max_leaves)]
+
+
+# ------------------------------------------------------------------ multi-stage search
+
+def stage_array(stages, block_k):
+    """A stage list [(chunk_size, k), ...] in tokens, as InfiniteHiP configures it
+    (the first k is None: every chunk of the initial partition is kept), as the
+    oracle's C array in blocks: (chunk blocks, chunks kept per round)."""
+    arr = (Stage * len(stages))()
+    for j, (chunk, k) in enumerate(stages):
+        assert chunk % block_k == 0, "chunk sizes are multiples of block_k"
+        arr[j].chunk = chunk // block_k
+        if k is None:
+            arr[j].keep = 0
+        else:
+            assert k % chunk == 0, "k is a multiple of the stage's chunk size"
+            arr[j].keep = k // chunk
+    return arr
+
+
+def mask_stages_all(q, K, stages, *, T, block_k, causal=1, sink=0, window=0, threads=None,
+                    lib=None):
+    """The multi-stage search on every problem (block_q = 1): indices
+    [B,Hkv,Tq,K_b], nnz, and the min relative cut margin per problem."""
+    lib = lib or load()
+    kb = stages[-1][1] // block_k
+    s = shape(q, K, T=T, k=kb * block_k, block_k=block_k, block_q=1, causal=causal, sink=sink,
+              window=window)
+    st = stage_array(stages, block_k)
+    idx = np.full((s.B, s.Hkv, s.Tq, kb), -1, np.int32)
+    nnz = np.zeros((s.B, s.Hkv, s.Tq), np.int32)
+    margin = np.zeros((s.B, s.Hkv, s.Tq), np.float64)
+    rc = lib.or_mask_stages_all(C.byref(s), st, len(stages), _ptr(q), _ptr(K), idx.ctypes.data,
+                                nnz.ctypes.data, margin.ctypes.data, nthreads(threads))
+    assert rc == 0, rc
+    return idx, nnz, margin
+
+
+def mask_stages_reach(q, K, b, g, i, stages, *, T, block_k, causal=1, sink=0, window=0, tol=1e-4,
+                      target=None, max_leaves=256, max_nodes=200000, lib=None):
+    """mask_reach over a stage list (problem b, KV head g, query row i)."""
+    lib = lib or load()
+    kb = stages[-1][1] // block_k
+    s = shape(q, K, T=T, k=kb * block_k, block_k=block_k, block_q=1, causal=causal, sink=sink,
+              window=window)
+    st = stage_array(stages, block_k)
+    leaves = np.full((max_leaves, kb), -1, np.int32)
+    tgt = None if target is None else np.ascontiguousarray(target, np.int32)
+    n = lib.or_mask_stages_reach(C.byref(s), st, len(stages), _ptr(q), _ptr(K), b, g, i, tol,
+                                 None if tgt is None else tgt.ctypes.data, leaves.ctypes.data,
+                                 max_leaves, max_nodes)
+    if n < 0:
+        raise RuntimeError(f"or_mask_stages_reach failed ({n})")
+    return int(n), leaves[:min(n, max_leaves)]
+
+
+def mask_stages_one(q, K, b, g, i, stages, *, T, block_k, causal=1, sink=0, window=0, lib=None,
+                    max_rounds=64, cap=8192):
+    """One problem of the multi-stage search with its per-round trace (the
+    rounds of every stage after the first, in order; candidates sorted by rank)."""
+    lib = lib or load()
+    kb = stages[-1][1] // block_k
+    s = shape(q, K, T=T, k=kb * block_k, block_k=block_k, block_q=1, causal=causal, sink=sink,
+              window=window)
+    st = stage_array(stages, block_k)
+    idx = np.full(kb, -1, np.int32)
+    nnz = np.zeros(1, np.int32)
+    margin = np.zeros(1, np.float64)
+    bufs = dict(n_cand=np.zeros(max_rounds, np.int32),
+                cand_start=np.zeros((max_rounds, cap), np.int64),
+                cand_end=np.zeros((max_rounds, cap), np.int64),
+                cand_centre=np.zeros((max_rounds, cap), np.int64),
+                cand_score=np.zeros((max_rounds, cap), np.float64),
+                cand_kept=np.zeros((max_rounds, cap), np.int32),
+                rel_margin=np.zeros(max_rounds, np.float64))
+    tr = Trace(max_rounds, cap, 0, *(bufs[n].ctypes.data for n in
+                                     ("n_cand", "cand_start", "cand_end", "cand_centre",
+                                      "cand_score", "cand_kept", "rel_margin")))
+    rc = lib.or_mask_stages_one(C.byref(s), st, len(stages), _ptr(q), _ptr(K), b, g, i,
+                                idx.ctypes.data, nnz.ctypes.data, margin.ctypes.data, C.byref(tr))
+    assert rc == 0, rc
+    rounds = []
+    for r in range(tr.rounds):
+        n = int(bufs["n_cand"][r])
+        rounds.append({"start": bufs["cand_start"][r, :n].copy(), "end": bufs["cand_end"][r, :n].copy(),
+                       "centre": bufs["cand_centre"][r, :n].copy(),
+                       "score": bufs["cand_score"][r, :n].copy(),
+                       "kept": bufs["cand_kept"][r, :n].astype(bool),
+                       "rel_margin": float(bufs["rel_margin"][r])})
+    return {"indices": idx, "nnz": int(nnz[0]), "margin": float(margin[0]), "rounds": rounds}

@@ -58,6 +58,8 @@
  *     only, so the index list holds searched blocks; attention takes the
  *     union of the dense blocks and the listed ones (a listed id inside a
  *     dense range adds nothing).
+ *  R11 multi-stage search (a stage list, as InfiniteHiP configures it): see
+ *     or_mask_stages_one.
  *
  * or_mask_reach (near-tie-tolerant search) follows the same steps but lets
  * every score move by half a relative tolerance, branching at each cut the
@@ -162,12 +164,14 @@ static void initial_chunks(int64_t first, int64_t M, int64_t Kb, int64_t *ca, in
   }
 }
 
-/* R3: the candidates of a round, the halves of every kept chunk of >= 2
- * blocks and every one-block chunk unchanged; returns their number. */
-static int64_t halve_all(const int64_t *ca, const int64_t *ce, int64_t Kb, int64_t *a, int64_t *e) {
+/* R3: the candidates of a round, the halves of every kept chunk of more than
+ * tb blocks and every other chunk unchanged (tb = 1 in the one-stage search;
+ * R11: a stage's chunk size in the multi-stage search); returns their number. */
+static int64_t halve_all(const int64_t *ca, const int64_t *ce, int64_t Kb, int64_t tb, int64_t *a,
+                         int64_t *e) {
   int64_t n = 0;
   for (int64_t i = 0; i < Kb; i++) {
-    if (ce[i] - ca[i] >= 2) {
+    if (ce[i] - ca[i] > tb) {
       int64_t m = ca[i] + (ce[i] - ca[i]) / 2;
       a[n] = ca[i]; e[n] = m; n++;
       a[n] = m; e[n] = ce[i]; n++;
@@ -197,6 +201,13 @@ static double chunk_score(const or_shape *s, const void *q, const void *K, int64
     }
   *t_out = t;
   return best;
+}
+
+/* Relative score gap at a top-k cut between the last kept score hiS and the
+ * first dropped score loS (0 when both are 0). */
+static double cut_margin(double hiS, double loS) {
+  double den = fabs(hiS) > fabs(loS) ? fabs(hiS) : fabs(loS);
+  return den == 0.0 ? 0.0 : (hiS - loS) / den;
 }
 
 /* R6: true when x ranks before y. */
@@ -248,7 +259,7 @@ int or_mask_one(const or_shape *s, const void *q, const void *K, int64_t b, int6
     if (!wide) break; /* Step 4 exit: every chunk is a single block */
 
     /* Step 2: halve every chunk (R3). */
-    const int64_t n = halve_all(ca, ce, Kb, ha, he);
+    const int64_t n = halve_all(ca, ce, Kb, 1, ha, he);
     for (int64_t c = 0; c < n; c++) { cand[c].a = ha[c]; cand[c].e = he[c]; }
 
     /* Step 3: score each candidate by its centre key (R4, R5). */
@@ -263,11 +274,7 @@ int or_mask_one(const or_shape *s, const void *q, const void *K, int64_t b, int6
       cand[j + 1] = x;
     }
     double rel = INFINITY;
-    if (n > Kb && cand[Kb].score != -INFINITY) {
-      double hiS = cand[Kb - 1].score, loS = cand[Kb].score;
-      double den = fabs(hiS) > fabs(loS) ? fabs(hiS) : fabs(loS);
-      rel = den == 0.0 ? 0.0 : (hiS - loS) / den;
-    }
+    if (n > Kb && cand[Kb].score != -INFINITY) rel = cut_margin(cand[Kb - 1].score, cand[Kb].score);
     if (rel < min_rel) min_rel = rel;
 
     if (tr && round < tr->max_rounds) {
@@ -333,9 +340,17 @@ int or_mask_all(const or_shape *s, const void *q, const void *K, int32_t *indice
  * allocation failure.
  * ------------------------------------------------------------------------ */
 typedef struct {
+  int64_t chunk; /* blocks: stage 0 cuts chunks of this size; a later stage halves kept chunks
+                    until none is larger */
+  int64_t keep;  /* chunks kept per round (0 for stage 0: every chunk) */
+} or_stage;
+
+typedef struct {
   const or_shape *s;
   const void *q, *K;
   int64_t b, g, r0, r1, Tp, Kb;
+  const or_stage *st; /* stages 1.. of the search (st[0] unused) */
+  int32_t nst;
   double tol;
   const int32_t *target;
   int32_t *leaves;
@@ -351,9 +366,10 @@ static int contains_target(const reach_ctx *c, int64_t a, int64_t e) {
   return 0;
 }
 
-static void reach_leaf(reach_ctx *c, const int64_t *ca) {
-  for (int64_t i = 0; i < c->Kb; i++) c->leaf_buf[i] = (int32_t)ca[i];
-  qsort(c->leaf_buf, (size_t)c->Kb, sizeof(int32_t), cmp_i32);
+static void reach_leaf(reach_ctx *c, const int64_t *ca, int64_t nk) {
+  for (int64_t i = 0; i < nk; i++) c->leaf_buf[i] = (int32_t)ca[i];
+  qsort(c->leaf_buf, (size_t)nk, sizeof(int32_t), cmp_i32);
+  for (int64_t i = nk; i < c->Kb; i++) c->leaf_buf[i] = -1;
   if (c->target) {
     if (c->n_found == 0 && memcmp(c->leaf_buf, c->target, sizeof(int32_t) * c->Kb) == 0) {
       c->n_found = 1;
@@ -371,31 +387,40 @@ static void reach_leaf(reach_ctx *c, const int64_t *ca) {
   c->n_found++;
 }
 
-/* Visits every allowed kept set of the round whose chunks are (ca, ce). */
-static void reach_round(reach_ctx *c, const int64_t *ca, const int64_t *ce) {
-  const int64_t Kb = c->Kb;
+/* Visits every allowed kept set of the round of stage `stage` whose nk
+ * chunks are (ca, ce). */
+static void reach_round(reach_ctx *c, int32_t stage, const int64_t *ca, const int64_t *ce,
+                        int64_t nk) {
   if (c->status || (c->target && c->n_found)) return;
+  const int64_t tb = c->st[stage].chunk, Kb = c->st[stage].keep;
   int wide = 0;
-  for (int64_t i = 0; i < Kb; i++) wide |= (ce[i] - ca[i] >= 2);
-  if (!wide) { reach_leaf(c, ca); return; }
+  for (int64_t i = 0; i < nk; i++) wide |= (ce[i] - ca[i] > tb);
+  if (!wide) { /* the stage is done: the next one, or the result */
+    if (stage + 1 < c->nst) reach_round(c, stage + 1, ca, ce, nk);
+    else reach_leaf(c, ca, nk);
+    return;
+  }
   if (++c->nodes > c->max_nodes) { c->status = -1; return; }
 
   /* halve (R3) and score (R4, R5) every chunk */
   int64_t n = 0;
-  int64_t *a = malloc(sizeof(int64_t) * 2 * Kb), *e = malloc(sizeof(int64_t) * 2 * Kb);
-  double *lo = malloc(sizeof(double) * 2 * Kb), *hi = malloc(sizeof(double) * 2 * Kb);
-  double *th = malloc(sizeof(double) * 4 * Kb);
-  char *req = malloc((size_t)(2 * Kb)), *in = malloc((size_t)(2 * Kb));
-  int64_t *pool = malloc(sizeof(int64_t) * 2 * Kb), *pick = malloc(sizeof(int64_t) * 2 * Kb);
-  int64_t *na = malloc(sizeof(int64_t) * Kb), *ne = malloc(sizeof(int64_t) * Kb);
+  const int64_t cap = 2 * nk;
+  int64_t *a = malloc(sizeof(int64_t) * cap), *e = malloc(sizeof(int64_t) * cap);
+  double *lo = malloc(sizeof(double) * cap), *hi = malloc(sizeof(double) * cap);
+  double *th = malloc(sizeof(double) * 2 * cap);
+  char *req = malloc((size_t)cap), *in = malloc((size_t)cap);
+  int64_t *pool = malloc(sizeof(int64_t) * cap), *pick = malloc(sizeof(int64_t) * cap);
+  int64_t *na = malloc(sizeof(int64_t) * cap), *ne = malloc(sizeof(int64_t) * cap);
   /* kept sets already visited this round (as candidate membership strings) */
   int64_t seen_cap = 16, n_seen = 0;
-  char *seen = malloc((size_t)(seen_cap * 2 * Kb));
+  char *seen = malloc((size_t)(seen_cap * cap));
+  int64_t keep = 0;
   if (!a || !e || !lo || !hi || !th || !req || !in || !pool || !pick || !na || !ne || !seen) {
     c->status = -2;
     goto done;
   }
-  n = halve_all(ca, ce, Kb, a, e);
+  n = halve_all(ca, ce, nk, tb, a, e);
+  keep = n < Kb ? n : Kb;
   int64_t n_req = 0;
   for (int64_t j = 0; j < n; j++) {
     int64_t t;
@@ -408,7 +433,7 @@ static void reach_round(reach_ctx *c, const int64_t *ca, const int64_t *ce) {
     req[j] = c->target ? (char)contains_target(c, a[j], e[j]) : 0;
     n_req += req[j];
   }
-  if (n_req > Kb) goto done; /* the target's blocks cannot all survive */
+  if (n_req > keep) goto done; /* the target's blocks cannot all survive */
 
   /* A kept set S is allowed iff some threshold th has every member with
    * hi >= th and every other candidate with lo <= th; it suffices to try
@@ -428,27 +453,27 @@ static void reach_round(reach_ctx *c, const int64_t *ca, const int64_t *ce) {
         if (!must_out) pool[np++] = j;
       }
     }
-    const int64_t need = Kb - base;
+    const int64_t need = keep - base;
     if (bad || need < 0 || need > np) continue;
     /* every choice of `need` free candidates, in lexicographic order */
     for (int64_t i = 0; i < need; i++) pick[i] = i;
     for (;;) {
       for (int64_t i = 0; i < need; i++) in[pool[pick[i]]] = 1;
       int dup = 0;
-      for (int64_t v = 0; v < n_seen && !dup; v++) dup = memcmp(seen + v * 2 * Kb, in, (size_t)n) == 0;
+      for (int64_t v = 0; v < n_seen && !dup; v++) dup = memcmp(seen + v * cap, in, (size_t)n) == 0;
       if (!dup) {
         if (n_seen == seen_cap) {
-          char *grown = realloc(seen, (size_t)(2 * seen_cap * 2 * Kb));
+          char *grown = realloc(seen, (size_t)(2 * seen_cap * cap));
           if (!grown) { c->status = -2; break; }
           seen = grown;
           seen_cap *= 2;
         }
-        memcpy(seen + n_seen * 2 * Kb, in, (size_t)n);
+        memcpy(seen + n_seen * cap, in, (size_t)n);
         n_seen++;
         int64_t m = 0;
         for (int64_t j = 0; j < n; j++)
           if (in[j]) { na[m] = a[j]; ne[m] = e[j]; m++; }
-        reach_round(c, na, ne);
+        reach_round(c, stage, na, ne, m);
         if (c->status || (c->target && c->n_found)) break;
       }
       for (int64_t i = 0; i < need; i++) in[pool[pick[i]]] = 0;
@@ -474,7 +499,8 @@ int64_t or_mask_reach(const or_shape *s, const void *q, const void *K, int64_t b
   int64_t sb, wb;
   dense_blocks(s, Np, &sb, &wb);
   const int64_t first = sb, M = Np - sb - wb;
-  reach_ctx c = {s, q, K, b, g, r0, r1, Tp, Kb, tol, target, leaves, max_leaves, 0, 0,
+  const or_stage one[2] = {{0, 0}, {1, Kb}}; /* one stage: halve to single blocks, keep K_b */
+  reach_ctx c = {s, q, K, b, g, r0, r1, Tp, Kb, one, 2, tol, target, leaves, max_leaves, 0, 0,
                  0, max_nodes, NULL, 0};
   if (Kb >= M) { /* R7: one possible result */
     int ok = 1;
@@ -487,7 +513,188 @@ int64_t or_mask_reach(const or_shape *s, const void *q, const void *K, int64_t b
   c.leaf_buf = malloc(sizeof(int32_t) * Kb);
   if (!ca || !ce || !c.leaf_buf) { free(ca); free(ce); free(c.leaf_buf); return -2; }
   initial_chunks(first, M, Kb, ca, ce);
-  reach_round(&c, ca, ce);
+  reach_round(&c, 1, ca, ce, Kb);
+  free(ca); free(ce); free(c.leaf_buf);
+  return c.status ? c.status : c.n_found;
+}
+
+/* ------------------------------------------------------------------------
+ * R11 multi-stage search (InfiniteHiP's stage list).
+ *
+ * The SGLang pull request's layer configuration lists stages, each with a
+ * chunk size and a number of keys kept (stage_chunk_size 128 -> 32 -> 8,
+ * stage_k null -> 32768 -> 8192), and the InfiniteHiP pages describe the
+ * pruning as modular and hierarchical; the rebuttal page (reviewer KprR, W3;
+ * reviewer T2wK, Q1) says users now choose per iteration how many chunks are
+ * kept and how each chunk is broken down.  Reading, with sizes in key blocks:
+ *  - stage 0 (its k is null) cuts the searched blocks into consecutive
+ *    chunks of st[0].chunk blocks (the last one takes what is left) and
+ *    keeps every one;
+ *  - a later stage s runs the one-stage iteration on the chunks the previous
+ *    stage kept: every chunk larger than st[s].chunk blocks is halved as in
+ *    R3 (others pass through and are scored again), the candidates are
+ *    scored as in R4/R5 and the st[s].keep best (R6) are kept, until no kept
+ *    chunk is larger than st[s].chunk (a stage whose chunks already fit runs
+ *    no round and keeps them all);
+ *  - the last stage's chunk size is one block, so its kept chunks are the
+ *    result: ascending, nnz = their count (at most st[last].keep);
+ *  - if the searched blocks number at most st[last].keep, all are selected
+ *    (R7).
+ * The stage's query block size and stride (which query rows of a chunked-
+ * prefill block vote) are not part of this reading: it serves per-row
+ * problems.  With st[0].chunk = M / K_b (M a multiple of K_b) and one later
+ * stage {1, K_b}, this is the one-stage search (or_mask_one) exactly.
+ * Returns -3 for an invalid stage list: nst >= 2, st[0].keep == 0,
+ * st[s].keep >= 1 and st[s].chunk < st[s-1].chunk for s >= 1, the last
+ * chunk 1, and k == st[last].keep * block_k.
+ * ------------------------------------------------------------------------ */
+/* R11 stage 0: consecutive chunks of c0 blocks over the M searched blocks
+ * from block `first`, the last one taking what is left; returns their number. */
+static int64_t stage0_chunks(int64_t first, int64_t M, int64_t c0, int64_t *ca, int64_t *ce) {
+  const int64_t n = (M + c0 - 1) / c0;
+  for (int64_t j = 0; j < n; j++) {
+    ca[j] = first + j * c0;
+    ce[j] = first + (j + 1) * c0 < first + M ? first + (j + 1) * c0 : first + M;
+  }
+  return n;
+}
+
+static int stages_valid(const or_shape *s, const or_stage *st, int32_t nst) {
+  if (nst < 2 || st[0].keep != 0 || st[0].chunk < 1 || st[nst - 1].chunk != 1) return 0;
+  for (int32_t j = 1; j < nst; j++)
+    if (st[j].keep < 1 || st[j].chunk >= st[j - 1].chunk) return 0;
+  return s->k == st[nst - 1].keep * s->block_k;
+}
+
+int or_mask_stages_one(const or_shape *s, const or_stage *st, int32_t nst, const void *q,
+                       const void *K, int64_t b, int64_t g, int64_t qb, int32_t *idx,
+                       int32_t *nnz, double *margin, or_trace *tr) {
+  if (!stages_valid(s, st, nst)) return -3;
+  const int64_t Kb = st[nst - 1].keep;
+  int64_t r0, r1;
+  const int64_t Tp = rows_and_tp(s, qb, &r0, &r1);
+  const int64_t Np = (Tp + s->block_k - 1) / s->block_k;
+  int64_t sb, wb;
+  dense_blocks(s, Np, &sb, &wb);
+  const int64_t first = sb, M = Np - sb - wb;
+  for (int64_t j = 0; j < Kb; j++) idx[j] = -1;
+  *margin = INFINITY;
+  if (tr) tr->rounds = 0;
+  if (Kb >= M) { /* R7 */
+    for (int64_t j = 0; j < M; j++) idx[j] = (int32_t)(first + j);
+    *nnz = (int32_t)M;
+    return 0;
+  }
+  /* stage 0: consecutive chunks of st[0].chunk blocks */
+  const int64_t c0 = st[0].chunk, n0 = (M + c0 - 1) / c0;
+  int64_t cap = 2 * n0;
+  for (int32_t j = 1; j < nst; j++) cap = cap > 2 * st[j].keep ? cap : 2 * st[j].keep;
+  int64_t *ca = malloc(sizeof(int64_t) * cap), *ce = malloc(sizeof(int64_t) * cap);
+  int64_t *ha = malloc(sizeof(int64_t) * cap), *he = malloc(sizeof(int64_t) * cap);
+  cand_t *cand = malloc(sizeof(cand_t) * cap);
+  if (!ca || !ce || !ha || !he || !cand) {
+    free(ca); free(ce); free(ha); free(he); free(cand);
+    return -1;
+  }
+  int64_t nk = stage0_chunks(first, M, c0, ca, ce);
+  double min_rel = INFINITY;
+  for (int32_t stage = 1; stage < nst; stage++) {
+    const int64_t tb = st[stage].chunk, keep = st[stage].keep;
+    for (;;) {
+      int wide = 0;
+      for (int64_t i = 0; i < nk; i++)
+        if (ce[i] - ca[i] > tb) wide = 1;
+      if (!wide) break; /* the stage is done */
+      const int64_t n = halve_all(ca, ce, nk, tb, ha, he);
+      for (int64_t c = 0; c < n; c++) {
+        cand[c].a = ha[c];
+        cand[c].e = he[c];
+        cand[c].score = chunk_score(s, q, K, b, g, r0, r1, Tp, ha[c], he[c], &cand[c].t);
+      }
+      /* global top-keep by (score desc, start asc): a stable insertion sort */
+      for (int64_t c = 1; c < n; c++) {
+        cand_t x = cand[c];
+        int64_t j = c - 1;
+        while (j >= 0 && ranks_before(&x, &cand[j])) { cand[j + 1] = cand[j]; j--; }
+        cand[j + 1] = x;
+      }
+      const int64_t kept = n < keep ? n : keep;
+      double rel = INFINITY;
+      if (n > keep && cand[keep].score != -INFINITY) rel = cut_margin(cand[keep - 1].score, cand[keep].score);
+      if (rel < min_rel) min_rel = rel;
+      if (tr && tr->rounds < tr->max_rounds) {
+        const int32_t r = tr->rounds++;
+        tr->n_cand[r] = (int32_t)n;
+        tr->rel_margin[r] = rel;
+        for (int64_t c = 0; c < n && c < tr->cap; c++) {
+          const int64_t o = (int64_t)r * tr->cap + c;
+          tr->cand_start[o] = cand[c].a;
+          tr->cand_end[o] = cand[c].e;
+          tr->cand_centre[o] = cand[c].t;
+          tr->cand_score[o] = cand[c].score;
+          tr->cand_kept[o] = c < kept;
+        }
+      }
+      for (int64_t i = 0; i < kept; i++) { ca[i] = cand[i].a; ce[i] = cand[i].e; }
+      nk = kept;
+    }
+  }
+  int rc = 0;
+  if (nk > Kb) { /* cannot happen: the last stage keeps at most K_b chunks */
+    rc = -1;
+  } else {
+    for (int64_t i = 0; i < nk; i++) idx[i] = (int32_t)ca[i];
+    qsort(idx, (size_t)nk, sizeof(int32_t), cmp_i32);
+    *nnz = (int32_t)nk;
+    *margin = min_rel;
+  }
+  free(ca); free(ce); free(ha); free(he); free(cand);
+  return rc;
+}
+
+int or_mask_stages_all(const or_shape *s, const or_stage *st, int32_t nst, const void *q,
+                       const void *K, int32_t *indices, int32_t *nnz, double *margin,
+                       int32_t nthreads) {
+  if (!stages_valid(s, st, nst)) return -3;
+  const int64_t Kb = st[nst - 1].keep, nqb = nqb_of(s);
+  const int64_t P = s->B * s->Hkv * nqb;
+  int err = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads) reduction(| : err)
+  for (int64_t p = 0; p < P; p++) {
+    int64_t b = p / (s->Hkv * nqb), g = (p / nqb) % s->Hkv, qb = p % nqb;
+    err |= or_mask_stages_one(s, st, nst, q, K, b, g, qb, indices + p * Kb, nnz + p, margin + p,
+                              NULL);
+  }
+  return err ? -1 : 0;
+}
+
+/* The near-tie-tolerant search over a stage list (see or_mask_reach). */
+int64_t or_mask_stages_reach(const or_shape *s, const or_stage *st, int32_t nst, const void *q,
+                             const void *K, int64_t b, int64_t g, int64_t qb, double tol,
+                             const int32_t *target, int32_t *leaves, int64_t max_leaves,
+                             int64_t max_nodes) {
+  if (!stages_valid(s, st, nst)) return -3;
+  const int64_t Kb = st[nst - 1].keep;
+  int64_t r0, r1;
+  const int64_t Tp = rows_and_tp(s, qb, &r0, &r1);
+  const int64_t Np = (Tp + s->block_k - 1) / s->block_k;
+  int64_t sb, wb;
+  dense_blocks(s, Np, &sb, &wb);
+  const int64_t first = sb, M = Np - sb - wb;
+  reach_ctx c = {s, q, K, b, g, r0, r1, Tp, Kb, st, nst, tol, target, leaves, max_leaves, 0, 0,
+                 0, max_nodes, NULL, 0};
+  if (Kb >= M) { /* R7: one possible result */
+    int ok = 1;
+    for (int64_t j = 0; j < Kb && target; j++) ok &= target[j] == (j < M ? first + j : -1);
+    if (leaves && max_leaves > 0 && ok)
+      for (int64_t j = 0; j < Kb; j++) leaves[j] = (int32_t)(j < M ? first + j : -1);
+    return ok;
+  }
+  const int64_t c0 = st[0].chunk, n0 = (M + c0 - 1) / c0;
+  int64_t *ca = malloc(sizeof(int64_t) * n0), *ce = malloc(sizeof(int64_t) * n0);
+  c.leaf_buf = malloc(sizeof(int32_t) * Kb);
+  if (!ca || !ce || !c.leaf_buf) { free(ca); free(ce); free(c.leaf_buf); return -2; }
+  reach_round(&c, 1, ca, ce, stage0_chunks(first, M, c0, ca, ce));
   free(ca); free(ce); free(c.leaf_buf);
   return c.status ? c.status : c.n_found;
 }

@@ -568,6 +568,137 @@ def pin_reach_target_agrees(lib):
             assert got == ((a, b) in reach), (a, b)
 
 
+# ---------------------------------------------------------------- multi-stage search
+
+def _stages_golden(lib, name):
+    g = _golden(name)
+    sh = g["shape"]
+    q, K, _ = _line_inputs(_s_from(g, sh["T"]))
+    stages = [(c, k) for c, k in g["stages"]]
+    r = oracle.mask_stages_one(q, K, 0, 0, 0, stages, T=sh["T"], block_k=sh["block_k"],
+                               causal=sh["causal"], lib=lib)
+    rounds = [t for t in g["trace"] if t["stage"] > 0]
+    _check_trace(r["rounds"], rounds)
+    assert r["indices"].tolist() == g["expected_indices"] + [-1] * (len(r["indices"]) -
+                                                                  len(g["expected_indices"]))
+    assert r["nnz"] == len(g["expected_indices"])
+    assert abs(r["margin"] - g["expected_margin"]) < 1e-12, r["margin"]
+
+
+def pin_stages_three_golden(lib):
+    """Hand-traced: fixed-size stage 0 with a partial chunk, a pass-through."""
+    _stages_golden(lib, "stages_three.json")
+
+
+def pin_stages_two_rounds_golden(lib):
+    """Hand-traced: a stage that needs two rounds, a tie broken by start."""
+    _stages_golden(lib, "stages_two_rounds.json")
+
+
+def pin_stages_identity(lib):
+    """A stage list whose stage 0 is the uniform partition (M a multiple of
+    K_b) and whose one later stage keeps K_b single blocks is the one-stage
+    search: indices, counts and margins equal or_mask_one's exactly, over
+    several shapes (query rows, groups, block sizes, a dense part)."""
+    import synth_inputs as si
+    cases = [(si.workload("decode_32k", T=8192, Hq=8, Hkv=2, Tq=1, k=512, seed=81), 0, 0),
+             (si.workload("decode_32k", T=4096, Hq=16, Hkv=1, Tq=1, block_k=16, k=256, seed=82), 0, 0),
+             (si.workload("decode_32k", T=8192 + 64 * 12, Hq=4, Hkv=4, Tq=1, k=256, seed=83), 64 * 4,
+              64 * 8)]
+    for w, sink, window in cases:
+        x = si.make_inputs(w)
+        kw = dict(T=w.T, causal=w.causal, sink=sink, window=window)
+        idx, nnz, margin = oracle.mask_all(x["q"], x["K"], k=w.k, block_k=w.block_k, block_q=1,
+                                           lib=lib, **kw)
+        M = -(-w.T // w.block_k) - sink // w.block_k - window // w.block_k
+        assert M % w.kb == 0, (w, M)
+        stages = [((M // w.kb) * w.block_k, None), (w.block_k, w.k)]
+        s_idx, s_nnz, s_margin = oracle.mask_stages_all(x["q"], x["K"], stages, block_k=w.block_k,
+                                                        lib=lib, **kw)
+        assert (s_idx == idx).all() and (s_nnz == nnz).all(), w
+        assert np.array_equal(s_margin, margin), w
+
+
+def pin_stages_structure(lib):
+    """Counts and tree structure of a multi-stage search on seeded data: each
+    round keeps min(stage keep, candidates); a candidate is a half of a kept
+    chunk larger than the stage's size or such a chunk itself; the result
+    lists the last stage's single blocks, each inside a chunk kept in every
+    round; every stage-0 block range is covered by the first round."""
+    import synth_inputs as si
+    w = si.workload("decode_32k", T=5000, Hq=8, Hkv=2, Tq=1, block_k=8, k=256, seed=84)
+    x = si.make_inputs(w)
+    stages = [(128, None), (32, 2048), (16, 1024), (8, 256)]  # chunks 16 -> 4 -> 2 -> 1 blocks
+    keeps = [None, 64, 64, 32]
+    M = -(-w.T // 8)
+    r = oracle.mask_stages_one(x["q"], x["K"], 0, 0, 0, stages, T=w.T, block_k=8, lib=lib)
+    rounds = r["rounds"]
+    # stage 1 from 16-block chunks to 4: two rounds; stage 2 (4 -> 2): one; stage 3 (2 -> 1): one
+    assert len(rounds) == 4, len(rounds)
+    first = rounds[0]
+    assert sorted(first["start"].tolist())[0] == 0 and max(first["end"]) == M
+    covered = sorted(zip(first["start"].tolist(), first["end"].tolist()))
+    assert all(a == b for (_, a), (b, _) in zip(covered, covered[1:]))  # the halves tile [0, M)
+    stage_of_round = [1, 1, 2, 3]
+    prev = None
+    for ri, rd in enumerate(rounds):
+        keep = keeps[stage_of_round[ri]]
+        assert rd["kept"].sum() == min(keep, len(rd["kept"]))
+        if prev is not None:
+            tb = {1: 4, 2: 2, 3: 1}[stage_of_round[ri]]  # this round's stage chunk size
+            kept_prev = [(a, e) for a, e, k in zip(prev["start"], prev["end"], prev["kept"]) if k]
+            for a, e in zip(rd["start"], rd["end"]):
+                assert any(pa <= a and e <= pe and (e - a == pe - pa if pe - pa <= tb
+                                                    else e - a in ((pe - pa) // 2, pe - pa - (pe - pa) // 2))
+                           for pa, pe in kept_prev), (ri, a, e)
+        prev = rd
+    final = [a for a, k in zip(rounds[-1]["start"], rounds[-1]["kept"]) if k]
+    assert sorted(final) == r["indices"][:r["nnz"]].tolist() and r["nnz"] == 32
+    for rd in rounds:
+        kept = [(a, e) for a, e, k in zip(rd["start"], rd["end"], rd["kept"]) if k]
+        assert all(any(a <= t < e for a, e in kept) for t in final)
+
+
+def pin_stages_reach_identity(lib):
+    """The tolerant search over a stage list: without near ties exactly the
+    greedy result; with them the greedy result is among its results."""
+    import synth_inputs as si
+    w = si.workload("decode_32k", T=6000, Hq=8, Hkv=2, Tq=6, block_k=16, k=256, seed=85)
+    x = si.make_inputs(w)
+    stages = [(256, None), (64, 1024), (16, 256)]
+    idx, nnz, margin = oracle.mask_stages_all(x["q"], x["K"], stages, T=w.T, block_k=16, lib=lib)
+    safe = 0
+    for b, g, i in np.ndindex(*margin.shape):
+        n, lists = oracle.mask_stages_reach(x["q"], x["K"], b, g, i, stages, T=w.T, block_k=16,
+                                            lib=lib)
+        exact = idx[b, g, i].tolist()
+        if margin[b, g, i] > 1e-4:
+            safe += 1
+            assert n == 1 and lists[0].tolist() == exact, (b, g, i, n)
+        else:
+            assert exact in [l.tolist() for l in lists]
+    assert safe >= 6
+
+
+def pin_stages_exact_topk(lib):
+    """block_k = 1, exact scores increasing inside each stage-0 chunk with
+    pairwise disjoint value ranges between chunks: every stage keeps the
+    chunks holding the largest scores, so the result is the brute-force top."""
+    rng = np.random.default_rng(7)
+    for trial in range(20):
+        T = int(rng.integers(40, 200))
+        c0 = int(rng.choice([8, 16]))
+        n0 = -(-T // c0)
+        base = rng.permutation(n0) * 10.0  # chunk value ranges [10 j, 10 j + 1)
+        s = [float(base[t // c0] + (t % c0) / (2 * c0)) for t in range(T)]
+        keep_last = int(rng.integers(1, 5))
+        stages = [(c0, None), (c0 // 4, (c0 // 4) * keep_last), (1, keep_last)]
+        q, K, _ = _line_inputs(s)
+        r = oracle.mask_stages_one(q, K, 0, 0, 0, stages, T=T, block_k=1, lib=lib)
+        brute = sorted(np.argsort(s)[::-1][:keep_last].tolist())
+        assert r["indices"][:r["nnz"]].tolist() == brute, (trial, r["indices"], brute)
+
+
 ALL_PINS = [
     pin_monotone_counterexample, pin_centre_tokens, pin_centre_blocks, pin_centre_partial_block,
     pin_uneven_partition, pin_causal_vote, pin_group_max, pin_dense_reduction,
@@ -575,5 +706,7 @@ ALL_PINS = [
     pin_tree_structure, pin_zero_query_ties, pin_attention_invariants, pin_mask_invariances,
     pin_e5m2_codes, pin_e5m2_kv, pin_dense_part_trace, pin_dense_part_reduction,
     pin_dense_part_search_range, pin_dense_part_union, pin_reach_branch_golden,
-    pin_reach_identity, pin_reach_target_agrees,
+    pin_reach_identity, pin_reach_target_agrees, pin_stages_three_golden,
+    pin_stages_two_rounds_golden, pin_stages_identity, pin_stages_structure,
+    pin_stages_reach_identity, pin_stages_exact_topk,
 ]

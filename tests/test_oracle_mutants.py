@@ -34,7 +34,7 @@ MUTANTS = [
     ("attn_no_causal_mask", "if (t > limit) continue;\n      double w", "double w"),
     ("attn_value_head_of_query", "int64_t vo = ((b * s->Hkv + g) * s->T_cap + t) * s->d;",
      "int64_t vo = ((b * s->Hkv + h % s->Hkv) * s->T_cap + t) * s->d;"),
-    ("margin_not_relative", "rel = den == 0.0 ? 0.0 : (hiS - loS) / den;", "rel = hiS - loS;"),
+    ("margin_not_relative", "return den == 0.0 ? 0.0 : (hiS - loS) / den;", "return hiS - loS;"),
     ("dense_case_skipped", "if (M <= Kb) {", "if (M < 0) {"),
     ("score_sum_over_group", "if (v > best) best = v;",
      "best = (best == -INFINITY) ? v : best + v;"),
@@ -60,6 +60,17 @@ MUTANTS = [
     ("reach_band_inverted", "lo[j] = sc - dl;\n    hi[j] = sc + dl;", "lo[j] = sc + dl;\n    hi[j] = sc - dl;"),
     ("reach_one_threshold_only", "for (int64_t k = 0; k < 2 * n && !c->status; k++) {",
      "for (int64_t k = 0; k < 1 && !c->status; k++) {"),
+    # multi-stage search
+    ("stage0_partial_chunk_dropped", "const int64_t n = (M + c0 - 1) / c0;", "const int64_t n = M / c0;"),
+    ("stage0_chunks_overlap", "ce[j] = first + (j + 1) * c0 < first + M ? first + (j + 1) * c0 : first + M;",
+     "ce[j] = first + (j + 2) * c0 < first + M ? first + (j + 2) * c0 : first + M;"),
+    ("stage_keeps_one_less", "const int64_t kept = n < keep ? n : keep;",
+     "const int64_t kept = n < keep ? n : (keep > 1 ? keep - 1 : keep);"),
+    ("stage_ends_a_round_early", "        if (ce[i] - ca[i] > tb) wide = 1;",
+     "        if (ce[i] - ca[i] > 2 * tb) wide = 1;"),
+    ("stage0_ignores_sink_offset", "    ca[j] = first + j * c0;", "    ca[j] = j * c0;"),
+    ("stage_halving_to_one_block", "const int64_t n = halve_all(ca, ce, nk, tb, ha, he);",
+     "const int64_t n = halve_all(ca, ce, nk, 1, ha, he);"),
     ("reach_required_dropped", "req[j] = c->target ? (char)contains_target(c, a[j], e[j]) : 0;",
      "req[j] = c->target ? (char)!contains_target(c, a[j], e[j]) : 0;"),
 ]
