@@ -388,15 +388,15 @@ static void reach_leaf(reach_ctx *c, const int64_t *ca, int64_t nk) {
 }
 
 /* Visits every allowed kept set of the round of stage `stage` whose nk
- * chunks are (ca, ce). */
-static void reach_round(reach_ctx *c, int32_t stage, const int64_t *ca, const int64_t *ce,
-                        int64_t nk) {
+ * chunks are (ca, ce); `fresh`: the stage's first round, which always runs. */
+static void reach_round(reach_ctx *c, int32_t stage, int fresh, const int64_t *ca,
+                        const int64_t *ce, int64_t nk) {
   if (c->status || (c->target && c->n_found)) return;
   const int64_t tb = c->st[stage].chunk, Kb = c->st[stage].keep;
   int wide = 0;
   for (int64_t i = 0; i < nk; i++) wide |= (ce[i] - ca[i] > tb);
-  if (!wide) { /* the stage is done: the next one, or the result */
-    if (stage + 1 < c->nst) reach_round(c, stage + 1, ca, ce, nk);
+  if (!wide && !fresh) { /* the stage is done: the next one, or the result */
+    if (stage + 1 < c->nst) reach_round(c, stage + 1, 1, ca, ce, nk);
     else reach_leaf(c, ca, nk);
     return;
   }
@@ -473,7 +473,7 @@ static void reach_round(reach_ctx *c, int32_t stage, const int64_t *ca, const in
         int64_t m = 0;
         for (int64_t j = 0; j < n; j++)
           if (in[j]) { na[m] = a[j]; ne[m] = e[j]; m++; }
-        reach_round(c, stage, na, ne, m);
+        reach_round(c, stage, 0, na, ne, m);
         if (c->status || (c->target && c->n_found)) break;
       }
       for (int64_t i = 0; i < need; i++) in[pool[pick[i]]] = 0;
@@ -513,7 +513,7 @@ int64_t or_mask_reach(const or_shape *s, const void *q, const void *K, int64_t b
   c.leaf_buf = malloc(sizeof(int32_t) * Kb);
   if (!ca || !ce || !c.leaf_buf) { free(ca); free(ce); free(c.leaf_buf); return -2; }
   initial_chunks(first, M, Kb, ca, ce);
-  reach_round(&c, 1, ca, ce, Kb);
+  reach_round(&c, 1, 1, ca, ce, Kb);
   free(ca); free(ce); free(c.leaf_buf);
   return c.status ? c.status : c.n_found;
 }
@@ -533,9 +533,10 @@ int64_t or_mask_reach(const or_shape *s, const void *q, const void *K, int64_t b
  *  - a later stage s runs the one-stage iteration on the chunks the previous
  *    stage kept: every chunk larger than st[s].chunk blocks is halved as in
  *    R3 (others pass through and are scored again), the candidates are
- *    scored as in R4/R5 and the st[s].keep best (R6) are kept, until no kept
- *    chunk is larger than st[s].chunk (a stage whose chunks already fit runs
- *    no round and keeps them all);
+ *    scored as in R4/R5 and the st[s].keep best (R6) are kept; rounds repeat
+ *    while a kept chunk is larger than st[s].chunk.  A stage runs at least
+ *    one round, so it always applies its own kept count (chunks that already
+ *    fit are only scored again and ranked);
  *  - the last stage's chunk size is one block, so its kept chunks are the
  *    result: ascending, nnz = their count (at most st[last].keep);
  *  - if the searched blocks number at most st[last].keep, all are selected
@@ -600,11 +601,11 @@ int or_mask_stages_one(const or_shape *s, const or_stage *st, int32_t nst, const
   double min_rel = INFINITY;
   for (int32_t stage = 1; stage < nst; stage++) {
     const int64_t tb = st[stage].chunk, keep = st[stage].keep;
-    for (;;) {
+    for (int fresh = 1;; fresh = 0) {
       int wide = 0;
       for (int64_t i = 0; i < nk; i++)
         if (ce[i] - ca[i] > tb) wide = 1;
-      if (!wide) break; /* the stage is done */
+      if (!wide && !fresh) break; /* the stage is done */
       const int64_t n = halve_all(ca, ce, nk, tb, ha, he);
       for (int64_t c = 0; c < n; c++) {
         cand[c].a = ha[c];
@@ -694,7 +695,7 @@ int64_t or_mask_stages_reach(const or_shape *s, const or_stage *st, int32_t nst,
   int64_t *ca = malloc(sizeof(int64_t) * n0), *ce = malloc(sizeof(int64_t) * n0);
   c.leaf_buf = malloc(sizeof(int32_t) * Kb);
   if (!ca || !ce || !c.leaf_buf) { free(ca); free(ce); free(c.leaf_buf); return -2; }
-  reach_round(&c, 1, ca, ce, stage0_chunks(first, M, c0, ca, ce));
+  reach_round(&c, 1, 1, ca, ce, stage0_chunks(first, M, c0, ca, ce));
   free(ca); free(ce); free(c.leaf_buf);
   return c.status ? c.status : c.n_found;
 }

@@ -595,6 +595,11 @@ def pin_stages_two_rounds_golden(lib):
     _stages_golden(lib, "stages_two_rounds.json")
 
 
+def pin_stages_fit_first_round_golden(lib):
+    """Hand-traced: a stage whose incoming chunks already fit still ranks them."""
+    _stages_golden(lib, "stages_fit_first_round.json")
+
+
 def pin_stages_identity(lib):
     """A stage list whose stage 0 is the uniform partition (M a multiple of
     K_b) and whose one later stage keeps K_b single blocks is the one-stage
@@ -707,6 +712,6 @@ ALL_PINS = [
     pin_e5m2_codes, pin_e5m2_kv, pin_dense_part_trace, pin_dense_part_reduction,
     pin_dense_part_search_range, pin_dense_part_union, pin_reach_branch_golden,
     pin_reach_identity, pin_reach_target_agrees, pin_stages_three_golden,
-    pin_stages_two_rounds_golden, pin_stages_identity, pin_stages_structure,
+    pin_stages_two_rounds_golden, pin_stages_fit_first_round_golden, pin_stages_identity, pin_stages_structure,
     pin_stages_reach_identity, pin_stages_exact_topk,
 ]

@@ -69,6 +69,8 @@ MUTANTS = [
     ("stage_ends_a_round_early", "        if (ce[i] - ca[i] > tb) wide = 1;",
      "        if (ce[i] - ca[i] > 2 * tb) wide = 1;"),
     ("stage0_ignores_sink_offset", "    ca[j] = first + j * c0;", "    ca[j] = j * c0;"),
+    ("stage_without_first_round", "      if (!wide && !fresh) break; /* the stage is done */",
+     "      if (!wide) break; /* the stage is done */"),
     ("stage_halving_to_one_block", "const int64_t n = halve_all(ca, ce, nk, tb, ha, he);",
      "const int64_t n = halve_all(ca, ce, nk, 1, ha, he);"),
     ("reach_required_dropped", "req[j] = c->target ? (char)contains_target(c, a[j], e[j]) : 0;",
