@@ -1,0 +1,144 @@
+// Scoring of candidate chunks of a per-row problem by their centre keys: the
+// query operands (loaded once) and one round's scores, shared by the
+// one-stage and multi-stage decode mask kernels.
+//
+// Method: rebuttal page "A Training-free Sub-quadratic Cost Transformer Model
+// Serving Framework With Hierarchically Pruned Attention", reviewer RsGC, Q2,
+// step 3 (a chunk's importance is the dot product of the query with the key
+// at its centre).  For a bf16 query each wave scores 16 candidates per
+// v_mfma_f32_16x16x32_bf16 tile against the query heads of the group
+// (zero-padded to 16 rows) and takes the max over the valid head rows of the
+// accumulator; fp32 queries use 16-byte VALU dot products with DPP sums.
+// fp8 (E5M2) keys are loaded as 8-byte slices and widened exactly to bf16
+// operands.  Every load of a batch is issued before any is used (an empty slot
+// reads row 0 and discards it), so a round pays one memory latency per batch.
+#pragma once
+
+#include <type_traits>
+
+#include "hipsa_internal.h"
+
+namespace hipsa {
+
+// Query operands of a problem's group of query heads.  MFMA: lane l holds
+// head l%16 (zero when past the group), dims 32*ks + 8*(l/16) .. +7.  VALU:
+// every head, dims cs*VEC .. +VEC-1 for the lane's column slice cs.
+template <typename E, int D, int GMAX>
+struct QueryOps {
+  static constexpr bool kMfma = std::is_same<E, uint16_t>::value;
+  static constexpr int VEC = Vec<E>::N;
+  static constexpr int TPR = D / VEC;  // VALU path: lanes per key row
+  static constexpr int KS = D / 32;    // MFMA path: k-steps of 32 over the head dim
+  uint4 qa[kMfma ? KS : 1];
+  float qv[kMfma ? 1 : GMAX][VEC];
+
+  // qbase: head 0 of the group at the problem's query row; hstride: elements
+  // between consecutive heads' rows.
+  __device__ __forceinline__ void load(const E *qbase, int64_t hstride, int G) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    if constexpr (kMfma) {
+      const int h = lane & 15;
+#pragma unroll
+      for (int ks = 0; ks < KS; ks++) {
+        const uint4 r = Vec<E>::raw(qbase + (int64_t)min(h, G - 1) * hstride + 32 * ks + 8 * (lane >> 4));
+        qa[ks] = h < G ? r : make_uint4(0, 0, 0, 0);
+      }
+    } else {
+      const int cs = tid % TPR;
+      uint4 r[GMAX];
+#pragma unroll
+      for (int h = 0; h < GMAX; h++) r[h] = Vec<E>::raw(qbase + (int64_t)min(h, G - 1) * hstride + cs * VEC);
+#pragma unroll
+      for (int h = 0; h < GMAX; h++) Vec<E>::widen(r[h], h < G, qv[h]);
+    }
+  }
+};
+
+// Scores candidate slots [0, n) with chunks (ca[c], ce[c]) in blocks (start
+// -1: an empty slot) and writes key[c] = rank_key(score, start), or 0 for an
+// empty slot.  Tp: the row's visible length; row_of(t): element offset of the
+// K row of position t.  Called by all 256 threads; LDS reads of ca/ce, no
+// barrier.
+template <typename E, typename KE, int D, int GMAX, int UNROLL, typename RowOf>
+__device__ __forceinline__ void score_slots(const QueryOps<E, D, GMAX> &qo, const KE *Kbase, RowOf row_of,
+                                            const int32_t *ca, const int32_t *ce, int n, int32_t Tp,
+                                            const Shape &s, uint64_t *key) {
+  constexpr bool kMfma = QueryOps<E, D, GMAX>::kMfma;
+  constexpr int VEC = QueryOps<E, D, GMAX>::VEC;
+  constexpr int TPR = QueryOps<E, D, GMAX>::TPR;
+  constexpr int RPP = 256 / TPR;  // VALU path: rows per pass
+  constexpr int KS = QueryOps<E, D, GMAX>::KS;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint4 *qa = qo.qa;
+  const auto &qv = qo.qv;
+  if constexpr (kMfma) {
+    const int ntile = (n + 15) / 16;
+    for (int t0 = wave; t0 < ntile; t0 += 4 * UNROLL) {
+      typename Kv8<KE>::raw_t kr[UNROLL][KS];
+      bool live[UNROLL];
+#pragma unroll
+      for (int u = 0; u < UNROLL; u++) {
+        const int c = 16 * (t0 + 4 * u) + (lane & 15);
+        const int cc = c < n ? c : 0;
+        const int32_t lo_b = ca[cc], hi_b = ce[cc];
+        live[u] = c < n && lo_b >= 0;
+        const int32_t lo = lo_b << s.bk_shift, hi = min(hi_b << s.bk_shift, Tp);
+        const int32_t t = live[u] ? (lo + hi) >> 1 : 0;  // centre token (upper middle)
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++)
+          kr[u][ks] = Kv8<KE>::raw(Kbase + row_of(t) + 32 * ks + 8 * (lane >> 4));
+      }
+#pragma unroll
+      for (int u = 0; u < UNROLL; u++) {
+        const int c = 16 * (t0 + 4 * u) + (lane & 15);
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[ks]),
+                                                        as_bf16x8(Kv8<KE>::bf16(kr[u][ks])), acc, 0, 0, 0);
+        // acc[r] = score of head 4*(lane/16)+r for candidate lane%16
+        float best = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+          if (4 * (lane >> 4) + r < s.G) best = fmaxf(best, acc[r]);
+        if (GMAX > 4) best = fmaxf(best, __shfl_xor(best, 16, 64));
+        if (GMAX > 8) best = fmaxf(best, __shfl_xor(best, 32, 64));
+        if (lane < 16 && c < n) key[c] = live[u] ? rank_key(best, ca[c]) : 0ull;
+      }
+    }
+  } else {
+    const int rg = tid / TPR, cs = tid % TPR;
+    for (int base = 0; base < n; base += RPP * UNROLL) {
+      uint4 raw[UNROLL];
+      bool live[UNROLL];
+#pragma unroll
+      for (int u = 0; u < UNROLL; u++) {
+        const int c = base + u * RPP + rg;
+        const int cc = c < n ? c : 0;
+        const int32_t lo_b = ca[cc], hi_b = ce[cc];
+        live[u] = c < n && lo_b >= 0;
+        const int32_t lo = lo_b << s.bk_shift, hi = min(hi_b << s.bk_shift, Tp);
+        const int32_t t = live[u] ? (lo + hi) >> 1 : 0;  // centre token (upper middle)
+        raw[u] = Vec<E>::raw(Kbase + row_of(t) + cs * VEC);
+      }
+#pragma unroll
+      for (int u = 0; u < UNROLL; u++) {
+        const int c = base + u * RPP + rg;
+        float kv[VEC];
+        Vec<E>::widen(raw[u], live[u], kv);
+        float best = -INFINITY;
+#pragma unroll
+        for (int h = 0; h < GMAX; h++) {
+          float p = 0.f;
+#pragma unroll
+          for (int e = 0; e < VEC; e++) p = fmaf(qv[h][e], kv[e], p);
+          p = group_sum<TPR>(p);
+          if (h < s.G) best = fmaxf(best, p);
+        }
+        if (cs == 0 && c < n) key[c] = live[u] ? rank_key(best, ca[c]) : 0ull;
+      }
+    }
+  }
+}
+
+}  // namespace hipsa

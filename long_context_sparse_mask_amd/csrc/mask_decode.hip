@@ -33,6 +33,7 @@
 // centre row costs no extra memory trip.
 #include <type_traits>
 
+#include "decode_score.h"
 #include "decode_search.h"
 #include "hipsa_internal.h"
 #include "mask_select.h"
@@ -42,13 +43,8 @@ namespace {
 
 template <typename E, typename KE, int D, int GMAX, int UNROLL, bool PAGED>
 __global__ __launch_bounds__(256) void mask_decode_kernel(MaskArgs a) {
-  constexpr bool kMfma = std::is_same<E, uint16_t>::value;
-  constexpr int VEC = Vec<E>::N;
-  constexpr int TPR = D / VEC;   // VALU path: lanes per key row
-  constexpr int RPP = 256 / TPR; // VALU path: rows per pass
-  constexpr int KS = D / 32;     // MFMA path: k-steps of 32 over the head dim
   const Shape &s = a.s;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
 
   const uint32_t prob = xcd_swizzle(blockIdx.x, gridDim.x);
   const uint32_t Tq = (uint32_t)s.Tq, Hkv = (uint32_t)s.Hkv;
@@ -84,27 +80,8 @@ __global__ __launch_bounds__(256) void mask_decode_kernel(MaskArgs a) {
     else return kvoff + (int64_t)t * D;
   };
 
-  // Query operands, loaded once.  MFMA: lane l holds head l%16 (zero when
-  // past the group), dims 32*ks + 8*(l/16) .. +7.  VALU: every head, dims
-  // cs*VEC .. +VEC-1.
-  uint4 qa[kMfma ? KS : 1];
-  float qv[kMfma ? 1 : GMAX][VEC];
-  if constexpr (kMfma) {
-    const int h = lane & 15;
-#pragma unroll
-    for (int ks = 0; ks < KS; ks++) {
-      const uint4 r = Vec<E>::raw(qbase + (int64_t)min(h, s.G - 1) * Tq * D + 32 * ks + 8 * (lane >> 4));
-      qa[ks] = h < s.G ? r : make_uint4(0, 0, 0, 0);
-    }
-  } else {
-    const int cs = tid % TPR;
-    uint4 r[GMAX];
-#pragma unroll
-    for (int h = 0; h < GMAX; h++)
-      r[h] = Vec<E>::raw(qbase + (int64_t)min(h, s.G - 1) * Tq * D + cs * VEC);
-#pragma unroll
-    for (int h = 0; h < GMAX; h++) Vec<E>::widen(r[h], h < s.G, qv[h]);
-  }
+  QueryOps<E, D, GMAX> qo;
+  qo.load(qbase, (int64_t)Tq * D, s.G);
 
   const int n = 2 * Kb;
   // paged: page numbers to LDS, issued after the query loads so that both
@@ -123,74 +100,7 @@ __global__ __launch_bounds__(256) void mask_decode_kernel(MaskArgs a) {
     for (int c = tid; c < n; c += 256) rk[c] = 0;  // rank counts of this round
 
     // ---- 1. scoring
-    if constexpr (kMfma) {
-      const int ntile = (n + 15) / 16;
-      for (int t0 = wave; t0 < ntile; t0 += 4 * UNROLL) {
-        typename Kv8<KE>::raw_t kr[UNROLL][KS];
-        bool live[UNROLL];
-#pragma unroll
-        for (int u = 0; u < UNROLL; u++) {
-          const int c = 16 * (t0 + 4 * u) + (lane & 15);
-          const int cc = c < n ? c : 0;
-          const int32_t lo_b = ca[cc], hi_b = ce[cc];
-          live[u] = c < n && lo_b >= 0;
-          const int32_t lo = lo_b << s.bk_shift, hi = min(hi_b << s.bk_shift, Tp);
-          const int32_t t = live[u] ? (lo + hi) >> 1 : 0;  // centre token (upper middle)
-#pragma unroll
-          for (int ks = 0; ks < KS; ks++)
-            kr[u][ks] = Kv8<KE>::raw(Kbase + row_of(t) + 32 * ks + 8 * (lane >> 4));
-        }
-#pragma unroll
-        for (int u = 0; u < UNROLL; u++) {
-          const int c = 16 * (t0 + 4 * u) + (lane & 15);
-          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < KS; ks++)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[ks]),
-                                                          as_bf16x8(Kv8<KE>::bf16(kr[u][ks])), acc, 0, 0, 0);
-          // acc[r] = score of head 4*(lane/16)+r for candidate lane%16
-          float best = -INFINITY;
-#pragma unroll
-          for (int r = 0; r < 4; r++)
-            if (4 * (lane >> 4) + r < s.G) best = fmaxf(best, acc[r]);
-          if (GMAX > 4) best = fmaxf(best, __shfl_xor(best, 16, 64));
-          if (GMAX > 8) best = fmaxf(best, __shfl_xor(best, 32, 64));
-          if (lane < 16 && c < n) key[c] = live[u] ? rank_key(best, ca[c]) : 0ull;
-        }
-      }
-    } else {
-      const int rg = tid / TPR, cs = tid % TPR;
-      for (int base = 0; base < n; base += RPP * UNROLL) {
-        uint4 raw[UNROLL];
-        bool live[UNROLL];
-#pragma unroll
-        for (int u = 0; u < UNROLL; u++) {
-          const int c = base + u * RPP + rg;
-          const int cc = c < n ? c : 0;
-          const int32_t lo_b = ca[cc], hi_b = ce[cc];
-          live[u] = c < n && lo_b >= 0;
-          const int32_t lo = lo_b << s.bk_shift, hi = min(hi_b << s.bk_shift, Tp);
-          const int32_t t = live[u] ? (lo + hi) >> 1 : 0;  // centre token (upper middle)
-          raw[u] = Vec<E>::raw(Kbase + row_of(t) + cs * VEC);
-        }
-#pragma unroll
-        for (int u = 0; u < UNROLL; u++) {
-          const int c = base + u * RPP + rg;
-          float kv[VEC];
-          Vec<E>::widen(raw[u], live[u], kv);
-          float best = -INFINITY;
-#pragma unroll
-          for (int h = 0; h < GMAX; h++) {
-            float p = 0.f;
-#pragma unroll
-            for (int e = 0; e < VEC; e++) p = fmaf(qv[h][e], kv[e], p);
-            p = group_sum<TPR>(p);
-            if (h < s.G) best = fmaxf(best, p);
-          }
-          if (cs == 0 && c < n) key[c] = live[u] ? rank_key(best, ca[c]) : 0ull;
-        }
-      }
-    }
+    score_slots<E, KE, D, GMAX, UNROLL>(qo, Kbase, row_of, ca, ce, n, Tp, s, key);
     __syncthreads();
 
     // ---- 2. selection: the K_b best write their halves into the other buffer
