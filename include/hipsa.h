@@ -78,7 +78,8 @@ typedef enum {
   HIPSA_ERR_WORKSPACE = -5, /* workspace smaller than hipsa_workspace_bytes()       */
   HIPSA_ERR_HIP = -6,       /* a HIP runtime call or kernel launch failed           */
   HIPSA_ERR_ALIGN = -7,     /* q, K, V or out is not 16-byte aligned                */
-  HIPSA_ERR_PAGES = -8      /* invalid paged-KV description                         */
+  HIPSA_ERR_PAGES = -8,     /* invalid paged-KV description                         */
+  HIPSA_ERR_STAGES = -9     /* invalid stage list (hip_mask_estimate_stages)        */
 } hipsa_status;
 
 typedef struct hipsa_desc {
@@ -212,6 +213,51 @@ int hip_sparse_attn_ex(const hipsa_desc *desc, const hipsa_ext *ext, const void 
 
 size_t hipsa_workspace_bytes_ex(const hipsa_desc *desc, const hipsa_ext *ext, int64_t k,
                                 int64_t block_k, int64_t block_q);
+
+/*
+ * Multi-stage search (per-row problems, block_q = 1).  InfiniteHiP is served
+ * with a list of pruning stages per layer, each naming a chunk size and a
+ * number of keys kept (SGLang pull request "Support Efficient Sparse HiP
+ * Attention (InfiniteHiP) ...", the layer configuration's stage_chunk_size
+ * and stage_k, the first k null); the rebuttal page (reviewer KprR, W3;
+ * reviewer T2wK, Q1) says how many chunks each iteration keeps and how each
+ * chunk is broken down are chosen freely.  With sizes in tokens:
+ *   - stage 0 cuts the searched blocks of a row into consecutive chunks of
+ *     stages[0].chunk_size tokens (the last one takes what is left) and
+ *     keeps them all (stages[0].k must be 0);
+ *   - stage j >= 1 runs rounds of hip_mask_estimate's iteration on the
+ *     chunks kept so far: every chunk wider than stages[j].chunk_size is
+ *     halved (narrower ones pass through and are scored again), candidates
+ *     are scored by their centre token as in hip_mask_estimate, and the
+ *     stages[j].k / stages[j].chunk_size best (score descending, start
+ *     ascending) are kept.  A stage runs at least one round, and more while a
+ *     kept chunk is wider than its chunk size;
+ *   - the last stage's chunk_size is block_k, so its kept chunks are single
+ *     blocks: indices[b,g,i,0..nnz-1] ascending, -1 after them, with
+ *     K_b = stages[last].k / block_k columns (nnz < K_b when fewer reach the
+ *     last stage).  A row that sees at most K_b searched blocks selects them
+ *     all, as in hip_mask_estimate.
+ * With stages {{c0, 0}, {block_k, k}}, c0 = N_p * block_k / K_b for every
+ * row (N_p a multiple of K_b), this is hip_mask_estimate's search exactly.
+ *   stages: HOST array of nstages entries, 2 <= nstages <= 8; chunk sizes
+ *     positive multiples of block_k, strictly decreasing, the last block_k;
+ *     for j >= 1, k a positive multiple of chunk_size with
+ *     k / chunk_size <= 2048; ceil(ceil(T / block_k) * block_k /
+ *     stages[0].chunk_size) <= 2048 stage-0 chunks.  HIPSA_ERR_STAGES
+ *     otherwise.
+ *   ext: dense part and paged layout as in the *_ex calls, or NULL.
+ *   q, K, indices, nnz: as in hip_mask_estimate with block_q = 1 and
+ *     k = stages[last].k.
+ */
+typedef struct hipsa_stage {
+  int64_t chunk_size; /* tokens                                        */
+  int64_t k;          /* tokens kept per round (0 for stage 0: all)     */
+} hipsa_stage;
+
+int hip_mask_estimate_stages(const hipsa_desc *desc, const hipsa_ext *ext,
+                             const hipsa_stage *stages, int32_t nstages, const void *q,
+                             const void *K, int64_t block_k, int32_t *indices, int32_t *nnz,
+                             void *stream);
 
 /*
  * One decode step (block_q = 1): hip_mask_estimate followed by hip_sparse_attn

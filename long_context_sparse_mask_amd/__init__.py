@@ -24,7 +24,7 @@ import torch  # loads the HIP runtime first, so libhipsa binds to the same one
 
 __all__ = ["hip_mask_estimate", "hip_sparse_attn", "hip_mask_estimate_paged",
            "hip_sparse_attn_paged", "hip_mask_estimate_ex", "hip_sparse_attn_ex",
-           "hip_sparse_attn_noalloc", "hip_decode_step", "hipsa_decode_step_workspace_bytes",
+           "hip_sparse_attn_noalloc", "hip_decode_step", "hip_mask_estimate_stages", "hipsa_decode_step_workspace_bytes",
            "hipsa_workspace_bytes", "hipsa_workspace_bytes_ex",
            "HipsaError", "LIB_PATH", "lib", "NOALLOC_SCRATCH_BYTES"]
 
@@ -54,6 +54,10 @@ class Ext(C.Structure):
     _fields_ = [("pages", C.POINTER(Pages)), ("sink", C.c_int64), ("window", C.c_int64)]
 
 
+class Stage(C.Structure):
+    _fields_ = [("chunk_size", C.c_int64), ("k", C.c_int64)]
+
+
 _P, _I64, _SZ = C.c_void_p, C.c_int64, C.c_size_t
 lib.hip_mask_estimate.argtypes = [C.POINTER(Desc), _P, _P, _I64, _I64, _I64, _P, _P, _P, _SZ, _P]
 lib.hip_mask_estimate.restype = C.c_int
@@ -72,6 +76,9 @@ lib.hip_mask_estimate_ex.restype = C.c_int
 lib.hip_sparse_attn_ex.argtypes = [C.POINTER(Desc), C.POINTER(Ext), _P, _P, _P, _P, _P, _I64, _I64,
                                    _I64, _P, _P, _SZ, _P]
 lib.hip_sparse_attn_ex.restype = C.c_int
+lib.hip_mask_estimate_stages.argtypes = [C.POINTER(Desc), C.POINTER(Ext), C.POINTER(Stage),
+                                         C.c_int32, _P, _P, _I64, _P, _P, _P]
+lib.hip_mask_estimate_stages.restype = C.c_int
 lib.hip_decode_step.argtypes = [C.POINTER(Desc), C.POINTER(Ext), _P, _P, _P, _I64, _I64, _P, _P, _P,
                                 _P, _SZ, _P]
 lib.hip_decode_step.restype = C.c_int
@@ -359,6 +366,29 @@ def hip_mask_estimate_ex(q, K, k: int, block_k: int, block_q: int = 1, *, T=None
                                     p(K, "K"),
                                     k, block_k, block_q, p(indices, "indices"),
                                     p(nnz, "nnz"), None, 0, _stream(q.device, stream)))
+    return indices, nnz
+
+
+def hip_mask_estimate_stages(q, K, stages, block_k: int, *, T=None, causal=True, sink=0, window=0,
+                             block_table=None, indices=None, nnz=None, stream=None):
+    """Multi-stage search for per-row problems (block_q = 1).  stages: a list of
+    (chunk_size, k) in tokens, the first k None (stage 0 keeps every chunk), the
+    last chunk_size block_k.  Returns (indices, nnz) with k = stages[-1][1]."""
+    p = _on(q.device)  # device pointer of a tensor on q's device
+    desc, ext, _pages = _ext_desc(q, K, T, causal, sink, window, block_table)
+    arr = (Stage * max(len(stages), 1))(*[Stage(c, 0 if k is None else k) for c, k in stages])
+    k_last = stages[-1][1] if stages and stages[-1][1] is not None else 0
+    kb = k_last // block_k if block_k > 0 else 0
+    if indices is None:
+        indices = torch.empty((desc.B, desc.Hkv, desc.Tq, kb), dtype=torch.int32, device=q.device)
+    if nnz is None:
+        nnz = torch.empty((desc.B, desc.Hkv, desc.Tq), dtype=torch.int32, device=q.device)
+    _check_lists(indices, nnz, desc, desc.Tq, kb, q.device)
+    if desc.B * desc.Tq == 0:
+        return indices, nnz
+    _check(lib.hip_mask_estimate_stages(C.byref(desc), C.byref(ext), arr, len(stages), p(q, "q"),
+                                        p(K, "K"), block_k, p(indices, "indices"),
+                                        p(nnz, "nnz"), _stream(q.device, stream)))
     return indices, nnz
 
 

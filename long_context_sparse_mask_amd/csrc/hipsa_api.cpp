@@ -263,6 +263,69 @@ int hip_mask_estimate_paged(const hipsa_desc *desc, const hipsa_pages *pages, co
                               workspace_bytes, stream);
 }
 
+int hip_mask_estimate_stages(const hipsa_desc *desc, const hipsa_ext *ext,
+                             const hipsa_stage *stages, int32_t nstages, const void *q,
+                             const void *K, int64_t block_k, int32_t *indices, int32_t *nnz,
+                             void *stream) {
+  if (!stages) return fail(HIPSA_ERR_NULL, "stages is NULL");
+  if (nstages < 2 || nstages > hipsa::kMaxStages)
+    return fail(HIPSA_ERR_STAGES, "nstages=%d must be in [2, %d]", (int)nstages, hipsa::kMaxStages);
+  if (block_k < 1) return fail(HIPSA_ERR_BLOCK, "block_k=%lld must be positive", (long long)block_k);
+  hipsa::StageArgs a{};
+  a.nst = nstages;
+  int64_t cap = 0;
+  for (int32_t j = 0; j < nstages; j++) {
+    const int64_t c = stages[j].chunk_size, k = stages[j].k;
+    if (c < block_k || c % block_k != 0)
+      return fail(HIPSA_ERR_STAGES, "stage %d: chunk_size=%lld must be a positive multiple of "
+                  "block_k=%lld", (int)j, (long long)c, (long long)block_k);
+    if (j > 0 && c >= stages[j - 1].chunk_size)
+      return fail(HIPSA_ERR_STAGES, "stage %d: chunk_size=%lld must be below the previous "
+                  "stage's %lld", (int)j, (long long)c, (long long)stages[j - 1].chunk_size);
+    if (j == 0 && k != 0)
+      return fail(HIPSA_ERR_STAGES, "stage 0 keeps every chunk: its k must be 0 (got %lld)",
+                  (long long)k);
+    if (j > 0 && (k < c || k % c != 0 || k / c > hipsa::kMaxStageChunks))
+      return fail(HIPSA_ERR_STAGES, "stage %d: k=%lld must be a multiple of chunk_size=%lld "
+                  "keeping 1 to %d chunks", (int)j, (long long)k, (long long)c,
+                  hipsa::kMaxStageChunks);
+    if (c / block_k > INT32_MAX)
+      return fail(HIPSA_ERR_STAGES, "stage %d: chunk_size=%lld is too large", (int)j, (long long)c);
+    a.chunk[j] = (int32_t)(c / block_k);
+    a.keep[j] = j > 0 ? (int32_t)(k / c) : 0;
+    if (a.keep[j] > cap) cap = a.keep[j];
+  }
+  if (stages[nstages - 1].chunk_size != block_k)
+    return fail(HIPSA_ERR_STAGES, "the last stage's chunk_size=%lld must be block_k=%lld",
+                (long long)stages[nstages - 1].chunk_size, (long long)block_k);
+  hipsa::Shape s;
+  hipsa::Pages pg;
+  int rc = prepare(desc, ext, stages[nstages - 1].k, block_k, 1, true, &s, &pg);
+  if (rc) return rc;
+  const int64_t blocks = (s.T + block_k - 1) / block_k;
+  const int64_t n0 = (blocks + a.chunk[0] - 1) / a.chunk[0];
+  if (n0 > hipsa::kMaxStageChunks)
+    return fail(HIPSA_ERR_STAGES, "stage 0 cuts up to %lld chunks of %lld tokens; at most %d "
+                "are supported", (long long)n0, (long long)stages[0].chunk_size,
+                hipsa::kMaxStageChunks);
+  if (n0 > cap) cap = n0;
+  if (s.problems == 0) return ok();
+  if (!q || !K || !indices || !nnz)
+    return fail(HIPSA_ERR_NULL, "q, K, indices and nnz must be non-NULL");
+  if (pg.max_pages > 0 && !pg.table)
+    return fail(HIPSA_ERR_NULL, "pages->table must be non-NULL");
+  {
+    const void *p[] = {q, K};
+    const char *nm[] = {"q", "K"};
+    if ((rc = check_aligned(p, nm, 2))) return rc;
+  }
+  a.m = hipsa::MaskArgs{q, K, indices, nnz, s, pg};
+  a.cap = (int32_t)cap;
+  hipError_t e = hipsa::launch_mask_stages(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "multi-stage mask estimation launch");
+  return ok();
+}
+
 int hip_sparse_attn(const hipsa_desc *desc, const void *q, const void *K, const void *V,
                     const int32_t *indices, const int32_t *nnz, int64_t k, int64_t block_k,
                     int64_t block_q, void *out, void *workspace, size_t workspace_bytes,

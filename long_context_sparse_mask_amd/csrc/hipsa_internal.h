@@ -64,6 +64,21 @@ struct StepArgs {
   uint32_t *arrived;  // per problem: split workgroups done (zero between calls)
 };
 
+// Multi-stage search (per-row problems): stage 0 cuts chunks of chunk[0]
+// blocks and keeps them all; stage j >= 1 halves the kept chunks wider than
+// chunk[j] blocks and keeps the keep[j] best per round.
+constexpr int kMaxStages = 8;
+constexpr int kMaxStageChunks = 2048;  // largest stage-0 chunk count and per-round keep
+struct StageArgs {
+  MaskArgs m;           // m.s.Kb = keep[nst - 1]
+  int32_t nst;
+  int32_t chunk[kMaxStages];  // blocks, strictly decreasing, chunk[nst - 1] == 1
+  int32_t keep[kMaxStages];   // keep[0] unused
+  int32_t cap;          // LDS capacity in chunks: stage-0 count and every keep fit
+};
+hipError_t launch_mask_stages(const StageArgs &a, hipStream_t st);
+size_t mask_stages_lds(const StageArgs &a);  // dynamic LDS bytes of one workgroup
+
 // Decode / per-row problems (block_q == 1).
 hipError_t launch_mask_decode(const MaskArgs &a, hipStream_t st);
 hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t st);

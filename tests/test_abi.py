@@ -23,7 +23,7 @@ def test_header_declares_the_boundary():
     assert _declared() == sorted(["hip_mask_estimate", "hip_sparse_attn", "hip_mask_estimate_paged",
                                   "hip_sparse_attn_paged", "hip_mask_estimate_ex",
                                   "hip_sparse_attn_ex", "hip_sparse_attn_noalloc", "hip_decode_step",
-                                  "hipsa_decode_step_workspace_bytes",
+                                  "hipsa_decode_step_workspace_bytes", "hip_mask_estimate_stages",
                                   "hipsa_workspace_bytes", "hipsa_workspace_bytes_ex",
                                   "hipsa_last_error"])
 
@@ -57,6 +57,7 @@ def _mask(desc, k=2048, bk=64, bq=1, ptrs=(FAKE, FAKE, FAKE, FAKE)):
 
 
 ERR_NULL, ERR_SHAPE, ERR_BLOCK, ERR_DTYPE, ERR_WS, ERR_ALIGN, ERR_PAGES = -1, -2, -3, -4, -5, -7, -8
+ERR_STAGES = -9
 
 
 @pytest.mark.parametrize("kw,k,bk,bq,code", [
@@ -246,6 +247,53 @@ def test_dense_part_validation_and_workspace():
     assert hs.lib.hip_sparse_attn_ex(C.byref(d), C.byref(hs.Ext(None, 32, 0)), *args) == ERR_BLOCK
     assert hs.lib.hip_mask_estimate_ex(C.byref(d), C.byref(hs.Ext(None, 0, 64 * 300)), FAKE, FAKE,
                                        2048, 64, 1, FAKE, FAKE, None, 0, None) == ERR_BLOCK
+
+
+def _stages(desc, stages, bk=64, ext=None, ptrs=(FAKE, FAKE, FAKE, FAKE)):
+    import long_context_sparse_mask_amd as hs
+    arr = (hs.Stage * max(len(stages), 1))(*[hs.Stage(c, k) for c, k in stages])
+    q, K, idx, nnz = ptrs
+    return hs.lib.hip_mask_estimate_stages(C.byref(desc), ext, arr, len(stages), q, K, bk, idx,
+                                           nnz, None)
+
+
+GOOD_STAGES = [(512, 0), (128, 8192), (64, 2048)]
+
+
+@pytest.mark.parametrize("stages,bk,dkw,code", [
+    ([(512, 0)], 64, {}, ERR_STAGES),                              # one stage
+    ([(4096 >> j, 0 if j == 0 else 64) for j in range(9)], 16, {}, ERR_STAGES),  # nine stages
+    ([(512, 64), (64, 2048)], 64, {}, ERR_STAGES),                 # stage 0 keeps a count
+    ([(512, 0), (512, 2048), (64, 2048)], 64, {}, ERR_STAGES),     # chunk size not decreasing
+    ([(512, 0), (96, 2048), (64, 2048)], 64, {}, ERR_STAGES),      # not a multiple of block_k
+    ([(512, 0), (128, 8000), (64, 2048)], 64, {}, ERR_STAGES),     # k not a multiple of the chunk
+    ([(512, 0), (128, 0), (64, 2048)], 64, {}, ERR_STAGES),        # a later stage keeps nothing
+    ([(512, 0), (128, 128 * 2049), (64, 2048)], 64, {}, ERR_STAGES),  # keeps over 2048 chunks
+    ([(512, 0), (128, 8192)], 64, {}, ERR_STAGES),                 # last chunk is not block_k
+    ([(128, 0), (64, 2048)], 64, dict(T=64 * 4097, T_cap=64 * 4097), ERR_STAGES),  # 2049 stage-0 chunks
+    ([(512, 0), (128, 8192), (64, 64 * 513)], 64, {}, ERR_BLOCK),  # K_b above 512
+    (GOOD_STAGES, 48, {}, ERR_STAGES),                             # chunk sizes vs block_k 48
+    (GOOD_STAGES, 64, dict(Hq=30), ERR_SHAPE),                     # the shared checks still apply
+])
+def test_stages_reject_invalid_lists(stages, bk, dkw, code):
+    import long_context_sparse_mask_amd as hs
+    assert _stages(_desc(**dkw), stages, bk) == code, hs.lib.hipsa_last_error().decode()
+
+
+def test_stages_null_alignment_and_empty_problems():
+    import long_context_sparse_mask_amd as hs
+    d = _desc()
+    assert _stages(d, GOOD_STAGES, ptrs=(None, FAKE, FAKE, FAKE)) == ERR_NULL
+    assert _stages(d, GOOD_STAGES, ptrs=(C.c_void_p(0x1008), FAKE, FAKE, FAKE)) == ERR_ALIGN
+    assert hs.lib.hip_mask_estimate_stages(C.byref(d), None, None, 3, FAKE, FAKE, 64, FAKE, FAKE,
+                                           None) == ERR_NULL
+    # exactly 2048 stage-0 chunks is accepted as far as the pointers (NULL q here)
+    big = _desc(T=64 * 4096, T_cap=64 * 4096)
+    assert _stages(big, [(128, 0), (64, 2048)], ptrs=(None, FAKE, FAKE, FAKE)) == ERR_NULL
+    for e in (_desc(B=0), _desc(Tq=0)):
+        assert _stages(e, GOOD_STAGES, ptrs=(None, None, None, None)) == 0
+    # the dense part's checks apply (sink not a multiple of block_k)
+    assert _stages(d, GOOD_STAGES, ext=C.byref(hs.Ext(None, 32, 0))) == ERR_BLOCK
 
 
 def test_paged_empty_problem_is_a_no_op():
