@@ -11,7 +11,9 @@ the whole batch; the value is microseconds per step (lower is better).  With
 the default workload the line also carries the 32k and 1M-token decodes
 (`decode_32k`, `decode_1m_needles`, the latter with needle recall), the step
 as two calls, the chunked-prefill throughput (4096-token chunk at the end of
-a 32k sequence, `prefill`) and the fp8, paged and dense-part variants.
+a 32k sequence, `prefill`), the fp8, paged and dense-part variants, and the
+multi-stage search (`multi_stage`: a stage list per workload, alone and
+followed by the sparse attention).
 
 Timing: the K timed steps (and the W warm-up steps) are captured as HIP
 graphs of C-ABI launches on torch's capture stream and replayed, so host
@@ -419,21 +421,84 @@ def run_workload(w, steps, warmup, torch, hs, si, n_layers=N_LAYER_COPIES, n_q=N
     return res
 
 
-def needle_recall(w, x, indices):
-    """Share of (problem, needle block) pairs whose needle block is in the
-    problem's list: the GPU's lists (`indices`) and the oracle's, on the first
-    query set and layer copy (no roll, so the needles sit where drawn)."""
-    import numpy as np
-    import oracle
-    kw = dict(T=w.T, k=w.k, block_k=w.block_k, block_q=w.block_q, causal=w.causal)
-    o_idx, _, _ = oracle.mask_all(x["q"], x["K"], **kw)
-    needles = np.array(x["needles"])
+# Stage lists (tokens) of the multi-stage leg: stage 0 chunks of 8 blocks, a
+# middle stage keeping four times the final keys in 2-block chunks, then
+# single blocks; the same shape as the PR page's 128 -> 32 -> 8 chunks with
+# stage_k falling by 4.
+STAGES = {"decode_128k_b4": [(512, None), (128, 8192), (64, 2048)],
+          "decode_1m_needles": [(512, None), (128, 16384), (64, 4096)]}
 
-    def share(lists):
-        hits = [np.isin(needles, lists[b, g, 0]).sum() for b in range(w.B) for g in range(w.Hkv)]
-        return round(float(sum(hits)) / (len(hits) * len(needles)), 4)
-    return {"gpu": share(indices), "oracle": share(o_idx), "needles": len(needles),
-            "lists_equal": bool((indices == o_idx).all())}
+
+def run_stages(w, stages, steps, warmup, torch, hs, si, n_layers=N_LAYER_COPIES,
+               n_q=N_QUERY_SETS, x=None):
+    """The multi-stage search (hip_mask_estimate_stages) alone, and followed by
+    hip_sparse_attn over its lists, timed like the step; the lists of the
+    first query set and layer copy, and their overlap with the one-stage
+    search's."""
+    dev = torch.device("cuda:0")
+    x = x if x is not None else si.make_inputs(w)
+    layers, qs, _ = setup(w, x, torch, dev, n_layers, n_q)
+    idx = torch.empty((w.B, w.Hkv, w.Tq, w.kb), dtype=torch.int32, device=dev)
+    nnz = torch.empty((w.B, w.Hkv, w.Tq), dtype=torch.int32, device=dev)
+    out = torch.empty_like(qs[0])
+    ws = torch.zeros(max(hs.hipsa_workspace_bytes(qs[0], x["K"], w.k, w.block_k, 1, T=w.T), 1),
+                     dtype=torch.uint8, device=dev)
+
+    def mask(j):
+        q, L = qs[j % len(qs)], layers[j % len(layers)]
+        hs.hip_mask_estimate_stages(q, L[0], stages, w.block_k, T=w.T, indices=idx, nnz=nnz)
+
+    def step(j):
+        mask(j)
+        q, L = qs[j % len(qs)], layers[j % len(layers)]
+        hs.hip_sparse_attn(q, L[0], L[1], idx, nnz, w.k, w.block_k, 1, T=w.T, out=out,
+                           workspace=ws)
+
+    mask(0)
+    torch.cuda.synchronize()
+    first = idx.cpu().numpy()
+    one, _ = hs.hip_mask_estimate(qs[0], layers[0][0], w.k, w.block_k, 1, T=w.T)
+    one = one.cpu().numpy()
+    common = sum(len(set(a.tolist()) & set(b.tolist()))
+                 for a, b in zip(first.reshape(-1, w.kb), one.reshape(-1, w.kb)))
+
+    def timed(fn, n):
+        g = graph_of(fn, max(warmup, 1), torch)
+        g.replay()
+        del g
+        g = graph_of(fn, n, torch)
+        t = time_graph(g, 1, torch) / n
+        del g
+        return t
+    res = {"ms_mask": timed(mask, steps), "ms_step": timed(step, steps), "first": first,
+           "shared_with_one_stage": round(common / first.size, 4)}
+    del layers, qs
+    torch.cuda.empty_cache()
+    return res
+
+
+def stages_line(w, stages, r) -> dict:
+    nb = decode_bytes(w)
+    return {"workload": w.name, "stages": [[c, k] for c, k in stages],
+            "mask_us": round(r["ms_mask"] * 1e3, 3), "step_us": round(r["ms_step"] * 1e3, 3),
+            "step_frac": round(nb["attn"] / (r["ms_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "blocks_shared_with_one_stage": r["shared_with_one_stage"]}
+
+
+def needle_recall(x, indices):
+    """Needle recall of the GPU's lists (`indices`) on the first query set and
+    layer copy (no roll, so the needles sit where drawn)."""
+    return {"gpu": needle_share(x, indices), "needles": len(x["needles"])}
+
+
+def needle_share(x, lists):
+    """Share of (problem, needle block) pairs with the needle block in the
+    problem's list (query row 0)."""
+    import numpy as np
+    needles = np.array(x["needles"])
+    B, Hkv = lists.shape[:2]
+    hits = [np.isin(needles, lists[b, g, 0]).sum() for b in range(B) for g in range(Hkv)]
+    return round(float(sum(hits)) / (len(hits) * len(needles)), 4)
 
 
 def decode_line(w, r) -> dict:
@@ -466,6 +531,7 @@ def main():
     ap.add_argument("--window", type=int, default=4096, help="window tokens of the dense-part leg")
     ap.add_argument("--no-other-decodes", action="store_true",
                     help="skip the 32k and 1M-token decode legs")
+    ap.add_argument("--no-stages", action="store_true", help="skip the multi-stage search leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--only-step", action="store_true",
@@ -483,7 +549,7 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     if args.only_step:
-        args.no_fp8 = args.no_paged = args.no_dense = args.no_other_decodes = True
+        args.no_fp8 = args.no_paged = args.no_dense = args.no_other_decodes = args.no_stages = True
         args.no_prefill = args.no_cpu_baseline = True
 
     import torch
@@ -570,8 +636,20 @@ def main():
         r4 = run_workload(w4, small["steps"], small["warmup"], torch, hs, si, 4, args.query_sets,
                           x=x4)
         line["decode_1m_needles"] = decode_line(w4, r4)
-        line["decode_1m_needles"]["needle_recall"] = needle_recall(w4, x4, r4["first"]["indices"])
+        line["decode_1m_needles"]["needle_recall"] = needle_recall(x4, r4["first"]["indices"])
+        if not args.no_stages:
+            st4 = STAGES[w4.name]
+            rs4 = run_stages(w4, st4, small["steps"], small["warmup"], torch, hs, si, 4,
+                             args.query_sets, x=x4)
+            line.setdefault("multi_stage", {})[w4.name] = dict(
+                stages_line(w4, st4, rs4), needle_recall_gpu=needle_share(x4, rs4["first"]))
         del x4
+    if headline and not args.no_stages:
+        # the multi-stage search on the headline shape, then attention over its lists
+        st = STAGES[w.name]
+        rs = run_stages(w, st, args.steps, args.warmup, torch, hs, si, args.layer_copies,
+                        args.query_sets)
+        line.setdefault("multi_stage", {})[w.name] = stages_line(w, st, rs)
     if headline and not args.no_fp8:
         # the same step with an fp8 (E5M2) KV cache: half the K/V bytes
         w8 = si.workload(args.workload, dtype="bf16_e5m2")

@@ -248,6 +248,13 @@ size_t hipsa_workspace_bytes_ex(const hipsa_desc *desc, const hipsa_ext *ext, in
  *   ext: dense part and paged layout as in the *_ex calls, or NULL.
  *   q, K, indices, nnz: as in hip_mask_estimate with block_q = 1 and
  *     k = stages[last].k.
+ *   workspace: hipsa_stages_workspace_bytes() bytes (NULL and 0 when that is
+ *     0), 16-byte aligned, zero-filled before its first use.  A wide first
+ *     round (more than 1024 candidates) is scored by several workgroups per
+ *     row, which leave their keys and an arrival counter per row there;
+ *     every call leaves the counters at zero, so a workspace serves any
+ *     number of later calls.  Calls sharing a workspace must be ordered on
+ *     one stream.
  */
 typedef struct hipsa_stage {
   int64_t chunk_size; /* tokens                                        */
@@ -257,7 +264,12 @@ typedef struct hipsa_stage {
 int hip_mask_estimate_stages(const hipsa_desc *desc, const hipsa_ext *ext,
                              const hipsa_stage *stages, int32_t nstages, const void *q,
                              const void *K, int64_t block_k, int32_t *indices, int32_t *nnz,
-                             void *stream);
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes of hip_mask_estimate_stages for this shape and stage list
+ * (SIZE_MAX when the arguments are invalid). */
+size_t hipsa_stages_workspace_bytes(const hipsa_desc *desc, const hipsa_ext *ext,
+                                    const hipsa_stage *stages, int32_t nstages, int64_t block_k);
 
 /*
  * One decode step (block_q = 1): hip_mask_estimate followed by hip_sparse_attn

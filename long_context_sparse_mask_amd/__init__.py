@@ -24,7 +24,8 @@ import torch  # loads the HIP runtime first, so libhipsa binds to the same one
 
 __all__ = ["hip_mask_estimate", "hip_sparse_attn", "hip_mask_estimate_paged",
            "hip_sparse_attn_paged", "hip_mask_estimate_ex", "hip_sparse_attn_ex",
-           "hip_sparse_attn_noalloc", "hip_decode_step", "hip_mask_estimate_stages", "hipsa_decode_step_workspace_bytes",
+           "hip_sparse_attn_noalloc", "hip_decode_step", "hip_mask_estimate_stages",
+           "hipsa_stages_workspace_bytes", "hipsa_decode_step_workspace_bytes",
            "hipsa_workspace_bytes", "hipsa_workspace_bytes_ex",
            "HipsaError", "LIB_PATH", "lib", "NOALLOC_SCRATCH_BYTES"]
 
@@ -77,8 +78,11 @@ lib.hip_sparse_attn_ex.argtypes = [C.POINTER(Desc), C.POINTER(Ext), _P, _P, _P, 
                                    _I64, _P, _P, _SZ, _P]
 lib.hip_sparse_attn_ex.restype = C.c_int
 lib.hip_mask_estimate_stages.argtypes = [C.POINTER(Desc), C.POINTER(Ext), C.POINTER(Stage),
-                                         C.c_int32, _P, _P, _I64, _P, _P, _P]
+                                         C.c_int32, _P, _P, _I64, _P, _P, _P, _SZ, _P]
 lib.hip_mask_estimate_stages.restype = C.c_int
+lib.hipsa_stages_workspace_bytes.argtypes = [C.POINTER(Desc), C.POINTER(Ext), C.POINTER(Stage),
+                                             C.c_int32, _I64]
+lib.hipsa_stages_workspace_bytes.restype = _SZ
 lib.hip_decode_step.argtypes = [C.POINTER(Desc), C.POINTER(Ext), _P, _P, _P, _I64, _I64, _P, _P, _P,
                                 _P, _SZ, _P]
 lib.hip_decode_step.restype = C.c_int
@@ -369,14 +373,31 @@ def hip_mask_estimate_ex(q, K, k: int, block_k: int, block_q: int = 1, *, T=None
     return indices, nnz
 
 
+def _stage_array(stages):
+    return (Stage * max(len(stages), 1))(*[Stage(c, 0 if k is None else k) for c, k in stages])
+
+
+def hipsa_stages_workspace_bytes(q, K, stages, block_k: int, *, T=None, causal=True, sink=0,
+                                 window=0, block_table=None) -> int:
+    desc, ext, _pages = _ext_desc(q, K, T, causal, sink, window, block_table)
+    n = lib.hipsa_stages_workspace_bytes(C.byref(desc), C.byref(ext), _stage_array(stages),
+                                         len(stages), block_k)
+    if n == SIZE_MAX:
+        raise HipsaError(-9, lib.hipsa_last_error().decode())
+    return n
+
+
 def hip_mask_estimate_stages(q, K, stages, block_k: int, *, T=None, causal=True, sink=0, window=0,
-                             block_table=None, indices=None, nnz=None, stream=None):
+                             block_table=None, indices=None, nnz=None, workspace=None,
+                             stream=None):
     """Multi-stage search for per-row problems (block_q = 1).  stages: a list of
     (chunk_size, k) in tokens, the first k None (stage 0 keeps every chunk), the
-    last chunk_size block_k.  Returns (indices, nnz) with k = stages[-1][1]."""
+    last chunk_size block_k.  Returns (indices, nnz) with k = stages[-1][1].
+    `workspace`: hipsa_stages_workspace_bytes() bytes, zero-filled before its
+    first use (allocated, zeroed, when None and needed)."""
     p = _on(q.device)  # device pointer of a tensor on q's device
     desc, ext, _pages = _ext_desc(q, K, T, causal, sink, window, block_table)
-    arr = (Stage * max(len(stages), 1))(*[Stage(c, 0 if k is None else k) for c, k in stages])
+    arr = _stage_array(stages)
     k_last = stages[-1][1] if stages and stages[-1][1] is not None else 0
     kb = k_last // block_k if block_k > 0 else 0
     if indices is None:
@@ -386,9 +407,14 @@ def hip_mask_estimate_stages(q, K, stages, block_k: int, *, T=None, causal=True,
     _check_lists(indices, nnz, desc, desc.Tq, kb, q.device)
     if desc.B * desc.Tq == 0:
         return indices, nnz
+    need = lib.hipsa_stages_workspace_bytes(C.byref(desc), C.byref(ext), arr, len(stages), block_k)
+    if workspace is None and 0 < need < SIZE_MAX:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = p(workspace, "workspace") if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.hip_mask_estimate_stages(C.byref(desc), C.byref(ext), arr, len(stages), p(q, "q"),
                                         p(K, "K"), block_k, p(indices, "indices"),
-                                        p(nnz, "nnz"), _stream(q.device, stream)))
+                                        p(nnz, "nnz"), ws_ptr, ws_len, _stream(q.device, stream)))
     return indices, nnz
 
 

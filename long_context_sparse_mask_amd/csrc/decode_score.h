@@ -57,9 +57,11 @@ struct QueryOps {
 // Scores candidate slots [0, n) with chunks (ca[c], ce[c]) in blocks (start
 // -1: an empty slot) and writes key[c] = rank_key(score, start), or 0 for an
 // empty slot.  Tp: the row's visible length; row_of(t): element offset of the
-// K row of position t.  Called by all 256 threads; LDS reads of ca/ce, no
-// barrier.
-template <typename E, typename KE, int D, int GMAX, int UNROLL, typename RowOf>
+// K row of position t.  UNROLL: tiles (MFMA) or rows (VALU) per lane whose
+// loads are issued together; TRIM: the MFMA path skips a batch's tiles past
+// n (for callers whose n varies below what UNROLL was sized for).  Called by
+// all 256 threads; LDS reads of ca/ce, no barrier.
+template <typename E, typename KE, int D, int GMAX, int UNROLL, bool TRIM = false, typename RowOf>
 __device__ __forceinline__ void score_slots(const QueryOps<E, D, GMAX> &qo, const KE *Kbase, RowOf row_of,
                                             const int32_t *ca, const int32_t *ce, int n, int32_t Tp,
                                             const Shape &s, uint64_t *key) {
@@ -78,6 +80,7 @@ __device__ __forceinline__ void score_slots(const QueryOps<E, D, GMAX> &qo, cons
       bool live[UNROLL];
 #pragma unroll
       for (int u = 0; u < UNROLL; u++) {
+        if (TRIM && t0 + 4 * u >= ntile) break;  // uniform: the wave's tiles are done
         const int c = 16 * (t0 + 4 * u) + (lane & 15);
         const int cc = c < n ? c : 0;
         const int32_t lo_b = ca[cc], hi_b = ce[cc];
@@ -90,6 +93,7 @@ __device__ __forceinline__ void score_slots(const QueryOps<E, D, GMAX> &qo, cons
       }
 #pragma unroll
       for (int u = 0; u < UNROLL; u++) {
+        if (TRIM && t0 + 4 * u >= ntile) break;
         const int c = 16 * (t0 + 4 * u) + (lane & 15);
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll

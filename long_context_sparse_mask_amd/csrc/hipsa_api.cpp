@@ -263,16 +263,20 @@ int hip_mask_estimate_paged(const hipsa_desc *desc, const hipsa_pages *pages, co
                               workspace_bytes, stream);
 }
 
-int hip_mask_estimate_stages(const hipsa_desc *desc, const hipsa_ext *ext,
-                             const hipsa_stage *stages, int32_t nstages, const void *q,
-                             const void *K, int64_t block_k, int32_t *indices, int32_t *nnz,
-                             void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks of a stage list and the shape; fills `a` (all but the pointers) and
+// returns the workspace bytes in *ws.
+int prepare_stages(const hipsa_desc *desc, const hipsa_ext *ext, const hipsa_stage *stages,
+                   int32_t nstages, int64_t block_k, hipsa::StageArgs *a, size_t *ws) {
   if (!stages) return fail(HIPSA_ERR_NULL, "stages is NULL");
   if (nstages < 2 || nstages > hipsa::kMaxStages)
     return fail(HIPSA_ERR_STAGES, "nstages=%d must be in [2, %d]", (int)nstages, hipsa::kMaxStages);
   if (block_k < 1) return fail(HIPSA_ERR_BLOCK, "block_k=%lld must be positive", (long long)block_k);
-  hipsa::StageArgs a{};
-  a.nst = nstages;
+  *a = hipsa::StageArgs{};
+  a->nst = nstages;
   int64_t cap = 0;
   for (int32_t j = 0; j < nstages; j++) {
     const int64_t c = stages[j].chunk_size, k = stages[j].k;
@@ -291,39 +295,77 @@ int hip_mask_estimate_stages(const hipsa_desc *desc, const hipsa_ext *ext,
                   hipsa::kMaxStageChunks);
     if (c / block_k > INT32_MAX)
       return fail(HIPSA_ERR_STAGES, "stage %d: chunk_size=%lld is too large", (int)j, (long long)c);
-    a.chunk[j] = (int32_t)(c / block_k);
-    a.keep[j] = j > 0 ? (int32_t)(k / c) : 0;
-    if (a.keep[j] > cap) cap = a.keep[j];
+    a->chunk[j] = (int32_t)(c / block_k);
+    a->keep[j] = j > 0 ? (int32_t)(k / c) : 0;
+    if (a->keep[j] > cap) cap = a->keep[j];
   }
   if (stages[nstages - 1].chunk_size != block_k)
     return fail(HIPSA_ERR_STAGES, "the last stage's chunk_size=%lld must be block_k=%lld",
                 (long long)stages[nstages - 1].chunk_size, (long long)block_k);
-  hipsa::Shape s;
   hipsa::Pages pg;
-  int rc = prepare(desc, ext, stages[nstages - 1].k, block_k, 1, true, &s, &pg);
+  int rc = prepare(desc, ext, stages[nstages - 1].k, block_k, 1, true, &a->m.s, &pg);
   if (rc) return rc;
-  const int64_t blocks = (s.T + block_k - 1) / block_k;
-  const int64_t n0 = (blocks + a.chunk[0] - 1) / a.chunk[0];
+  a->m.pg = pg;
+  const int64_t blocks = (a->m.s.T + block_k - 1) / block_k;
+  const int64_t n0 = (blocks + a->chunk[0] - 1) / a->chunk[0];
   if (n0 > hipsa::kMaxStageChunks)
     return fail(HIPSA_ERR_STAGES, "stage 0 cuts up to %lld chunks of %lld tokens; at most %d "
                 "are supported", (long long)n0, (long long)stages[0].chunk_size,
                 hipsa::kMaxStageChunks);
   if (n0 > cap) cap = n0;
-  if (s.problems == 0) return ok();
+  a->cap = (int32_t)cap;
+  *ws = hipsa::mask_stages_plan(a);
+  return HIPSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hip_mask_estimate_stages(const hipsa_desc *desc, const hipsa_ext *ext,
+                             const hipsa_stage *stages, int32_t nstages, const void *q,
+                             const void *K, int64_t block_k, int32_t *indices, int32_t *nnz,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+  hipsa::StageArgs a;
+  size_t need = 0;
+  int rc = prepare_stages(desc, ext, stages, nstages, block_k, &a, &need);
+  if (rc) return rc;
+  if (a.m.s.problems == 0) return ok();
   if (!q || !K || !indices || !nnz)
     return fail(HIPSA_ERR_NULL, "q, K, indices and nnz must be non-NULL");
-  if (pg.max_pages > 0 && !pg.table)
+  if (a.m.pg.max_pages > 0 && !a.m.pg.table)
     return fail(HIPSA_ERR_NULL, "pages->table must be non-NULL");
   {
     const void *p[] = {q, K};
     const char *nm[] = {"q", "K"};
     if ((rc = check_aligned(p, nm, 2))) return rc;
   }
-  a.m = hipsa::MaskArgs{q, K, indices, nnz, s, pg};
-  a.cap = (int32_t)cap;
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(HIPSA_ERR_WORKSPACE, "workspace of %zu bytes at %p is too small: need %zu",
+                  workspace_bytes, workspace, need);
+    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+      return fail(HIPSA_ERR_ALIGN, "workspace at %p is not 16-byte aligned", workspace);
+    a.keys = static_cast<uint64_t *>(workspace);
+    a.arrived = reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) + need -
+                                             (size_t)a.m.s.problems * sizeof(uint32_t));
+  }
+  a.m.q = q;
+  a.m.K = K;
+  a.m.indices = indices;
+  a.m.nnz = nnz;
   hipError_t e = hipsa::launch_mask_stages(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "multi-stage mask estimation launch");
   return ok();
+}
+
+size_t hipsa_stages_workspace_bytes(const hipsa_desc *desc, const hipsa_ext *ext,
+                                    const hipsa_stage *stages, int32_t nstages, int64_t block_k) {
+  hipsa::StageArgs a;
+  size_t need = 0;
+  if (prepare_stages(desc, ext, stages, nstages, block_k, &a, &need)) return SIZE_MAX;
+  g_err.clear();
+  return need;
 }
 
 int hip_sparse_attn(const hipsa_desc *desc, const void *q, const void *K, const void *V,

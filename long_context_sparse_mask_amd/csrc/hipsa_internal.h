@@ -75,9 +75,20 @@ struct StageArgs {
   int32_t chunk[kMaxStages];  // blocks, strictly decreasing, chunk[nst - 1] == 1
   int32_t keep[kMaxStages];   // keep[0] unused
   int32_t cap;          // LDS capacity in chunks: stage-0 count and every keep fit
+  // Wide first rounds: `splits` workgroups per problem score the first round
+  // of stage 1 (2 * stage-0 chunks slots), store the keys in `keys`
+  // [problems, n1max], and the last to arrive (`arrived`, zero between calls)
+  // runs the rest of the search.  splits == 1: one workgroup does it all.
+  int32_t splits;
+  int32_t n1max;
+  uint64_t *keys;
+  uint32_t *arrived;
 };
 hipError_t launch_mask_stages(const StageArgs &a, hipStream_t st);
 size_t mask_stages_lds(const StageArgs &a);  // dynamic LDS bytes of one workgroup
+// Workgroups per problem for the first round (fills splits), and the
+// workspace bytes that needs (keys, then one arrival counter per problem).
+size_t mask_stages_plan(StageArgs *a);
 
 // Decode / per-row problems (block_q == 1).
 hipError_t launch_mask_decode(const MaskArgs &a, hipStream_t st);

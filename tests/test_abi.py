@@ -24,6 +24,7 @@ def test_header_declares_the_boundary():
                                   "hip_sparse_attn_paged", "hip_mask_estimate_ex",
                                   "hip_sparse_attn_ex", "hip_sparse_attn_noalloc", "hip_decode_step",
                                   "hipsa_decode_step_workspace_bytes", "hip_mask_estimate_stages",
+                                  "hipsa_stages_workspace_bytes",
                                   "hipsa_workspace_bytes", "hipsa_workspace_bytes_ex",
                                   "hipsa_last_error"])
 
@@ -249,12 +250,16 @@ def test_dense_part_validation_and_workspace():
                                        2048, 64, 1, FAKE, FAKE, None, 0, None) == ERR_BLOCK
 
 
-def _stages(desc, stages, bk=64, ext=None, ptrs=(FAKE, FAKE, FAKE, FAKE)):
+def _stage_arr(stages):
     import long_context_sparse_mask_amd as hs
-    arr = (hs.Stage * max(len(stages), 1))(*[hs.Stage(c, k) for c, k in stages])
+    return (hs.Stage * max(len(stages), 1))(*[hs.Stage(c, k) for c, k in stages])
+
+
+def _stages(desc, stages, bk=64, ext=None, ptrs=(FAKE, FAKE, FAKE, FAKE), ws=None, ws_bytes=0):
+    import long_context_sparse_mask_amd as hs
     q, K, idx, nnz = ptrs
-    return hs.lib.hip_mask_estimate_stages(C.byref(desc), ext, arr, len(stages), q, K, bk, idx,
-                                           nnz, None)
+    return hs.lib.hip_mask_estimate_stages(C.byref(desc), ext, _stage_arr(stages), len(stages), q,
+                                           K, bk, idx, nnz, ws, ws_bytes, None)
 
 
 GOOD_STAGES = [(512, 0), (128, 8192), (64, 2048)]
@@ -286,7 +291,7 @@ def test_stages_null_alignment_and_empty_problems():
     assert _stages(d, GOOD_STAGES, ptrs=(None, FAKE, FAKE, FAKE)) == ERR_NULL
     assert _stages(d, GOOD_STAGES, ptrs=(C.c_void_p(0x1008), FAKE, FAKE, FAKE)) == ERR_ALIGN
     assert hs.lib.hip_mask_estimate_stages(C.byref(d), None, None, 3, FAKE, FAKE, 64, FAKE, FAKE,
-                                           None) == ERR_NULL
+                                           None, 0, None) == ERR_NULL
     # exactly 2048 stage-0 chunks is accepted as far as the pointers (NULL q here)
     big = _desc(T=64 * 4096, T_cap=64 * 4096)
     assert _stages(big, [(128, 0), (64, 2048)], ptrs=(None, FAKE, FAKE, FAKE)) == ERR_NULL
@@ -294,6 +299,27 @@ def test_stages_null_alignment_and_empty_problems():
         assert _stages(e, GOOD_STAGES, ptrs=(None, None, None, None)) == 0
     # the dense part's checks apply (sink not a multiple of block_k)
     assert _stages(d, GOOD_STAGES, ext=C.byref(hs.Ext(None, 32, 0))) == ERR_BLOCK
+
+
+def test_stages_workspace():
+    """A first round of more than 1024 candidates is spread over workgroups
+    (at most one per CU, at least 128 slots each), whose keys and arrival
+    counters need a workspace; narrower first rounds need none."""
+    import long_context_sparse_mask_amd as hs
+
+    def ws(d, stages, bk=64):
+        return hs.lib.hipsa_stages_workspace_bytes(C.byref(d), None, _stage_arr(stages),
+                                                   len(stages), bk)
+    assert ws(_desc(B=4, T=131072, T_cap=131072), GOOD_STAGES) == 0   # 512 first-round slots
+    one_m = _desc(T=1 << 20, T_cap=1 << 20)
+    st = [(512, 0), (128, 16384), (64, 4096)]
+    # 2048 stage-0 chunks: 4096 slots per row, 8 rows, keys 8 B each, then 8 counters
+    assert ws(one_m, st) == 8 * 4096 * 8 + 8 * 4
+    assert ws(one_m, [(512, 0)]) == hs.SIZE_MAX
+    rc = _stages(one_m, st, ptrs=(FAKE, FAKE, FAKE, FAKE), ws=FAKE, ws_bytes=8 * 4096 * 8)
+    assert rc == ERR_WS and "too small" in hs.lib.hipsa_last_error().decode()
+    assert _stages(one_m, st, ws=None, ws_bytes=0) == ERR_WS
+    assert _stages(one_m, st, ws=C.c_void_p(0x1008), ws_bytes=1 << 20) == ERR_ALIGN
 
 
 def test_paged_empty_problem_is_a_no_op():

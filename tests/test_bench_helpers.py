@@ -120,3 +120,22 @@ def test_source_hash_ignores_comments_only(tmp_path):
     assert bench.kernel_source_sha(str(tmp_path)) != base
     (tmp_path / "k.hip").write_text(src.replace("a + 1", "a + 2"))
     assert bench.kernel_source_sha(str(tmp_path)) != base
+
+
+def test_needle_share():
+    """Needle recall counts (KV head, needle) pairs whose block is listed."""
+    import numpy as np
+    x = {"needles": [5, 9]}
+    lists = np.full((1, 2, 1, 4), -1, np.int32)
+    lists[0, 0, 0, :2] = [5, 9]   # head 0 finds both
+    lists[0, 1, 0, :2] = [1, 9]   # head 1 finds one
+    assert bench.needle_share(x, lists) == 0.75
+    assert bench.needle_recall(x, lists) == {"gpu": 0.75, "needles": 2}
+
+
+def test_stage_lists_end_at_the_workload_k():
+    """The multi-stage leg's lists keep the workload's k in single blocks."""
+    for name, stages in bench.STAGES.items():
+        w = si.workload(name)
+        assert stages[0][1] is None and stages[-1] == (w.block_k, w.k)
+        assert all(a[0] > b[0] for a, b in zip(stages, stages[1:]))

@@ -114,6 +114,21 @@ CASES = {
     "paged": (dict(name="decode_32k", B=2, Hq=8, Hkv=2, T=7000), THREE, dict(page_size=128)),
     "paged_e5m2_sink": (dict(name="decode_32k", B=2, Hq=8, Hkv=2, T=7000, dtype="bf16_e5m2"),
                         THREE, dict(page_size=256, sink=64, window=512)),
+    # first rounds of more than 1024 candidates: scored by several workgroups
+    # per row (keys through the workspace, the last to arrive goes on); rows
+    # of different lengths and a dense part give some workgroups no slots
+    "split_first_round_rows": (dict(name="decode_32k", Hq=8, Hkv=2, T=200000, Tq=16,
+                                    block_k=16, k=1024),
+                               [(128, None), (32, 4096), (16, 1024)], dict(sink=16, window=256)),
+    "split_first_round_fp32": (dict(name="tiny_decode", Hq=2, Hkv=1, T=65536, k=256),
+                               [(64, None), (16, 1024), (8, 256)], {}),
+    "split_first_round_paged_e5m2": (dict(name="decode_32k", B=2, Hq=8, Hkv=2, T=100000,
+                                          block_k=16, k=1024, dtype="bf16_e5m2"),
+                                     [(128, None), (32, 4096), (16, 1024)], dict(page_size=256)),
+    # 256 rows (one workgroup per CU already): a 2048-candidate first round
+    # stays in one workgroup per row
+    "wide_first_round_in_one_workgroup": (dict(name="decode_32k", B=4, Tq=8, block_k=8, k=512),
+                                          [(32, None), (16, 2048), (8, 512)], {}),
 }
 
 
@@ -141,3 +156,29 @@ def test_one_stage_list_is_the_plain_search():
     safe = o_margin >= MARGIN
     assert (nnz == p_nnz).all()
     assert (idx[safe] == p_idx[safe]).all()
+
+
+def test_split_workspace_is_reused():
+    """Several calls share one workspace: each leaves its arrival counters at
+    zero, and each call's lists are those of a fresh workspace."""
+    import long_context_sparse_mask_amd as hs
+    w = si.workload("decode_32k", Hq=8, Hkv=2, d=64, T=150000, block_k=16, k=1024)
+    stages = [(128, None), (32, 4096), (16, 1024)]
+    x = si.make_inputs(w)
+    q, K = x["q"].cuda(), x["K"].cuda()
+    need = hs.hipsa_stages_workspace_bytes(q, K, stages, w.block_k, T=w.T)
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    results = []
+    for j in range(3):
+        qj = q if j == 0 else torch.roll(q, j, dims=-1).contiguous()
+        idx, nnz = hs.hip_mask_estimate_stages(qj, K, stages, w.block_k, T=w.T, workspace=ws)
+        fresh, fnnz = hs.hip_mask_estimate_stages(qj, K, stages, w.block_k, T=w.T)
+        torch.cuda.synchronize()
+        assert torch.equal(idx, fresh) and torch.equal(nnz, fnnz)
+        assert int(ws[need - 4 * w.B * w.Hkv:].view(torch.int32).abs().sum()) == 0
+        results.append(idx.cpu())
+    assert not torch.equal(results[0], results[1])
+    o_idx, o_nnz, o_margin = oracle.mask_stages_all(x["q"], x["K"], stages, T=w.T,
+                                                    block_k=w.block_k, causal=1)
+    compare_stage_masks(results[0].numpy(), o_nnz, o_idx, o_nnz, o_margin, x, w, stages)
