@@ -20,6 +20,15 @@
 
 namespace hipsa {
 
+// LDS tiles per wave of the row-by-row gathers (score_slots' `stage`: 4 waves
+// x kStageTiles x TileGather<KE, D>::kBytes).
+constexpr int kStageTiles = 2;
+template <typename E, typename KE, int D>
+constexpr int stage_bytes() {
+  if constexpr (std::is_same<E, uint16_t>::value) return 4 * kStageTiles * TileGather<KE, D>::kBytes;
+  else return 16;  // the VALU path stages nothing
+}
+
 // Query operands of a problem's group of query heads.  MFMA: lane l holds
 // head l%16 (zero when past the group), dims 32*ks + 8*(l/16) .. +7.  VALU:
 // every head, dims cs*VEC .. +VEC-1 for the lane's column slice cs.
@@ -64,7 +73,7 @@ struct QueryOps {
 template <typename E, typename KE, int D, int GMAX, int UNROLL, bool TRIM = false, typename RowOf>
 __device__ __forceinline__ void score_slots(const QueryOps<E, D, GMAX> &qo, const KE *Kbase, RowOf row_of,
                                             const int32_t *ca, const int32_t *ce, int n, int32_t Tp,
-                                            const Shape &s, uint64_t *key) {
+                                            const Shape &s, uint64_t *key, uint8_t *stage = nullptr) {
   constexpr bool kMfma = QueryOps<E, D, GMAX>::kMfma;
   constexpr int VEC = QueryOps<E, D, GMAX>::VEC;
   constexpr int TPR = QueryOps<E, D, GMAX>::TPR;
@@ -75,6 +84,55 @@ __device__ __forceinline__ void score_slots(const QueryOps<E, D, GMAX> &qo, cons
   const auto &qv = qo.qv;
   if constexpr (kMfma) {
     const int ntile = (n + 15) / 16;
+    if (stage) {  // uniform: rows gathered row by row, through the wave's LDS tiles
+      using TG = TileGather<KE, D>;
+      uint8_t *mine = stage + wave * kStageTiles * TG::kBytes;
+      // centre token of slot c (0 for an empty slot: row 0 is read and discarded)
+      auto centre = [&](int c) -> int32_t {
+        const int cc = c < n ? c : 0;
+        const int32_t lo_b = ca[cc], hi_b = ce[cc];
+        const int32_t lo = lo_b << s.bk_shift, hi = min(hi_b << s.bk_shift, Tp);
+        return c < n && lo_b >= 0 ? (lo + hi) >> 1 : 0;
+      };
+      for (int t0 = wave; t0 < ntile; t0 += 4 * UNROLL) {
+        uint4 v[UNROLL][TG::kLoads];
+#pragma unroll
+        for (int u = 0; u < UNROLL; u++) {
+          if (TRIM && t0 + 4 * u >= ntile) break;  // uniform
+#pragma unroll
+          for (int j = 0; j < TG::kLoads; j++) v[u][j] = TG::load(Kbase + row_of(centre(16 * (t0 + 4 * u) + TG::row(j))));
+        }
+#pragma unroll
+        for (int u0 = 0; u0 < UNROLL; u0 += kStageTiles) {
+#pragma unroll
+          for (int du = 0; du < kStageTiles; du++)
+            if (u0 + du < UNROLL && (!TRIM || t0 + 4 * (u0 + du) < ntile)) TG::put(v[u0 + du], mine + du * TG::kBytes);
+          wave_lds_sync();
+#pragma unroll
+          for (int du = 0; du < kStageTiles; du++) {
+            const int u = u0 + du;
+            if (u >= UNROLL || (TRIM && t0 + 4 * u >= ntile)) break;
+            typename TG::raw_t kr[KS];
+            TG::get(mine + du * TG::kBytes, kr);
+            const int c = 16 * (t0 + 4 * u) + (lane & 15);
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ks++)
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[ks]), as_bf16x8(Kv8<KE>::bf16(kr[ks])),
+                                                            acc, 0, 0, 0);
+            float best = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+              if (4 * (lane >> 4) + r < s.G) best = fmaxf(best, acc[r]);
+            if (GMAX > 4) best = fmaxf(best, __shfl_xor(best, 16, 64));
+            if (GMAX > 8) best = fmaxf(best, __shfl_xor(best, 32, 64));
+            if (lane < 16 && c < n) key[c] = ca[c] >= 0 ? rank_key(best, ca[c]) : 0ull;
+          }
+          wave_lds_sync();  // the next tiles overwrite these
+        }
+      }
+      return;
+    }
     for (int t0 = wave; t0 < ntile; t0 += 4 * UNROLL) {
       typename Kv8<KE>::raw_t kr[UNROLL][KS];
       bool live[UNROLL];

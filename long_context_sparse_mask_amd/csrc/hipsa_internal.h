@@ -83,6 +83,7 @@ struct StageArgs {
   int32_t n1max;
   uint64_t *keys;
   uint32_t *arrived;
+  int32_t stage_off;  // byte offset in dynamic LDS of the row-gather tiles, -1: none
 };
 hipError_t launch_mask_stages(const StageArgs &a, hipStream_t st);
 size_t mask_stages_lds(const StageArgs &a);  // dynamic LDS bytes of one workgroup
@@ -257,6 +258,56 @@ template <> struct Kv8<uint8_t> {
                       e5m2x2_to_bf16x2<false>(r.y), e5m2x2_to_bf16x2<true>(r.y));
   }
 };
+
+// Gathers of 16 key rows in matrix-core operand layout, through LDS.  In the
+// operand layout the 16 lanes of a quarter-wave read 16 different rows, and a
+// CU then fetches each 128-byte line of a row in two halves: measured on
+// MI355X, one workgroup gathers random 256-byte rows at about 17 GB/s that
+// way and at about 30 GB/s when the lanes of a quarter-wave read one row
+// together (16 bytes each).  So a tile is loaded row by row
+// (kLanesPerRow lanes per row, kRowsPerLoad rows per load), written to a
+// per-wave LDS tile whose rows are padded by 16 bytes (the transposed reads
+// then hit distinct banks), and read back in operand layout: lane l gets row
+// l % 16, elements 32 ks + 8 (l / 16) .. + 7 of k-step ks.
+template <typename KE, int D>
+struct TileGather {
+  static constexpr int kRowBytes = D * (int)sizeof(KE);
+  static constexpr int kLanesPerRow = kRowBytes / 16;
+  static constexpr int kRowsPerLoad = 64 / kLanesPerRow;
+  static constexpr int kLoads = 16 / kRowsPerLoad;
+  static constexpr int kStride = kRowBytes + 16;
+  static constexpr int kBytes = 16 * kStride;  // LDS bytes of one tile
+  static constexpr int KS = D / 32;
+  using raw_t = typename Kv8<KE>::raw_t;
+
+  // tile row that this lane loads in load j
+  __device__ static int row(int j) { return j * kRowsPerLoad + (int)(threadIdx.x & 63) / kLanesPerRow; }
+  // this lane's 16 bytes of the row that starts at `p`
+  __device__ static uint4 load(const KE *p) {
+    return *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(p) +
+                                            16 * ((int)(threadIdx.x & 63) % kLanesPerRow));
+  }
+  __device__ static void put(const uint4 (&v)[kLoads], uint8_t *tile) {
+#pragma unroll
+    for (int j = 0; j < kLoads; j++)
+      *reinterpret_cast<uint4 *>(tile + row(j) * kStride + 16 * ((int)(threadIdx.x & 63) % kLanesPerRow)) = v[j];
+  }
+  __device__ static void get(const uint8_t *tile, raw_t (&out)[KS]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++)
+      out[ks] = *reinterpret_cast<const raw_t *>(tile + (lane & 15) * kStride +
+                                                 (32 * ks + 8 * (lane >> 4)) * (int)sizeof(KE));
+  }
+};
+
+// Orders a wave's LDS accesses before and after it (a wave reading back what
+// it wrote itself).
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 // N consecutive elements of a V row (N*sizeof(KE) = 2, 4, 8 or 16 bytes)
 // widened to fp32; a load that is not kept reads as zeros.

@@ -68,6 +68,8 @@ __global__ __launch_bounds__(256) void mask_decode_kernel(MaskArgs a) {
   __shared__ uint64_t key[2 * kMaxKb + kSpan];
   __shared__ int32_t rk[2 * kMaxKb];
   __shared__ int32_t flag[2];
+  constexpr bool kMfma = std::is_same<E, uint16_t>::value;
+  __shared__ __align__(16) uint8_t stage[stage_bytes<E, KE, D>()];
   extern __shared__ int32_t ptab[];  // paged: the sequence's page numbers
 
   const E *qbase = reinterpret_cast<const E *>(a.q) + ((int64_t)(b * s.Hq + g * s.G) * Tq + i) * D;
@@ -100,7 +102,7 @@ __global__ __launch_bounds__(256) void mask_decode_kernel(MaskArgs a) {
     for (int c = tid; c < n; c += 256) rk[c] = 0;  // rank counts of this round
 
     // ---- 1. scoring
-    score_slots<E, KE, D, GMAX, UNROLL>(qo, Kbase, row_of, ca, ce, n, Tp, s, key);
+    score_slots<E, KE, D, GMAX, UNROLL>(qo, Kbase, row_of, ca, ce, n, Tp, s, key, kMfma ? stage : nullptr);
     __syncthreads();
 
     // ---- 2. selection: the K_b best write their halves into the other buffer

@@ -194,13 +194,15 @@ __global__ __launch_bounds__(256) void mask_stages_kernel(StageArgs a) {
     return;
   }
 
-  extern __shared__ uint64_t lds[];
+  extern __shared__ __align__(16) uint64_t lds[];
   const int cap = a.cap;
   uint64_t *key = lds;                                         // [2 cap]
   int32_t *bs = reinterpret_cast<int32_t *>(key + 2 * cap);    // [2 cap]
   int32_t *be = bs + 2 * cap;                                  // [2 cap]
   int32_t *as = be + 2 * cap, *ae = as + cap;                  // [cap] each
   int32_t *ptab = ae + cap;                                    // paged: the sequence's pages
+  // row-gather tiles (when the launch has room for them)
+  uint8_t *stg = a.stage_off >= 0 ? reinterpret_cast<uint8_t *>(lds) + a.stage_off : nullptr;
   __shared__ uint32_t hist[3 * 256];
   __shared__ int32_t wcnt[4];
   __shared__ int32_t flag[2];  // by round parity: a kept chunk is wider than the stage's size
@@ -239,7 +241,7 @@ __global__ __launch_bounds__(256) void mask_stages_kernel(StageArgs a) {
     const int c_lo = min((int)split * per, n1), cnt = min(c_lo + per, n1) - c_lo;
     for (int c = tid; c < cnt; c += 256) first_slot(c_lo + c, &bs[c], &be[c]);
     __syncthreads();
-    score_slots<E, KE, D, GMAX, UNROLL, true>(qo, Kbase, row_of, bs, be, cnt, Tp, s, key);
+    score_slots<E, KE, D, GMAX, UNROLL, true>(qo, Kbase, row_of, bs, be, cnt, Tp, s, key, stg);
     __syncthreads();
     uint64_t *gk = a.keys + (int64_t)prob * a.n1max;
     for (int c = tid; c < cnt; c += 256)
@@ -295,7 +297,7 @@ __global__ __launch_bounds__(256) void mask_stages_kernel(StageArgs a) {
         be[2 * j + 1] = halve ? hi : -1;
       }
       __syncthreads();
-      score_slots<E, KE, D, GMAX, UNROLL, true>(qo, Kbase, row_of, bs, be, n, Tp, s, key);
+      score_slots<E, KE, D, GMAX, UNROLL, true>(qo, Kbase, row_of, bs, be, n, Tp, s, key, stg);
       __syncthreads();
     }
     scored = false;
@@ -370,10 +372,27 @@ void launch_layout(const StageArgs &a, size_t lds, hipStream_t st) {
 
 }  // namespace
 
-size_t mask_stages_lds(const StageArgs &a) {
-  // key (8 bytes) and B (8 bytes) per slot, two slots per chunk; A 8 bytes per chunk
+// Dynamic LDS of one workgroup: key (8 bytes) and B (8 bytes) per slot, two
+// slots per chunk, A 8 bytes per chunk, the page numbers when paged, then the
+// row-gather tiles of the matrix-core path when they fit beside the rest.
+constexpr size_t kLdsBudget = 160 * 1024 - 4096;  // per workgroup, less the static arrays
+
+size_t lists_lds(const StageArgs &a) {
   const size_t chunks = (size_t)a.cap * (2 * 8 + 2 * 8 + 8);
-  return chunks + (a.m.pg.table ? (size_t)a.m.pg.seq_pages * sizeof(int32_t) : 0);
+  const size_t pages = a.m.pg.table ? (size_t)a.m.pg.seq_pages * sizeof(int32_t) : 0;
+  return (chunks + pages + 15) / 16 * 16;
+}
+
+size_t tiles_lds(const StageArgs &a) {
+  if (a.m.s.dtype == HIPSA_F32) return 0;
+  const bool d64 = a.m.s.d == 64;
+  if (a.m.s.dtype == HIPSA_BF16)
+    return d64 ? stage_bytes<uint16_t, uint16_t, 64>() : stage_bytes<uint16_t, uint16_t, 128>();
+  return d64 ? stage_bytes<uint16_t, uint8_t, 64>() : stage_bytes<uint16_t, uint8_t, 128>();
+}
+
+size_t mask_stages_lds(const StageArgs &a) {
+  return lists_lds(a) + (a.stage_off >= 0 ? tiles_lds(a) : 0);
 }
 
 // The first round of stage 1 holds 2 * n0 candidates (n0 stage-0 chunks);
@@ -401,7 +420,10 @@ size_t mask_stages_plan(StageArgs *a) {
   return keys + (size_t)s.problems * sizeof(uint32_t);
 }
 
-hipError_t launch_mask_stages(const StageArgs &a, hipStream_t st) {
+hipError_t launch_mask_stages(const StageArgs &a0, hipStream_t st) {
+  StageArgs a = a0;
+  const size_t tiles = tiles_lds(a);
+  a.stage_off = tiles > 0 && lists_lds(a) + tiles <= kLdsBudget ? (int32_t)lists_lds(a) : -1;
   const size_t lds = mask_stages_lds(a);
   if (a.m.pg.table) launch_layout<true>(a, lds, st);
   else launch_layout<false>(a, lds, st);

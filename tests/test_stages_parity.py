@@ -125,6 +125,11 @@ CASES = {
     "split_first_round_paged_e5m2": (dict(name="decode_32k", B=2, Hq=8, Hkv=2, T=100000,
                                           block_k=16, k=1024, dtype="bf16_e5m2"),
                                      [(128, None), (32, 4096), (16, 1024)], dict(page_size=256)),
+    # 16384 pages of 16 tokens and 2048 stage-0 chunks: the page numbers and
+    # chunk lists leave no LDS for the row-gather tiles (operand-layout loads)
+    "paged_lists_fill_lds": (dict(name="decode_32k", Hq=4, Hkv=1, d=64, T=262144, block_k=16,
+                                  k=1024),
+                             [(128, None), (32, 4096), (16, 1024)], dict(page_size=16)),
     # 256 rows (one workgroup per CU already): a 2048-candidate first round
     # stays in one workgroup per row
     "wide_first_round_in_one_workgroup": (dict(name="decode_32k", B=4, Tq=8, block_k=8, k=512),
