@@ -25,10 +25,15 @@ namespace hipsa {
 // the plain kernel is faster.
 constexpr int kPipeMaxKb = 32;
 
-template <typename KE, int D, int GMAX, int TPW, typename RowOf>
+// Scores slots [0, nslot): the current candidates (ca, ce), or with
+// `children` child (cs & 1) of current candidate cs / 2, or with INIT the
+// first round's slots computed in registers from (first, M, K_b) (no LDS, so
+// no barrier has to precede it).  Wave wi of nw takes tiles wi, wi + nw, ...
+template <typename KE, int D, int GMAX, int TPW, bool INIT = false, typename RowOf>
 __device__ inline void score_children(const KE *Kbase, RowOf row_of, const uint4 *qa, int32_t Tp, int bk_shift,
                                       int G, const int32_t *ca, const int32_t *ce, int nslot,
-                                      bool children, int wi, int nw, uint64_t *dst) {
+                                      bool children, int wi, int nw, uint64_t *dst, int32_t first = 0,
+                                      int32_t M = 0, int Kb = 1) {
   constexpr int KS = D / 32;
   const int lane = threadIdx.x & 63;
   const int ntile = (nslot + 15) / 16;
@@ -42,7 +47,9 @@ __device__ inline void score_children(const KE *Kbase, RowOf row_of, const uint4
       // slot cs: a current candidate, or child (cs & 1) of current candidate cs >> 1
       const int c = children ? (cs >> 1) : cs;
       const int cc = c < (children ? nslot / 2 : nslot) ? c : 0;
-      const int32_t plo = ca[cc], phi = ce[cc];
+      int32_t plo, phi;
+      if constexpr (INIT) initial_slot(first, M, Kb, cc, &plo, &phi);
+      else plo = ca[cc], phi = ce[cc];
       int32_t lo = plo, hi = phi;
       bool ok = cs < nslot && plo >= 0;
       if (children) {
@@ -125,10 +132,12 @@ __device__ __forceinline__ void search_pipe(const void *q, const void *K, const 
   for (int c = tid; c < n; c += 256) srcs[0][c] = c;
   if (tid < kSpan) key[n + tid] = 0;
   if (tid == 0) flag[0] = 1;  // M > K_b: the first round always runs
-  __syncthreads();
-  // keys of the first candidates (all waves), kept where round 0 looks them up
-  score_children<KE, D, GMAX, TPW>(Kbase, row_of, qa, Tp, s.bk_shift, s.G, cand_a[0], cand_e[0], n, false,
-                               wave, 4, spec[1]);
+  if constexpr (PAGED) __syncthreads();  // the page numbers
+  // keys of the first candidates (all waves), kept where round 0 looks them
+  // up; the slots come from registers, so these gathers issue beside the
+  // query loads instead of after a barrier
+  score_children<KE, D, GMAX, TPW, true>(Kbase, row_of, qa, Tp, s.bk_shift, s.G, nullptr, nullptr, n, false,
+                                     wave, 4, spec[1], first, M, Kb);
   __syncthreads();
 
   int cur = 0;

@@ -73,20 +73,23 @@ __device__ inline void write_ascending(const int32_t *fin, int Kb, int32_t *out)
   }
 }
 
-// Candidate slots 2c, 2c+1 from the halves of initial chunk c of the uniform
-// partition of the M searched blocks from block `first`:
-// first + [floor(c*M/K_b), floor((c+1)*M/K_b)) (exact in double).
+// Candidate slot cs (of 2 K_b) of the first round: half cs % 2 of initial
+// chunk cs / 2 of the uniform partition of the M searched blocks from block
+// `first`, first + [floor(c*M/K_b), floor((c+1)*M/K_b)) (exact in double); a
+// one-block chunk fills slot 2c and leaves slot 2c+1 empty (start -1).
+__device__ inline void initial_slot(int32_t first, int32_t M, int Kb, int cs, int32_t *a, int32_t *e) {
+  const int c = cs >> 1;
+  const int32_t lo = first + (int32_t)((double)c * M / Kb);
+  const int32_t hi = first + (int32_t)((double)(c + 1) * M / Kb);
+  const bool split = hi - lo >= 2;
+  const int32_t m = lo + (hi - lo) / 2;
+  *a = (cs & 1) ? (split ? m : -1) : lo;
+  *e = (cs & 1) ? (split ? hi : -1) : (split ? m : hi);
+}
+
+// All 2 K_b first-round slots into (ca, ce).
 __device__ inline void initial_candidates(int32_t first, int32_t M, int Kb, int32_t *ca, int32_t *ce) {
-  for (int c = threadIdx.x; c < Kb; c += 256) {
-    const int32_t lo = first + (int32_t)((double)c * M / Kb);
-    const int32_t hi = first + (int32_t)((double)(c + 1) * M / Kb);
-    const bool split = hi - lo >= 2;
-    const int32_t m = lo + (hi - lo) / 2;
-    ca[2 * c] = lo;
-    ce[2 * c] = split ? m : hi;
-    ca[2 * c + 1] = split ? m : -1;
-    ce[2 * c + 1] = split ? hi : -1;
-  }
+  for (int cs = threadIdx.x; cs < 2 * Kb; cs += 256) initial_slot(first, M, Kb, cs, &ca[cs], &ce[cs]);
 }
 
 }  // namespace hipsa
