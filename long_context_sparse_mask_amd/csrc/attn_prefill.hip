@@ -60,11 +60,11 @@ __device__ inline uint2 lds_read_tr16(const uint16_t *p) {
 
 // Online softmax of one query tile over one key tile.  sacc[kt][r] holds the
 // score of key kt*32 + 8*(r/4) + 4*half + r%4 for this lane's query.  The
-// scores are copied to plain registers and masked there with selects: a
-// conditional write into the matrix-core accumulator vectors themselves
-// (under divergent control flow, with the accumulators spread over AGPRs)
-// lost updates at this kernel's register pressure.  Produces P^T in bf16 as
-// MFMA B operands and updates the running max m, sum l and output o.
+// scores are copied to plain registers and masked there with selects (a
+// variant that masked the accumulator vectors in place, under divergent
+// control flow, failed the parity tests; the cause was not isolated).
+// Produces P^T in bf16 as MFMA B operands and updates the running max m,
+// sum l and output o.
 template <int DT>
 __device__ inline void online_softmax(const f32x16_t (&sacc)[2], bool masked, const int32_t *tokrow,
                                       bool qvalid, int32_t qpos, bool causal, int half, float sl2,
