@@ -477,12 +477,66 @@ def run_stages(w, stages, steps, warmup, torch, hs, si, n_layers=N_LAYER_COPIES,
     return res
 
 
+def stage_candidates(w, stages) -> list:
+    """Candidates scored per round by the multi-stage search on a row that
+    sees all ceil(T / block_k) blocks, when every chunk of a round has the
+    same width (the workloads' sizes divide evenly): stage 0 cuts chunks of
+    its size; each later stage halves the chunks wider than its size, at
+    least once per stage and until they fit, keeping k / chunk_size."""
+    Np = -(-w.T // w.block_k)
+    c0 = stages[0][0] // w.block_k
+    nk, width = -(-Np // c0), c0
+    counts = []
+    for chunk, k in stages[1:]:
+        tb, keep = chunk // w.block_k, k // chunk
+        fresh = True
+        while fresh or width > tb:
+            fresh = False
+            halve = width > tb
+            n = nk * (2 if halve else 1)
+            counts.append(n)
+            width = width - width // 2 if halve else width  # the larger half
+            nk = min(keep, n)
+    return counts
+
+
+def stage_mask_bytes(w, stages) -> int:
+    """Algorithmic HBM bytes of one multi-stage search over every problem:
+    the centre rows of every round's candidates, the query rows, the lists."""
+    qsz, kvsz = ELEM_BYTES[w.dtype]
+    P = w.B * w.Hkv * w.Tq
+    return P * (sum(stage_candidates(w, stages)) * w.d * kvsz + w.G * w.d * qsz + 4 * (w.kb + 1))
+
+
 def stages_line(w, stages, r) -> dict:
     nb = decode_bytes(w)
-    return {"workload": w.name, "stages": [[c, k] for c, k in stages],
-            "mask_us": round(r["ms_mask"] * 1e3, 3), "step_us": round(r["ms_step"] * 1e3, 3),
-            "step_frac": round(nb["attn"] / (r["ms_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "blocks_shared_with_one_stage": r["shared_with_one_stage"]}
+    mb = stage_mask_bytes(w, stages)
+    d = {"workload": w.name, "stages": [[c, k] for c, k in stages],
+         "candidates_per_round": stage_candidates(w, stages),
+         "mask_us": round(r["ms_mask"] * 1e3, 3), "step_us": round(r["ms_step"] * 1e3, 3),
+         "mask_bytes": mb, "mask_frac": round(mb / (r["ms_mask"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+         "step_frac": round((mb + nb["attn"]) / (r["ms_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+         "blocks_shared_with_one_stage": r["shared_with_one_stage"]}
+    if "cpu_baseline" in r:
+        d["cpu_baseline"] = r["cpu_baseline"]
+    return d
+
+
+def cpu_baseline_stages(x, w, stages, budget_s: float) -> dict:
+    """The CPU oracle's multi-stage search plus the attention over its lists on
+    one whole decode step of the workload (first query set and layer copy),
+    with every host thread."""
+    import oracle
+    nt = oracle.nthreads()
+    kw = dict(T=w.T, block_k=w.block_k, causal=w.causal)
+
+    def step():
+        idx, nnz, _ = oracle.mask_stages_all(x["q"], x["K"], stages, threads=nt, **kw)
+        oracle.attn_all(x["q"], x["K"], x["V"], idx, nnz, k=w.k, block_q=1, threads=nt, **kw)
+    t = _time_oracle(step, budget_s, 2, 500)
+    return {"value": round(statistics.median(t) * 1e6, 1), "unit": "us/step", "cores": nt,
+            "kind": "oracle", "sample": f"whole {w.name} step with the stage list, median of "
+                                        f"{len(t)} runs ({sum(t):.1f} s), fp64 C + OpenMP"}
 
 
 def needle_recall(x, indices):
@@ -649,6 +703,10 @@ def main():
         st = STAGES[w.name]
         rs = run_stages(w, st, args.steps, args.warmup, torch, hs, si, args.layer_copies,
                         args.query_sets)
+        if not args.no_cpu_baseline:
+            xs = si.make_inputs(w)
+            rs["cpu_baseline"] = cpu_baseline_stages(xs, w, st, args.cpu_budget / 2)
+            del xs
         line.setdefault("multi_stage", {})[w.name] = stages_line(w, st, rs)
     if headline and not args.no_fp8:
         # the same step with an fp8 (E5M2) KV cache: half the K/V bytes

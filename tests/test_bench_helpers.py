@@ -139,3 +139,31 @@ def test_stage_lists_end_at_the_workload_k():
         w = si.workload(name)
         assert stages[0][1] is None and stages[-1] == (w.block_k, w.k)
         assert all(a[0] > b[0] for a, b in zip(stages, stages[1:]))
+
+
+def test_stage_candidates():
+    """Rounds of the bench's stage lists, traced by hand: 128k x 4 has 2048
+    blocks, 256 stage-0 chunks of 8; stage 1 (2-block chunks, keep 64) halves
+    them twice (512, then 128 candidates), stage 2 (single blocks, keep 32)
+    once (128).  1M: 16384 blocks, 2048 chunks: 4096, 256, 256."""
+    assert bench.stage_candidates(si.workload("decode_128k_b4"), bench.STAGES["decode_128k_b4"]) == [512, 128, 128]
+    assert bench.stage_candidates(si.workload("decode_1m_needles"), bench.STAGES["decode_1m_needles"]) == [4096, 256, 256]
+    # 40 blocks in 8 stage-0 chunks of 5: stage 1 (4-block chunks, keep 8)
+    # halves once (16 candidates, widths 3); stage 2 (3-block chunks, keep 6)
+    # finds them fitting and still ranks them (8); stage 3 (single blocks,
+    # keep 4) halves twice (12, then 8)
+    w = si.workload("tiny_decode", T=320, block_k=8, k=32)
+    assert bench.stage_candidates(w, [(40, None), (32, 256), (24, 144), (8, 32)]) == [16, 8, 12, 8]
+    nb = bench.stage_mask_bytes(si.workload("decode_128k_b4"), bench.STAGES["decode_128k_b4"])
+    assert nb == 32 * (768 * 256 + 4 * 256 + 4 * 33)
+
+
+def test_stage_candidates_match_the_oracle_trace():
+    """The bench's round counts equal the candidates the oracle's stage search
+    scores per round (trace of one problem)."""
+    import oracle
+    w = si.workload("decode_32k", Hq=4, Hkv=1)
+    x = si.make_inputs(w)
+    st = bench.STAGES["decode_128k_b4"]
+    tr = oracle.mask_stages_one(x["q"], x["K"], 0, 0, 0, st, T=w.T, block_k=w.block_k)
+    assert [len(r["start"]) for r in tr["rounds"]] == bench.stage_candidates(w, st) == [128, 128, 128]
