@@ -736,7 +736,10 @@ def main():
                                   keys_per_row=args.sink + args.window + w.k)
     if headline and not args.no_prefill:
         wp = si.workload("prefill_32k_chunk4k")
-        psteps, pwarm = max(4, args.steps // 20), max(1, args.warmup // 10)
+        # 40 chunks per timed graph at the default 200 steps: replays of short graphs
+        # measured slower per call (10 attention calls: 190-200 us each; 30 or more,
+        # eager calls and kernel traces: 155-163 us)
+        psteps, pwarm = max(8, args.steps // 5), max(2, args.warmup // 5)
         rp = run_workload(wp, psteps, pwarm, torch, hs, si, 4)
         fl = prefill_flops(wp)
         line["prefill"] = {"workload": wp.name,
