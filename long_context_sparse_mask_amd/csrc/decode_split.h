@@ -288,24 +288,29 @@ __device__ __forceinline__ void attend_split(const AttnArgs &a, uint32_t prob, u
 }
 
 // Merge of the S split partials (max m, sum l, unnormalised output o[D]) of
-// one (problem, query head) for output dimension x, partial s at
-// ph + s * sstride: every load of a batch of CH partials is issued before any
-// is used; per batch the maximum is a tree and the weights are independent
-// exponentials, so the dependent chain is one step per batch rather than one
-// per partial.  load(p) reads one float of the workspace.
-template <int CH, typename Load>
-__device__ __forceinline__ float merge_partials(const float *ph, int S, int64_t sstride, int x,
-                                                Load load) {
-  float M = -INFINITY, L = 0.f, acc = 0.f;
+// one (problem, query head) for the NX output dimensions x[], partial s at
+// ph + s * sstride: every load of a batch of CH partials (m and l once, o for
+// each x) is issued before any is used; per batch the maximum is a tree and
+// the weights are independent exponentials, so the dependent chain is one
+// step per batch rather than one per partial.  Each output takes the same
+// operations in the same order whatever NX.  load(p) reads one float of the
+// workspace.
+template <int CH, int NX, typename Load>
+__device__ __forceinline__ void merge_partials_nx(const float *ph, int S, int64_t sstride, const int (&x)[NX],
+                                                  Load load, float (&res)[NX]) {
+  float M = -INFINITY, L = 0.f, acc[NX];
+#pragma unroll
+  for (int j = 0; j < NX; j++) acc[j] = 0.f;
   int s0 = 0;
   do {
-    float mm[CH], ll[CH], oo[CH];
+    float mm[CH], ll[CH], oo[CH][NX];
 #pragma unroll
     for (int u = 0; u < CH; u++) {
       const int sp = min(s0 + u, S - 1);
       mm[u] = s0 + u < S ? load(ph + sp * sstride) : -INFINITY;
       ll[u] = load(ph + sp * sstride + 1);
-      oo[u] = load(ph + sp * sstride + 2 + x);
+#pragma unroll
+      for (int j = 0; j < NX; j++) oo[u][j] = load(ph + sp * sstride + 2 + x[j]);
     }
     // batch max as a tree, then independent weights
     float bm[CH];
@@ -317,19 +322,32 @@ __device__ __forceinline__ float merge_partials(const float *ph, int S, int64_t 
       for (int u = 0; u < w; u++) bm[u] = fmaxf(bm[u], bm[u + w]);
     const float Mn = fmaxf(M, bm[0]);
     const float c0 = M == -INFINITY ? 0.f : __expf(M - Mn);
-    float Lb = 0.f, Ab = 0.f;
+    float Lb = 0.f, Ab[NX];
+#pragma unroll
+    for (int j = 0; j < NX; j++) Ab[j] = 0.f;
 #pragma unroll
     for (int u = 0; u < CH; u++) {
       const float c = mm[u] == -INFINITY ? 0.f : __expf(mm[u] - Mn);
       Lb = fmaf(c, ll[u], Lb);
-      Ab = fmaf(c, oo[u], Ab);
+#pragma unroll
+      for (int j = 0; j < NX; j++) Ab[j] = fmaf(c, oo[u][j], Ab[j]);
     }
     L = fmaf(L, c0, Lb);
-    acc = fmaf(acc, c0, Ab);
+#pragma unroll
+    for (int j = 0; j < NX; j++) acc[j] = fmaf(acc[j], c0, Ab[j]);
     M = Mn;
     s0 += CH;
   } while (s0 < S);
-  return L > 0.f ? acc / L : 0.f;
+#pragma unroll
+  for (int j = 0; j < NX; j++) res[j] = L > 0.f ? acc[j] / L : 0.f;
+}
+
+template <int CH, typename Load>
+__device__ __forceinline__ float merge_partials(const float *ph, int S, int64_t sstride, int x, Load load) {
+  const int xs[1] = {x};
+  float r[1];
+  merge_partials_nx<CH, 1>(ph, S, sstride, xs, load, r);
+  return r[0];
 }
 
 }  // namespace hipsa

@@ -87,14 +87,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   auto load = [](const float *p) {
     return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
-  uint16_t *out = reinterpret_cast<uint16_t *>(a.at.out);
-  for (int oi = tid; oi < (int)G * D; oi += 256) {
-    const int h = oi / D, x = oi % D;
-    const float *ph = a.at.ws + ((int64_t)prob * S * G + h) * (D + 2);
-    const float v = S <= 16 ? merge_partials<16>(ph, (int)S, sstride, x, load)
-                            : merge_partials<32>(ph, (int)S, sstride, x, load);
-    store_elem(out + ((int64_t)(b * s.Hq + g * G + h) * Tq + i) * D + x, v);
-  }
+  // thread tid merges NX dimensions of head tid / TPH, so the m and l of a
+  // head's partials are loaded once beside its o values: one memory round trip
+  constexpr int NX = D * GMAX / 256 > 1 ? D * GMAX / 256 : 1;
+  constexpr int TPH = D / NX;  // threads per head
+  const uint32_t h = tid / TPH;
+  if (h >= G) return;
+  int xs[NX];
+#pragma unroll
+  for (int j = 0; j < NX; j++) xs[j] = tid % TPH + j * TPH;
+  const float *ph = a.at.ws + ((int64_t)prob * S * G + h) * (D + 2);
+  float v[NX];
+  if (S <= 16) merge_partials_nx<16, NX>(ph, (int)S, sstride, xs, load, v);
+  else merge_partials_nx<32, NX>(ph, (int)S, sstride, xs, load, v);
+  uint16_t *out = reinterpret_cast<uint16_t *>(a.at.out) + ((int64_t)(b * s.Hq + g * G + h) * Tq + i) * D;
+#pragma unroll
+  for (int j = 0; j < NX; j++) store_elem(out + xs[j], v[j]);
 }
 
 template <int D, int GMAX, int TPW>
