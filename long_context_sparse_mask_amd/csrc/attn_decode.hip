@@ -232,12 +232,16 @@ __global__ __launch_bounds__(128) void attn_decode_combine(const float *ws, void
 // sequence is used whenever it can (one split: the split workgroup writes the
 // output and no merge follows).
 //  * bf16 query, groups of up to 8 query heads: 256, 128 or 64, the largest
-//    that still gives at least kMinSplitGrid workgroups (one per CU).  The
-//    one-launch decode step runs the problem's search in every split
-//    workgroup, so more than one workgroup per CU slows its search; the
-//    attention reads measured even between 128- and 256-token splits at
-//    128k x 4.  256-token splits read V rows 16 bytes per lane, which keeps a
-//    wave under its 63 loads in flight.
+//    that still gives at least kMinSplitGrid workgroups (one per CU), or half
+//    that many for shapes the one-launch decode step serves (bf16 keys,
+//    K_b <= kPipeMaxKb).  That step runs the problem's search in every split
+//    workgroup, so more than one workgroup per CU slows its search, and fewer
+//    splits per problem mean fewer searches and a shorter merge: at 32k
+//    (8 problems) 16 splits of 128 tokens measured 16.8 us per step against
+//    18.4 us for the two calls over 32 splits of 64, and the attention call
+//    alone 8.4 against 8.7 us.  The attention reads measured even between
+//    128- and 256-token splits at 128k x 4.  256-token splits read V rows 16
+//    bytes per lane, which keeps a wave under its 63 loads in flight.
 //  * fp32: 128 or 64, the larger when it gives >= 512 workgroups; 64 at
 //    d = 128 (a lane's K and V rows must fit in registers).
 //  * groups of more than 8 query heads: 64 (the per-head probabilities and
@@ -253,8 +257,9 @@ int tokens_per_split(const Shape &s) {
   const int64_t total = entry_tokens(s);
   if (s.G > 8) return 64;
   if constexpr (std::is_same<E, uint16_t>::value) {
+    const int64_t min_grid = s.dtype == HIPSA_BF16 && s.Kb <= kPipeMaxKb ? kMinSplitGrid / 2 : kMinSplitGrid;
     for (int tok = 256; tok >= 128; tok /= 2)
-      if (total <= tok || s.problems * ((total + tok - 1) / tok) >= kMinSplitGrid) return tok;
+      if (total <= tok || s.problems * ((total + tok - 1) / tok) >= min_grid) return tok;
     return 64;
   }
   if (max_tokens<E, D>() >= 128 && (total <= 128 || s.problems * ((total + 127) / 128) >= 512))

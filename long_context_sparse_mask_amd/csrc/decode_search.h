@@ -22,8 +22,7 @@ namespace hipsa {
 // candidate's key).  The speculation doubles the rows gathered per round,
 // which pays while a round's gather costs mostly latency (up to 128 rows);
 // at K_b = 64 (256 rows per round, and a 128-candidate ranking on one wave)
-// the plain kernel is faster.
-constexpr int kPipeMaxKb = 32;
+// the plain kernel is faster.  The limit, kPipeMaxKb, is in hipsa_internal.h.
 
 // Scores slots [0, nslot): the current candidates (ca, ce), or with
 // `children` child (cs & 1) of current candidate cs / 2, or with INIT the

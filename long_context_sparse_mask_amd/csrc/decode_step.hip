@@ -146,10 +146,10 @@ void launch_d(const StepArgs &a, hipStream_t st) {
 // The one-launch form runs a problem's search once per split workgroup.  It
 // pays while the grid has at most one workgroup per CU and a problem few
 // splits: measured against the two calls, it saves 1.1 us per 128k x 4 step
-// (32 problems x 8 splits) but costs 2.0 us at 32k (8 problems x 32 splits:
-// 32 searches of the same rows and a 32-way merge in one workgroup) and
-// 19.7 us with a 4096-token window (32 problems x 25 splits: about three
-// searches per CU).
+// (32 problems x 8 splits) and 1.6 us at 32k (8 problems x 16 splits), but
+// cost 2.0 us at 32k over 32 splits (32 searches of the same rows and a
+// 32-way merge in one workgroup) and 19.7 us with a 4096-token window
+// (32 problems x 25 splits: about three searches per CU).
 constexpr int64_t kMaxStepGrid = 256;
 constexpr int32_t kMaxStepSplits = 16;
 
