@@ -233,8 +233,8 @@ __global__ __launch_bounds__(128) void attn_decode_combine(const float *ws, void
 // output and no merge follows).
 //  * bf16 query, groups of up to 8 query heads: 256, 128 or 64, the largest
 //    that still gives at least kMinSplitGrid workgroups (one per CU), or half
-//    that many for shapes the one-launch decode step serves (bf16 keys,
-//    K_b <= kPipeMaxKb).  That step runs the problem's search in every split
+//    that many when K_b <= kStepMaxKb (the shapes whose contiguous caches
+//    the one-launch decode step serves).  That step runs the problem's search in every split
 //    workgroup, so more than one workgroup per CU slows its search, and fewer
 //    splits per problem mean fewer searches and a shorter merge: at 32k
 //    (8 problems) 16 splits of 128 tokens measured 16.8 us per step against
@@ -257,7 +257,7 @@ int tokens_per_split(const Shape &s) {
   const int64_t total = entry_tokens(s);
   if (s.G > 8) return 64;
   if constexpr (std::is_same<E, uint16_t>::value) {
-    const int64_t min_grid = s.dtype == HIPSA_BF16 && s.Kb <= kPipeMaxKb ? kMinSplitGrid / 2 : kMinSplitGrid;
+    const int64_t min_grid = s.Kb <= kStepMaxKb ? kMinSplitGrid / 2 : kMinSplitGrid;
     for (int tok = 256; tok >= 128; tok /= 2)
       if (total <= tok || s.problems * ((total + tok - 1) / tok) >= min_grid) return tok;
     return 64;

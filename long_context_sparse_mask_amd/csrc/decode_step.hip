@@ -8,7 +8,7 @@
 // (summary page, Limitations: the mask refresh interval).  Run as two
 // launches, the attention kernel waits for the mask kernel to end and then
 // reads the lists back from memory.  Here every split workgroup of a problem
-// runs the problem's search itself (search_pipe), holds the kept blocks in
+// runs the problem's search itself (search_row), holds the kept blocks in
 // LDS and attends its share of them (attend_split); no workgroup waits for
 // another.  The search is latency-bound (serially dependent rounds of row
 // gathers) and cheap, so running it once per split costs little time: the
@@ -21,6 +21,8 @@
 // hip_mask_estimate followed by hip_sparse_attn: the same search, the same
 // split assignment of the same ascending list, the same merge arithmetic
 // (merge_partials).
+#include <type_traits>
+
 #include "decode_search.h"
 #include "decode_split.h"
 #include "hipsa_internal.h"
@@ -29,8 +31,9 @@
 namespace hipsa {
 namespace {
 
-// bf16 query and keys, contiguous layout, K_b <= kPipeMaxKb.
-template <int D, int GMAX, int TPW, int TOK, bool WIDE>
+// bf16 query, bf16 or fp8 (E5M2) K/V, contiguous layout, K_b <= kStepMaxKb;
+// UNROLL as the mask kernel takes it (search_tiles_per_wave).
+template <typename KE, int D, int GMAX, int UNROLL, int TOK, bool WIDE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void decode_step_kernel(StepArgs a) {
   const Shape &s = a.at.s;
   const int tid = threadIdx.x;
@@ -45,13 +48,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   const Dense dn(s, Np);  // the search covers the M blocks from `first` between the dense parts
   const int32_t first = dn.Sb, M = Np - dn.Sb - dn.Wb;
 
-  __shared__ int32_t list[kPipeMaxKb];
+  __shared__ int32_t list[kStepMaxKb];
   __shared__ int32_t cnt;
   if (M <= Kb) {  // the row sees few enough blocks to keep them all
     for (int j = tid; j < Kb; j += 256) list[j] = j < M ? first + j : -1;
     if (tid == 0) cnt = M;
   } else {
-    search_pipe<uint16_t, D, GMAX, TPW, false>(a.at.q, a.at.K, s, a.at.pg, b, g, i, Tp, first, M, list);
+    search_row<uint16_t, KE, D, GMAX, UNROLL, false>(a.at.q, a.at.K, s, a.at.pg, b, g, i, Tp, first, M, list);
     if (tid == 0) cnt = Kb;
   }
   __syncthreads();
@@ -60,7 +63,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     for (int j = tid; j < Kb; j += 256) out[j] = list[j];
     if (tid == 0) a.nnz[prob] = cnt;
   }
-  attend_split<uint16_t, D, GMAX, TOK, false, WIDE, true>(a.at, prob, split, list, &cnt);
+  attend_split<KE, D, GMAX, TOK, false, WIDE, true>(a.at, prob, split, list, &cnt);
   if (S == 1) return;  // the only split wrote the output
 
   // Arrival: the last split workgroup of the problem to finish merges the S
@@ -105,40 +108,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   for (int j = 0; j < NX; j++) store_elem(out + xs[j], v[j]);
 }
 
-template <int D, int GMAX, int TPW>
+template <typename KE, int D, int GMAX, int UNROLL>
 void launch_tok(const StepArgs &a, hipStream_t st) {
   const dim3 grid((unsigned)(a.at.s.problems * a.at.splits)), block(256);
   const bool wide = (int64_t)a.at.s.problems * a.at.splits >= kWideGrid;
   const int tok = attn_decode_tokens(a.at.s);
   constexpr int G8 = GMAX <= 8 ? GMAX : 8;
   if (GMAX <= 8 && tok == 256) {
-    hipLaunchKernelGGL((decode_step_kernel<D, G8, TPW, 256, true>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((decode_step_kernel<KE, D, G8, UNROLL, 256, true>), grid, block, 0, st, a);
   } else if (GMAX <= 8 && tok == 128) {
-    if (wide) hipLaunchKernelGGL((decode_step_kernel<D, G8, TPW, 128, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((decode_step_kernel<D, G8, TPW, 128, false>), grid, block, 0, st, a);
+    if (wide) hipLaunchKernelGGL((decode_step_kernel<KE, D, G8, UNROLL, 128, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((decode_step_kernel<KE, D, G8, UNROLL, 128, false>), grid, block, 0, st, a);
   } else {
-    if (wide) hipLaunchKernelGGL((decode_step_kernel<D, GMAX, TPW, 64, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((decode_step_kernel<D, GMAX, TPW, 64, false>), grid, block, 0, st, a);
+    if (wide) hipLaunchKernelGGL((decode_step_kernel<KE, D, GMAX, UNROLL, 64, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((decode_step_kernel<KE, D, GMAX, UNROLL, 64, false>), grid, block, 0, st, a);
   }
 }
 
-template <int D, int GMAX>
+template <typename KE, int D, int GMAX>
 void launch_g(const StepArgs &a, hipStream_t st) {
-  const int tiles = (4 * a.at.s.Kb + 15) / 16;  // child tiles per round, over 3 waves
-  const int per = (tiles + 2) / 3;
-  if (per <= 1) launch_tok<D, GMAX, 1>(a, st);
-  else if (per <= 2) launch_tok<D, GMAX, 2>(a, st);
-  else launch_tok<D, GMAX, 4>(a, st);
+  static_assert(((2 * kStepMaxKb + 15) / 16 + 3) / 4 <= 2, "UNROLL 1 or 2 covers K_b <= kStepMaxKb");
+  if (search_tiles_per_wave(a.at.s.Kb) <= 1) launch_tok<KE, D, GMAX, 1>(a, st);
+  else launch_tok<KE, D, GMAX, 2>(a, st);
 }
 
-template <int D>
+template <typename KE, int D>
 void launch_d(const StepArgs &a, hipStream_t st) {
   const int G = a.at.s.G;
-  if (G <= 1) launch_g<D, 1>(a, st);
-  else if (G <= 2) launch_g<D, 2>(a, st);
-  else if (G <= 4) launch_g<D, 4>(a, st);
-  else if (G <= 8) launch_g<D, 8>(a, st);
-  else launch_g<D, 16>(a, st);
+  if (G <= 1) launch_g<KE, D, 1>(a, st);
+  else if (G <= 2) launch_g<KE, D, 2>(a, st);
+  else if (G <= 4) launch_g<KE, D, 4>(a, st);
+  else if (G <= 8) launch_g<KE, D, 8>(a, st);
+  else launch_g<KE, D, 16>(a, st);
 }
 
 }  // namespace
@@ -154,16 +155,16 @@ constexpr int64_t kMaxStepGrid = 256;
 constexpr int32_t kMaxStepSplits = 16;
 
 bool one_launch(const Shape &s, int32_t splits) {
-  return s.dtype == HIPSA_BF16 && s.Kb <= kPipeMaxKb && splits <= kMaxStepSplits &&
+  return s.dtype != HIPSA_F32 && s.Kb <= kStepMaxKb && splits <= kMaxStepSplits &&
          s.problems * splits <= kMaxStepGrid;
 }
 
 hipError_t launch_decode_step(const StepArgs &a, hipStream_t st) {
   const Shape &s = a.at.s;
-  // The one-launch form needs the pipelined search (bf16 keys in the
-  // contiguous layout, K_b <= kPipeMaxKb); otherwise, or when its redundant
-  // searches would cost more than the launch they save, the two calls'
-  // kernels run in turn on the same lists.
+  // The one-launch form serves a bf16 query with bf16 or fp8 keys in the
+  // contiguous layout and K_b <= kStepMaxKb; otherwise, or when its
+  // redundant searches would cost more than the launch they save, the two
+  // calls' kernels run in turn on the same lists.
   if (a.at.pg.table || !one_launch(s, a.at.splits)) {
     MaskArgs m{a.at.q, a.at.K, a.indices, a.nnz, s, a.at.pg};
     hipError_t e = launch_mask_decode(m, st);
@@ -173,8 +174,13 @@ hipError_t launch_decode_step(const StepArgs &a, hipStream_t st) {
     at.nnz = a.nnz;
     return launch_attn_decode(at, st);
   }
-  if (s.d == 64) launch_d<64>(a, st);
-  else launch_d<128>(a, st);
+  if (s.dtype == HIPSA_BF16_E5M2) {
+    if (s.d == 64) launch_d<uint8_t, 64>(a, st);
+    else launch_d<uint8_t, 128>(a, st);
+  } else {
+    if (s.d == 64) launch_d<uint16_t, 64>(a, st);
+    else launch_d<uint16_t, 128>(a, st);
+  }
   return hipGetLastError();  // the last split workgroup of each problem merged the partials
 }
 

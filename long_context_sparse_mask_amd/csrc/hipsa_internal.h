@@ -36,9 +36,9 @@ struct Pages {
   int32_t last_page;     // num_pages - 1: table entries are clamped to [0, last_page]
   int32_t seq_pages;     // ceil(T / page_size): the table entries a sequence uses
 };
-constexpr int kMaxSeqPagesOnChip = 16384;
-// Largest K_b of the pipelined bf16 search (decode mask and one-launch step).
-constexpr int kPipeMaxKb = 32;  // mask kernels stage a sequence's pages in LDS
+constexpr int kMaxSeqPagesOnChip = 16384;  // mask kernels stage a sequence's pages in LDS
+// Largest K_b of the one-launch decode step (its kept blocks stay in LDS).
+constexpr int kStepMaxKb = 64;
 
 struct MaskArgs {
   const void *q, *K;
