@@ -233,8 +233,8 @@ __global__ __launch_bounds__(128) void attn_decode_combine(const float *ws, void
 // output and no merge follows).
 //  * bf16 query, groups of up to 8 query heads: 256, 128 or 64, the largest
 //    that still gives at least kMinSplitGrid workgroups (one per CU), or half
-//    that many when K_b <= kStepMaxKb (the shapes whose contiguous caches
-//    the one-launch decode step serves).  That step runs the problem's search in every split
+//    that many when K_b <= kStepMaxKb (the shapes the one-launch decode
+//    step serves).  That step runs the problem's search in every split
 //    workgroup, so more than one workgroup per CU slows its search, and fewer
 //    splits per problem mean fewer searches and a shorter merge: at 32k
 //    (8 problems) 16 splits of 128 tokens measured 16.8 us per step against

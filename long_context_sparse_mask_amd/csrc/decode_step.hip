@@ -21,6 +21,7 @@
 // hip_mask_estimate followed by hip_sparse_attn: the same search, the same
 // split assignment of the same ascending list, the same merge arithmetic
 // (merge_partials).
+#include <cstdint>
 #include <type_traits>
 
 #include "decode_search.h"
@@ -31,9 +32,10 @@
 namespace hipsa {
 namespace {
 
-// bf16 query, bf16 or fp8 (E5M2) K/V, contiguous layout, K_b <= kStepMaxKb;
-// UNROLL as the mask kernel takes it (search_tiles_per_wave).
-template <typename KE, int D, int GMAX, int UNROLL, int TOK, bool WIDE>
+// bf16 query, bf16 or fp8 (E5M2) K/V, K_b <= kStepMaxKb; UNROLL as the mask
+// kernel takes it (search_tiles_per_wave).  PAGED: the search stages the
+// sequence's page numbers in dynamic LDS, as the mask kernel does.
+template <typename KE, int D, int GMAX, int UNROLL, int TOK, bool WIDE, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void decode_step_kernel(StepArgs a) {
   const Shape &s = a.at.s;
   const int tid = threadIdx.x;
@@ -54,7 +56,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     for (int j = tid; j < Kb; j += 256) list[j] = j < M ? first + j : -1;
     if (tid == 0) cnt = M;
   } else {
-    search_row<uint16_t, KE, D, GMAX, UNROLL, false>(a.at.q, a.at.K, s, a.at.pg, b, g, i, Tp, first, M, list);
+    search_row<uint16_t, KE, D, GMAX, UNROLL, PAGED>(a.at.q, a.at.K, s, a.at.pg, b, g, i, Tp, first, M, list);
     if (tid == 0) cnt = Kb;
   }
   __syncthreads();
@@ -63,7 +65,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     for (int j = tid; j < Kb; j += 256) out[j] = list[j];
     if (tid == 0) a.nnz[prob] = cnt;
   }
-  attend_split<KE, D, GMAX, TOK, false, WIDE, true>(a.at, prob, split, list, &cnt);
+  attend_split<KE, D, GMAX, TOK, PAGED, WIDE, true>(a.at, prob, split, list, &cnt);
   if (S == 1) return;  // the only split wrote the output
 
   // Arrival: the last split workgroup of the problem to finish merges the S
@@ -108,38 +110,69 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   for (int j = 0; j < NX; j++) store_elem(out + xs[j], v[j]);
 }
 
-template <typename KE, int D, int GMAX, int UNROLL>
-void launch_tok(const StepArgs &a, hipStream_t st) {
+constexpr size_t kLdsPerWorkgroup = 160 * 1024;
+
+// Static LDS bytes of a kernel (SIZE_MAX when the query fails; the error is
+// cleared, so that it is not reported by a later call).
+size_t static_lds(const void *kernel) {
+  hipFuncAttributes at;
+  if (hipFuncGetAttributes(&at, kernel) == hipSuccess) return at.sharedSizeBytes;
+  (void)hipGetLastError();
+  return SIZE_MAX;
+}
+
+// Launches one instantiation; with a paged cache only if its static LDS and
+// the sequence's page numbers fit a workgroup (false: nothing launched).
+template <typename KE, int D, int GMAX, int UNROLL, int TOK, bool WIDE, bool PAGED>
+bool launch_one(const StepArgs &a, hipStream_t st) {
   const dim3 grid((unsigned)(a.at.s.problems * a.at.splits)), block(256);
+  auto kernel = decode_step_kernel<KE, D, GMAX, UNROLL, TOK, WIDE, PAGED>;
+  size_t lds = 0;
+  if constexpr (PAGED) {
+    static const size_t fixed = static_lds(reinterpret_cast<const void *>(kernel));
+    lds = (size_t)a.at.pg.seq_pages * sizeof(int32_t);
+    if (fixed == SIZE_MAX || fixed + lds > kLdsPerWorkgroup) return false;
+  }
+  hipLaunchKernelGGL(kernel, grid, block, lds, st, a);
+  return true;
+}
+
+template <typename KE, int D, int GMAX, int UNROLL, bool PAGED>
+bool launch_tok(const StepArgs &a, hipStream_t st) {
   const bool wide = (int64_t)a.at.s.problems * a.at.splits >= kWideGrid;
   const int tok = attn_decode_tokens(a.at.s);
   constexpr int G8 = GMAX <= 8 ? GMAX : 8;
-  if (GMAX <= 8 && tok == 256) {
-    hipLaunchKernelGGL((decode_step_kernel<KE, D, G8, UNROLL, 256, true>), grid, block, 0, st, a);
-  } else if (GMAX <= 8 && tok == 128) {
-    if (wide) hipLaunchKernelGGL((decode_step_kernel<KE, D, G8, UNROLL, 128, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((decode_step_kernel<KE, D, G8, UNROLL, 128, false>), grid, block, 0, st, a);
-  } else {
-    if (wide) hipLaunchKernelGGL((decode_step_kernel<KE, D, GMAX, UNROLL, 64, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((decode_step_kernel<KE, D, GMAX, UNROLL, 64, false>), grid, block, 0, st, a);
-  }
+  if (GMAX <= 8 && tok == 256) return launch_one<KE, D, G8, UNROLL, 256, true, PAGED>(a, st);
+  if (GMAX <= 8 && tok == 128)
+    return wide ? launch_one<KE, D, G8, UNROLL, 128, true, PAGED>(a, st)
+                : launch_one<KE, D, G8, UNROLL, 128, false, PAGED>(a, st);
+  return wide ? launch_one<KE, D, GMAX, UNROLL, 64, true, PAGED>(a, st)
+              : launch_one<KE, D, GMAX, UNROLL, 64, false, PAGED>(a, st);
 }
 
-template <typename KE, int D, int GMAX>
-void launch_g(const StepArgs &a, hipStream_t st) {
+template <typename KE, int D, int GMAX, bool PAGED>
+bool launch_g(const StepArgs &a, hipStream_t st) {
   static_assert(((2 * kStepMaxKb + 15) / 16 + 3) / 4 <= 2, "UNROLL 1 or 2 covers K_b <= kStepMaxKb");
-  if (search_tiles_per_wave(a.at.s.Kb) <= 1) launch_tok<KE, D, GMAX, 1>(a, st);
-  else launch_tok<KE, D, GMAX, 2>(a, st);
+  if (search_tiles_per_wave(a.at.s.Kb) <= 1) return launch_tok<KE, D, GMAX, 1, PAGED>(a, st);
+  return launch_tok<KE, D, GMAX, 2, PAGED>(a, st);
 }
 
-template <typename KE, int D>
-void launch_d(const StepArgs &a, hipStream_t st) {
+template <typename KE, int D, bool PAGED>
+bool launch_d(const StepArgs &a, hipStream_t st) {
   const int G = a.at.s.G;
-  if (G <= 1) launch_g<KE, D, 1>(a, st);
-  else if (G <= 2) launch_g<KE, D, 2>(a, st);
-  else if (G <= 4) launch_g<KE, D, 4>(a, st);
-  else if (G <= 8) launch_g<KE, D, 8>(a, st);
-  else launch_g<KE, D, 16>(a, st);
+  if (G <= 1) return launch_g<KE, D, 1, PAGED>(a, st);
+  if (G <= 2) return launch_g<KE, D, 2, PAGED>(a, st);
+  if (G <= 4) return launch_g<KE, D, 4, PAGED>(a, st);
+  if (G <= 8) return launch_g<KE, D, 8, PAGED>(a, st);
+  return launch_g<KE, D, 16, PAGED>(a, st);
+}
+
+template <bool PAGED>
+bool launch_layout(const StepArgs &a, hipStream_t st) {
+  const Shape &s = a.at.s;
+  if (s.dtype == HIPSA_BF16_E5M2)
+    return s.d == 64 ? launch_d<uint8_t, 64, PAGED>(a, st) : launch_d<uint8_t, 128, PAGED>(a, st);
+  return s.d == 64 ? launch_d<uint16_t, 64, PAGED>(a, st) : launch_d<uint16_t, 128, PAGED>(a, st);
 }
 
 }  // namespace
@@ -161,11 +194,14 @@ bool one_launch(const Shape &s, int32_t splits) {
 
 hipError_t launch_decode_step(const StepArgs &a, hipStream_t st) {
   const Shape &s = a.at.s;
-  // The one-launch form serves a bf16 query with bf16 or fp8 keys in the
-  // contiguous layout and K_b <= kStepMaxKb; otherwise, or when its
-  // redundant searches would cost more than the launch they save, the two
-  // calls' kernels run in turn on the same lists.
-  if (a.at.pg.table || !one_launch(s, a.at.splits)) {
+  // The one-launch form serves a bf16 query with bf16 or fp8 keys, either
+  // layout, and K_b <= kStepMaxKb (paged: if the page numbers fit in LDS
+  // beside the kernel's own arrays); otherwise, or when its redundant
+  // searches would cost more than the launch they save, the two calls'
+  // kernels run in turn on the same lists.
+  const bool fused = one_launch(s, a.at.splits) &&
+                     (a.at.pg.table ? launch_layout<true>(a, st) : launch_layout<false>(a, st));
+  if (!fused) {
     MaskArgs m{a.at.q, a.at.K, a.indices, a.nnz, s, a.at.pg};
     hipError_t e = launch_mask_decode(m, st);
     if (e != hipSuccess) return e;
@@ -173,13 +209,6 @@ hipError_t launch_decode_step(const StepArgs &a, hipStream_t st) {
     at.indices = a.indices;
     at.nnz = a.nnz;
     return launch_attn_decode(at, st);
-  }
-  if (s.dtype == HIPSA_BF16_E5M2) {
-    if (s.d == 64) launch_d<uint8_t, 64>(a, st);
-    else launch_d<uint8_t, 128>(a, st);
-  } else {
-    if (s.d == 64) launch_d<uint16_t, 64>(a, st);
-    else launch_d<uint16_t, 128>(a, st);
   }
   return hipGetLastError();  // the last split workgroup of each problem merged the partials
 }

@@ -6,8 +6,10 @@ inputs (the one-launch kernel runs the same search, split assignment and
 merge), and (2) the oracle's acceptance: index lists equal to the oracle's
 or, for near ties, reachable by its tolerant search; outputs within 2e-2 of
 the oracle's attention on the GPU's lists.  Cases cover the one-launch form
-(bf16, contiguous, K_b <= 32) and the cases that run the two calls' kernels
-in turn (fp32, fp8 K/V, paged, K_b > 32).
+(bf16 query, bf16 or fp8 K/V, contiguous or paged, K_b <= 64) and the cases
+that run the two calls' kernels in turn (fp32, K_b > 64, more than 16 splits
+or workgroups beyond one per CU, page numbers that do not fit in LDS beside
+the kernel's own arrays).
 """
 import numpy as np
 import pytest
@@ -78,10 +80,12 @@ CASES = {
     "ragged_batch3": dict(base="decode_32k", B=3, Hq=8, Hkv=2, T=7001, k=1024),
     "wide_grid": dict(base="decode_32k", Hq=32, Hkv=8, Tq=16, T=4096, k=1024),
     "wide_grid_d64_ragged": dict(base="decode_32k", Hq=16, Hkv=8, Tq=16, T=4001, d=64, k=1024),
+    "e5m2": dict(base="decode_32k", dtype="bf16_e5m2", Hq=8, Hkv=2, T=9000, k=1024),
+    "e5m2_d64_group8": dict(base="decode_32k", dtype="bf16_e5m2", Hq=16, Hkv=2, d=64, T=7000, k=1024),
+    # K_b = 64: two tiles per wave and round in the search
+    "kb64": dict(base="decode_32k", Hq=8, Hkv=2, T=20000, k=4096),
     # the two calls' kernels in turn
     "f32_d128": dict(base="decode_32k", dtype="f32", B=2, Hq=4, Hkv=2, T=6000, k=1024),
-    "e5m2": dict(base="decode_32k", dtype="bf16_e5m2", Hq=8, Hkv=2, T=9000, k=1024),
-    "kb64": dict(base="decode_32k", Hq=8, Hkv=2, T=20000, k=4096),
     "bk8_kb512": dict(base="decode_32k", Hq=8, Hkv=2, T=20000, block_k=8, k=4096),
 }
 
@@ -103,8 +107,20 @@ def test_step_dense_part_128k():
 
 
 def test_step_paged():
-    """A paged KV cache (the two calls' kernels in turn)."""
+    """A paged KV cache (one launch; the search stages the page numbers in LDS)."""
     check_step("paged", si.workload("decode_32k", Hq=8, Hkv=2, T=8192, k=1024), page=128)
+
+
+def test_step_paged_fp8():
+    check_step("paged_fp8", si.workload("decode_32k", dtype="bf16_e5m2", B=2, Hq=8, Hkv=2, T=7000,
+                                        k=1024), page=64)
+
+
+def test_step_paged_pages_fill_lds():
+    """16384 pages of 16 tokens beside a 16-head group's arrays: more than a
+    workgroup's LDS, so the two calls' kernels run in turn (same results)."""
+    check_step("paged_pages_fill_lds", si.workload("decode_32k", Hq=16, Hkv=1, T=262144,
+                                                   block_k=16, k=1024), page=16)
 
 
 def test_step_zero_query_ties_exact():
