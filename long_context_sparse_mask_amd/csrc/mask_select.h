@@ -30,16 +30,33 @@ __device__ inline void select_top(const int32_t *ca, const int32_t *ce, const ui
                                   int32_t *rk, int n, int Kb, int32_t *na, int32_t *ne,
                                   int32_t *more) {
   const int parts = (n + kSpan - 1) / kSpan;
-  for (int t = threadIdx.x; t < n * parts; t += 256) {
-    const int c = t % n, j0 = (t / n) * kSpan;
+  if (256 % n == 0) {
+    // every batch of thread t is for the same candidate t % n: the batches'
+    // reads are issued together and the counts meet in one atomic
+    const int c = threadIdx.x % n, stride = 256 / n;
     const uint64_t kc = key[c];
-    uint64_t kk[kSpan];
-#pragma unroll
-    for (int u = 0; u < kSpan; u++) kk[u] = key[j0 + u];
     int r = 0;
+#pragma unroll 4
+    for (int p = threadIdx.x / n; p < parts; p += stride) {
+      uint64_t kk[kSpan];
 #pragma unroll
-    for (int u = 0; u < kSpan; u++) r += kk[u] > kc;
+      for (int u = 0; u < kSpan; u++) kk[u] = key[p * kSpan + u];
+#pragma unroll
+      for (int u = 0; u < kSpan; u++) r += kk[u] > kc;
+    }
     if (r && kc) atomicAdd(&rk[c], r);
+  } else {
+    for (int t = threadIdx.x; t < n * parts; t += 256) {
+      const int c = t % n, j0 = (t / n) * kSpan;
+      const uint64_t kc = key[c];
+      uint64_t kk[kSpan];
+#pragma unroll
+      for (int u = 0; u < kSpan; u++) kk[u] = key[j0 + u];
+      int r = 0;
+#pragma unroll
+      for (int u = 0; u < kSpan; u++) r += kk[u] > kc;
+      if (r && kc) atomicAdd(&rk[c], r);
+    }
   }
   __syncthreads();
   for (int c = threadIdx.x; c < n; c += 256) {
@@ -62,12 +79,13 @@ __device__ inline void write_ascending(const int32_t *fin, int Kb, int32_t *out)
   for (int c = threadIdx.x; c < Kb; c += 256) {
     const int32_t v = fin[2 * c];
     int r = 0;
-    for (int j0 = 0; j0 < Kb; j0 += kSpan) {
+#pragma unroll 4
+    for (int j0 = 0; j0 < Kb; j0 += kSpan) {  // batches' reads issued together
       int32_t kk[kSpan];
 #pragma unroll
       for (int u = 0; u < kSpan; u++) kk[u] = fin[2 * min(j0 + u, Kb - 1)];
 #pragma unroll
-      for (int u = 0; u < kSpan; u++) r += (j0 + u < Kb) && kk[u] < v;
+      for (int u = 0; u < kSpan; u++) r += (j0 + u < Kb) & (kk[u] < v);
     }
     out[r] = v;
   }
