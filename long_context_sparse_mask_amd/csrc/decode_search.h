@@ -38,6 +38,7 @@ __device__ __forceinline__ void search_row(const void *q, const void *K, const S
   __shared__ uint64_t key[2 * kMaxKb + kSpan];
   __shared__ int32_t rk[2 * kMaxKb];
   __shared__ int32_t flag[2];
+  __shared__ int32_t pos[kMaxKb];  // places of the kept ids (write_ascending)
   constexpr bool kMfma = std::is_same<E, uint16_t>::value;
   __shared__ __align__(16) uint8_t stage[stage_bytes<E, KE, D>()];
   extern __shared__ int32_t ptab[];  // paged: the sequence's page numbers
@@ -62,6 +63,7 @@ __device__ __forceinline__ void search_row(const void *q, const void *K, const S
   initial_candidates(first, M, Kb, cand_a[0], cand_e[0]);
   if (tid < kSpan) key[n + tid] = 0;  // padding read by the rank batches
   if (tid == 0) flag[0] = 1;          // M > K_b: the first round always runs
+  for (int c = tid; c < Kb; c += 256) pos[c] = 0;
   __syncthreads();
 
   int cur = 0;
@@ -82,7 +84,7 @@ __device__ __forceinline__ void search_row(const void *q, const void *K, const S
 
 
   // the kept one-block chunks sit at the even slots of the current buffer
-  write_ascending(cand_a[cur], Kb, out);
+  write_ascending(cand_a[cur], Kb, pos, out);
 }
 
 }  // namespace hipsa

@@ -58,6 +58,7 @@ __global__ __launch_bounds__(256) void mask_prefill_kernel(MaskArgs a) {
   __shared__ int32_t cand_a[2][2 * kMaxKb], cand_e[2][2 * kMaxKb];
   __shared__ uint64_t key[2][2 * kMaxKb + kSpan];
   __shared__ int32_t rk[2 * kMaxKb];
+  __shared__ int32_t pos[kMaxKb];  // places of the kept ids (write_ascending)
   __shared__ int32_t flag[2];
 
   const uint16_t *Qb = reinterpret_cast<const uint16_t *>(a.q) + ((int64_t)(b * s.Hq + g * s.G) * Tq + r0) * D;
@@ -96,6 +97,7 @@ __global__ __launch_bounds__(256) void mask_prefill_kernel(MaskArgs a) {
   if constexpr (PAGED) stage_pages(a.pg, b, Tp, ptab);
   initial_candidates(first, M, Kb, cand_a[0], cand_e[0]);
   for (int c = tid; c < n + kSpan; c += 256) key[0][c] = key[1][c] = 0;
+  for (int c = tid; c < Kb; c += 256) pos[c] = 0;
   if (tid == 0) flag[0] = 1;
   __syncthreads();
 
@@ -192,7 +194,7 @@ __global__ __launch_bounds__(256) void mask_prefill_kernel(MaskArgs a) {
   }
 
 #undef HIPSA_LOAD_QUERIES
-  write_ascending(cand_a[cur], Kb, out);
+  write_ascending(cand_a[cur], Kb, pos, out);
   if (tid == 0) a.nnz[prob] = Kb;
 }
 

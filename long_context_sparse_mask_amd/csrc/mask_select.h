@@ -74,8 +74,29 @@ __device__ inline void select_top(const int32_t *ca, const int32_t *ce, const ui
 }
 
 // The K_b kept one-block chunks sit at the even slots of `fin`; writes their
-// block ids to out[0..K_b) in ascending order.
-__device__ inline void write_ascending(const int32_t *fin, int Kb, int32_t *out) {
+// block ids to out[0..K_b) in ascending order: an id's place is the number of
+// smaller ids.  When 256 is a multiple of K_b and 16 <= K_b <= 128, 256 / K_b
+// threads share an id's comparisons and the counts meet in `pos` (K_b zeros
+// on entry, visible to every thread: cleared before a barrier), one barrier;
+// otherwise thread c counts for id c alone.  Called by all 256 threads.
+__device__ inline void write_ascending(const int32_t *fin, int Kb, int32_t *pos, int32_t *out) {
+  if (256 % Kb == 0 && Kb >= 16 && Kb <= 128) {
+    const int parts = 256 / Kb, span = Kb / parts;  // a power of two, >= 1
+    const int c = threadIdx.x % Kb, j0 = (threadIdx.x / Kb) * span;
+    const int32_t v = fin[2 * c];
+    int r = 0;
+    for (int u0 = 0; u0 < span; u0 += 4) {
+      int32_t kk[4];
+#pragma unroll
+      for (int u = 0; u < 4; u++) kk[u] = fin[2 * (j0 + min(u0 + u, span - 1))];
+#pragma unroll
+      for (int u = 0; u < 4; u++) r += (u0 + u < span) & (kk[u] < v);
+    }
+    if (r) atomicAdd(&pos[c], r);
+    __syncthreads();
+    if (threadIdx.x < Kb) out[pos[c]] = v;
+    return;
+  }
   for (int c = threadIdx.x; c < Kb; c += 256) {
     const int32_t v = fin[2 * c];
     int r = 0;
