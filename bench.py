@@ -98,16 +98,14 @@ def prefill_flops(w) -> dict:
 
 # kernels behind each call, for matching the committed HBM counter summary
 CALL_KERNELS = {
-    ("decode", "hip_decode_step"): ("decode_step_kernel", "attn_decode_combine"),
+    # the one-launch form (the workloads measured here fit it: contiguous bf16
+    # or fp8 K/V, K_b <= 64, at most 16 splits and one split workgroup per CU)
+    ("decode", "hip_decode_step"): ("decode_step_kernel",),
     ("decode", "hip_sparse_attn"): ("attn_decode_mfma", "attn_decode_kernel", "attn_decode_combine"),
     ("decode", "hip_mask_estimate"): ("mask_decode",),
     ("prefill", "hip_sparse_attn"): ("attn_prefill_kernel",),
     ("prefill", "hip_mask_estimate"): ("mask_prefill_kernel",),
 }
-# hip_decode_step runs the one-launch kernel for bf16 K/V; for fp8 K/V it runs
-# the two calls' kernels in turn
-CALL_KERNELS[("decode", "hip_decode_step", "bf16_e5m2")] = (
-    "mask_decode_kernel", "attn_decode_mfma", "attn_decode_combine")
 
 
 # string and character literals (kept) or comments (dropped), in source order
@@ -137,8 +135,6 @@ def kernel_matches(kernel: str, dtype: str) -> bool:
     (unsigned char = E5M2 codes, unsigned short = bf16, float), the decode
     combine (which never reads K/V) by its output type."""
     args = kernel.split("<", 1)[1] if "<" in kernel else ""
-    if kernel.startswith("decode_step_kernel"):  # bf16 query and K/V only
-        return dtype == "bf16"
     if kernel.startswith("attn_decode_combine"):
         return ("float" in args) == (dtype == "f32")
     if "unsigned char" in args:

@@ -49,6 +49,9 @@ def test_traffic_lookup_separates_element_types():
     comb = "attn_decode_combine<unsigned short, 128>"
     assert m(comb, "bf16") and m(comb, "bf16_e5m2") and not m(comb, "f32")
     assert m("attn_decode_kernel<float, 64, 1, 64>", "f32")
+    st = "decode_step_kernel<unsigned short, 128, 4, 1, 256, true, false>"
+    st8 = "decode_step_kernel<unsigned char, 128, 4, 1, 256, true, false>"
+    assert m(st, "bf16") and not m(st, "bf16_e5m2") and m(st8, "bf16_e5m2") and not m(st8, "bf16")
 
 
 def test_decode_bytes_dense_case():
