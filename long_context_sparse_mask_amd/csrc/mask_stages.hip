@@ -206,6 +206,7 @@ __global__ __launch_bounds__(256) void mask_stages_kernel(StageArgs a) {
   __shared__ uint32_t hist[3 * 256];
   __shared__ int32_t wcnt[4];
   __shared__ int32_t flag[2];  // by round parity: a kept chunk is wider than the stage's size
+  __shared__ int32_t pos[128];  // places of the final list's ids (K_b <= 128)
 
   const E *qbase = reinterpret_cast<const E *>(a.m.q) + ((int64_t)(b * s.Hq + g * s.G) * Tq + i) * D;
   const KE *Kbase = reinterpret_cast<const KE *>(a.m.K);
@@ -270,6 +271,7 @@ __global__ __launch_bounds__(256) void mask_stages_kernel(StageArgs a) {
     ae[j] = min(first + (j + 1) * c0, first + M);
   }
   hist[tid] = hist[256 + tid] = hist[512 + tid] = 0;
+  if (tid < 128) pos[tid] = 0;
   __syncthreads();
 
   int stage = 1, r = 0, pass = 0;
@@ -313,7 +315,30 @@ __global__ __launch_bounds__(256) void mask_stages_kernel(StageArgs a) {
   }
 
   // the last stage's kept chunks are single blocks: the list, ascending (a
-  // block's place is the number of smaller kept blocks)
+  // block's place is the number of smaller kept blocks).  When 256 is a
+  // multiple of K_b and 16 <= K_b <= 128, 256 / K_b threads share a block's
+  // comparisons and the counts meet in `pos`.
+  if (256 % Kb == 0 && Kb >= 16 && Kb <= 128) {
+    const int parts = 256 / Kb, span = Kb / parts;
+    const int j = tid % Kb, u0 = (tid / Kb) * span;
+    const int32_t v = j < nk ? as[j] : 0;
+    int rk = 0;
+    for (int t0 = 0; t0 < span; t0 += 4) {
+      int32_t vv[4];
+#pragma unroll
+      for (int t = 0; t < 4; t++) vv[t] = as[max(min(u0 + min(t0 + t, span - 1), nk - 1), 0)];
+#pragma unroll
+      for (int t = 0; t < 4; t++) rk += (t0 + t < span) & (u0 + t0 + t < nk) & (vv[t] < v);
+    }
+    if (j < nk && rk) atomicAdd(&pos[j], rk);
+    __syncthreads();
+    if (tid < Kb) {
+      if (tid < nk) out[pos[tid]] = v;
+      else out[tid] = -1;
+    }
+    if (tid == 0) a.m.nnz[prob] = nk;
+    return;
+  }
   for (int j = tid; j < Kb; j += 256) {
     if (j < nk) {
       const int32_t v = as[j];
