@@ -277,12 +277,14 @@ size_t hipsa_stages_workspace_bytes(const hipsa_desc *desc, const hipsa_ext *ext
  * reported latency is masking plus sparse attention).  Results are bit for
  * bit those of the two calls: indices/nnz as hip_mask_estimate writes them
  * (so later steps may reuse the mask with hip_sparse_attn), out as
- * hip_sparse_attn computes it.  For bf16 K/V in the contiguous layout with
- * k / block_k <= 32, when the attention's split workgroups number at most one
- * per CU (256) and at most 16 per problem, the search and the attention run
- * in one launch: each split workgroup runs the problem's search itself,
- * attends its share of the kept blocks, and the last one of each problem to
- * finish merges the splits.  Other cases run the two calls' kernels in turn.
+ * hip_sparse_attn computes it.  For a bf16 query (bf16 or E5M2 K/V, either
+ * layout) with k / block_k <= 64, when the attention's split workgroups
+ * number at most one per CU (256) and at most 16 per problem (and, paged,
+ * when the sequence's page numbers fit in a workgroup's LDS beside the
+ * kernel's own arrays), the search and the attention run in one launch: each
+ * split workgroup runs the problem's search itself, attends its share of the
+ * kept blocks, and the last one of each problem to finish merges the splits.
+ * Other cases run the two calls' kernels in turn.
  *   ext: dense part and paged layout as in the *_ex calls, or NULL.
  *   workspace: hipsa_decode_step_workspace_bytes() bytes, 16-byte aligned,
  *     zero-filled before its first use (it holds one arrival counter per

@@ -65,7 +65,7 @@ def check_dense(name, w, sink, window, x=None, **kw):
 CASES = {
     # a window of 4096 tokens and one sink block, as a serving configuration would use
     "decode_32k": ("decode_32k", 64, 4096, dict(B=2, Hq=8, Hkv=2)),
-    # block_k 8, K_b 512 (the mask kernel without speculation)
+    # block_k 8, K_b 512 (eight candidate tiles per wave and round)
     "decode_bk8_kb512": ("decode_32k", 8, 512, dict(Hq=8, Hkv=2, T=20000, block_k=8, k=4096)),
     # the dense part covers every block (no search, nnz 0)
     "decode_all_dense": ("decode_32k", 64, 256, dict(Hq=4, Hkv=1, T=300, k=512)),

@@ -47,7 +47,7 @@ def test_decode_workload_full(name):
 DECODE_EDGE = {
     # d = 64: V rows of 2 codes per lane
     "d64_bk16_g2": dict(Hq=4, Hkv=2, d=64, T=5000, block_k=16, k=256),
-    # K_b = 512: the mask kernel without child speculation
+    # K_b = 512: eight candidate tiles per wave and round
     "bk8_kb512": dict(Hq=8, Hkv=2, T=20000, block_k=8, k=4096),
     "bk32_kb7": dict(Hq=4, Hkv=1, T=9000, block_k=32, k=224),
     "dense_k_ge_T": dict(Hq=4, Hkv=2, T=500, block_k=32, k=512),

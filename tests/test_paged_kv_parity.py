@@ -95,7 +95,7 @@ CASES = {
     "decode_ps64": ("decode_32k", 64, dict(B=2, Hq=8, Hkv=2)),
     # pages of 4 key blocks, ragged tail page
     "decode_ps256_ragged": ("decode_32k", 256, dict(Hq=8, Hkv=2, T=30001)),
-    # block_k 8 with pages of 8, several rows per call, K_b = 512 (mask without speculation)
+    # block_k 8 with pages of 8, several rows per call, K_b = 512 (eight tiles per wave and round)
     "decode_bk8_kb512": ("decode_32k", 8, dict(Hq=8, Hkv=2, T=20000, block_k=8, k=4096)),
     "decode_multi_row": ("decode_32k", 64, dict(Hq=8, Hkv=2, Tq=5, T=3000, k=512)),
     # fp32 path, d = 64
