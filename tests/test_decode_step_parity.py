@@ -170,3 +170,43 @@ def test_step_workspace_reused():
         torch.cuda.synchronize()
         assert torch.equal(idx, i2) and torch.equal(nnz, n2) and torch.equal(out, o2), r
         assert (ws[need - 4 * P:] == 0).all(), "arrival counters not back at zero"
+
+
+def _tied_scores(x):
+    """Scores with many exact ties: q is zero but for dimension 0, and K's
+    dimension 0 holds small integers, so every score is an exact integer on
+    both sides and a round's cut falls inside a group of equal scores (the
+    lower start wins)."""
+    g = torch.Generator().manual_seed(5)
+    q = torch.zeros_like(x["q"])
+    q[..., 0] = 1
+    K = x["K"].clone()
+    K[..., 0] = torch.randint(-2, 3, K.shape[:-1], generator=g).to(K.dtype)
+    return dict(x, q=q, K=K)
+
+
+TIE_INPUTS = {"zero_query": lambda x: dict(x, q=torch.zeros_like(x["q"])), "tied_scores": _tied_scores}
+TIE_SHAPES = {
+    "decode_128k_b4": dict(base="decode_128k_b4"),
+    "kb64": dict(base="decode_32k", Hq=8, Hkv=2, T=20000, k=4096),
+    "e5m2_ragged": dict(base="decode_32k", dtype="bf16_e5m2", B=3, Hq=8, Hkv=2, T=7001, k=1024),
+}
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("inputs", sorted(TIE_INPUTS))
+@pytest.mark.parametrize("shape", sorted(TIE_SHAPES))
+def test_step_exact_ties(shape, inputs):
+    """Exact score ties at the cuts: the one-launch step equals the two calls
+    bit for bit, and its lists equal the oracle's exactly (scores are exact
+    integers on both sides, so the lower-start rule decides every tie)."""
+    kw = dict(TIE_SHAPES[shape])
+    w = si.workload(kw.pop("base"), **kw)
+    print(f"[case] step ties {shape} {inputs} {w}", flush=True)
+    x = TIE_INPUTS[inputs](si.make_inputs(w))
+    (idx, nnz, out), (s_idx, s_nnz, s_out) = _two_calls(x, w, 0, 0)
+    assert (s_idx == idx).all() and (s_nnz == nnz).all(), "lists differ from the two calls"
+    assert torch.equal(s_out, out), "output differs from the two calls"
+    o_idx, o_nnz, _ = oracle.mask_all(x["q"], x["K"], T=w.T, k=w.k, block_k=w.block_k, block_q=1,
+                                      causal=w.causal)
+    assert (s_idx == o_idx).all() and (s_nnz == o_nnz).all(), "lists differ from the oracle"
