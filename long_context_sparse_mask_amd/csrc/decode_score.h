@@ -14,6 +14,7 @@
 // reads row 0 and discards it), so a round pays one memory latency per batch.
 #pragma once
 
+#include <cstddef>
 #include <type_traits>
 
 #include "hipsa_internal.h"
@@ -63,17 +64,80 @@ struct QueryOps {
   }
 };
 
+// Row-by-row gathers of one batch of a wave's candidate tiles (the tiles
+// t0, t0 + 4, ..., UNROLL of them): lane loads TileGather's 16-byte pieces of
+// the centre rows of slots 16 (t0 + 4u) + TG::row(j), centre(c) giving the
+// centre token of slot c (0 for an empty slot or c >= n: row 0 is read and
+// discarded).  TRIM: tiles from ntile on are skipped.
+template <typename KE, int D, int UNROLL, bool TRIM, typename RowOf, typename CentreOf>
+__device__ __forceinline__ void gather_batch(const KE *Kbase, RowOf row_of, CentreOf centre, int t0, int ntile,
+                                             uint4 (&v)[UNROLL][TileGather<KE, D>::kLoads]) {
+  using TG = TileGather<KE, D>;
+#pragma unroll
+  for (int u = 0; u < UNROLL; u++) {
+    if (TRIM && t0 + 4 * u >= ntile) break;  // uniform
+#pragma unroll
+    for (int j = 0; j < TG::kLoads; j++) v[u][j] = TG::load(Kbase + row_of(centre(16 * (t0 + 4 * u) + TG::row(j))));
+  }
+}
+
+// Scores one gathered batch (gather_batch): its tiles go through the wave's
+// LDS tiles (`mine`) into matrix-core operands, and key[c] = rank_key(max over
+// the group's heads, start) for the batch's slots c < n (0 for an empty slot).
+template <typename E, typename KE, int D, int GMAX, int UNROLL, bool TRIM>
+__device__ __forceinline__ void score_batch(const QueryOps<E, D, GMAX> &qo,
+                                            const uint4 (&v)[UNROLL][TileGather<KE, D>::kLoads], int t0,
+                                            int ntile, const int32_t *ca, int n, const Shape &s, uint64_t *key,
+                                            uint8_t *mine) {
+  using TG = TileGather<KE, D>;
+  constexpr int KS = QueryOps<E, D, GMAX>::KS;
+  const int lane = threadIdx.x & 63;
+  const uint4 *qa = qo.qa;
+#pragma unroll
+  for (int u0 = 0; u0 < UNROLL; u0 += kStageTiles) {
+#pragma unroll
+    for (int du = 0; du < kStageTiles; du++)
+      if (u0 + du < UNROLL && (!TRIM || t0 + 4 * (u0 + du) < ntile)) TG::put(v[u0 + du], mine + du * TG::kBytes);
+    wave_lds_sync();
+#pragma unroll
+    for (int du = 0; du < kStageTiles; du++) {
+      const int u = u0 + du;
+      if (u >= UNROLL || (TRIM && t0 + 4 * u >= ntile)) break;
+      typename TG::raw_t kr[KS];
+      TG::get(mine + du * TG::kBytes, kr);
+      const int c = 16 * (t0 + 4 * u) + (lane & 15);
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ks++)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[ks]), as_bf16x8(Kv8<KE>::bf16(kr[ks])), acc,
+                                                      0, 0, 0);
+      float best = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; r++)
+        if (4 * (lane >> 4) + r < s.G) best = fmaxf(best, acc[r]);
+      if (GMAX > 4) best = fmaxf(best, __shfl_xor(best, 16, 64));
+      if (GMAX > 8) best = fmaxf(best, __shfl_xor(best, 32, 64));
+      if (lane < 16 && c < n) key[c] = ca[c] >= 0 ? rank_key(best, ca[c]) : 0ull;
+    }
+    wave_lds_sync();  // the next tiles overwrite these
+  }
+}
+
 // Scores candidate slots [0, n) with chunks (ca[c], ce[c]) in blocks (start
 // -1: an empty slot) and writes key[c] = rank_key(score, start), or 0 for an
 // empty slot.  Tp: the row's visible length; row_of(t): element offset of the
 // K row of position t.  UNROLL: tiles (MFMA) or rows (VALU) per lane whose
 // loads are issued together; TRIM: the MFMA path skips a batch's tiles past
-// n (for callers whose n varies below what UNROLL was sized for).  Called by
+// n (for callers whose n varies below what UNROLL was sized for).  With
+// `first` non-null (MFMA, `stage` non-null) the wave's first batch was
+// gathered already (gather_batch with t0 = the wave) into *first.  Called by
 // all 256 threads; LDS reads of ca/ce, no barrier.
-template <typename E, typename KE, int D, int GMAX, int UNROLL, bool TRIM = false, typename RowOf>
+template <typename E, typename KE, int D, int GMAX, int UNROLL, bool TRIM = false, typename RowOf,
+          typename FirstT = std::nullptr_t>
 __device__ __forceinline__ void score_slots(const QueryOps<E, D, GMAX> &qo, const KE *Kbase, RowOf row_of,
                                             const int32_t *ca, const int32_t *ce, int n, int32_t Tp,
-                                            const Shape &s, uint64_t *key, uint8_t *stage = nullptr) {
+                                            const Shape &s, uint64_t *key, uint8_t *stage = nullptr,
+                                            FirstT first = nullptr) {
   constexpr bool kMfma = QueryOps<E, D, GMAX>::kMfma;
   constexpr int VEC = QueryOps<E, D, GMAX>::VEC;
   constexpr int TPR = QueryOps<E, D, GMAX>::TPR;
@@ -94,42 +158,15 @@ __device__ __forceinline__ void score_slots(const QueryOps<E, D, GMAX> &qo, cons
         const int32_t lo = lo_b << s.bk_shift, hi = min(hi_b << s.bk_shift, Tp);
         return c < n && lo_b >= 0 ? (lo + hi) >> 1 : 0;
       };
-      for (int t0 = wave; t0 < ntile; t0 += 4 * UNROLL) {
+      int t0 = wave;
+      if constexpr (!std::is_same<FirstT, std::nullptr_t>::value) {
+        score_batch<E, KE, D, GMAX, UNROLL, TRIM>(qo, *first, t0, ntile, ca, n, s, key, mine);
+        t0 += 4 * UNROLL;
+      }
+      for (; t0 < ntile; t0 += 4 * UNROLL) {
         uint4 v[UNROLL][TG::kLoads];
-#pragma unroll
-        for (int u = 0; u < UNROLL; u++) {
-          if (TRIM && t0 + 4 * u >= ntile) break;  // uniform
-#pragma unroll
-          for (int j = 0; j < TG::kLoads; j++) v[u][j] = TG::load(Kbase + row_of(centre(16 * (t0 + 4 * u) + TG::row(j))));
-        }
-#pragma unroll
-        for (int u0 = 0; u0 < UNROLL; u0 += kStageTiles) {
-#pragma unroll
-          for (int du = 0; du < kStageTiles; du++)
-            if (u0 + du < UNROLL && (!TRIM || t0 + 4 * (u0 + du) < ntile)) TG::put(v[u0 + du], mine + du * TG::kBytes);
-          wave_lds_sync();
-#pragma unroll
-          for (int du = 0; du < kStageTiles; du++) {
-            const int u = u0 + du;
-            if (u >= UNROLL || (TRIM && t0 + 4 * u >= ntile)) break;
-            typename TG::raw_t kr[KS];
-            TG::get(mine + du * TG::kBytes, kr);
-            const int c = 16 * (t0 + 4 * u) + (lane & 15);
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ks++)
-              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[ks]), as_bf16x8(Kv8<KE>::bf16(kr[ks])),
-                                                            acc, 0, 0, 0);
-            float best = -INFINITY;
-#pragma unroll
-            for (int r = 0; r < 4; r++)
-              if (4 * (lane >> 4) + r < s.G) best = fmaxf(best, acc[r]);
-            if (GMAX > 4) best = fmaxf(best, __shfl_xor(best, 16, 64));
-            if (GMAX > 8) best = fmaxf(best, __shfl_xor(best, 32, 64));
-            if (lane < 16 && c < n) key[c] = ca[c] >= 0 ? rank_key(best, ca[c]) : 0ull;
-          }
-          wave_lds_sync();  // the next tiles overwrite these
-        }
+        gather_batch<KE, D, UNROLL, TRIM>(Kbase, row_of, centre, t0, ntile, v);
+        score_batch<E, KE, D, GMAX, UNROLL, TRIM>(qo, v, t0, ntile, ca, n, s, key, mine);
       }
       return;
     }

@@ -57,6 +57,23 @@ __device__ __forceinline__ void search_row(const void *q, const void *K, const S
   qo.load(qbase, (int64_t)Tq * D, s.G);
 
   const int n = 2 * Kb;
+  // Round 0's candidates are the halves of the initial chunks, known without
+  // LDS: with a contiguous cache and one tile per wave (K_b <= 32) the wave
+  // gathers its tile's centre rows now, beside the query loads, ahead of the
+  // set-up barrier (128k x 4 step 24.42 -> 23.99 us, three interleaved pairs;
+  // with two tiles per wave, K_b = 64 at 1M tokens, 32.79 -> 33.04 us).
+  constexpr bool kEarly = kMfma && !PAGED && UNROLL == 1;
+  using TG = TileGather<std::conditional_t<kEarly, KE, uint16_t>, D>;
+  uint4 first0[kEarly ? UNROLL : 1][kEarly ? TG::kLoads : 1];
+  if constexpr (kEarly) {
+    auto centre0 = [&](int c) -> int32_t {
+      int32_t a, e;
+      initial_slot(first, M, Kb, c < n ? c : 0, &a, &e);
+      const int32_t lo = a << s.bk_shift, hi = min(e << s.bk_shift, Tp);
+      return c < n && a >= 0 ? (lo + hi) >> 1 : 0;
+    };
+    gather_batch<KE, D, UNROLL, false>(Kbase, row_of, centre0, tid >> 6, (n + 15) / 16, first0);
+  }
   // paged: page numbers to LDS, issued after the query loads so that both
   // are in flight together (read after the first barrier)
   if constexpr (PAGED) stage_pages(pg, b, Tp, ptab);
@@ -74,7 +91,14 @@ __device__ __forceinline__ void search_row(const void *q, const void *K, const S
     for (int c = tid; c < n; c += 256) rk[c] = 0;  // rank counts of this round
 
     // ---- 1. scoring
-    score_slots<E, KE, D, GMAX, UNROLL>(qo, Kbase, row_of, ca, ce, n, Tp, s, key, kMfma ? stage : nullptr);
+    if constexpr (kEarly) {
+      if (round == 0)
+        score_slots<E, KE, D, GMAX, UNROLL>(qo, Kbase, row_of, ca, ce, n, Tp, s, key, stage, &first0);
+      else
+        score_slots<E, KE, D, GMAX, UNROLL>(qo, Kbase, row_of, ca, ce, n, Tp, s, key, stage);
+    } else {
+      score_slots<E, KE, D, GMAX, UNROLL>(qo, Kbase, row_of, ca, ce, n, Tp, s, key, kMfma ? stage : nullptr);
+    }
     __syncthreads();
 
     // ---- 2. selection: the K_b best write their halves into the other buffer
