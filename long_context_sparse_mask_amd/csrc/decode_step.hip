@@ -35,12 +35,26 @@ namespace {
 // bf16 query, bf16 or fp8 (E5M2) K/V, K_b <= kStepMaxKb; UNROLL as the mask
 // kernel takes it (search_tiles_per_wave).  PAGED: the search stages the
 // sequence's page numbers in dynamic LDS, as the mask kernel does.
+//
+// The search's operands lead the argument list as scalars (q, K, the grid
+// size and the shape fields it reads, 12 dwords; `packed` holds bk_shift in
+// bits 0-3, causal in bit 4, G in bits 5-9, K_b in bits 10-17, `dense` the
+// sink and window blocks in its halves): the dispatcher preloads them into
+// scalar registers, so the query and round-0 loads issue without waiting for
+// a kernel-argument read; the rest of `a` is read from memory when the
+// attention needs it.
 template <typename KE, int D, int GMAX, int UNROLL, int TOK, bool WIDE, bool PAGED>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void decode_step_kernel(StepArgs a) {
-  const Shape &s = a.at.s;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void decode_step_kernel(
+    const void *q, const void *K, uint32_t nwg, int32_t splits, int32_t Tq_, int32_t Hkv_, int32_t T_,
+    int32_t T_cap, uint32_t packed, uint32_t dense, StepArgs a) {
+  Shape s = a.at.s;  // the fields the search reads, from the preloaded arguments
+  s.Tq = Tq_; s.Hkv = Hkv_; s.T = T_; s.T_cap = T_cap;
+  s.bk_shift = (int32_t)(packed & 15); s.bk = 1 << s.bk_shift; s.causal = (int32_t)((packed >> 4) & 1);
+  s.G = (int32_t)((packed >> 5) & 31); s.Kb = (int32_t)((packed >> 10) & 255); s.Hq = (int64_t)s.G * Hkv_;
+  s.sink_b = (int32_t)(dense & 0xffff); s.window_b = (int32_t)(dense >> 16);
   const int tid = threadIdx.x;
-  const uint32_t S = (uint32_t)a.at.splits;
-  const uint32_t wgi = xcd_swizzle(blockIdx.x, gridDim.x);
+  const uint32_t S = (uint32_t)splits;
+  const uint32_t wgi = xcd_swizzle(blockIdx.x, nwg);
   const uint32_t split = wgi % S, prob = wgi / S;
   const uint32_t Tq = (uint32_t)s.Tq, Hkv = (uint32_t)s.Hkv;
   const uint32_t i = prob % Tq, g = (prob / Tq) % Hkv, b = prob / (Tq * Hkv);
@@ -56,7 +70,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     for (int j = tid; j < Kb; j += 256) list[j] = j < M ? first + j : -1;
     if (tid == 0) cnt = M;
   } else {
-    search_row<uint16_t, KE, D, GMAX, UNROLL, PAGED>(a.at.q, a.at.K, s, a.at.pg, b, g, i, Tp, first, M, list);
+    search_row<uint16_t, KE, D, GMAX, UNROLL, PAGED>(q, K, s, a.at.pg, b, g, i, Tp, first, M, list);
     if (tid == 0) cnt = Kb;
   }
   __syncthreads();
@@ -133,7 +147,14 @@ bool launch_one(const StepArgs &a, hipStream_t st) {
     lds = (size_t)a.at.pg.seq_pages * sizeof(int32_t);
     if (fixed == SIZE_MAX || fixed + lds > kLdsPerWorkgroup) return false;
   }
-  hipLaunchKernelGGL(kernel, grid, block, lds, st, a);
+  const Shape &s = a.at.s;
+  // packed fields: bk_shift <= 6, G <= 16, K_b <= kStepMaxKb, sink and window blocks <= kMaxDenseBlocks
+  static_assert(kStepMaxKb <= 255 && kMaxGroup <= 31 && kMaxDenseBlocks <= 0xffff, "packed step arguments");
+  const uint32_t packed = (uint32_t)s.bk_shift | (uint32_t)(s.causal != 0) << 4 | (uint32_t)s.G << 5 |
+                          (uint32_t)s.Kb << 10;
+  const uint32_t dense = (uint32_t)s.sink_b | (uint32_t)s.window_b << 16;
+  hipLaunchKernelGGL(kernel, grid, block, lds, st, a.at.q, a.at.K, grid.x, a.at.splits, (int32_t)s.Tq,
+                     (int32_t)s.Hkv, (int32_t)s.T, (int32_t)s.T_cap, packed, dense, a);
   return true;
 }
 
