@@ -27,10 +27,18 @@ namespace hipsa {
 // (2 K_b candidates over 4 waves), used by the mask kernel and the step alike.
 inline int search_tiles_per_wave(int Kb) { return ((2 * Kb + 15) / 16 + 3) / 4; }
 
-template <typename E, typename KE, int D, int GMAX, int UNROLL, bool PAGED>
+//
+// SPREAD (one-launch step): the problem's S split workgroups run the same
+// search at the same time on one XCD, so after each round's scoring split
+// `split` also loads its 1/S share of the centre rows of all halves of the
+// current candidates: a superset of the next round's candidates, whose rows
+// the next round then finds in the XCD's L2.  The prefetched values are only
+// folded into a sink (they complete before the next round's gathers, which
+// are issued after them).
+template <typename E, typename KE, int D, int GMAX, int UNROLL, bool PAGED, bool SPREAD = false>
 __device__ __forceinline__ void search_row(const void *q, const void *K, const Shape &s, const Pages &pg,
                                              uint32_t b, uint32_t g, uint32_t i, int32_t Tp, int32_t first,
-                                             int32_t M, int32_t *out) {
+                                             int32_t M, int32_t *out, int split = 0, int S = 1) {
   const int tid = threadIdx.x;
   const uint32_t Tq = (uint32_t)s.Tq, Hkv = (uint32_t)s.Hkv;
   const int32_t Kb = s.Kb;
@@ -83,6 +91,8 @@ __device__ __forceinline__ void search_row(const void *q, const void *K, const S
   for (int c = tid; c < Kb; c += 256) pos[c] = 0;
   __syncthreads();
 
+  uint4 pf = make_uint4(0u, 0u, 0u, 0u);  // SPREAD: the last prefetched slice
+  uint32_t sink = 0;
   int cur = 0;
   for (int round = 0;; round++, cur ^= 1) {
     if (!flag[round & 1]) break;  // uniform: read after a barrier
@@ -99,6 +109,23 @@ __device__ __forceinline__ void search_row(const void *q, const void *K, const S
     } else {
       score_slots<E, KE, D, GMAX, UNROLL>(qo, Kbase, row_of, ca, ce, n, Tp, s, key, kMfma ? stage : nullptr);
     }
+    if (SPREAD && S > 1) {  // uniform
+      sink ^= pf.x ^ pf.w;  // issued before this round's gathers: complete
+      // this split's share of the 2n halves (half j of slot j / 2), one
+      // 16-byte piece per lane, rows of LPR lanes; branch-free (row 0 when
+      // there is nothing to load)
+      constexpr int LPR = D * (int)sizeof(KE) / 16;
+      const int per = (2 * n + S - 1) / S, r = tid / LPR, ch = split * per + r;
+      const int c = (ch >> 1) < n ? (ch >> 1) : 0;
+      const int32_t lo_b = ca[c], hi_b = ce[c];
+      const bool halves = hi_b - lo_b >= 2;
+      const int32_t m = lo_b + (hi_b - lo_b) / 2;
+      const int32_t a2 = (ch & 1) ? (halves ? m : -1) : lo_b, e2 = (ch & 1) || halves ? (ch & 1 ? hi_b : m) : hi_b;
+      const bool live = r < per && ch < 2 * n && lo_b >= 0 && a2 >= 0;
+      const int32_t lo = a2 << s.bk_shift, hi = min(e2 << s.bk_shift, Tp);
+      const int32_t t = live ? (lo + hi) >> 1 : 0;
+      pf = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(Kbase + row_of(t)) + 16 * (tid % LPR));
+    }
     __syncthreads();
 
     // ---- 2. selection: the K_b best write their halves into the other buffer
@@ -109,6 +136,8 @@ __device__ __forceinline__ void search_row(const void *q, const void *K, const S
 
   // the kept one-block chunks sit at the even slots of the current buffer
   write_ascending(cand_a[cur], Kb, pos, out);
+  if constexpr (SPREAD)
+    if (Tp < 0 && sink == 0x9e3779b9u) out[0] = (int32_t)sink;  // never: keeps the prefetches
 }
 
 }  // namespace hipsa

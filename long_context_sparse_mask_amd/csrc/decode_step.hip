@@ -70,7 +70,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     for (int j = tid; j < Kb; j += 256) list[j] = j < M ? first + j : -1;
     if (tid == 0) cnt = M;
   } else {
-    search_row<uint16_t, KE, D, GMAX, UNROLL, PAGED>(q, K, s, a.at.pg, b, g, i, Tp, first, M, list);
+    search_row<uint16_t, KE, D, GMAX, UNROLL, PAGED, true>(q, K, s, a.at.pg, b, g, i, Tp, first, M, list,
+                                                          (int)split, (int)S);
     if (tid == 0) cnt = Kb;
   }
   __syncthreads();
