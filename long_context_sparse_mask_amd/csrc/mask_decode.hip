@@ -43,12 +43,17 @@
 namespace hipsa {
 namespace {
 
+// With a bf16 query, `S` workgroups per problem (its splits, on one XCD by
+// xcd_swizzle) run the same search, each prefetching its share of every
+// round's next candidates into the XCD's L2 (search_row's SPREAD); split 0
+// writes the list.  The grid holds problems * S workgroups.
 template <typename E, typename KE, int D, int GMAX, int UNROLL, bool PAGED>
-__global__ __launch_bounds__(256) void mask_decode_kernel(MaskArgs a) {
+__global__ __launch_bounds__(256) void mask_decode_kernel(MaskArgs a, int S) {
   const Shape &s = a.s;
   const int tid = threadIdx.x;
 
-  const uint32_t prob = xcd_swizzle(blockIdx.x, gridDim.x);
+  const uint32_t wgi = xcd_swizzle(blockIdx.x, gridDim.x);
+  const uint32_t prob = wgi / (uint32_t)S, split = wgi % (uint32_t)S;
   const uint32_t Tq = (uint32_t)s.Tq, Hkv = (uint32_t)s.Hkv;
   const uint32_t i = prob % Tq, g = (prob / Tq) % Hkv, b = prob / (Tq * Hkv);
   const int32_t Tp = s.causal ? (int32_t)(s.T - s.Tq + i + 1) : (int32_t)s.T;
@@ -61,13 +66,20 @@ __global__ __launch_bounds__(256) void mask_decode_kernel(MaskArgs a) {
   const Dense dn(s, Np);
   const int32_t first = dn.Sb, M = Np - dn.Sb - dn.Wb;
   if (M <= Kb) {  // the row sees few enough blocks to keep them all
+    if (split != 0) return;
     for (int j = tid; j < Kb; j += 256) out[j] = j < M ? first + j : -1;
     if (tid == 0) a.nnz[prob] = M;
     return;
   }
 
-  search_row<E, KE, D, GMAX, UNROLL, PAGED>(a.q, a.K, s, a.pg, b, g, i, Tp, first, M, out);
-  if (tid == 0) a.nnz[prob] = Kb;
+  if constexpr (std::is_same<E, uint16_t>::value) {
+    __shared__ int32_t discard[kMaxKb];  // the list of splits other than 0
+    search_row<E, KE, D, GMAX, UNROLL, PAGED, true>(a.q, a.K, s, a.pg, b, g, i, Tp, first, M,
+                                                    split == 0 ? out : discard, (int)split, S);
+  } else {
+    search_row<E, KE, D, GMAX, UNROLL, PAGED>(a.q, a.K, s, a.pg, b, g, i, Tp, first, M, out);
+  }
+  if (tid == 0 && split == 0) a.nnz[prob] = Kb;
 }
 
 // dynamic LDS: the page numbers of a whole sequence when paged
@@ -81,12 +93,16 @@ void launch_g(const MaskArgs &a, hipStream_t st) {
   // loads in flight per lane per round: candidate tiles per wave (MFMA) or
   // candidate rows per lane (VALU)
   const int per = kMfma ? search_tiles_per_wave(a.s.Kb) : (n + RPP - 1) / RPP;
-  const dim3 grid((unsigned)a.s.problems), block(256);
+  // splits per problem: up to 8 while the grid stays within one workgroup per CU (bf16 query)
+  int S = 1;
+  if (kMfma)
+    while (S < 8 && a.s.problems * (2 * S) <= 256) S *= 2;
+  const dim3 grid((unsigned)(a.s.problems * S)), block(256);
   const size_t lds = page_lds(a);
-  if (per <= 1) hipLaunchKernelGGL((mask_decode_kernel<E, KE, D, GMAX, 1, PAGED>), grid, block, lds, st, a);
-  else if (per <= 2) hipLaunchKernelGGL((mask_decode_kernel<E, KE, D, GMAX, 2, PAGED>), grid, block, lds, st, a);
-  else if (per <= 4) hipLaunchKernelGGL((mask_decode_kernel<E, KE, D, GMAX, 4, PAGED>), grid, block, lds, st, a);
-  else hipLaunchKernelGGL((mask_decode_kernel<E, KE, D, GMAX, 8, PAGED>), grid, block, lds, st, a);
+  if (per <= 1) hipLaunchKernelGGL((mask_decode_kernel<E, KE, D, GMAX, 1, PAGED>), grid, block, lds, st, a, S);
+  else if (per <= 2) hipLaunchKernelGGL((mask_decode_kernel<E, KE, D, GMAX, 2, PAGED>), grid, block, lds, st, a, S);
+  else if (per <= 4) hipLaunchKernelGGL((mask_decode_kernel<E, KE, D, GMAX, 4, PAGED>), grid, block, lds, st, a, S);
+  else hipLaunchKernelGGL((mask_decode_kernel<E, KE, D, GMAX, 8, PAGED>), grid, block, lds, st, a, S);
 }
 
 // E: query element type; KE: key element type (E itself, or E5M2 codes
