@@ -13,7 +13,9 @@
 // another.  The search is latency-bound (serially dependent rounds of row
 // gathers) and cheap, so running it once per split costs little time: the
 // splits of a problem run on one XCD (xcd_swizzle), where they read the
-// same centre rows through its L2.  Split 0 also writes the lists, so a
+// same centre rows through its L2, and after each round each split loads
+// its share of the rows the next round may need, so that round finds them
+// all in the L2 (search_row's SPREAD).  Split 0 also writes the lists, so a
 // later step can reuse the mask through hip_sparse_attn.
 //
 // The last split workgroup of a problem to finish merges the splits'
