@@ -70,6 +70,13 @@ EDGE = {
     # 128 listed tokens: one split workgroup writes the output, no merge launch
     "one_split_bf16": dict(base="decode_32k", Hq=8, Hkv=2, Tq=2, T=3000, k=128),
     "one_split_f32_d128": dict(base="decode_32k", dtype="f32", Hq=4, Hkv=2, T=3000, k=64),
+    # 16 or more problems with a bf16 query: the mask kernel runs 8 (or 2) workgroups per
+    # problem, each prefetching its share of the next round's rows; split 0 writes the list
+    "split_mask_16_ragged": dict(base="decode_32k", B=2, Hq=16, Hkv=8, T=7001, k=1024),
+    "split_mask_e5m2_kb64": dict(base="decode_32k", dtype="bf16_e5m2", B=2, Hq=32, Hkv=8, T=30000,
+                                 k=4096),
+    "split_mask_rows_causal": dict(base="decode_32k", Hq=16, Hkv=4, Tq=4, T=9000, k=512),
+    "split_mask_d64_g1": dict(base="decode_32k", B=4, Hq=8, Hkv=8, d=64, T=5000, k=1024),
 }
 
 
